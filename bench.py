@@ -1,0 +1,276 @@
+"""Benchmark one Uno draft+verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the gated-LoRA forward of the mixed batch through every projection of the
+layer stack (with the layer glue), fresh Philox uniforms, and block
+verification of every sequence's drafted block.  Inputs (weights, hidden
+states, logits, drafted tokens) are resident in HBM before timing starts.
+
+Default workload: 32 layers x 7 projections of an 8B-shaped model
+(4096 -> 4096/1024/1024/4096 and 4096 -> 14336 -> 4096, rank-128 LoRA,
+alpha 256), 32 sequences x [16 verify | 16 draft] rows, verification of a
+16-token block per sequence over a 128256-token vocabulary (draft noise
+sigma = 1, T = 1).  Weights are random-initialised bf16; data is synthetic.
+
+Prints one JSON line: verified tokens/s (emitted tokens summed over the timed
+steps / elapsed time), the roofline of the dominant kernel (the gated-LoRA
+GEMM, bf16 MFMA), and the oracle timed on the host cores on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+RANK = 128
+SCALE = 2.0                   # alpha / r = 256 / 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack32_b32", choices=["stack32_b32", "layer_b1", "layer_b64"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def gemm_flops(M, Md, K, N, r=RANK):
+    """Algorithmic flops of one gated projection: 2MKN + 2 Md r (K + N)."""
+    return 2.0 * M * K * N + 2.0 * Md * r * (K + N)
+
+
+def verify_bytes(B, L, V, esz=2, redraws=None):
+    """Algorithmic bytes of block verification: both logit arrays once, the redraw row pair
+    of each sequence that redraws, tokens, uniforms and outputs."""
+    redraws = B if redraws is None else redraws
+    return 2.0 * B * L * V * esz + redraws * 2.0 * V * esz + B * L * 4 + B * (L + 1) * 4 + B * (L + 3) * 4
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "lossless_speculative_drafting_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lossless_speculative_drafting_amd as uno
+    from synthetic import WORKLOADS, gate_vector
+    from synthetic import device as sdev
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    B, L, V = wl.n_seq, wl.block, wl.vocab
+    M = wl.rows
+    Md = wl.n_seq * wl.draft_rows
+    T = wl.temperatures[0]
+    sigma = 1.0 if 1.0 in wl.draft_sigmas else wl.draft_sigmas[0]
+
+    # ---------------- resident inputs
+    layers = [sdev.layer_weights(wl.projections, wl.seed * 1000 + 100 * i) for i in range(wl.layers)]
+    gate_np = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
+    gate = torch.from_numpy(gate_np).to(dev)
+    stack = uno.GatedLoraStack(layers, gate, SCALE)
+    x0 = sdev.randn((M, wl.projections[0][1]), 1.0, wl.seed)
+    z, d = sdev.verify_logits(B, L, V, wl.seed, kind=wl.logits, target_sigma=wl.target_sigma,
+                              draft_sigma=sigma)
+    drafts = uno.draft_sample(d, uno.philox_uniforms(0, 1, 0, B * L, device=dev), T)
+    u = torch.empty(B * (L + 1), dtype=torch.float32, device=dev)
+    total_steps = args.warmup + args.steps
+    n_acc = torch.empty((total_steps, B), dtype=torch.int32, device=dev)
+    out_tok = torch.empty((total_steps, B, L + 1), dtype=torch.int32, device=dev)
+    n_emit = torch.empty((total_steps, B), dtype=torch.int32, device=dev)
+    vws = uno.Workspace(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        stack.forward(x0)
+        uno.philox_uniforms(0, 0, i * B * (L + 1), B * (L + 1), out=u)
+        uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[i], out_tok[i], n_emit[i]), workspace=vws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.warmup, total_steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed = max(wall, gpu_ms / 1e3)
+    tokens = int(n_emit[args.warmup:].sum().item())
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = tokens / elapsed
+
+    # ---------------- dominant kernel: the gated-LoRA projection, timed per launch with HIP events
+    trace = {}
+    stack.forward(x0, trace_layer=0, trace=trace)
+    torch.cuda.synchronize()
+    layer0 = layers[0]
+    durations, flops = [], []
+    for name, K, N in wl.projections:
+        inp, _ = trace[name]
+        w, a, b = layer0[name]
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            uno.gated_lora_fwd(inp, w, a, b, gate, SCALE, out=out, workspace=stack.ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.kernel_reps):
+            uno.gated_lora_fwd(inp, w, a, b, gate, SCALE, out=out, workspace=stack.ws)
+        e1.record()
+        torch.cuda.synchronize()
+        durations.append(e0.elapsed_time(e1) / args.kernel_reps / 1e3)
+        flops.append(gemm_flops(M, Md, K, N))
+    gemm_achieved = sum(flops) / sum(durations) / 1e12
+    digest = source_digest("gemm.hip")
+    traffic = committed_traffic("gated_gemm", digest)
+
+    # verify kernel chain, timed alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[0], out_tok[0], n_emit[0]), workspace=vws)
+    e0.record()
+    for _ in range(args.kernel_reps):
+        uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[0], out_tok[0], n_emit[0]), workspace=vws)
+    e1.record()
+    torch.cuda.synchronize()
+    vt = e0.elapsed_time(e1) / args.kernel_reps / 1e3
+    redraws = int((n_acc[0] < L).sum().item())
+    v_gbs = verify_bytes(B, L, V, 2, redraws) / vt / 1e9
+
+    result = {
+        "metric": "verified tokens/s per draft+verify step",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init bf16 weights and logits)",
+        "config": {
+            "workload": f"{args.workload}: {wl.layers} layers x {len(wl.projections)} gated-LoRA projections "
+                        f"(8B shapes, r=128, alpha=256), {wl.n_seq} seqs x [{wl.verify_rows} verify | "
+                        f"{wl.draft_rows} draft] rows, verify block {L} over V={V}, sigma={sigma}, T={T}",
+            "rows": M,
+            "draft_rows": Md,
+            "sequences": B,
+            "block": L,
+            "vocab": V,
+            "tokens_per_step": round(tokens / args.steps, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gated-LoRA projection (uno_gated_lora_fwd), 7 shapes of one layer",
+            "achieved": round(gemm_achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(sum(durations) / len(durations) * 1e6, 3),
+            "algorithmic_gflop_per_launch": round(sum(flops) / len(flops) / 1e9, 4),
+        },
+        "verify_roofline": {
+            "bound": "hbm",
+            "achieved": round(v_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(v_gbs / PEAK_HBM_GBS, 4),
+            "us_per_call": round(vt * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers, trace, x0, z, d, drafts, u, gate_np, T, L,
+                                              tokens / args.steps)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, layers, trace, x0, z, d, drafts, u, gate_np, T, L, gpu_tokens_per_step):
+    """The fp64 oracle on the host cores: one layer of the stack and verification of a few sequences,
+    scaled to a full step (layers x layer time + sequences x per-sequence verify time)."""
+    import numpy as np
+
+    import oracle
+    from oracle import stack as ost
+
+    cores = len(os.sched_getaffinity(0))
+    h = lambda t: t.float().cpu().numpy()  # noqa: E731
+    lw = {n: tuple(h(t) for t in layers[0][n]) for n, _, _ in wl.projections}
+    x = h(x0)
+    t0 = time.perf_counter()
+    hn = ost.rmsnorm(x)
+    q = oracle.gated_lora(hn, *lw["q"], gate_np, SCALE)
+    oracle.gated_lora(hn, *lw["k"], gate_np, SCALE)
+    oracle.gated_lora(hn, *lw["v"], gate_np, SCALE)
+    x1 = ost.residual_add(x, oracle.gated_lora(q, *lw["o"], gate_np, SCALE))
+    hn = ost.rmsnorm(x1)
+    act = ost.silu_mul(oracle.gated_lora(hn, *lw["gate"], gate_np, SCALE),
+                       oracle.gated_lora(hn, *lw["up"], gate_np, SCALE))
+    ost.residual_add(x1, oracle.gated_lora(act, *lw["down"], gate_np, SCALE))
+    layer_s = time.perf_counter() - t0
+    n_seq = 4
+    zz, dd = h(z[:n_seq]), h(d[:n_seq])
+    uu = u.cpu().numpy().astype(np.float64).reshape(-1, L + 1)[:n_seq]
+    t0 = time.perf_counter()
+    res = oracle.block_verify(zz, dd, drafts[:n_seq].cpu().numpy(), uu, T, False)
+    verify_s = time.perf_counter() - t0
+    B = wl.n_seq
+    step_s = wl.layers * layer_s + B / n_seq * verify_s
+    tokens = float(res["n_emitted"].sum()) * B / n_seq
+    return {
+        "value": round(tokens / step_s, 4),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"one of {wl.layers} layers (7 fp64 gated-LoRA projections + glue, {layer_s:.2f} s) and "
+                   f"verification of {n_seq} of {B} sequences ({verify_s:.2f} s), scaled to one step "
+                   f"({step_s:.1f} s); numpy BLAS on {cores} cores"),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * uno.h -- C ABI of the Uno hot-path library (libuno.so, gfx950 / MI355X).
+ *
+ * The method ("Uno", from the pages about "Unlocking Lossless Speedups in LLMs
+ * via Discrete Diffusion") adds a rank-128, alpha-256 LoRA pathway to every
+ * projection of an autoregressive transformer; draft tokens run the AR
+ * weights plus the adapter and verification tokens run the AR weights alone,
+ * and a sampler accepts the longest drafted prefix that speculative-style
+ * rejection sampling against the AR model allows, keeping the AR output
+ * distribution exact.  This library provides the two data-parallel pieces of
+ * one draft+verify step -- the gated-LoRA projection and block verification --
+ * plus the counter-based uniform generator they consume.
+ *
+ * Conventions shared by every call
+ *  - Pointers named as device memory are caller-owned device allocations; the
+ *    library never allocates, frees or retains them.  Scalars are passed by
+ *    value.  Work that needs scratch space takes a caller-provided device
+ *    workspace whose minimum size comes from the matching *_workspace_size().
+ *  - All work is enqueued asynchronously on `stream` (0 = the null stream).
+ *    No call synchronises the host.
+ *  - Argument errors (null pointers, sizes, dtypes, alignment, workspace) are
+ *    detected on the host before anything is launched and returned as a
+ *    status; uno_last_error_message() then describes the problem.  A failed
+ *    launch returns UNO_ERR_HIP.  Faults inside a kernel surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - Device-side precondition failures never trap: they are reported through
+ *    sentinel values documented per call.
+ *  - Two calls that share a workspace must not overlap in time.
+ */
+#ifndef UNO_H_
+#define UNO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum uno_status {
+    UNO_OK = 0,
+    UNO_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, bad alignment */
+    UNO_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported domain            */
+    UNO_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size()    */
+    UNO_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed               */
+} uno_status;
+
+typedef enum uno_dtype {
+    UNO_BF16 = 0, /* bfloat16, round-to-nearest-even on output */
+    UNO_F32 = 1   /* IEEE binary32                             */
+} uno_dtype;
+
+/* ABI revision of this header; bumped on any incompatible change. */
+#define UNO_ABI_VERSION 1
+int32_t uno_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* uno_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling host thread
+ * (empty string if none).  The pointer stays valid until the next call. */
+const char* uno_last_error_message(void);
+
+/* ------------------------------------------------------------------------
+ * Counter-based uniforms (Philox4x32-10; Salmon et al., "Parallel random
+ * numbers: as easy as 1, 2, 3", SC'11).  The rejection sampler of the pages
+ * ("The Psi-Spec Sampler" on the aifromscratch.in page) needs one uniform per
+ * acceptance test and one per redraw; they are generated here and passed to
+ * uno_block_verify / uno_draft_sample as plain inputs.
+ *
+ *   out[j] = (w >> 8) * 2^-24,  j in [0, n),
+ *   w = word ((offset + j) % 4) of Philox4x32-10 with
+ *       key     = (seed mod 2^32, seed >> 32),
+ *       counter = (b mod 2^32, b >> 32, stream_id mod 2^32, stream_id >> 32),
+ *       b       = (offset + j) / 4.
+ * Every value lies in [0, 1 - 2^-24] and is exact in binary32.  One call over
+ * [0, n) equals two calls over [0, k) and [k, n).
+ *
+ * out : device float[n].  n = 0 is a no-op.  offset + n must not exceed 2^64.
+ * ------------------------------------------------------------------------ */
+uno_status uno_philox_uniforms(uint64_t seed, uint64_t stream_id, uint64_t offset, int64_t n,
+                               float* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Gated-LoRA projection ("Two Decoupled Weight Sets" on the aifromscratch.in
+ * page; "How Uno works" on the cctest.ai page): frozen AR weights W_AR plus a
+ * LoRA adapter (A, B) of rank r, applied only on draft rows:
+ *
+ *   y[m, :] = x[m, :] W_AR + gate[m] * scale * (x[m, :] A) B
+ *
+ * with scale = alpha / r (2.0 for r = 128, alpha = 256).  Storage follows the
+ * nn.Linear convention, all row-major:
+ *   x      [M, K]   activations (dtype)
+ *   w      [N, K]   W_AR transposed (dtype)
+ *   lora_a [r, K]   A transposed (dtype)
+ *   lora_b [N, r]   B transposed (dtype)
+ *   gate   [M]      uint8, 1 = draft row, 0 = verify row
+ *   y      [M, N]   output (dtype); must not alias any input
+ * Arithmetic: products accumulate in fp32.  For UNO_BF16 the adapter's
+ * intermediate scale * (x A) is rounded once to bf16, and y is rounded to
+ * bf16 (nearest even).  UNO_F32 keeps every intermediate in fp32.
+ * Rows with gate 0 run exactly the instruction sequence of a call whose gates
+ * are all 0, so they are bitwise identical to it.
+ *
+ * Domain: M >= 0 (M = 0 is a no-op), 1 <= N, 1 <= K; K and N multiples of 8
+ * and 16-byte aligned pointers for UNO_BF16; 1 <= r <= 256 and r a multiple
+ * of 16; scale finite.  A gate byte other than 0/1 is treated as 1.
+ * workspace: device memory of at least uno_gated_lora_workspace_size() bytes
+ * (256-byte aligned).
+ * ------------------------------------------------------------------------ */
+size_t uno_gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype);
+uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a,
+                              const void* lora_b, const uint8_t* gate, void* y,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float scale,
+                              int32_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Block verification ("The Psi-Spec Sampler" on the aifromscratch.in page:
+ * rejection-sample the drafted block against the AR model and keep the
+ * longest valid prefix, with the AR distribution preserved; "What 'lossless'
+ * means here" on the cctest.ai page: the AR model rejects or adjusts
+ * candidates).  For each of B sequences with L drafted tokens x_i:
+ *
+ *   p_i = softmax(z_i / T),  q_i = softmax(d_i / T)
+ *   accept_i  <=>  u[s, i] < min(1, p_i(x_i) / q_i(x_i))
+ *   n_acc     =  index of the first rejected position (L if none)
+ *   if n_acc < L : y ~ normalize(max(0, p_j - q_j)), j = n_acc
+ *                  (from p_j if that residual has zero mass)
+ *   elif has_bonus: y ~ p_L (target row L)
+ *   draws use the inverse CDF with u[s, L]: the smallest k with C_k > u R.
+ *   out_tokens[s] = x_0 .. x_{n_acc-1}, y, then -1 padding
+ *   n_emitted[s]  = n_acc + 1 if a token was drawn, else L
+ *
+ * target_logits : device, dtype; row (s, i), i < L + has_bonus, starts at
+ *                 s * target_seq_stride + i * V elements
+ * draft_logits  : device, dtype; row (s, i), i < L, at s * draft_seq_stride + i * V
+ *                 (a stride of 0 broadcasts one block to every sequence)
+ * draft_tokens  : device int32 [B, L]
+ * uniforms      : device float [B, L + 1]; slots 0..L-1 accept, slot L draw
+ * n_accepted    : device int32 [B]; -1 if some draft token lies outside [0, V)
+ *                 (then n_emitted = 0 and out_tokens are all -1)
+ * out_tokens    : device int32 [B, L + 1]
+ * n_emitted     : device int32 [B]
+ * Arithmetic: row maxima and sums of exp stream in fp32 per element with
+ * fp64 accumulation; the acceptance ratio is formed in fp64 in log space;
+ * the redraw CDF sums fp32 weights of 16-token segments and carries across
+ * segments in fp64.
+ *
+ * Domain: B >= 0 (B = 0 is a no-op), 1 <= L <= 64 (L <= 63 with has_bonus),
+ * V >= 1, T > 0 and finite, logits UNO_BF16 or UNO_F32, each row holding at
+ * least one finite logit (NaN and +inf are outside the contract; -inf masks
+ * a token).  Stride 0 is allowed for either logit array.
+ * workspace: at least uno_block_verify_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+size_t uno_block_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
+uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
+                            int64_t target_seq_stride, int64_t draft_seq_stride,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            int64_t B, int32_t L, int64_t V, int32_t has_bonus,
+                            float temperature, int32_t logits_dtype,
+                            int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Draft proposal: one token per drafted position, drawn in parallel from the
+ * diffusion pathway's distribution q_i = softmax(d_i / T) by inverse CDF
+ * ("The Psi-Spec Sampler" on the aifromscratch.in page: the diffusion
+ * pathway proposes a block in parallel; the linear sampler takes one
+ * candidate per position).
+ *
+ *   tokens[s, i] = smallest k with C_k > u[s, i] * R over the weights q_i
+ *
+ * draft_logits : device, dtype; row (s, i) at s * seq_stride + i * V elements
+ * uniforms     : device float [B, L]
+ * tokens       : device int32 [B, L]
+ * Same arithmetic and domain as uno_block_verify (no upper limit on L).
+ * workspace: at least uno_draft_sample_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+size_t uno_draft_sample_workspace_size(int64_t B, int32_t L, int64_t V);
+uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
+                            const float* uniforms, int64_t B, int32_t L, int64_t V,
+                            float temperature, int32_t logits_dtype, int32_t* tokens,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Glue between projections of a layer with the attention mixing left out
+ * (the pages add the LoRA pathway to each transformer layer -- "How It Works:
+ * The 'Uno' Architecture" on the aifromscratch.in page -- but describe no
+ * other part of the layer).  bf16 in and out, fp32 arithmetic.
+ *
+ * uno_rmsnorm      : y[m, :] = x[m, :] / sqrt(mean_k x[m, k]^2 + eps), x, y [M, K]
+ * uno_silu_mul     : out = silu(gate) * up elementwise, silu(t) = t / (1 + e^-t)
+ * uno_residual_add : out = a + b elementwise (out may alias a or b)
+ * Domain: sizes >= 0; K <= 65536 for uno_rmsnorm; eps >= 0; only UNO_BF16.
+ * ------------------------------------------------------------------------ */
+uno_status uno_rmsnorm(const void* x, void* y, int64_t M, int64_t K, float eps, int32_t dtype,
+                       hipStream_t stream);
+uno_status uno_silu_mul(const void* gate, const void* up, void* out, int64_t n, int32_t dtype,
+                        hipStream_t stream);
+uno_status uno_residual_add(const void* a, const void* b, void* out, int64_t n, int32_t dtype,
+                            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNO_H_ */

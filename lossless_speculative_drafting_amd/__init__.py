@@ -1,0 +1,34 @@
+"""MI355X-native hot path of Uno's draft+verify step.
+
+Python binding over libuno.so (hand-written HIP for gfx950):
+
+* gated_lora_fwd  -- y = x W_AR + g * (alpha/r) * (x A) B on a mixed batch of
+                     draft (g = 1) and verify (g = 0) rows;
+* block_verify    -- lossless speculative verification of drafted blocks;
+* draft_sample    -- parallel inverse-CDF proposal of draft tokens;
+* philox_uniforms -- the counter-based uniforms both consume;
+* rmsnorm, silu_mul, residual_add -- glue of the synthetic layer stack.
+
+Importing the package loads the shared library; there is no CPU fallback.
+"""
+
+from ._lib import (  # noqa: F401
+    UNO_BF16,
+    UNO_F32,
+    UnoError,
+    Workspace,
+    block_verify,
+    block_verify_workspace_size,
+    draft_sample,
+    draft_sample_workspace_size,
+    gated_lora_fwd,
+    gated_lora_workspace_size,
+    header_symbols,
+    library,
+    philox_uniforms,
+    residual_add,
+    rmsnorm,
+    silu_mul,
+    status_string,
+)
+from .stack import GatedLoraStack  # noqa: F401

@@ -1,0 +1,280 @@
+"""ctypes binding to libuno.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers, sizes and the current HIP stream to the C ABI declared in
+include/uno.h, and returns tensors the caller owns.  Workspaces are plain
+torch byte tensors sized by the library's own *_workspace_size queries.  No
+computation happens here; if the shared library is missing the import fails.
+"""
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("UNO_LIB", os.path.join(_HERE, "libuno.so"))
+
+UNO_BF16 = 0
+UNO_F32 = 1
+
+_c_int32, _c_int64, _c_uint64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+_c_size, _c_float, _c_ptr = ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+
+# name: (restype, argtypes) -- mirrors include/uno.h
+SIGNATURES = {
+    "uno_abi_version": (_c_int32, []),
+    "uno_status_string": (ctypes.c_char_p, [_c_int32]),
+    "uno_last_error_message": (ctypes.c_char_p, []),
+    "uno_philox_uniforms": (_c_int32, [_c_uint64, _c_uint64, _c_uint64, _c_int64, _c_ptr, _c_ptr]),
+    "uno_gated_lora_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32, _c_int32]),
+    "uno_gated_lora_fwd": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64,
+                                      _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_block_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int32]),
+    "uno_block_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
+                                    _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                    _c_size, _c_ptr]),
+    "uno_draft_sample_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64]),
+    "uno_draft_sample": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_int64, _c_int32, _c_int64, _c_float,
+                                    _c_int32, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "uno_rmsnorm": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_float, _c_int32, _c_ptr]),
+    "uno_silu_mul": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
+    "uno_residual_add": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
+}
+
+
+class UnoError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libuno.so not found at {LIB_PATH}; build it with "
+            "`python -m lossless_speculative_drafting_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+def status_string(status):
+    return _lib.uno_status_string(status).decode()
+
+
+def _check(status):
+    if status != 0:
+        raise UnoError(status, _lib.uno_last_error_message().decode())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return UNO_BF16
+    if dt == torch.float32:
+        return UNO_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+class Workspace:
+    """A grow-only device byte buffer reused across calls on one stream."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        key = (device.index if device.index is not None else torch.cuda.current_device())
+        ws = _default_ws.setdefault(key, Workspace(device))
+    return ws.get(nbytes)
+
+
+# ------------------------------------------------------------------ Philox
+
+def philox_uniforms(seed, stream_id, offset, n, out=None, device="cuda", stream=None):
+    """float32 uniforms for Philox words offset .. offset+n-1 of (seed, stream_id)."""
+    if out is None:
+        out = torch.empty(int(n), dtype=torch.float32, device=device)
+    _need_cuda(out)
+    if out.numel() < n or out.dtype != torch.float32:
+        raise ValueError("out must be a float32 tensor with at least n elements")
+    _check(_lib.uno_philox_uniforms(int(seed), int(stream_id), int(offset), int(n), _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ gated LoRA
+
+def gated_lora_workspace_size(M, N, K, r, dtype):
+    return int(_lib.uno_gated_lora_workspace_size(M, N, K, r, _dtype_code(dtype)))
+
+
+def gated_lora_fwd(x, w, lora_a, lora_b, gate, scale=2.0, out=None, workspace=None, stream=None):
+    """y = x W_AR + gate * scale * (x A) B with storage w [N,K], lora_a [r,K], lora_b [N,r]."""
+    _need_cuda(x, w, lora_a, lora_b, gate)
+    M, K = x.shape
+    N = w.shape[0]
+    r = lora_a.shape[0]
+    if w.shape != (N, K) or lora_a.shape != (r, K) or lora_b.shape != (N, r) or gate.shape != (M,):
+        raise ValueError("shape mismatch: x [M,K], w [N,K], lora_a [r,K], lora_b [N,r], gate [M]")
+    if gate.dtype != torch.uint8:
+        raise TypeError("gate must be uint8")
+    if not (x.dtype == w.dtype == lora_a.dtype == lora_b.dtype):
+        raise TypeError("x, w, lora_a and lora_b must share a dtype")
+    dt = _dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _need_cuda(out)
+    need = int(_lib.uno_gated_lora_workspace_size(M, N, K, r, dt))
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_gated_lora_fwd(_ptr(x), _ptr(w), _ptr(lora_a), _ptr(lora_b), _ptr(gate), _ptr(out),
+                                   M, N, K, r, float(scale), dt, _ptr(ws), need, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ verification
+
+def block_verify_workspace_size(B, L, V, has_bonus=False):
+    return int(_lib.uno_block_verify_workspace_size(B, L, V, int(bool(has_bonus))))
+
+
+def block_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature=1.0, has_bonus=False,
+                 B=None, L=None, V=None, target_seq_stride=None, draft_seq_stride=None,
+                 outputs=None, workspace=None, stream=None):
+    """Verify one drafted block per sequence.
+
+    By default target_logits is [B, L + has_bonus, V] and draft_logits [B, L, V]
+    (a leading dimension of 1 broadcasts with stride 0).  Explicit B, L, V and
+    strides (in elements) address logits inside a larger buffer.
+    Returns (n_accepted [B], out_tokens [B, L+1], n_emitted [B]) int32 tensors.
+    """
+    _need_cuda(target_logits, draft_logits, draft_tokens, uniforms)
+    nb = 1 if has_bonus else 0
+    if B is None:
+        B, L = draft_tokens.shape
+    if V is None:
+        V = target_logits.shape[-1]
+    if target_seq_stride is None:
+        target_seq_stride = 0 if target_logits.shape[0] == 1 and B != 1 else (L + nb) * V
+    if draft_seq_stride is None:
+        draft_seq_stride = 0 if draft_logits.shape[0] == 1 and B != 1 else L * V
+    if target_logits.dtype != draft_logits.dtype:
+        raise TypeError("target and draft logits must share a dtype")
+    if draft_tokens.dtype != torch.int32 or uniforms.dtype != torch.float32:
+        raise TypeError("draft_tokens must be int32 and uniforms float32")
+    if draft_tokens.numel() < B * L or uniforms.numel() < B * (L + 1):
+        raise ValueError("draft_tokens must hold B*L and uniforms B*(L+1) values")
+    for t, stride, rows in ((target_logits, target_seq_stride, L + nb), (draft_logits, draft_seq_stride, L)):
+        if B > 0 and (B - 1) * stride + rows * V > t.numel():
+            raise ValueError("logit buffer too small for the given B, L, V and stride")
+    dev = target_logits.device
+    if outputs is None:
+        outputs = (torch.empty(B, dtype=torch.int32, device=dev),
+                   torch.empty((B, L + 1), dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev))
+    n_acc, out_tok, n_emit = outputs
+    need = int(_lib.uno_block_verify_workspace_size(B, L, V, nb))
+    ws = _workspace(workspace, need, dev)
+    _check(_lib.uno_block_verify(_ptr(target_logits), _ptr(draft_logits), int(target_seq_stride),
+                                 int(draft_seq_stride), _ptr(draft_tokens), _ptr(uniforms), int(B), int(L),
+                                 int(V), nb, float(temperature), _dtype_code(target_logits.dtype),
+                                 _ptr(n_acc), _ptr(out_tok), _ptr(n_emit), _ptr(ws), need, _stream(stream)))
+    return n_acc, out_tok, n_emit
+
+
+def draft_sample_workspace_size(B, L, V):
+    return int(_lib.uno_draft_sample_workspace_size(B, L, V))
+
+
+def draft_sample(draft_logits, uniforms, temperature=1.0, B=None, L=None, V=None, seq_stride=None,
+                 out=None, workspace=None, stream=None):
+    """One token per drafted row from softmax(d / T) by inverse CDF; returns int32 [B, L]."""
+    _need_cuda(draft_logits, uniforms)
+    if B is None:
+        B, L, V = draft_logits.shape
+    if seq_stride is None:
+        seq_stride = L * V
+    if uniforms.dtype != torch.float32 or uniforms.numel() < B * L:
+        raise ValueError("uniforms must be float32 with B*L values")
+    if B > 0 and (B - 1) * seq_stride + L * V > draft_logits.numel():
+        raise ValueError("logit buffer too small for the given B, L, V and stride")
+    if out is None:
+        out = torch.empty((B, L), dtype=torch.int32, device=draft_logits.device)
+    need = int(_lib.uno_draft_sample_workspace_size(B, L, V))
+    ws = _workspace(workspace, need, draft_logits.device)
+    _check(_lib.uno_draft_sample(_ptr(draft_logits), int(seq_stride), _ptr(uniforms), int(B), int(L), int(V),
+                                 float(temperature), _dtype_code(draft_logits.dtype), _ptr(out), _ptr(ws), need,
+                                 _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------ glue
+
+def rmsnorm(x, eps=1e-5, out=None, stream=None):
+    _need_cuda(x)
+    M, K = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check(_lib.uno_rmsnorm(_ptr(x), _ptr(out), M, K, float(eps), _dtype_code(x.dtype), _stream(stream)))
+    return out
+
+
+def silu_mul(gate, up, out=None, stream=None):
+    _need_cuda(gate, up)
+    out = torch.empty_like(gate) if out is None else out
+    _check(_lib.uno_silu_mul(_ptr(gate), _ptr(up), _ptr(out), gate.numel(), _dtype_code(gate.dtype),
+                             _stream(stream)))
+    return out
+
+
+def residual_add(a, b, out=None, stream=None):
+    _need_cuda(a, b)
+    out = torch.empty_like(a) if out is None else out
+    _check(_lib.uno_residual_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _dtype_code(a.dtype), _stream(stream)))
+    return out
+
+
+def header_symbols(header_path):
+    """Names of the functions declared in include/uno.h (for ABI checks)."""
+    text = open(header_path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uno_[a-z0-9_]+)\s*\(", text)))
+

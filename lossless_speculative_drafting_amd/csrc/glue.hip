@@ -1,0 +1,116 @@
+// Glue between the projections of the synthetic layer stack: weightless
+// RMSNorm, silu(gate) * up and the residual add, bf16 in/out with fp32
+// arithmetic.  The pages put the LoRA pathway into every transformer layer
+// ("How It Works: The 'Uno' Architecture" on the aifromscratch.in page) but
+// describe nothing else of the layer; these are the plainest Llama-like steps.
+#include "uno_device.h"
+#include "uno_internal.h"
+
+namespace uno {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+
+// One workgroup per row; K % 8 == 0 and 16-byte aligned rows (checked by the host).
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ y, int64_t K,
+                                                          float eps) {
+    const int64_t row = blockIdx.x;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+    uint4* yr = reinterpret_cast<uint4*>(y + row * K);
+    const int64_t nv = K / 8;
+    float ss = 0.f;
+    for (int64_t v = threadIdx.x; v < nv; v += kThreads) {
+        float f[8];
+        unpack8(xr[v], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    __shared__ float sh[kThreads / kWave];
+    if ((threadIdx.x % kWave) == 0) sh[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    const float tot = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    const float inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+    for (int64_t v = threadIdx.x; v < nv; v += kThreads) {
+        float f[8];
+        unpack8(xr[v], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] *= inv;
+        yr[v] = pack8(f);
+    }
+}
+
+template <int OP>  // 0: silu(a) * b, 1: a + b
+__global__ __launch_bounds__(kThreads) void eltwise_kernel(const uint16_t* __restrict__ a,
+                                                          const uint16_t* __restrict__ b,
+                                                          uint16_t* out, int64_t n) {
+    const int64_t nv = n / 8;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < nv; v += stride) {
+        float fa[8], fb[8];
+        unpack8(reinterpret_cast<const uint4*>(a)[v], fa);
+        unpack8(reinterpret_cast<const uint4*>(b)[v], fb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (OP == 0) {
+                fa[j] = fa[j] / (1.0f + __expf(-fa[j])) * fb[j];
+            } else {
+                fa[j] = fa[j] + fb[j];
+            }
+        }
+        reinterpret_cast<uint4*>(out)[v] = pack8(fa);
+    }
+    // scalar tail
+    const int64_t t = nv * 8 + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (t < n && t >= nv * 8) {
+        const float fa = bf16_bits_to_f32(a[t]);
+        const float fb = bf16_bits_to_f32(b[t]);
+        const float r = (OP == 0) ? fa / (1.0f + __expf(-fa)) * fb : fa + fb;
+        out[t] = static_cast<uint16_t>(f32_to_bf16_bits(r));
+    }
+}
+
+uint32_t eltwise_grid(int64_t n) {
+    const int64_t nv = (n + 7) / 8;
+    int64_t g = (nv + kThreads - 1) / kThreads;
+    if (g > 65536) g = 65536;
+    if (g < 1) g = 1;
+    return static_cast<uint32_t>(g);
+}
+
+}  // namespace
+
+hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), K, eps);
+    return hipGetLastError();
+}
+
+hipError_t silu_mul_launch(const void* gate, const void* up, void* out, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(eltwise_kernel<0>, dim3(eltwise_grid(n)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
+                       static_cast<uint16_t*>(out), n);
+    return hipGetLastError();
+}
+
+hipError_t residual_add_launch(const void* a, const void* b, void* out, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(eltwise_kernel<1>, dim3(eltwise_grid(n)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+                       static_cast<uint16_t*>(out), n);
+    return hipGetLastError();
+}
+
+}  // namespace uno

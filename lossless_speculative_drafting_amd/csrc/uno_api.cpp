@@ -1,0 +1,261 @@
+// C ABI of libuno: argument validation, workspace checks and dispatch to the
+// kernel launchers.  Every check runs on the host before anything is
+// enqueued, so a rejected call leaves the stream untouched.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/uno.h"
+#include "uno_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+uno_status fail(uno_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+uno_status ok() {
+    g_last_error.clear();
+    return UNO_OK;
+}
+
+uno_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(UNO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+constexpr int64_t kMaxGridX = 2147483647LL;
+constexpr int64_t kMaxGridYZ = 65535LL;
+
+uno_status check_workspace(void* ws, size_t have, size_t need) {
+    if (need == 0) return UNO_OK;
+    if (ws == nullptr) return fail(UNO_ERR_WORKSPACE, "workspace is null but %zu bytes are required", need);
+    if (!aligned256(ws)) return fail(UNO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (have < need) return fail(UNO_ERR_WORKSPACE, "workspace has %zu bytes, %zu required", have, need);
+    return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t uno_abi_version(void) { return UNO_ABI_VERSION; }
+
+const char* uno_status_string(int32_t status) {
+    switch (status) {
+        case UNO_OK: return "UNO_OK";
+        case UNO_ERR_INVALID_ARG: return "UNO_ERR_INVALID_ARG";
+        case UNO_ERR_UNSUPPORTED: return "UNO_ERR_UNSUPPORTED";
+        case UNO_ERR_WORKSPACE: return "UNO_ERR_WORKSPACE";
+        case UNO_ERR_HIP: return "UNO_ERR_HIP";
+        default: return "UNO_ERR_UNKNOWN";
+    }
+}
+
+const char* uno_last_error_message(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ Philox
+uno_status uno_philox_uniforms(uint64_t seed, uint64_t stream_id, uint64_t offset, int64_t n, float* out,
+                               hipStream_t stream) {
+    if (n < 0) return fail(UNO_ERR_INVALID_ARG, "n must be >= 0 (got %lld)", static_cast<long long>(n));
+    if (n == 0) return ok();
+    if (out == nullptr) return fail(UNO_ERR_INVALID_ARG, "out is null");
+    if (static_cast<uint64_t>(n) - 1u > ~offset) return fail(UNO_ERR_INVALID_ARG, "offset + n exceeds 2^64");
+    const uint64_t blocks4 = ((offset + static_cast<uint64_t>(n) - 1u) >> 2) - (offset >> 2) + 1u;
+    if ((blocks4 + 255u) / 256u > static_cast<uint64_t>(kMaxGridX))
+        return fail(UNO_ERR_UNSUPPORTED, "n too large for one launch");
+    return from_hip(uno::philox_uniforms_launch(seed, stream_id, offset, n, out, stream), "philox launch");
+}
+
+// ------------------------------------------------------------------ gated LoRA
+static uno_status check_gemm(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
+    if (dtype != UNO_BF16 && dtype != UNO_F32) return fail(UNO_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (M < 0 || N < 1 || K < 1) return fail(UNO_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
+    if (M > 2147483647LL - 64 || N > 2147483647LL || K > 2147483647LL)
+        return fail(UNO_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+    if (r < 1 || r > 256) return fail(UNO_ERR_UNSUPPORTED, "rank r must be in [1, 256] (got %d)", r);
+    if (dtype == UNO_BF16) {
+        if (K % 8 != 0) return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs K %% 8 == 0 (got %lld)", static_cast<long long>(K));
+        if (r % 8 != 0) return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs r %% 8 == 0 (got %d)", r);
+        const int64_t rows_cap = (M + 31) / 32 * 32 + 32;
+        if ((rows_cap + 63) / 64 > kMaxGridYZ) return fail(UNO_ERR_UNSUPPORTED, "M too large for the tile grid");
+        if ((N + 127) / 128 > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "N too large for the tile grid");
+    } else {
+        if (M * N > kMaxGridX * 256 || M * r > kMaxGridX * 256) return fail(UNO_ERR_UNSUPPORTED, "problem too large for the fp32 path");
+    }
+    return UNO_OK;
+}
+
+size_t uno_gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype) {
+    if (check_gemm(M, N, K, r, dtype) != UNO_OK) return 0;
+    ok();
+    return uno::gated_lora_workspace_size(M, N, K, r, dtype == UNO_BF16);
+}
+
+uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a, const void* lora_b,
+                              const uint8_t* gate, void* y, int64_t M, int64_t N, int64_t K, int32_t r,
+                              float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    uno_status st = check_gemm(M, N, K, r, dtype);
+    if (st != UNO_OK) return st;
+    if (!std::isfinite(scale)) return fail(UNO_ERR_INVALID_ARG, "scale must be finite");
+    if (M == 0) return ok();
+    if (!x || !w || !lora_a || !lora_b || !gate || !y) return fail(UNO_ERR_INVALID_ARG, "null tensor pointer");
+    if (dtype == UNO_BF16) {
+        if (!aligned16(x) || !aligned16(w) || !aligned16(lora_a) || !aligned16(lora_b))
+            return fail(UNO_ERR_INVALID_ARG, "bf16 inputs must be 16-byte aligned");
+        if (!aligned16(y)) return fail(UNO_ERR_INVALID_ARG, "y must be 16-byte aligned");
+    } else {
+        if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(lora_a) |
+             reinterpret_cast<uintptr_t>(lora_b) | reinterpret_cast<uintptr_t>(y)) & 3u)
+            return fail(UNO_ERR_INVALID_ARG, "fp32 tensors must be 4-byte aligned");
+    }
+    const size_t need = uno::gated_lora_workspace_size(M, N, K, r, dtype == UNO_BF16);
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != UNO_OK) return st;
+    uno::GemmProblem p{x, w, lora_a, lora_b, gate, y, M, N, K, r, scale, dtype == UNO_BF16};
+    return from_hip(uno::gated_lora_launch(p, workspace, workspace_bytes, stream), "gated lora launch");
+}
+
+// ------------------------------------------------------------------ verification
+static uno_status check_logits(int64_t B, int32_t L, int64_t V, float T, int32_t dtype) {
+    if (dtype != UNO_BF16 && dtype != UNO_F32) return fail(UNO_ERR_INVALID_ARG, "unknown logits dtype %d", dtype);
+    if (B < 0) return fail(UNO_ERR_INVALID_ARG, "B must be >= 0");
+    if (L < 1) return fail(UNO_ERR_INVALID_ARG, "L must be >= 1");
+    if (V < 1 || V > 2147483647LL) return fail(UNO_ERR_INVALID_ARG, "V must be in [1, 2^31)");
+    if (!(T > 0.0f) || !std::isfinite(T)) return fail(UNO_ERR_UNSUPPORTED, "temperature must be positive and finite");
+    return UNO_OK;
+}
+
+size_t uno_block_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
+    if (B < 0 || L < 1 || L > 64 || V < 1) return 0;
+    ok();
+    return uno::verify_workspace_size(B, L, V, has_bonus ? 1 : 0);
+}
+
+uno_status uno_block_verify(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
+                            int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms, int64_t B,
+                            int32_t L, int64_t V, int32_t has_bonus, float temperature, int32_t logits_dtype,
+                            int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_logits(B, L, V, temperature, logits_dtype);
+    if (st != UNO_OK) return st;
+    if (has_bonus != 0 && has_bonus != 1) return fail(UNO_ERR_INVALID_ARG, "has_bonus must be 0 or 1");
+    if (L > 64 || (has_bonus && L > 63))
+        return fail(UNO_ERR_UNSUPPORTED, "block length must be <= 64 (<= 63 with a bonus row)");
+    if (target_seq_stride < 0 || draft_seq_stride < 0) return fail(UNO_ERR_INVALID_ARG, "strides must be >= 0");
+    if (B == 0) return ok();
+    if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !n_accepted || !out_tokens || !n_emitted)
+        return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    const size_t esz = logits_dtype == UNO_BF16 ? 2 : 4;
+    if ((reinterpret_cast<uintptr_t>(target_logits) | reinterpret_cast<uintptr_t>(draft_logits)) % esz)
+        return fail(UNO_ERR_INVALID_ARG, "logits must be aligned to their element size");
+    const int64_t rows = B * (L + has_bonus);
+    const int64_t max_chunks = (V + 2047) / 2048;
+    if (rows * max_chunks > kMaxGridX || B > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "problem too large for one launch");
+    const size_t need = uno::verify_workspace_size(B, L, V, has_bonus);
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != UNO_OK) return st;
+    uno::VerifyProblem p{};
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.t_stride = target_seq_stride;
+    p.d_stride = draft_seq_stride;
+    p.tokens = draft_tokens;
+    p.uniforms = uniforms;
+    p.B = B;
+    p.L = L;
+    p.V = V;
+    p.has_bonus = has_bonus;
+    p.temperature = temperature;
+    p.bf16 = logits_dtype == UNO_BF16;
+    p.n_accepted = n_accepted;
+    p.out_tokens = out_tokens;
+    p.n_emitted = n_emitted;
+    return from_hip(uno::block_verify_launch(p, workspace, stream), "block verify launch");
+}
+
+size_t uno_draft_sample_workspace_size(int64_t B, int32_t L, int64_t V) {
+    if (B < 0 || L < 1 || V < 1) return 0;
+    ok();
+    return uno::draft_sample_workspace_size(B, L, V);
+}
+
+uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride, const float* uniforms, int64_t B, int32_t L,
+                            int64_t V, float temperature, int32_t logits_dtype, int32_t* tokens, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_logits(B, L, V, temperature, logits_dtype);
+    if (st != UNO_OK) return st;
+    if (seq_stride < 0) return fail(UNO_ERR_INVALID_ARG, "seq_stride must be >= 0");
+    if (B == 0) return ok();
+    if (!draft_logits || !uniforms || !tokens) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    const size_t esz = logits_dtype == UNO_BF16 ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(draft_logits) % esz)
+        return fail(UNO_ERR_INVALID_ARG, "logits must be aligned to their element size");
+    const int64_t rows = B * L;
+    const int64_t max_chunks = (V + 2047) / 2048;
+    if (rows * max_chunks > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "problem too large for one launch");
+    const size_t need = uno::draft_sample_workspace_size(B, L, V);
+    st = check_workspace(workspace, workspace_bytes, need);
+    if (st != UNO_OK) return st;
+    uno::VerifyProblem p{};
+    p.draft = draft_logits;
+    p.d_stride = seq_stride;
+    p.uniforms = uniforms;
+    p.B = B;
+    p.L = L;
+    p.V = V;
+    p.temperature = temperature;
+    p.bf16 = logits_dtype == UNO_BF16;
+    p.sampled = tokens;
+    return from_hip(uno::draft_sample_launch(p, workspace, stream), "draft sample launch");
+}
+
+// ------------------------------------------------------------------ glue
+uno_status uno_rmsnorm(const void* x, void* y, int64_t M, int64_t K, float eps, int32_t dtype, hipStream_t stream) {
+    if (dtype != UNO_BF16) return fail(UNO_ERR_UNSUPPORTED, "rmsnorm supports bf16 only");
+    if (M < 0 || K < 0) return fail(UNO_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(UNO_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (M == 0 || K == 0) return ok();
+    if (K % 8 != 0 || K > 65536) return fail(UNO_ERR_UNSUPPORTED, "rmsnorm needs K %% 8 == 0 and K <= 65536");
+    if (M > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "too many rows");
+    if (!x || !y) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(y)) return fail(UNO_ERR_INVALID_ARG, "rmsnorm tensors must be 16-byte aligned");
+    return from_hip(uno::rmsnorm_launch(x, y, M, K, eps, stream), "rmsnorm launch");
+}
+
+static uno_status check_eltwise(const void* a, const void* b, void* out, int64_t n, int32_t dtype) {
+    if (dtype != UNO_BF16) return fail(UNO_ERR_UNSUPPORTED, "elementwise glue supports bf16 only");
+    if (n < 0) return fail(UNO_ERR_INVALID_ARG, "n must be >= 0");
+    if (n == 0) return UNO_OK;
+    if (!a || !b || !out) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return fail(UNO_ERR_INVALID_ARG, "elementwise tensors must be 16-byte aligned");
+    return UNO_OK;
+}
+
+uno_status uno_silu_mul(const void* gate, const void* up, void* out, int64_t n, int32_t dtype, hipStream_t stream) {
+    const uno_status st = check_eltwise(gate, up, out, n, dtype);
+    if (st != UNO_OK) return st;
+    return from_hip(uno::silu_mul_launch(gate, up, out, n, stream), "silu_mul launch");
+}
+
+uno_status uno_residual_add(const void* a, const void* b, void* out, int64_t n, int32_t dtype, hipStream_t stream) {
+    const uno_status st = check_eltwise(a, b, out, n, dtype);
+    if (st != UNO_OK) return st;
+    return from_hip(uno::residual_add_launch(a, b, out, n, stream), "residual_add launch");
+}
+
+}  // extern "C"

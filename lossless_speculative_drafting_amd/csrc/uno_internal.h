@@ -1,0 +1,70 @@
+// Host-side interface between the C-ABI layer (uno_api.cpp) and the kernel
+// translation units.  Every function here assumes its arguments were already
+// validated by the C-ABI layer and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace uno {
+
+constexpr size_t kWorkspaceAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- Philox uniforms -------------------------------------------------------
+hipError_t philox_uniforms_launch(uint64_t seed, uint64_t stream_id, uint64_t offset, int64_t n,
+                                  float* out, hipStream_t stream);
+
+// ---- verification and draft sampling -----------------------------------------
+struct VerifyProblem {
+    const void* target;      // rows (s, i) at s * t_stride + i * V
+    const void* draft;       // rows (s, i) at s * d_stride + i * V (may be null: draft sampling)
+    int64_t t_stride;
+    int64_t d_stride;
+    const int32_t* tokens;   // [B, L] (verify only)
+    const float* uniforms;   // verify: [B, L+1]; draft sampling: [B, L]
+    int64_t B;
+    int32_t L;
+    int64_t V;
+    int32_t has_bonus;
+    float temperature;
+    bool bf16;               // logits dtype
+    int32_t* n_accepted;     // verify outputs
+    int32_t* out_tokens;
+    int32_t* n_emitted;
+    int32_t* sampled;        // draft sampling output [B, L]
+};
+
+size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
+size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V);
+hipError_t block_verify_launch(const VerifyProblem& p, void* ws, hipStream_t stream);
+hipError_t draft_sample_launch(const VerifyProblem& p, void* ws, hipStream_t stream);
+
+// ---- gated-LoRA projection ----------------------------------------------------
+struct GemmProblem {
+    const void* x;        // [M, K]
+    const void* w;        // [N, K]
+    const void* a;        // [r, K]
+    const void* b;        // [N, r]
+    const uint8_t* gate;  // [M]
+    void* y;              // [M, N]
+    int64_t M, N, K;
+    int32_t r;
+    float scale;
+    bool bf16;
+};
+
+size_t gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, bool bf16);
+hipError_t gated_lora_launch(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// ---- layer glue ----------------------------------------------------------------
+hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps,
+                          hipStream_t stream);
+hipError_t silu_mul_launch(const void* gate, const void* up, void* out, int64_t n,
+                           hipStream_t stream);
+hipError_t residual_add_launch(const void* a, const void* b, void* out, int64_t n,
+                               hipStream_t stream);
+
+}  // namespace uno

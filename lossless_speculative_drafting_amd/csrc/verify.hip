@@ -1,0 +1,700 @@
+// Block verification and draft sampling for the Uno sampler (gfx950).
+//
+// What is computed is the linear speculative rejection sampler the pages
+// describe ("The Psi-Spec Sampler" on the aifromscratch.in page: propose a
+// block in parallel, rejection-sample it against the AR model, keep the
+// longest valid prefix, preserve the AR distribution; "What 'lossless' means
+// here" on the cctest.ai page: the AR model rejects or adjusts candidates).
+//
+// The work is one streaming pass over every logit row plus one redraw pass
+// over at most one row pair per sequence:
+//
+//   row_stats      grid = rows x chunks.  Each workgroup streams one chunk
+//                  of a target row and (if present) the matching draft row
+//                  with 16-byte loads and keeps a per-lane online
+//                  (max, sum exp) pair: fp32 exponentials (hardware exp2 of
+//                  the max-subtracted logit times log2(e)/T), summed 8 at a
+//                  time in fp32 and accumulated in fp64.  Lane pairs merge in
+//                  a fixed xor-shuffle tree, waves merge in order.
+//   verify_decide  one wavefront per sequence, lane i = position i.  Chunk
+//                  statistics merge in fp64; the acceptance ratio is formed
+//                  in log space in fp64; a ballot gives the first rejection.
+//                  Lane 0 writes the redraw job for the sequence.
+//   redraw_mass    grid = jobs x chunks.  Each lane owns 16-token segments
+//                  of the redraw row and writes their fp32 weight sums
+//                  (residual max(0, p - q) and, for the zero-mass fallback,
+//                  p itself).
+//   redraw_select  one workgroup per job.  Segment sums are carried in fp64
+//                  (per-lane sequential sums, then a block scan), the target
+//                  u * R is located, and the owning lane re-forms its
+//                  segment's weights with the same code as redraw_mass to find
+//                  the smallest token whose running sum exceeds the target.
+//
+// Floating-point contraction is disabled in this file so that the weights
+// recomputed by redraw_select are bit-identical to those summed by
+// redraw_mass.
+#pragma clang fp contract(off)
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "uno_device.h"
+#include "uno_internal.h"
+
+namespace uno {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;    // tokens per 16-byte (bf16) vector
+constexpr int kSeg = 16;   // tokens per redraw segment
+constexpr int kStatTile = kThreads * kVec;
+
+struct ChunkStat {
+    double sA, sB;  // sum of exp((v - m) / T) for the target / draft row
+    float mA, mB;   // chunk maxima (raw logits)
+};
+
+enum : int32_t { kJobNone = 0, kJobResidual = 1, kJobSingle = 2 };
+
+struct RedrawJob {
+    const void* a;  // row whose distribution is drawn from (target row, or draft row)
+    const void* b;  // draft row subtracted in residual mode
+    int32_t* out;   // where the token goes
+    float Ma, invSa, Mb, invSb;
+    float u;
+    int32_t mode;
+};
+
+struct Online {
+    float m;
+    double s;
+};
+
+template <bool BF16>
+__device__ __forceinline__ float load_one(const void* row, int64_t k) {
+    if constexpr (BF16) {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(row)[k]);
+    } else {
+        return static_cast<const float*>(row)[k];
+    }
+}
+
+// Eight consecutive logits starting at k; tokens at or beyond V read as -inf.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load8(const void* row, int64_t k, int64_t V, float* f) {
+    if constexpr (VEC) {
+        if constexpr (BF16) {
+            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k);
+            unpack8(v, f);
+        } else {
+            const float4 v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k);
+            const float4 v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k + 4);
+            f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
+            f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) f[j] = (k + j < V) ? load_one<BF16>(row, k + j) : -INFINITY;
+    }
+}
+
+__device__ __forceinline__ void online_add8(Online& o, const float* v, float c2) {
+    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                           fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    if (vm > o.m) {
+        o.s *= static_cast<double>(fast_exp2((o.m - vm) * c2));
+        o.m = vm;
+    }
+    if (o.m != -INFINITY) {
+        float e[kVec];
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) e[j] = fast_exp2((v[j] - o.m) * c2);
+        const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        o.s += static_cast<double>(t);
+    }
+}
+
+__device__ __forceinline__ Online online_merge(Online a, Online b, float c2) {
+    const float m = fmaxf(a.m, b.m);
+    if (m == -INFINITY) return Online{m, 0.0};
+    const double s = a.s * static_cast<double>(fast_exp2((a.m - m) * c2)) +
+                     b.s * static_cast<double>(fast_exp2((b.m - m) * c2));
+    return Online{m, s};
+}
+
+__device__ __forceinline__ Online wave_merge(Online o, float c2) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        Online p{__shfl_xor(o.m, off), __shfl_xor(o.s, off)};
+        o = online_merge(o, p, c2);
+    }
+    return o;
+}
+
+// ---------------------------------------------------------------- row_stats
+// Rows are (s, i) with i < rows_per_seq; array B exists for i < rows_with_b.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(
+    const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
+    int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
+    ChunkStat* __restrict__ stats) {
+    const int64_t blk = blockIdx.x;
+    const int64_t row = blk / n_chunks;
+    const int32_t c = static_cast<int32_t>(blk % n_chunks);
+    const int64_t s = row / rows_per_seq;
+    const int32_t i = static_cast<int32_t>(row % rows_per_seq);
+    const size_t esz = BF16 ? 2 : 4;
+    const char* arow = static_cast<const char*>(A) + (s * a_stride + static_cast<int64_t>(i) * V) * esz;
+    const bool has_b = (B != nullptr) && (i < rows_with_b);
+    const char* brow = has_b ? static_cast<const char*>(B) + (s * b_stride + static_cast<int64_t>(i) * V) * esz
+                             : nullptr;
+    const int64_t k0 = static_cast<int64_t>(c) * chunk;
+    const int64_t k1 = min(V, k0 + chunk);
+
+    Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
+    int64_t k = k0 + static_cast<int64_t>(threadIdx.x) * kVec;
+    // two vectors per array in flight per iteration
+    for (; k + kStatTile < k1; k += 2 * kStatTile) {
+        float va0[kVec], va1[kVec];
+        load8<BF16, VEC>(arow, k, V, va0);
+        load8<BF16, VEC>(arow, k + kStatTile, V, va1);
+        if (has_b) {
+            float vb0[kVec], vb1[kVec];
+            load8<BF16, VEC>(brow, k, V, vb0);
+            load8<BF16, VEC>(brow, k + kStatTile, V, vb1);
+            online_add8(ob, vb0, c2);
+            online_add8(ob, vb1, c2);
+        }
+        online_add8(oa, va0, c2);
+        online_add8(oa, va1, c2);
+    }
+    if (k < k1) {
+        float va[kVec];
+        load8<BF16, VEC>(arow, k, V, va);
+        online_add8(oa, va, c2);
+        if (has_b) {
+            float vb[kVec];
+            load8<BF16, VEC>(brow, k, V, vb);
+            online_add8(ob, vb, c2);
+        }
+    }
+
+    oa = wave_merge(oa, c2);
+    ob = wave_merge(ob, c2);
+    __shared__ Online sha[kThreads / kWave], shb[kThreads / kWave];
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) {
+        sha[wave] = oa;
+        shb[wave] = ob;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Online ra = sha[0], rb = shb[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) {
+            ra = online_merge(ra, sha[w], c2);
+            rb = online_merge(rb, shb[w], c2);
+        }
+        ChunkStat st;
+        st.sA = ra.s;
+        st.mA = ra.m;
+        st.sB = rb.s;
+        st.mB = rb.m;
+        stats[row * n_chunks + c] = st;
+    }
+}
+
+// Merge the chunk statistics of one row in fp64: M = max, S = sum s_c e^{(m_c - M)/T}.
+__device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, bool use_b,
+                                             double invT, float& M, double& S) {
+    float m = -INFINITY;
+    for (int32_t c = 0; c < n; ++c) m = fmaxf(m, use_b ? st[c].mB : st[c].mA);
+    double s = 0.0;
+    if (m != -INFINITY) {
+        for (int32_t c = 0; c < n; ++c) {
+            const float mc = use_b ? st[c].mB : st[c].mA;
+            if (mc == -INFINITY) continue;
+            const double sc = use_b ? st[c].sB : st[c].sA;
+            s += sc * exp((static_cast<double>(mc) - static_cast<double>(m)) * invT);
+        }
+    }
+    M = m;
+    S = s;
+}
+
+// ---------------------------------------------------------------- verify_decide
+struct DecideArgs {
+    const void* target;
+    const void* draft;
+    int64_t t_stride, d_stride;
+    const int32_t* tokens;
+    const float* uniforms;
+    int64_t B;
+    int32_t L, nb;
+    int64_t V;
+    double invT;
+    const ChunkStat* stats;
+    int32_t n_chunks;
+    RedrawJob* jobs;
+    int32_t* n_accepted;
+    int32_t* out_tokens;
+    int32_t* n_emitted;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
+    const int32_t L = a.L;
+    const int32_t rows = L + a.nb;
+    const size_t esz = BF16 ? 2 : 4;
+
+    float Mz = -INFINITY, Md = -INFINITY;
+    double Sz = 0.0, Sd = 0.0;
+    if (lane < rows) {
+        const ChunkStat* st = a.stats + (s * rows + lane) * a.n_chunks;
+        merge_chunks(st, a.n_chunks, false, a.invT, Mz, Sz);
+        if (lane < L) merge_chunks(st, a.n_chunks, true, a.invT, Md, Sd);
+    }
+
+    int32_t x = 0;
+    bool valid = true;
+    bool acc = true;
+    if (lane < L) {
+        x = a.tokens[s * L + lane];
+        valid = (x >= 0) && (static_cast<int64_t>(x) < a.V);
+        acc = false;
+        if (valid) {
+            const char* zrow = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(lane) * a.V) * esz;
+            const char* drow = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(lane) * a.V) * esz;
+            const float zx = load_one<BF16>(zrow, x);
+            const float dx = load_one<BF16>(drow, x);
+            double prob;
+            if (zx == -INFINITY) {
+                prob = 0.0;
+            } else if (dx == -INFINITY) {
+                prob = 1.0;
+            } else {
+                const double lp = (static_cast<double>(zx) - static_cast<double>(Mz)) * a.invT - log(Sz);
+                const double lq = (static_cast<double>(dx) - static_cast<double>(Md)) * a.invT - log(Sd);
+                prob = exp(fmin(0.0, lp - lq));
+            }
+            acc = static_cast<double>(a.uniforms[s * (L + 1) + lane]) < prob;
+        }
+    }
+    const uint64_t bad = __ballot(!valid);
+    const uint64_t rej = __ballot(!acc);
+    const int32_t n_acc = rej ? static_cast<int32_t>(__builtin_ctzll(rej)) : L;
+
+    const int32_t j = n_acc & (kWave - 1);
+    const float Mz_j = __shfl(Mz, j);
+    const double Sz_j = __shfl(Sz, j);
+    const float Md_j = __shfl(Md, j);
+    const double Sd_j = __shfl(Sd, j);
+
+    int32_t* out = a.out_tokens + s * (L + 1);
+    if (lane < L) out[lane] = (!bad && lane < n_acc) ? x : -1;
+    if (lane == 0) {
+        out[L] = -1;  // slot L: filled later only by a bonus draw
+        RedrawJob job;
+        job.a = nullptr;
+        job.b = nullptr;
+        job.out = out + n_acc;
+        job.Ma = Mz_j;
+        job.invSa = static_cast<float>(1.0 / Sz_j);
+        job.Mb = Md_j;
+        job.invSb = static_cast<float>(1.0 / Sd_j);
+        job.u = a.uniforms[s * (L + 1) + L];
+        job.mode = kJobNone;
+        if (bad) {
+            a.n_accepted[s] = -1;
+            a.n_emitted[s] = 0;
+        } else {
+            a.n_accepted[s] = n_acc;
+            if (n_acc < L) {
+                job.mode = kJobResidual;
+                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
+                job.b = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
+                a.n_emitted[s] = n_acc + 1;
+            } else if (a.nb) {
+                job.mode = kJobSingle;
+                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(L) * a.V) * esz;
+                a.n_emitted[s] = L + 1;
+            } else {
+                a.n_emitted[s] = L;
+            }
+        }
+        a.jobs[s] = job;
+    }
+}
+
+// ---------------------------------------------------------------- draft_decide
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void draft_decide_kernel(
+    const void* D, int64_t d_stride, int32_t L, int64_t V, int64_t rows, double invT,
+    const ChunkStat* stats, int32_t n_chunks, const float* uniforms, int32_t* sampled,
+    RedrawJob* jobs) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (row >= rows) return;
+    const int64_t s = row / L;
+    const int32_t i = static_cast<int32_t>(row % L);
+    float M;
+    double S;
+    merge_chunks(stats + row * n_chunks, n_chunks, false, invT, M, S);
+    RedrawJob job;
+    job.a = static_cast<const char*>(D) + (s * d_stride + static_cast<int64_t>(i) * V) * (BF16 ? 2 : 4);
+    job.b = nullptr;
+    job.out = sampled + row;
+    job.Ma = M;
+    job.invSa = static_cast<float>(1.0 / S);
+    job.Mb = 0.f;
+    job.invSb = 0.f;
+    job.u = uniforms[row];
+    job.mode = kJobSingle;
+    jobs[row] = job;
+}
+
+// ---------------------------------------------------------------- redraw weights
+// Weights of the 16 tokens of segment g, formed identically by redraw_mass
+// and redraw_select.  use_p selects p itself in residual mode (zero-mass
+// fallback).  Tokens at or beyond V get weight 0.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void segment_weights(const RedrawJob& job, int64_t g, int64_t V, float c2,
+                                                bool use_p, float* w) {
+    float va[kSeg];
+    const int64_t k = g * kSeg;
+    load8<BF16, VEC>(job.a, k, V, va);
+    if (k + kVec < V) {
+        load8<BF16, VEC>(job.a, k + kVec, V, va + kVec);
+    } else {
+#pragma unroll
+        for (int j = kVec; j < kSeg; ++j) va[j] = -INFINITY;
+    }
+    if (job.mode == kJobResidual && !use_p) {
+        float vb[kSeg];
+        load8<BF16, VEC>(job.b, k, V, vb);
+        if (k + kVec < V) {
+            load8<BF16, VEC>(job.b, k + kVec, V, vb + kVec);
+        } else {
+#pragma unroll
+            for (int j = kVec; j < kSeg; ++j) vb[j] = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) {
+            const float p = fast_exp2((va[j] - job.Ma) * c2) * job.invSa;
+            const float q = fast_exp2((vb[j] - job.Mb) * c2) * job.invSb;
+            w[j] = fmaxf(0.f, p - q);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) w[j] = fast_exp2((va[j] - job.Ma) * c2) * job.invSa;
+    }
+}
+
+// ---------------------------------------------------------------- redraw_mass
+// seg layout: [job][n_arr][nseg]; array 0 = drawn weights, array 1 = p (residual jobs).
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void redraw_mass_kernel(const RedrawJob* __restrict__ jobs,
+                                                              int32_t n_chunks, int64_t seg_per_chunk,
+                                                              int64_t nseg, int32_t n_arr, int64_t V,
+                                                              float c2, float* __restrict__ seg) {
+    const int64_t jid = blockIdx.x / n_chunks;
+    const int32_t c = static_cast<int32_t>(blockIdx.x % n_chunks);
+    const RedrawJob job = jobs[jid];
+    if (job.mode == kJobNone) return;
+    float* out0 = seg + jid * n_arr * nseg;
+    const int64_t g0 = static_cast<int64_t>(c) * seg_per_chunk;
+    const int64_t g1 = min(nseg, g0 + seg_per_chunk);
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kThreads) {
+        float w[kSeg];
+        segment_weights<BF16, VEC>(job, g, V, c2, false, w);
+        float sr = 0.f;
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) sr += w[j];
+        out0[g] = sr;
+        if (job.mode == kJobResidual && n_arr > 1) {
+            float wp[kSeg];
+            segment_weights<BF16, VEC>(job, g, V, c2, true, wp);
+            float sp = 0.f;
+#pragma unroll
+            for (int j = 0; j < kSeg; ++j) sp += wp[j];
+            out0[nseg + g] = sp;
+        }
+    }
+}
+
+// Exclusive block scan of one double per thread (fixed order); returns the
+// exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ double block_excl_scan(double v, double* sh, double* total) {
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    double incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+    }
+    if (lane == kWave - 1) sh[wave] = incl;
+    __syncthreads();
+    double base = 0.0;
+    for (int w = 0; w < wave; ++w) base += sh[w];
+    double tot = 0.0;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += sh[w];
+    __syncthreads();
+    *total = tot;
+    return base + (incl - v);
+}
+
+// ---------------------------------------------------------------- redraw_select
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob* __restrict__ jobs,
+                                                                int64_t nseg, int32_t n_arr,
+                                                                int64_t V, float c2,
+                                                                const float* __restrict__ seg) {
+    const RedrawJob job = jobs[blockIdx.x];
+    if (job.mode == kJobNone) return;
+    __shared__ double sh[kThreads / kWave];
+    __shared__ int32_t first_wave_lane[kThreads / kWave];
+    __shared__ int32_t chosen;
+
+    const int64_t per = (nseg + kThreads - 1) / kThreads;
+    const int64_t g0 = min(nseg, static_cast<int64_t>(threadIdx.x) * per);
+    const int64_t g1 = min(nseg, g0 + per);
+
+    bool use_p = false;
+    const float* sg = seg + static_cast<int64_t>(blockIdx.x) * n_arr * nseg;
+    double tot = 0.0;
+    for (int64_t g = g0; g < g1; ++g) tot += static_cast<double>(sg[g]);
+    double R;
+    double excl = block_excl_scan(tot, sh, &R);
+    if (job.mode == kJobResidual && R == 0.0 && n_arr > 1) {
+        // The residual lost all mass to rounding: draw from p instead.
+        use_p = true;
+        sg += nseg;
+        tot = 0.0;
+        for (int64_t g = g0; g < g1; ++g) tot += static_cast<double>(sg[g]);
+        excl = block_excl_scan(tot, sh, &R);
+    }
+    const double target = static_cast<double>(job.u) * R;
+
+    // Walk this lane's segments in order; the running value at the end is the
+    // lane's inclusive prefix as the select walk below will see it.
+    double run = excl;
+    for (int64_t g = g0; g < g1; ++g) run += static_cast<double>(sg[g]);
+    const bool cand = (g1 > g0) && (run > target);
+    const uint64_t m = __ballot(cand);
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0) first_wave_lane[wave] = m ? static_cast<int32_t>(__builtin_ctzll(m)) : -1;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t ch = -1;
+        for (int w = 0; w < kThreads / kWave; ++w) {
+            if (first_wave_lane[w] >= 0) {
+                ch = w * kWave + first_wave_lane[w];
+                break;
+            }
+        }
+        chosen = ch;
+    }
+    __syncthreads();
+
+    if (static_cast<int32_t>(threadIdx.x) == chosen) {
+        int64_t token = -1;
+        double r = excl;
+        for (int64_t g = g0; g < g1 && token < 0; ++g) {
+            const double next = r + static_cast<double>(sg[g]);
+            if (next > target && sg[g] > 0.f) {
+                float w[kSeg];
+                segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
+                float run32 = 0.f;
+                for (int j = 0; j < kSeg; ++j) {
+                    run32 += w[j];
+                    if (w[j] > 0.f && r + static_cast<double>(run32) > target) {
+                        token = g * kSeg + j;
+                        break;
+                    }
+                }
+            }
+            r = next;
+        }
+        if (token < 0) {
+            // Rounding left no crossing: take the last token with weight.
+            for (int64_t g = nseg - 1; g >= 0 && token < 0; --g) {
+                if (sg[g] > 0.f) {
+                    float w[kSeg];
+                    segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
+                    for (int j = kSeg - 1; j >= 0; --j) {
+                        if (w[j] > 0.f) {
+                            token = g * kSeg + j;
+                            break;
+                        }
+                    }
+                }
+            }
+            if (token < 0) token = 0;
+        }
+        *job.out = static_cast<int32_t>(token);
+    } else if (chosen < 0 && threadIdx.x == 0) {
+        // No lane crossed the target (only possible through rounding at the very
+        // end of the row): take the last token with weight.
+        int64_t token = -1;
+        for (int64_t g = nseg - 1; g >= 0 && token < 0; --g) {
+            if (sg[g] > 0.f) {
+                float w[kSeg];
+                segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
+                for (int j = kSeg - 1; j >= 0; --j) {
+                    if (w[j] > 0.f) {
+                        token = g * kSeg + j;
+                        break;
+                    }
+                }
+            }
+        }
+        *job.out = static_cast<int32_t>(token < 0 ? 0 : token);
+    }
+}
+
+// ---------------------------------------------------------------- planning
+
+struct Plan {
+    int32_t c1;       // chunks per row in row_stats
+    int64_t chunk1;   // tokens per chunk
+    int32_t c3;       // chunks per job in redraw_mass
+    int64_t spc3;     // segments per chunk
+    int64_t nseg;     // 16-token segments per row
+    int32_t n_arr;    // segment-sum arrays per job
+    int64_t rows;     // rows streamed by row_stats
+    int64_t n_jobs;
+    size_t off_stats, off_jobs, off_seg, total;
+};
+
+constexpr int64_t kTargetBlocks = 2048;
+
+Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
+    Plan p{};
+    p.rows = B * rows_per_seq;
+    const int64_t max_c1 = (V + kStatTile - 1) / kStatTile;
+    int64_t c1 = p.rows > 0 ? (kTargetBlocks + p.rows - 1) / p.rows : 1;
+    c1 = std::max<int64_t>(1, std::min(c1, max_c1));
+    int64_t chunk = (V + c1 - 1) / c1;
+    chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
+    p.chunk1 = chunk;
+    p.c1 = static_cast<int32_t>((V + chunk - 1) / chunk);
+    p.nseg = (V + kSeg - 1) / kSeg;
+    p.n_jobs = n_jobs;
+    const int64_t max_c3 = (p.nseg + kThreads - 1) / kThreads;
+    int64_t c3 = n_jobs > 0 ? (kTargetBlocks / 2 + n_jobs - 1) / n_jobs : 1;
+    c3 = std::max<int64_t>(1, std::min(c3, max_c3));
+    int64_t spc = (p.nseg + c3 - 1) / c3;
+    spc = (spc + kThreads - 1) / kThreads * kThreads;
+    p.spc3 = spc;
+    p.c3 = static_cast<int32_t>((p.nseg + spc - 1) / spc);
+    p.n_arr = n_arr;
+    size_t off = 0;
+    p.off_stats = off;
+    off = align_up(off + static_cast<size_t>(p.rows) * p.c1 * sizeof(ChunkStat), kWorkspaceAlign);
+    p.off_jobs = off;
+    off = align_up(off + static_cast<size_t>(n_jobs) * sizeof(RedrawJob), kWorkspaceAlign);
+    p.off_seg = off;
+    off = align_up(off + static_cast<size_t>(n_jobs) * n_arr * p.nseg * sizeof(float), kWorkspaceAlign);
+    p.total = off;
+    (void)L;
+    return p;
+}
+
+bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    return (V % kVec == 0) && (s0 % kVec == 0) && (s1 % kVec == 0) && al(p0) && (p1 == nullptr || al(p1));
+}
+
+template <bool BF16, bool VEC>
+hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+    const int32_t nb = pr.has_bonus ? 1 : 0;
+    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2);
+    char* base = static_cast<char*>(ws);
+    ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + p.off_stats);
+    RedrawJob* jobs = reinterpret_cast<RedrawJob*>(base + p.off_jobs);
+    float* seg = reinterpret_cast<float*>(base + p.off_seg);
+    const double invT = 1.0 / static_cast<double>(pr.temperature);
+    const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
+
+    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
+                       stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
+                       p.chunk1, p.c1, c2, stats);
+    DecideArgs da;
+    da.target = pr.target;
+    da.draft = pr.draft;
+    da.t_stride = pr.t_stride;
+    da.d_stride = pr.d_stride;
+    da.tokens = pr.tokens;
+    da.uniforms = pr.uniforms;
+    da.B = pr.B;
+    da.L = pr.L;
+    da.nb = nb;
+    da.V = pr.V;
+    da.invT = invT;
+    da.stats = stats;
+    da.n_chunks = p.c1;
+    da.jobs = jobs;
+    da.n_accepted = pr.n_accepted;
+    da.out_tokens = pr.out_tokens;
+    da.n_emitted = pr.n_emitted;
+    const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((verify_decide_kernel<BF16>), dim3(dblocks), dim3(kThreads), 0, stream, da);
+    hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * p.c3)), dim3(kThreads), 0,
+                       stream, jobs, p.c3, p.spc3, p.nseg, p.n_arr, pr.V, c2, seg);
+    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kThreads), 0, stream,
+                       jobs, p.nseg, p.n_arr, pr.V, c2, seg);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool VEC>
+hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+    const int64_t rows = pr.B * pr.L;
+    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L, rows, 1);
+    char* base = static_cast<char*>(ws);
+    ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + p.off_stats);
+    RedrawJob* jobs = reinterpret_cast<RedrawJob*>(base + p.off_jobs);
+    float* seg = reinterpret_cast<float*>(base + p.off_seg);
+    const double invT = 1.0 / static_cast<double>(pr.temperature);
+    const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
+    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
+                       stream, pr.draft, pr.d_stride, nullptr, int64_t(0), pr.L, 0, pr.V, p.chunk1, p.c1, c2,
+                       stats);
+    hipLaunchKernelGGL((draft_decide_kernel<BF16>), dim3(static_cast<uint32_t>((rows + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, invT, stats, p.c1,
+                       pr.uniforms, pr.sampled, jobs);
+    hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows * p.c3)), dim3(kThreads), 0,
+                       stream, jobs, p.c3, p.spc3, p.nseg, 1, pr.V, c2, seg);
+    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows)), dim3(kThreads), 0, stream,
+                       jobs, p.nseg, 1, pr.V, c2, seg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
+    const int32_t nb = has_bonus ? 1 : 0;
+    return make_plan(B, L, V, L + nb, B, 2).total;
+}
+
+size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V) {
+    return make_plan(B, L, V, L, B * L, 1).total;
+}
+
+hipError_t block_verify_launch(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+    const bool vec = vec_ok(pr.target, pr.draft, pr.V, pr.t_stride, pr.d_stride);
+    if (pr.bf16) return vec ? verify_impl<true, true>(pr, ws, stream) : verify_impl<true, false>(pr, ws, stream);
+    return vec ? verify_impl<false, true>(pr, ws, stream) : verify_impl<false, false>(pr, ws, stream);
+}
+
+hipError_t draft_sample_launch(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+    const bool vec = vec_ok(pr.draft, nullptr, pr.V, pr.d_stride, 0);
+    if (pr.bf16) return vec ? draft_impl<true, true>(pr, ws, stream) : draft_impl<true, false>(pr, ws, stream);
+    return vec ? draft_impl<false, true>(pr, ws, stream) : draft_impl<false, false>(pr, ws, stream);
+}
+
+}  // namespace uno

@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/uno.h declares, and rejects bad arguments on the host before any
+launch (only argument combinations that fail validation are passed, so
+nothing reaches the device)."""
+
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import lossless_speculative_drafting_amd as uno
+from lossless_speculative_drafting_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "uno.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: every call below fails validation first
+NULL = ctypes.c_void_p(0)
+STREAM = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return uno.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _lib.header_symbols(HEADER)
+    assert len(declared) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert hasattr(lib, s)
+    assert set(declared) == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.uno_abi_version() == 1
+    assert uno.status_string(0) == "UNO_OK"
+    assert uno.status_string(3) == "UNO_ERR_WORKSPACE"
+    assert uno.status_string(99) == "UNO_ERR_UNKNOWN"
+
+
+def _msg(lib):
+    return lib.uno_last_error_message().decode()
+
+
+def test_philox_validation(lib):
+    assert lib.uno_philox_uniforms(0, 0, 0, -1, FAKE, STREAM) == INVALID
+    assert lib.uno_philox_uniforms(0, 0, 0, 5, NULL, STREAM) == INVALID
+    assert lib.uno_philox_uniforms(0, 0, 2 ** 64 - 2, 5, FAKE, STREAM) == INVALID
+    assert "2^64" in _msg(lib)
+    assert lib.uno_philox_uniforms(0, 0, 0, 0, NULL, STREAM) == OK   # n = 0 is a no-op
+
+
+def test_gated_lora_validation(lib):
+    def call(M=4, N=16, K=16, r=16, dt=0, x=FAKE, ws=FAKE, wsb=1 << 30, scale=2.0):
+        return lib.uno_gated_lora_fwd(x, FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, r, scale, dt, ws, wsb, STREAM)
+    assert call(dt=7) == INVALID
+    assert call(N=0) == INVALID
+    assert call(M=-1) == INVALID
+    assert call(K=12) == UNSUPPORTED and "K % 8" in _msg(lib)
+    assert call(r=300) == UNSUPPORTED
+    assert call(r=12) == UNSUPPORTED
+    assert call(scale=float("inf")) == INVALID
+    assert call(x=NULL) == INVALID
+    assert call(ws=NULL) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE   # not 256-byte aligned
+    assert call(M=0, x=NULL) == OK                            # empty batch is a no-op
+    assert lib.uno_gated_lora_workspace_size(2048, 4096, 4096, 128, 0) > 0
+    assert lib.uno_gated_lora_workspace_size(24, 512, 512, 128, 1) == 24 * 128 * 4 + (256 - (24 * 128 * 4) % 256) % 256
+
+
+def test_block_verify_validation(lib):
+    def call(B=2, L=4, V=64, nb=0, T=1.0, dt=0, tok=FAKE, ws=FAKE, wsb=1 << 30, ts=256, ds=256):
+        return lib.uno_block_verify(FAKE, FAKE, ts, ds, tok, FAKE, B, L, V, nb, T, dt, FAKE, FAKE, FAKE, ws, wsb,
+                                    STREAM)
+    assert call(L=0) == INVALID
+    assert call(L=65) == UNSUPPORTED
+    assert call(L=64, nb=1) == UNSUPPORTED
+    assert call(nb=2) == INVALID
+    assert call(T=0.0) == UNSUPPORTED
+    assert call(T=float("nan")) == UNSUPPORTED
+    assert call(dt=3) == INVALID
+    assert call(V=0) == INVALID
+    assert call(ts=-1) == INVALID
+    assert call(tok=NULL) == INVALID
+    assert call(wsb=8) == WORKSPACE
+    assert call(B=0, tok=NULL) == OK
+    assert lib.uno_block_verify_workspace_size(64, 16, 128256, 0) > 0
+    assert lib.uno_block_verify_workspace_size(64, 65, 128256, 0) == 0
+
+
+def test_draft_sample_and_glue_validation(lib):
+    assert lib.uno_draft_sample(FAKE, 0, FAKE, 2, 0, 64, 1.0, 0, FAKE, FAKE, 1 << 30, STREAM) == INVALID
+    assert lib.uno_draft_sample(FAKE, 0, FAKE, 2, 4, 64, -1.0, 0, FAKE, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_draft_sample(FAKE, 0, FAKE, 2, 4, 64, 1.0, 0, FAKE, FAKE, 4, STREAM) == WORKSPACE
+    assert lib.uno_rmsnorm(FAKE, FAKE, 4, 12, 1e-5, 0, STREAM) == UNSUPPORTED
+    assert lib.uno_rmsnorm(FAKE, FAKE, 4, 16, 1e-5, 1, STREAM) == UNSUPPORTED
+    assert lib.uno_rmsnorm(FAKE, FAKE, 4, 16, -1.0, 0, STREAM) == INVALID
+    assert lib.uno_silu_mul(FAKE, NULL, FAKE, 16, 0, STREAM) == INVALID
+    assert lib.uno_residual_add(FAKE, FAKE, ctypes.c_void_p(0x100004), 16, 0, STREAM) == INVALID
+    assert lib.uno_silu_mul(NULL, NULL, NULL, 0, 0, STREAM) == OK

@@ -1,0 +1,120 @@
+"""Gated-LoRA projection on the GPU vs the fp64 oracle.
+
+Small cases run the oracle on every element; the full 8B-layer shapes run the
+GPU on the whole batch and the oracle on sampled rows (rows are independent).
+bf16 tolerance 2e-2 and fp32 tolerance 1e-4 in the RMS-floored relative error
+of tests/parity.py.  Rows with gate 0 must be bitwise equal to the same call
+with every gate 0.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_speculative_drafting_amd as uno
+import oracle
+from gpu_util import say, to_dev, to_host
+from parity import BF16_TOL, F32_TOL, floored_rel_err
+from synthetic import WORKLOADS, gate_vector, gemm_inputs
+
+
+def _run(inp, dtype, gate=None):
+    g = inp["gate"] if gate is None else gate
+    y = uno.gated_lora_fwd(to_dev(inp["x"], dtype), to_dev(inp["w"], dtype), to_dev(inp["a"], dtype),
+                           to_dev(inp["b"], dtype), to_dev(g, "u8"), scale=2.0)
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+@pytest.mark.gpu
+def test_tiny_f32_workload():
+    wl = WORKLOADS["tiny"]
+    _, K, N = wl.projections[0]
+    gate = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
+    inp = gemm_inputs(wl.rows, K, N, 128, wl.seed, "f32", gate=gate)
+    say("gemm tiny f32", wl.rows, K, N)
+    y = _run(inp, "f32")
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], inp["gate"], 2.0)
+    assert floored_rel_err(y, ref) <= F32_TOL
+    y0 = _run(inp, "f32", gate=np.zeros_like(gate))
+    assert np.array_equal(y[gate == 0], y0[gate == 0])
+
+
+SMALL = [  # (M, K, N, r, gate pattern)
+    (75, 520, 300, 128, "random"),
+    (1, 64, 16, 8, "draft"),
+    (1, 64, 16, 8, "verify"),
+    (33, 4096, 1024, 128, "random"),
+    (200, 136, 130, 256, "random"),
+    (130, 256, 384, 128, "draft"),
+    (130, 256, 384, 128, "verify"),
+    (64, 1024, 4096, 128, "seq"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,r,pattern", SMALL)
+def test_bf16_small_shapes(M, K, N, r, pattern):
+    rng = np.random.default_rng(M * 7 + K + N + r)
+    gate = {"random": (rng.random(M) < 0.5).astype(np.uint8), "draft": np.ones(M, np.uint8),
+            "verify": np.zeros(M, np.uint8), "seq": gate_vector(M // 32, 16, 16)}[pattern]
+    inp = gemm_inputs(M, K, N, r, seed=M + K + N, dtype="bf16", gate=gate)
+    say("gemm bf16", M, K, N, r, pattern)
+    y = _run(inp, "bf16")
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], gate, 2.0)
+    err = floored_rel_err(y, ref)
+    assert err <= BF16_TOL, err
+    y0 = _run(inp, "bf16", gate=np.zeros_like(gate))
+    assert np.array_equal(y[gate == 0], y0[gate == 0]), "verify rows must match the all-verify call bitwise"
+
+
+@pytest.mark.gpu
+def test_empty_batch_is_noop():
+    say("gemm empty batch")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((32, 16), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0,), dtype=torch.uint8, device="cuda")
+    assert uno.gated_lora_fwd(x, w, a, b, g).shape == (0, 32)
+
+
+def _full_shape_case(wl_name, proj):
+    wl = WORKLOADS[wl_name]
+    shapes = {n: (K, N) for n, K, N in wl.projections}
+    K, N = shapes[proj]
+    gate = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
+    inp = gemm_inputs(wl.rows, K, N, 128, seed=wl.seed + 17 * [n for n, _, _ in wl.projections].index(proj), dtype="bf16", gate=gate)
+    say("gemm full", wl_name, proj, wl.rows, K, N)
+    y = _run(inp, "bf16")
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, wl.rows - 1, wl.verify_rows, wl.verify_rows - 1],
+                                     rng.choice(wl.rows, size=min(60, wl.rows), replace=False)]))
+    ref = oracle.gated_lora(inp["x"][rows], inp["w"], inp["a"], inp["b"], gate[rows], 2.0)
+    err = floored_rel_err(y[rows], ref)
+    assert err <= BF16_TOL, err
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("proj", ["q", "k", "v", "o", "gate", "up", "down"])
+def test_layer_b1_projection(proj):
+    _full_shape_case("layer_b1", proj)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("proj", ["q", "k", "down"])
+def test_layer_b64_projection(proj):
+    _full_shape_case("layer_b64", proj)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("proj", ["up", "down"])
+def test_serve_b256_projection(proj):
+    _full_shape_case("serve_b256", proj)
+
+
+@pytest.mark.gpu
+def test_deterministic_repeat():
+    inp = gemm_inputs(300, 1024, 512, 128, seed=3, dtype="bf16")
+    say("gemm determinism")
+    assert np.array_equal(_run(inp, "bf16"), _run(inp, "bf16"))
