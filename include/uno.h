@@ -104,11 +104,19 @@ uno_status uno_philox_uniforms(uint64_t seed, uint64_t stream_id, uint64_t offse
  * Rows with gate 0 run exactly the instruction sequence of a call whose gates
  * are all 0, so they are bitwise identical to it.
  *
- * Domain: M >= 0 (M = 0 is a no-op), 1 <= N, 1 <= K; K and N multiples of 8
- * and 16-byte aligned pointers for UNO_BF16; 1 <= r <= 256 and r a multiple
- * of 16; scale finite.  A gate byte other than 0/1 is treated as 1.
+ * Domain: M >= 0 (M = 0 is a no-op), N >= 1, K >= 1, 1 <= r <= 256 and scale
+ * finite.  UNO_BF16 additionally needs K and r multiples of 8, 16-byte
+ * aligned tensors, and every operand under 2 GiB (M*K, N*K < 2^30 elements).
+ * A gate byte other than 0/1 is treated as 1.
  * workspace: device memory of at least uno_gated_lora_workspace_size() bytes
  * (256-byte aligned).
+ *
+ * For UNO_BF16 the call runs three steps, also exported below so that many
+ * projections over the same rows (a layer stack) can plan the rows once:
+ *   uno_segment_rows   rows -> a row plan (stable partition by gate into
+ *                      [verify | draft], each part padded to 32 rows)
+ *   uno_lora_down      T = scale * (x A) on the draft rows (bf16, plan order)
+ *   uno_gated_gemm     y = x W_AR, plus T B on the draft rows
  * ------------------------------------------------------------------------ */
 size_t uno_gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, int32_t dtype);
 uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a,
@@ -116,6 +124,31 @@ uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a,
                               int64_t M, int64_t N, int64_t K, int32_t r, float scale,
                               int32_t dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* Row plan: opaque device buffer of uno_row_plan_size(M) bytes (256-byte
+ * aligned) written by uno_segment_rows from gate [M] (device uint8).  It stays
+ * valid while the gate values are unchanged. */
+size_t uno_row_plan_size(int64_t M);
+uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size_t row_plan_bytes,
+                            hipStream_t stream);
+
+/* LoRA down-projection on draft rows (bf16): t receives scale * (x A) for the
+ * draft rows in plan order, zero rows for padding; t is a device buffer of
+ * uno_lora_t_size(M, r) bytes.  x [M, K], lora_a [r, K].  Same domain as
+ * uno_gated_lora_fwd with UNO_BF16. */
+size_t uno_lora_t_size(int64_t M, int32_t r);
+size_t uno_lora_down_workspace_size(int64_t M, int64_t K, int32_t r);
+uno_status uno_lora_down(const void* x, const void* lora_a, const void* row_plan, void* t, int64_t M,
+                         int64_t K, int32_t r, float scale, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Gated GEMM (bf16): y = x W_AR for every row plus T B for the draft rows of
+ * the plan, T from uno_lora_down with the same plan and rank.  x [M, K],
+ * w [N, K], lora_b [N, r], y [M, N] (must not alias inputs). */
+size_t uno_gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
+uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const void* lora_b,
+                          const void* row_plan, void* y, int64_t M, int64_t N, int64_t K, int32_t r,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Block verification ("The Psi-Spec Sampler" on the aifromscratch.in page:

@@ -15,16 +15,20 @@ Importing the package loads the shared library; there is no CPU fallback.
 from ._lib import (  # noqa: F401
     UNO_BF16,
     UNO_F32,
+    RowPlan,
     UnoError,
     Workspace,
     block_verify,
     block_verify_workspace_size,
     draft_sample,
     draft_sample_workspace_size,
+    gated_gemm,
     gated_lora_fwd,
     gated_lora_workspace_size,
     header_symbols,
     library,
+    lora_down,
+    lora_t_size,
     philox_uniforms,
     residual_add,
     rmsnorm,

@@ -31,6 +31,15 @@ SIGNATURES = {
     "uno_gated_lora_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32, _c_int32]),
     "uno_gated_lora_fwd": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64,
                                       _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_row_plan_size": (_c_size, [_c_int64]),
+    "uno_segment_rows": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_size, _c_ptr]),
+    "uno_lora_t_size": (_c_size, [_c_int64, _c_int32]),
+    "uno_lora_down_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int32]),
+    "uno_lora_down": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int32, _c_float, _c_ptr,
+                                 _c_size, _c_ptr]),
+    "uno_gated_gemm_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32]),
+    "uno_gated_gemm": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int64,
+                                  _c_int32, _c_ptr, _c_size, _c_ptr]),
     "uno_block_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int32]),
     "uno_block_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
                                     _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -168,6 +177,59 @@ def gated_lora_fwd(x, w, lora_a, lora_b, gate, scale=2.0, out=None, workspace=No
     ws = _workspace(workspace, need, x.device)
     _check(_lib.uno_gated_lora_fwd(_ptr(x), _ptr(w), _ptr(lora_a), _ptr(lora_b), _ptr(gate), _ptr(out),
                                    M, N, K, r, float(scale), dt, _ptr(ws), need, _stream(stream)))
+    return out
+
+
+class RowPlan:
+    """Device row plan for a gate vector (uno_segment_rows), reusable across projections."""
+
+    def __init__(self, gate, stream=None):
+        _need_cuda(gate)
+        if gate.dtype != torch.uint8 or gate.dim() != 1:
+            raise TypeError("gate must be a 1-D uint8 tensor")
+        self.M = gate.shape[0]
+        self.gate = gate
+        self.nbytes = int(_lib.uno_row_plan_size(self.M))
+        self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=gate.device)
+        _check(_lib.uno_segment_rows(_ptr(gate), self.M, _ptr(self.buf), self.nbytes, _stream(stream)))
+
+
+def lora_t_size(M, r):
+    return int(_lib.uno_lora_t_size(M, r))
+
+
+def lora_down(x, lora_a, plan, scale=2.0, t=None, workspace=None, stream=None):
+    """T = scale * (x A) on the plan's draft rows (bf16, plan order); returns the T buffer."""
+    _need_cuda(x, lora_a)
+    M, K = x.shape
+    r = lora_a.shape[0]
+    if lora_a.shape != (r, K) or plan.M != M:
+        raise ValueError("shape mismatch: x [M,K], lora_a [r,K], plan over M rows")
+    if t is None:
+        t = torch.empty(lora_t_size(M, r) // 2, dtype=torch.bfloat16, device=x.device)
+    need = int(_lib.uno_lora_down_workspace_size(M, K, r))
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_lora_down(_ptr(x), _ptr(lora_a), _ptr(plan.buf), _ptr(t), M, K, r, float(scale), _ptr(ws), need,
+                              _stream(stream)))
+    return t
+
+
+def gated_gemm(x, w, t, lora_b, plan, out=None, workspace=None, stream=None):
+    """y = x W_AR + T B on the plan's draft rows, T from lora_down with the same plan."""
+    _need_cuda(x, w, t, lora_b)
+    M, K = x.shape
+    N = w.shape[0]
+    r = lora_b.shape[1]
+    if w.shape != (N, K) or lora_b.shape != (N, r) or plan.M != M:
+        raise ValueError("shape mismatch: x [M,K], w [N,K], lora_b [N,r], plan over M rows")
+    if t.numel() * t.element_size() < lora_t_size(M, r):
+        raise ValueError("t buffer too small")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    need = int(_lib.uno_gated_gemm_workspace_size(M, N, K, r))
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_gated_gemm(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), _ptr(out), M, N, K, r,
+                               _ptr(ws), need, _stream(stream)))
     return out
 
 

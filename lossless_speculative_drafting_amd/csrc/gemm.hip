@@ -5,28 +5,37 @@
 // ("Two Decoupled Weight Sets" on the aifromscratch.in page: AR weights for
 // every row, the rank-128 alpha-256 LoRA adapter added on draft rows only.)
 //
-// bf16 path, three steps on the caller's stream:
-//   1. segment_rows   one workgroup: stable partition of the rows by gate into a
-//                     permuted order [verify rows | pad | draft rows | pad], each
-//                     segment padded to a multiple of 32 rows (the MFMA block
-//                     height), so every 32-row block is all-verify or all-draft.
-//   2. T = scale * x_d A   (LoRA down-projection, draft rows only) with the GEMM
-//                     kernel below in "T mode", rounded once to bf16.
-//   3. y = x W_AR (+ T B on draft blocks): MFMA 32x32x16 bf16 tiles of
-//                     BM x 128 x 64 staged through LDS (XOR-swizzled 16-byte
-//                     chunks, double buffered).  Draft 32-row blocks run r/64
-//                     more K-steps with (T, B) after the W_AR K-loop, into the
-//                     same fp32 accumulators; verify blocks skip them, so their
-//                     instruction sequence is the one a call with all gates 0
-//                     runs and their results are bitwise identical to it.
+// bf16 path, three steps on the caller's stream (each also exported on its
+// own so a layer stack can plan the rows once and reuse the plan):
+//   1. segment_rows  one workgroup: stable partition of the rows by gate into a
+//                    permuted order [verify rows | pad | draft rows | pad], each
+//                    segment padded to a multiple of 32 rows (the MFMA block
+//                    height), so every 32-row block is all-verify or all-draft.
+//   2. lora_down     T = scale * x_d A on the draft rows only, with the GEMM
+//                    kernel below in "T mode" (split over K when the tile grid
+//                    is small; fp32 partials summed in split order), rounded
+//                    once to bf16.
+//   3. gated_gemm    y = x W_AR, plus T B on draft blocks: bf16 MFMA 32x32x16
+//                    over BM x BN x 64 workgroup tiles, 4 wavefronts of
+//                    (BM/2) x (BN/2).  Operands are read with buffer loads
+//                    (out-of-range offsets return zero, which pads rows, N and
+//                    K without branches), staged in registers one K-step ahead
+//                    and double-buffered in LDS in XOR-swizzled 16-byte chunks.
+//                    Draft 32-row blocks run r/64 further K-steps with (T, B)
+//                    after the W_AR K-loop, into the same fp32 accumulators;
+//                    verify blocks skip them, so their instruction sequence is
+//                    the one a call with all gates 0 runs, and their results
+//                    are bitwise identical to it.
 // Rows are gathered on load and scattered on store through the permutation.
-// When the tile grid is too small to fill the chip, K is split across
-// workgroups; fp32 partials are summed in split order by a reduce kernel
-// (deterministic).
+// Workgroups are ordered so that each XCD works on a contiguous band of
+// output columns (its L2 then holds that band's weights).
 //
 // fp32 path (correctness path for small problems): plain FMA loops, T kept
 // in fp32.
+#include <stdlib.h>
+
 #include <algorithm>
+#include <type_traits>
 
 #include "uno_device.h"
 #include "uno_internal.h"
@@ -34,10 +43,11 @@
 namespace uno {
 namespace {
 
-constexpr int kBK = 64;       // K per pipeline stage
-constexpr int kBN = 128;      // output columns per workgroup
-constexpr int kRowAlign = 32; // segment padding = MFMA block height
+constexpr int kBK = 64;        // K per pipeline stage
+constexpr int kRowAlign = 32;  // segment padding = MFMA block height
 constexpr int kGemmThreads = 256;
+constexpr uint32_t kOOB = 0x80000000u;       // buffer offset past every range: loads return 0
+constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 struct SegInfo {
     int32_t Mv;      // verify rows
@@ -45,6 +55,11 @@ struct SegInfo {
     int32_t Pv;      // first permuted draft row (Mv rounded up to 32)
     int32_t Md_pad;  // Md rounded up to 32
 };
+
+// Row plan layout: SegInfo at byte 0, perm[rows_cap] at byte 256.
+constexpr size_t kPlanPermOffset = 256;
+
+int64_t rows_cap_for(int64_t M) { return (M + kRowAlign - 1) / kRowAlign * kRowAlign + kRowAlign; }
 
 // ------------------------------------------------------------ segmentation
 constexpr int kSegThreads = 1024;
@@ -101,14 +116,18 @@ __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t
 
 // ------------------------------------------------------------ MFMA GEMM
 struct GemmKArgs {
-    const uint16_t* x;    // activations [*, ldx]
+    const uint16_t* x;    // activations, rows gathered through perm
     int64_t ldx;
+    uint32_t x_bytes;
     const uint16_t* w;    // [N, ldw] (W_AR^T, or A^T in T mode)
     int64_t ldw;
+    uint32_t w_bytes;
     const uint16_t* t;    // T [Md_pad, ldt]
     int64_t ldt;
+    uint32_t t_bytes;
     const uint16_t* lb;   // B^T [N, ldb]
     int64_t ldb;
+    uint32_t b_bytes;
     const int32_t* perm;
     const SegInfo* info;
     uint16_t* y;          // output rows (scattered through perm in main mode)
@@ -119,69 +138,200 @@ struct GemmKArgs {
     int32_t r;
     int32_t splits;
     int64_t k_per_split;
+    int32_t m_tiles, n_tiles;
     float alpha;
 };
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// LDS tile: rows of 64 bf16 (eight 16-byte chunks); chunk c of row r lives at
-// chunk position c ^ (r & 7), which spreads the eight rows a quarter-wave
-// touches over all banks.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// Raw buffer descriptor: base, no stride, byte range, 32-bit format.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<uint32_t>(addr)));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<uint32_t>(addr >> 32)));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+    r.w = kRsrcWord3;
+    return r;
+}
 
-template <int BM, bool TMODE>
-__global__ __launch_bounds__(kGemmThreads, 2) void gated_gemm_kernel(const GemmKArgs a) {
-    constexpr int WM = BM / 2;        // wave tile rows (2 x 2 waves)
-    constexpr int MI = WM / 32;       // 32-row MFMA blocks per wave
-    constexpr int NJ = 2;             // 32-col MFMA blocks per wave (64 columns)
-    constexpr int AR = BM / 32;       // A chunks loaded per thread per stage
-    constexpr int BR = kBN / 32;      // B chunks loaded per thread per stage
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
+// Direct global -> LDS copy of one 16-byte chunk per lane: lane l's chunk lands
+// at LDS byte lds_addr + 16 * l (lds_addr must be wave-uniform); an offset past
+// the buffer's range writes zeros.  Issued as inline assembly so that the
+// compiler does not make every later LDS read wait for it; the kernel places
+// its own vmcnt waits before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
 
-    const SegInfo info = *a.info;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kBN;
-    const int32_t z = blockIdx.z;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    // generic -> LDS address-space conversion (a C-style cast is the spelling clang accepts)
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(p)));
+}
+
+// LDS tile rows hold 64 bf16 (eight 16-byte chunks); chunk c of row r lives at
+// chunk position c ^ s(r) with s(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
+// read has lanes 0..31 on 32 consecutive rows at one chunk; gfx950 serves a
+// 16-byte-per-lane LDS read 16 lanes at a time across 64 banks, and over any
+// 16 consecutive rows the pairs (r & 1, c ^ s(r)) are all distinct, so each
+// 16-lane group touches every bank once (measured: 4 LDS cycles per wave-wide
+// read, against 8 for the plain r & 7 swizzle).
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+    return row * kBK + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 3);
+}
+
+template <int BM, int BN>
+struct TileCfg {
+    static constexpr int WM = BM / 2;          // 2 x 2 wavefronts
+    static constexpr int WN = BN / 2;
+    static constexpr int MI = WM / 32;         // 32x32 MFMA blocks per wavefront
+    static constexpr int NJ = WN / 32;
+    static constexpr int AQ = BM / 32;         // 8-row DMA blocks per wavefront per stage (A)
+    static constexpr int BQ = BN / 32;         // (B)
+    static constexpr int DMA_PER_STAGE = AQ + BQ;
+    static constexpr int STAGE_ELEMS = (BM + BN) * kBK;
+    static constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;
+    static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
+    static_assert(4 * WM * WN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
+};
+
+template <int BM, int BN, bool TMODE>
+__global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_gemm_kernel(const GemmKArgs a) {
+    using C = TileCfg<BM, BN>;
+    constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
+
+    // ---- workgroup -> (m tile, n tile, split), each XCD taking a contiguous band of tiles
+    const int32_t total = a.m_tiles * a.n_tiles * a.splits;
+    int32_t lin = blockIdx.x;
+    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+    const int32_t per_split = a.m_tiles * a.n_tiles;
+    // (integer division is done in vector registers; the results are uniform)
+    const int32_t z = __builtin_amdgcn_readfirstlane(lin / per_split);
+    const int32_t tl = lin - z * per_split;
+    const int32_t nt = __builtin_amdgcn_readfirstlane(tl / a.m_tiles);
+    const int32_t mt = __builtin_amdgcn_readfirstlane(tl - nt * a.m_tiles);
+
+    // segment info is the same for every lane: keep it in scalar registers so
+    // that every decision derived from it is a uniform branch
+    SegInfo info = *a.info;
+    info.Mv = __builtin_amdgcn_readfirstlane(info.Mv);
+    info.Md = __builtin_amdgcn_readfirstlane(info.Md);
+    info.Pv = __builtin_amdgcn_readfirstlane(info.Pv);
+    info.Md_pad = __builtin_amdgcn_readfirstlane(info.Md_pad);
+    const int64_t m0 = static_cast<int64_t>(mt) * BM;
+    const int64_t n0 = static_cast<int64_t>(nt) * BN;
     const int64_t rows_valid = TMODE ? info.Md_pad : static_cast<int64_t>(info.Pv) + info.Md_pad;
-    if (m0 >= rows_valid) return;  // uniform for the block, before any barrier
+    if (m0 >= rows_valid) return;  // uniform for the workgroup, before any barrier
 
     const int tid = threadIdx.x;
-    const int lc = tid & 7;
-    const int lr = tid >> 3;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
+    const int lane = tid % kWave;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
 
-    // per-thread source rows for the A operand (x rows, and T rows for the extension)
-    int64_t a_src[AR];
-    int64_t a_trow[AR];
+    const i32x4 rx = make_rsrc(a.x, a.x_bytes);
+    const i32x4 rw = make_rsrc(a.w, a.w_bytes);
+
+    // DMA assignment: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the A
+    // tile (and likewise of B) in 8-row blocks; lane l takes row l/8 of a block
+    // and the logical chunk that belongs at physical position l%8.
+    const int lrow = lane >> 3;
+    const uint32_t kc0 = static_cast<uint32_t>(((lane & 7) ^ lrow) * 16);        // even blocks
+    const uint32_t kc1 = static_cast<uint32_t>(((lane & 7) ^ lrow ^ 1) * 16);    // odd blocks
+    // per-lane byte offsets of each DMA block at K = 0 (row offset + chunk offset)
+    uint32_t xoff[AQ], woff[BQ];
 #pragma unroll
-    for (int i = 0; i < AR; ++i) {
-        const int64_t p = m0 + lr + 32 * i;
+    for (int q = 0; q < AQ; ++q) {
+        const int64_t p = m0 + wave * (BM / 4) + q * 8 + lrow;
+        int64_t src;
         if constexpr (TMODE) {
-            a_src[i] = (p < info.Md) ? a.perm[info.Pv + p] : -1;
-            a_trow[i] = -1;
+            src = (p < info.Md) ? a.perm[info.Pv + p] : -1;
         } else {
-            a_src[i] = (p < rows_valid) ? a.perm[p] : -1;
-            a_trow[i] = (p >= info.Pv && p < static_cast<int64_t>(info.Pv) + info.Md_pad) ? p - info.Pv : -1;
+            src = (p < rows_valid) ? a.perm[p] : -1;
         }
+        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + ((q & 1) ? kc1 : kc0);
     }
-    bool b_ok[BR];
 #pragma unroll
-    for (int j = 0; j < BR; ++j) b_ok[j] = (n0 + lr + 32 * j) < a.N;
+    for (int q = 0; q < BQ; ++q) {
+        const int64_t n = n0 + wave * (BN / 4) + q * 8 + lrow;
+        woff[q] = (n < a.N ? static_cast<uint32_t>(n * a.ldw * 2) : kOOB) + ((q & 1) ? kc1 : kc0);
+    }
+    const uint32_t lds_base = lds_addr_of(smem);
+    auto sA_addr = [&](int buf) __attribute__((always_inline)) {
+        return lds_base + static_cast<uint32_t>(buf * C::STAGE_ELEMS * 2);
+    };
+    auto sB_addr = [&](int buf) __attribute__((always_inline)) {
+        return lds_base + static_cast<uint32_t>((buf * C::STAGE_ELEMS + BM * kBK) * 2);
+    };
 
     const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
     const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
     const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
-    const bool tile_has_draft = !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
+    const bool tile_has_draft =
+        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
     const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
-    const int nk = nk_main + (ext ? (a.r + kBK - 1) / kBK : 0);
+    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
+    const int nk = nk_main + nk_ext;
 
-    const int wave = tid / kWave;
-    const int lane = tid % kWave;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    bool blk_draft[MI];
+    // Copy K-stage `it` into LDS buffer `buf`.  Main stages read x / W_AR rows;
+    // extension stages read T / B rows.  A row offset of kOOB plus any in-range
+    // K offset stays out of range, so padding needs no select; chunks past the
+    // end of K are masked explicitly.
+    auto issue_stage = [&](int it, int buf) __attribute__((always_inline)) {
+        const uint32_t la = sA_addr(buf) + static_cast<uint32_t>(wave * (BM / 4) * kBK * 2);
+        const uint32_t lb = sB_addr(buf) + static_cast<uint32_t>(wave * (BN / 4) * kBK * 2);
+        if (it < nk_main) {
+            const int64_t k0 = kb + static_cast<int64_t>(it) * kBK;
+            const uint32_t kbytes = static_cast<uint32_t>(k0 * 2);
+            if (k0 + kBK <= ke) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) blk_draft[i] = !TMODE && (m0 + wm * WM + 32 * i >= info.Pv);
+                for (int q = 0; q < AQ; ++q) dma16(la + q * 8 * kBK * 2, xoff[q] + kbytes, rx);
+#pragma unroll
+                for (int q = 0; q < BQ; ++q) dma16(lb + q * 8 * kBK * 2, woff[q] + kbytes, rw);
+            } else {  // last stage runs past the end of K: mask the trailing chunks
+#pragma unroll
+                for (int q = 0; q < AQ; ++q) {
+                    const uint32_t kc = (q & 1) ? kc1 : kc0;
+                    dma16(la + q * 8 * kBK * 2, (k0 + kc / 2 < ke) ? xoff[q] + kbytes : kOOB, rx);
+                }
+#pragma unroll
+                for (int q = 0; q < BQ; ++q) {
+                    const uint32_t kc = (q & 1) ? kc1 : kc0;
+                    dma16(lb + q * 8 * kBK * 2, (k0 + kc / 2 < ke) ? woff[q] + kbytes : kOOB, rw);
+                }
+            }
+        } else {
+            const int k0 = (it - nk_main) * kBK;
+            const i32x4 rt = make_rsrc(a.t, a.t_bytes);
+            const i32x4 rbb = make_rsrc(a.lb, a.b_bytes);
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) {
+                const uint32_t kc = (q & 1) ? kc1 : kc0;
+                const int64_t trow = m0 + wave * (BM / 4) + q * 8 + lrow - info.Pv;
+                const bool ok = trow >= 0 && trow < info.Md_pad && k0 + static_cast<int>(kc / 2) < a.r;
+                dma16(la + q * 8 * kBK * 2,
+                      ok ? static_cast<uint32_t>(trow * a.ldt * 2 + k0 * 2) + kc : kOOB, rt);
+            }
+#pragma unroll
+            for (int q = 0; q < BQ; ++q) {
+                const uint32_t kc = (q & 1) ? kc1 : kc0;
+                const int64_t n = n0 + wave * (BN / 4) + q * 8 + lrow;
+                const bool ok = n < a.N && k0 + static_cast<int>(kc / 2) < a.r;
+                dma16(lb + q * 8 * kBK * 2, ok ? static_cast<uint32_t>(n * a.ldb * 2 + k0 * 2) + kc : kOOB, rbb);
+            }
+        }
+    };
 
     f32x16 acc[MI][NJ];
 #pragma unroll
@@ -191,83 +341,131 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gated_gemm_kernel(const GemmK
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    uint4 ra[AR], rb[BR];
-    auto load_stage = [&](int it) {
-        const uint4 zero = make_uint4(0, 0, 0, 0);
-        if (it < nk_main) {
-            const int64_t k = kb + static_cast<int64_t>(it) * kBK + lc * 8;
-            const bool kin = k < ke;
+    // Fragments are double-buffered in registers (set 0 / set 1): the reads for
+    // sub-step kk+1 are issued before the MFMAs of sub-step kk (sched_barrier
+    // fences keep the compiler from sinking them to their uses).  The hand-off
+    // to the next stage -- wait for its copy, barrier, start the copy of the
+    // stage after it, first fragment reads -- sits before the last sub-step's
+    // MFMAs, so the MFMA pipe stays busy meanwhile.
+    bf16x8 af[2][MI], bfr[2][NJ];
+    auto read_frags = [&](int buf, int kk, int set) __attribute__((always_inline)) {
+        const uint16_t* sa = smem + buf * C::STAGE_ELEMS;
+        const uint16_t* sb = sa + BM * kBK;
+        const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < AR; ++i) ra[i] = (kin && a_src[i] >= 0) ? ldg16(a.x + a_src[i] * a.ldx + k) : zero;
+        for (int i = 0; i < MI; ++i) {
+            const int row = wm * C::WM + i * 32 + (lane & 31);
+            af[set][i] = *reinterpret_cast<const bf16x8*>(&sa[lds_off(row, chunk)]);
+        }
 #pragma unroll
-            for (int j = 0; j < BR; ++j)
-                rb[j] = (kin && b_ok[j]) ? ldg16(a.w + (n0 + lr + 32 * j) * a.ldw + k) : zero;
-        } else {
-            const int64_t k = static_cast<int64_t>(it - nk_main) * kBK + lc * 8;
-            const bool kin = k < a.r;
-#pragma unroll
-            for (int i = 0; i < AR; ++i) ra[i] = (kin && a_trow[i] >= 0) ? ldg16(a.t + a_trow[i] * a.ldt + k) : zero;
-#pragma unroll
-            for (int j = 0; j < BR; ++j)
-                rb[j] = (kin && b_ok[j]) ? ldg16(a.lb + (n0 + lr + 32 * j) * a.ldb + k) : zero;
+        for (int j = 0; j < NJ; ++j) {
+            const int row = wn * C::WN + j * 32 + (lane & 31);
+            bfr[set][j] = *reinterpret_cast<const bf16x8*>(&sb[lds_off(row, chunk)]);
         }
     };
-    auto store_stage = [&](int buf) {
+    // Extension stages need no per-block test: verify rows read zero T rows
+    // (out-of-range copies write zeros), so their MFMAs add an exact zero to
+    // accumulators that started at +0 and therefore can never be -0 (round to
+    // nearest) -- the verify rows keep the bits of a call with all gates 0.
+    auto mfma_step = [&](int set, auto) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < AR; ++i) {
-            const int row = lr + 32 * i;
-            *reinterpret_cast<uint4*>(&sA[buf][lds_off(row, lc)]) = ra[i];
-        }
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < BR; ++j) {
-            const int row = lr + 32 * j;
-            *reinterpret_cast<uint4*>(&sB[buf][lds_off(row, lc)]) = rb[j];
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
+    };
+    // a stage followed by another: its copy was started one stage earlier
+    auto body_next = [&](int it, auto ext_c) __attribute__((always_inline)) {
+        const int buf = it & 1;
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+            read_frags(buf, kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(kk & 1, ext_c);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        wait_vmcnt<0>();  // this wavefront's copy of stage it+1 has landed
+        __syncthreads();  // ... every wavefront's; and buffer `buf` is no longer read
+        if (it + 2 < nk) issue_stage(it + 2, buf);
+        read_frags(buf ^ 1, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step((kBK / 16 - 1) & 1, ext_c);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto body_last = [&](int it, auto ext_c) __attribute__((always_inline)) {
+        const int buf = it & 1;
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
+            read_frags(buf, kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(kk & 1, ext_c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_step((kBK / 16 - 1) & 1, ext_c);
     };
 
     if (nk > 0) {
-        load_stage(0);
-        store_stage(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-        const int buf = it & 1;
-        const bool has_next = it + 1 < nk;
-        if (has_next) load_stage(it + 1);
-        const bool is_ext = it >= nk_main;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int chunk = kk * 2 + (lane >> 5);
-            bf16x8 af[MI], bfr[NJ];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm * WM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][lds_off(row, chunk)]);
-            }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int row = wn * 64 + j * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][lds_off(row, chunk)]);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                if (is_ext && !blk_draft[i]) continue;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            }
+        issue_stage(0, 0);
+        if (nk > 1) {
+            issue_stage(1, 1);
+            wait_vmcnt<C::DMA_PER_STAGE>();  // stage 0 landed; stage 1 may still be in flight
+        } else {
+            wait_vmcnt<0>();
         }
-        if (has_next) store_stage(buf ^ 1);
         __syncthreads();
+        read_frags(0, 0, 0);
+        // stage count is uniform; keep it scalar
+        const int nks = __builtin_amdgcn_readfirstlane(nk);
+        for (int it = 0; it < nks - 1; ++it) body_next(it, std::false_type{});
+        body_last(nks - 1, std::false_type{});
     }
 
-    // epilogue: lane holds D[row][col] with col = lane % 32 and
-    // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4 for v = 0..15
+    // ---- epilogue
+    // lane holds D[row][col] of each 32x32 block with col = lane % 32 and
+    // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4, v = 0..15.
+    if (a.splits == 1 && (a.N % 8) == 0) {
+        // Stage the wavefront's bf16 tile through LDS, then write whole 16-byte
+        // row segments (coalesced), scattering rows through the permutation.
+        __syncthreads();  // all stage buffers are free
+        // staging layout: [WM rows][WN cols] bf16; rows r and r+4 (written by one
+        // instruction) are offset by 32 columns (XOR) to land in different banks
+        uint16_t* st = smem + wave * C::WM * C::WN;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const int c = (j * 32 + (lane & 31)) ^ (((r >> 2) & 1) << 5);
+                    st[r * C::WN + c] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's staging writes are done
+        constexpr int CPR = C::WN / 8;  // 16-byte chunks per wavefront row
+        for (int e = lane; e < C::WM * CPR; e += kWave) {
+            const int r = e / CPR;
+            const int c = e - r * CPR;
+            const int64_t p = m0 + wm * C::WM + r;
+            const int64_t n = n0 + wn * C::WN + c * 8;
+            if (p >= rows_valid || n >= a.N) continue;
+            int64_t orow;
+            if constexpr (TMODE) {
+                orow = p;
+            } else {
+                orow = a.perm[p];
+            }
+            if (orow < 0) continue;
+            const int pc = c ^ (((r >> 2) & 1) << 2);
+            *reinterpret_cast<uint4*>(a.y + orow * a.ldy + n) =
+                *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int64_t p = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int64_t p = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (p >= rows_valid) continue;
             if (a.splits == 1) {
                 int64_t orow;
@@ -279,14 +477,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gated_gemm_kernel(const GemmK
                 if (orow < 0) continue;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+                    const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
                     if (n < a.N) a.y[orow * a.ldy + n] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
                 }
             } else {
                 float* prow = a.partial + (static_cast<int64_t>(z) * a.rows_cap + p) * a.N;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+                    const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
                     if (n < a.N) prow[n] = acc[i][j][v];
                 }
             }
@@ -317,8 +515,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------ fp32 path
-// T[m, j] = scale * sum_k x[m, k] a[j, k] for draft rows (computed for all rows,
-// read only for draft rows).
+// T[m, j] = scale * sum_k x[m, k] a[j, k] for draft rows (read only for draft rows).
 __global__ __launch_bounds__(256) void lora_t_f32_kernel(const float* __restrict__ x, const float* __restrict__ la,
                                                         const uint8_t* __restrict__ gate, int64_t M, int64_t K,
                                                         int32_t r, float scale, float* __restrict__ t) {
@@ -349,133 +546,230 @@ __global__ __launch_bounds__(256) void gated_gemm_f32_kernel(const float* __rest
 }
 
 // ------------------------------------------------------------ planning
-struct GemmPlan {
-    int bm;
-    int64_t rows_cap;     // permuted rows (both segments padded)
-    int64_t m_tiles;
-    int64_t n_tiles;
-    int32_t splits;
-    int64_t kps;
-    int64_t t_m_tiles;
-    int32_t t_splits;
-    int64_t t_kps;
-    size_t off_info, off_perm, off_t, off_part, off_tpart, total;
+struct Tile {
+    int bm, bn;
 };
 
-constexpr int64_t kTargetWorkgroups = 256;
+constexpr int kNumCUs = 256;
+
+// Workgroups that run at once per CU for a tile shape (LDS-limited).
+int occupancy(Tile t) { return (2 * (t.bm + t.bn) * kBK * 2 > 80 * 1024) ? 1 : 2; }
+
+// Relative MFMA efficiency of a workgroup tile (wave tile size sets the LDS
+// traffic per MFMA); used only to rank tile shapes.
+double tile_eff(Tile t) {
+    const int wt = (t.bm / 2) * (t.bn / 2);
+    if (wt >= 128 * 128) return 1.0;
+    if (wt >= 128 * 64) return 0.85;
+    if (wt >= 64 * 64) return 0.7;
+    return 0.45;
+}
+
+Tile env_tile() {
+    const char* s = getenv("UNO_GEMM_TILE");
+    Tile t{0, 0};
+    if (s && sscanf(s, "%dx%d", &t.bm, &t.bn) == 2) return t;
+    return Tile{0, 0};
+}
+
+bool tile_supported(Tile t) {
+    return (t.bm == 64 && t.bn == 128) || (t.bm == 128 && t.bn == 128) || (t.bm == 128 && t.bn == 256) ||
+           (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
+}
+
+Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K) {
+    const Tile forced = env_tile();
+    if (tile_supported(forced)) return forced;
+    const Tile cands[] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}, {64, 128}};
+    Tile best{64, 128};
+    double best_t = 1e300;
+    for (const Tile& t : cands) {
+        const int64_t tiles = ((rows_cap + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        const int64_t slots = static_cast<int64_t>(kNumCUs) * occupancy(t);
+        const int64_t waves = (tiles + slots - 1) / slots;
+        // time ~ waves x (tile work / efficiency / occupancy share)
+        const double est = static_cast<double>(waves) * t.bm * t.bn * static_cast<double>(K) /
+                           (tile_eff(t) * occupancy(t));
+        if (est < best_t * 0.999) {
+            best_t = est;
+            best = t;
+        }
+    }
+    return best;
+}
 
 void choose_split(int64_t tiles, int64_t K, int32_t& splits, int64_t& kps) {
     int64_t s = 1;
-    if (tiles < kTargetWorkgroups) {
-        s = (kTargetWorkgroups + tiles - 1) / tiles;
+    if (tiles < kNumCUs / 2) {
+        s = (kNumCUs + tiles - 1) / tiles;
         s = std::min<int64_t>(s, std::max<int64_t>(1, K / (4 * kBK)));
     }
     kps = ((K + s - 1) / s + kBK - 1) / kBK * kBK;
     splits = static_cast<int32_t>((K + kps - 1) / kps);
 }
 
-GemmPlan make_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t r) {
+struct GemmPlan {
+    Tile tile;
+    int64_t rows_cap, m_tiles, n_tiles;
+    int32_t splits;
+    int64_t kps;
+    size_t partial_bytes;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode) {
     GemmPlan p{};
-    p.rows_cap = (M + kRowAlign - 1) / kRowAlign * kRowAlign + kRowAlign;
-    p.bm = (p.rows_cap <= 128) ? 64 : 128;
-    p.m_tiles = (p.rows_cap + p.bm - 1) / p.bm;
-    p.n_tiles = (N + kBN - 1) / kBN;
+    p.rows_cap = rows_cap_for(M);
+    p.tile = tmode ? Tile{128, 128} : choose_tile(p.rows_cap, N, K);
+    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128};
+    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128};
+    p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
+    p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
     choose_split(p.m_tiles * p.n_tiles, K, p.splits, p.kps);
-    p.t_m_tiles = p.m_tiles;
-    choose_split(p.t_m_tiles * ((r + kBN - 1) / kBN), K, p.t_splits, p.t_kps);
-    size_t off = 0;
-    p.off_info = off;
-    off = align_up(off + sizeof(SegInfo), kWorkspaceAlign);
-    p.off_perm = off;
-    off = align_up(off + static_cast<size_t>(p.rows_cap) * sizeof(int32_t), kWorkspaceAlign);
-    p.off_t = off;
-    off = align_up(off + static_cast<size_t>(p.rows_cap) * r * sizeof(uint16_t), kWorkspaceAlign);
-    p.off_part = off;
-    if (p.splits > 1) off = align_up(off + static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float), kWorkspaceAlign);
-    p.off_tpart = off;
-    if (p.t_splits > 1) off = align_up(off + static_cast<size_t>(p.t_splits) * p.rows_cap * r * sizeof(float), kWorkspaceAlign);
-    p.total = off;
+    p.partial_bytes = p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float),
+                                              kWorkspaceAlign)
+                                   : 0;
     return p;
 }
 
-size_t f32_workspace(int64_t M, int32_t r) { return align_up(static_cast<size_t>(M) * r * sizeof(float), kWorkspaceAlign); }
+template <int BM, int BN, bool TMODE>
+void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, TMODE>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kGemmThreads), 0, stream, ka);
+}
 
-template <int BM>
-hipError_t launch_bf16(const GemmProblem& pr, const GemmPlan& p, char* ws, hipStream_t stream) {
-    SegInfo* info = reinterpret_cast<SegInfo*>(ws + p.off_info);
-    int32_t* perm = reinterpret_cast<int32_t*>(ws + p.off_perm);
-    uint16_t* T = reinterpret_cast<uint16_t*>(ws + p.off_t);
-    float* part = reinterpret_cast<float*>(ws + p.off_part);
-    float* tpart = reinterpret_cast<float*>(ws + p.off_tpart);
-
-    hipLaunchKernelGGL(segment_rows_kernel, dim3(1), dim3(kSegThreads), 0, stream, pr.gate, pr.M, p.rows_cap, perm,
-                       info);
-
-    // T = scale * x_d A  (bf16)
-    GemmKArgs ta{};
-    ta.x = static_cast<const uint16_t*>(pr.x);
-    ta.ldx = pr.K;
-    ta.w = static_cast<const uint16_t*>(pr.a);
-    ta.ldw = pr.K;
-    ta.perm = perm;
-    ta.info = info;
-    ta.y = T;
-    ta.ldy = pr.r;
-    ta.partial = tpart;
-    ta.rows_cap = p.rows_cap;
-    ta.N = pr.r;
-    ta.K = pr.K;
-    ta.r = 0;
-    ta.splits = p.t_splits;
-    ta.k_per_split = p.t_kps;
-    ta.alpha = pr.scale;
-    const dim3 tgrid(static_cast<uint32_t>((pr.r + kBN - 1) / kBN), static_cast<uint32_t>(p.t_m_tiles),
-                     static_cast<uint32_t>(p.t_splits));
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, true>), tgrid, dim3(kGemmThreads), 0, stream, ta);
-    if (p.t_splits > 1) {
-        hipLaunchKernelGGL((splitk_reduce_kernel<true>), dim3(256), dim3(256), 0, stream, tpart, p.t_splits,
-                           p.rows_cap, static_cast<int64_t>(pr.r), info, perm, pr.scale, T,
-                           static_cast<int64_t>(pr.r));
+template <bool TMODE>
+void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
+    ka.m_tiles = static_cast<int32_t>(p.m_tiles);
+    ka.n_tiles = static_cast<int32_t>(p.n_tiles);
+    ka.splits = p.splits;
+    ka.k_per_split = p.kps;
+    ka.rows_cap = p.rows_cap;
+    const int64_t blocks = p.m_tiles * p.n_tiles * p.splits;
+    const Tile t = p.tile;
+    if constexpr (TMODE) {
+        if (t.bm == 128) launch_tile<128, 128, true>(ka, blocks, stream);
+        else launch_tile<64, 128, true>(ka, blocks, stream);
+    } else {
+        if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, false>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, false>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, false>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128) launch_tile<128, 128, false>(ka, blocks, stream);
+        else launch_tile<64, 128, false>(ka, blocks, stream);
     }
-
-    GemmKArgs ma{};
-    ma.x = static_cast<const uint16_t*>(pr.x);
-    ma.ldx = pr.K;
-    ma.w = static_cast<const uint16_t*>(pr.w);
-    ma.ldw = pr.K;
-    ma.t = T;
-    ma.ldt = pr.r;
-    ma.lb = static_cast<const uint16_t*>(pr.b);
-    ma.ldb = pr.r;
-    ma.perm = perm;
-    ma.info = info;
-    ma.y = static_cast<uint16_t*>(pr.y);
-    ma.ldy = pr.N;
-    ma.partial = part;
-    ma.rows_cap = p.rows_cap;
-    ma.N = pr.N;
-    ma.K = pr.K;
-    ma.r = pr.r;
-    ma.splits = p.splits;
-    ma.k_per_split = p.kps;
-    ma.alpha = 1.0f;
-    const dim3 grid(static_cast<uint32_t>(p.n_tiles), static_cast<uint32_t>(p.m_tiles),
-                    static_cast<uint32_t>(p.splits));
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, false>), grid, dim3(kGemmThreads), 0, stream, ma);
     if (p.splits > 1) {
-        const int64_t elems = p.rows_cap * pr.N;
+        const int64_t elems = p.rows_cap * ka.N;
         const uint32_t rg = static_cast<uint32_t>(std::min<int64_t>(4096, (elems + 255) / 256));
-        hipLaunchKernelGGL((splitk_reduce_kernel<false>), dim3(rg), dim3(256), 0, stream, part, p.splits,
-                           p.rows_cap, pr.N, info, perm, 1.0f, static_cast<uint16_t*>(pr.y), pr.N);
+        hipLaunchKernelGGL((splitk_reduce_kernel<TMODE>), dim3(rg), dim3(256), 0, stream, ka.partial, p.splits,
+                           p.rows_cap, ka.N, ka.info, ka.perm, ka.alpha, ka.y, ka.ldy);
     }
-    return hipGetLastError();
+}
+
+const SegInfo* plan_info(const void* plan) { return static_cast<const SegInfo*>(plan); }
+const int32_t* plan_perm(const void* plan) {
+    return reinterpret_cast<const int32_t*>(static_cast<const char*>(plan) + kPlanPermOffset);
 }
 
 }  // namespace
 
+// ---------------------------------------------------------------- a1: row plan
+size_t row_plan_bytes(int64_t M) {
+    return align_up(kPlanPermOffset + static_cast<size_t>(rows_cap_for(M)) * sizeof(int32_t), kWorkspaceAlign);
+}
+
+hipError_t segment_rows_launch(const uint8_t* gate, int64_t M, void* plan, hipStream_t stream) {
+    hipLaunchKernelGGL(segment_rows_kernel, dim3(1), dim3(kSegThreads), 0, stream, gate, M, rows_cap_for(M),
+                       reinterpret_cast<int32_t*>(static_cast<char*>(plan) + kPlanPermOffset),
+                       static_cast<SegInfo*>(plan));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- a2: LoRA down-projection
+size_t lora_t_bytes(int64_t M, int32_t r) {
+    return align_up(static_cast<size_t>(rows_cap_for(M)) * r * sizeof(uint16_t), kWorkspaceAlign);
+}
+
+size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r) { return plan_gemm(M, r, K, true).partial_bytes; }
+
+hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan, void* t, int64_t M, int64_t K,
+                            int32_t r, float scale, void* ws, hipStream_t stream) {
+    const GemmPlan p = plan_gemm(M, r, K, true);
+    GemmKArgs ka{};
+    ka.x = static_cast<const uint16_t*>(x);
+    ka.ldx = K;
+    ka.x_bytes = static_cast<uint32_t>(M * K * 2);
+    ka.w = static_cast<const uint16_t*>(lora_a);
+    ka.ldw = K;
+    ka.w_bytes = static_cast<uint32_t>(static_cast<int64_t>(r) * K * 2);
+    ka.perm = plan_perm(plan);
+    ka.info = plan_info(plan);
+    ka.y = static_cast<uint16_t*>(t);
+    ka.ldy = r;
+    ka.partial = static_cast<float*>(ws);
+    ka.N = r;
+    ka.K = K;
+    ka.r = 0;
+    ka.alpha = scale;
+    launch_gemm<true>(p, ka, stream);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- a3: gated GEMM
+size_t gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K) { return plan_gemm(M, N, K, false).partial_bytes; }
+
+hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
+                             void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* ws, hipStream_t stream) {
+    const GemmPlan p = plan_gemm(M, N, K, false);
+    GemmKArgs ka{};
+    ka.x = static_cast<const uint16_t*>(x);
+    ka.ldx = K;
+    ka.x_bytes = static_cast<uint32_t>(M * K * 2);
+    ka.w = static_cast<const uint16_t*>(w);
+    ka.ldw = K;
+    ka.w_bytes = static_cast<uint32_t>(N * K * 2);
+    ka.t = static_cast<const uint16_t*>(t);
+    ka.ldt = r;
+    ka.t_bytes = static_cast<uint32_t>(rows_cap_for(M) * r * 2);
+    ka.lb = static_cast<const uint16_t*>(lora_b);
+    ka.ldb = r;
+    ka.b_bytes = static_cast<uint32_t>(N * r * 2);
+    ka.perm = plan_perm(plan);
+    ka.info = plan_info(plan);
+    ka.y = static_cast<uint16_t*>(y);
+    ka.ldy = N;
+    ka.partial = static_cast<float*>(ws);
+    ka.N = N;
+    ka.K = K;
+    ka.r = r;
+    ka.alpha = 1.0f;
+    launch_gemm<false>(p, ka, stream);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- full projection
+namespace {
+struct FwdLayout {
+    size_t plan, t, down_ws, gemm_ws, total;
+};
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+    FwdLayout l{};
+    size_t off = 0;
+    l.plan = off;
+    off += row_plan_bytes(M);
+    l.t = off;
+    off += lora_t_bytes(M, r);
+    l.down_ws = off;
+    off += align_up(lora_down_workspace_size(M, K, r), kWorkspaceAlign);
+    l.gemm_ws = off;
+    off += align_up(gated_gemm_workspace_size(M, N, K), kWorkspaceAlign);
+    l.total = off;
+    return l;
+}
+size_t f32_workspace(int64_t M, int32_t r) { return align_up(static_cast<size_t>(M) * r * sizeof(float), kWorkspaceAlign); }
+}  // namespace
+
 size_t gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, bool bf16) {
     if (!bf16) return f32_workspace(M, r);
-    return make_gemm_plan(M, N, K, r).total;
+    return fwd_layout(M, N, K, r).total;
 }
 
 hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -494,10 +788,14 @@ hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, h
                            static_cast<float*>(pr.y));
         return hipGetLastError();
     }
-    const GemmPlan p = make_gemm_plan(pr.M, pr.N, pr.K, pr.r);
+    const FwdLayout l = fwd_layout(pr.M, pr.N, pr.K, pr.r);
     char* base = static_cast<char*>(ws);
-    if (p.bm == 64) return launch_bf16<64>(pr, p, base, stream);
-    return launch_bf16<128>(pr, p, base, stream);
+    hipError_t e = segment_rows_launch(pr.gate, pr.M, base + l.plan, stream);
+    if (e != hipSuccess) return e;
+    e = lora_down_launch(pr.x, pr.a, base + l.plan, base + l.t, pr.M, pr.K, pr.r, pr.scale, base + l.down_ws, stream);
+    if (e != hipSuccess) return e;
+    return gated_gemm_launch(pr.x, pr.w, base + l.t, pr.b, base + l.plan, pr.y, pr.M, pr.N, pr.K, pr.r,
+                             base + l.gemm_ws, stream);
 }
 
 }  // namespace uno

@@ -90,8 +90,10 @@ static uno_status check_gemm(int64_t M, int64_t N, int64_t K, int32_t r, int32_t
         if (K % 8 != 0) return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs K %% 8 == 0 (got %lld)", static_cast<long long>(K));
         if (r % 8 != 0) return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs r %% 8 == 0 (got %d)", r);
         const int64_t rows_cap = (M + 31) / 32 * 32 + 32;
-        if ((rows_cap + 63) / 64 > kMaxGridYZ) return fail(UNO_ERR_UNSUPPORTED, "M too large for the tile grid");
-        if ((N + 127) / 128 > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "N too large for the tile grid");
+        if (M * K >= (1LL << 30) || N * K >= (1LL << 30) || rows_cap * r >= (1LL << 30))
+            return fail(UNO_ERR_UNSUPPORTED, "bf16 operands must stay under 2^30 elements each");
+        if (((rows_cap + 63) / 64) * ((N + 127) / 128) > kMaxGridX)
+            return fail(UNO_ERR_UNSUPPORTED, "problem too large for the tile grid");
     } else {
         if (M * N > kMaxGridX * 256 || M * r > kMaxGridX * 256) return fail(UNO_ERR_UNSUPPORTED, "problem too large for the fp32 path");
     }
@@ -127,6 +129,73 @@ uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a, 
     if (st != UNO_OK) return st;
     uno::GemmProblem p{x, w, lora_a, lora_b, gate, y, M, N, K, r, scale, dtype == UNO_BF16};
     return from_hip(uno::gated_lora_launch(p, workspace, workspace_bytes, stream), "gated lora launch");
+}
+
+// ------------------------------------------------------------------ split projection steps
+size_t uno_row_plan_size(int64_t M) {
+    if (M < 0 || M > 2147483647LL - 64) return 0;
+    ok();
+    return uno::row_plan_bytes(M);
+}
+
+uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size_t row_plan_bytes,
+                            hipStream_t stream) {
+    if (M < 0 || M > 2147483647LL - 64) return fail(UNO_ERR_INVALID_ARG, "M must be in [0, 2^31 - 64)");
+    if (row_plan == nullptr) return fail(UNO_ERR_INVALID_ARG, "row_plan is null");
+    if (!aligned256(row_plan)) return fail(UNO_ERR_INVALID_ARG, "row_plan must be 256-byte aligned");
+    if (row_plan_bytes < uno::row_plan_bytes(M))
+        return fail(UNO_ERR_WORKSPACE, "row_plan has %zu bytes, %zu required", row_plan_bytes, uno::row_plan_bytes(M));
+    if (M > 0 && gate == nullptr) return fail(UNO_ERR_INVALID_ARG, "gate is null");
+    return from_hip(uno::segment_rows_launch(gate, M, row_plan, stream), "segment rows launch");
+}
+
+size_t uno_lora_t_size(int64_t M, int32_t r) {
+    if (check_gemm(M, 8, 8, r, UNO_BF16) != UNO_OK) return 0;
+    ok();
+    return uno::lora_t_bytes(M, r);
+}
+
+size_t uno_lora_down_workspace_size(int64_t M, int64_t K, int32_t r) {
+    if (check_gemm(M, 8, K, r, UNO_BF16) != UNO_OK) return 0;
+    ok();
+    return uno::lora_down_workspace_size(M, K, r);
+}
+
+uno_status uno_lora_down(const void* x, const void* lora_a, const void* row_plan, void* t, int64_t M, int64_t K,
+                         int32_t r, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_gemm(M, 8, K, r, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (!std::isfinite(scale)) return fail(UNO_ERR_INVALID_ARG, "scale must be finite");
+    if (M == 0) return ok();
+    if (!x || !lora_a || !row_plan || !t) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(lora_a) || !aligned16(t) || !aligned256(row_plan))
+        return fail(UNO_ERR_INVALID_ARG, "x, lora_a and t must be 16-byte aligned, row_plan 256-byte aligned");
+    st = check_workspace(workspace, workspace_bytes, uno::lora_down_workspace_size(M, K, r));
+    if (st != UNO_OK) return st;
+    return from_hip(uno::lora_down_launch(x, lora_a, row_plan, t, M, K, r, scale, workspace, stream),
+                    "lora down launch");
+}
+
+size_t uno_gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
+    if (check_gemm(M, N, K, r, UNO_BF16) != UNO_OK) return 0;
+    ok();
+    return uno::gated_gemm_workspace_size(M, N, K);
+}
+
+uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const void* lora_b, const void* row_plan,
+                          void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_gemm(M, N, K, r, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (M == 0) return ok();
+    if (!x || !w || !t || !lora_b || !row_plan || !y) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(t) || !aligned16(lora_b) || !aligned16(y) ||
+        !aligned256(row_plan))
+        return fail(UNO_ERR_INVALID_ARG, "tensors must be 16-byte aligned, row_plan 256-byte aligned");
+    st = check_workspace(workspace, workspace_bytes, uno::gated_gemm_workspace_size(M, N, K));
+    if (st != UNO_OK) return st;
+    return from_hip(uno::gated_gemm_launch(x, w, t, lora_b, row_plan, y, M, N, K, r, workspace, stream),
+                    "gated gemm launch");
 }
 
 // ------------------------------------------------------------------ verification

@@ -59,6 +59,17 @@ struct GemmProblem {
 size_t gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, bool bf16);
 hipError_t gated_lora_launch(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// The three steps of the bf16 projection, exported separately.
+size_t row_plan_bytes(int64_t M);
+hipError_t segment_rows_launch(const uint8_t* gate, int64_t M, void* plan, hipStream_t stream);
+size_t lora_t_bytes(int64_t M, int32_t r);
+size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r);
+hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan, void* t, int64_t M, int64_t K,
+                            int32_t r, float scale, void* ws, hipStream_t stream);
+size_t gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
+                             void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* ws, hipStream_t stream);
+
 // ---- layer glue ----------------------------------------------------------------
 hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps,
                           hipStream_t stream);

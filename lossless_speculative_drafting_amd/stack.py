@@ -10,9 +10,10 @@ mixed batch of verify and draft rows:
     h = rmsnorm(x); q, k, v = P_q(h), P_k(h), P_v(h); x = x + P_o(q)
     h = rmsnorm(x); x = x + P_down(silu(P_gate(h)) * P_up(h))
 
-All intermediates live in buffers allocated once; a forward pass launches
-only library kernels on the current stream, so it can be captured into a HIP
-graph.
+All intermediates live in buffers allocated once.  The rows are planned
+once (uno_segment_rows) and every projection reuses the plan: one LoRA
+down-projection and one gated GEMM per projection.  After the first call a
+forward pass launches only library kernels on the current stream.
 """
 
 import torch
@@ -52,13 +53,18 @@ class GatedLoraStack:
         need = 0
         for name in PROJECTIONS:
             w = l0[name][0]
-            need = max(need, _lib.gated_lora_workspace_size(M, w.shape[0], w.shape[1], r, bf))
+            N, K = w.shape
+            need = max(need, int(_lib.library().uno_lora_down_workspace_size(M, K, r)),
+                       int(_lib.library().uno_gated_gemm_workspace_size(M, N, K, r)))
         self.ws = _lib.Workspace(dev)
         self.ws.get(need)
+        self.t = torch.empty(_lib.lora_t_size(M, r) // 2, dtype=bf, device=dev)
+        self.plan = None
 
     def _proj(self, layer, name, inp, out):
         w, a, b = layer[name]
-        _lib.gated_lora_fwd(inp, w, a, b, self.gate, self.scale, out=out, workspace=self.ws)
+        _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+        _lib.gated_gemm(inp, w, self.t, b, self.plan, out=out, workspace=self.ws)
 
     def forward(self, x_in, trace_layer=None, trace=None):
         """Run every layer on x_in [M, hidden] (not modified); returns the final hidden state.
@@ -67,6 +73,7 @@ class GatedLoraStack:
         `trace_layer` are cloned into it as trace[name] = (input, output).
         """
         self.x.copy_(x_in)
+        self.plan = _lib.RowPlan(self.gate) if self.plan is None else self.plan
         for li, layer in enumerate(self.layers):
             rec = trace is not None and li == trace_layer
             _lib.rmsnorm(self.x, self.eps, out=self.h)

@@ -118,3 +118,25 @@ def test_deterministic_repeat():
     inp = gemm_inputs(300, 1024, 512, 128, seed=3, dtype="bf16")
     say("gemm determinism")
     assert np.array_equal(_run(inp, "bf16"), _run(inp, "bf16"))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tile", ["64x128", "128x128", "128x256", "256x128", "256x256"])
+def test_every_tile_shape_ragged(tile, monkeypatch):
+    """Each workgroup tile on a problem ragged in M, N and K, through the split steps."""
+    monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    M, K, N, r = 300, 1000, 700, 128
+    rng = np.random.default_rng(11)
+    gate = (rng.random(M) < 0.4).astype(np.uint8)
+    inp = gemm_inputs(M, K, N, r, seed=21, dtype="bf16", gate=gate)
+    say("gemm tile", tile)
+    x, w = to_dev(inp["x"], "bf16"), to_dev(inp["w"], "bf16")
+    a, b = to_dev(inp["a"], "bf16"), to_dev(inp["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, a, plan, 2.0)
+    y = to_host(uno.gated_gemm(x, w, t, b, plan))
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], gate, 2.0)
+    err = floored_rel_err(y, ref)
+    assert err <= BF16_TOL, err
+    y_full = _run(inp, "bf16")
+    assert np.array_equal(y, y_full), "split steps and the one-call projection must agree bitwise"
