@@ -15,17 +15,19 @@
 //                    kernel below in "T mode" (split over K when the tile grid
 //                    is small; fp32 partials summed in split order), rounded
 //                    once to bf16.
-//   3. gated_gemm    y = x W_AR, plus T B on draft blocks: bf16 MFMA 32x32x16
+//   3. gated_gemm    y = x W_AR, plus T B on draft tiles: bf16 MFMA 32x32x16
 //                    over BM x BN x 64 workgroup tiles, 4 wavefronts of
-//                    (BM/2) x (BN/2).  Operands are read with buffer loads
-//                    (out-of-range offsets return zero, which pads rows, N and
-//                    K without branches), staged in registers one K-step ahead
-//                    and double-buffered in LDS in XOR-swizzled 16-byte chunks.
-//                    Draft 32-row blocks run r/64 further K-steps with (T, B)
-//                    after the W_AR K-loop, into the same fp32 accumulators;
-//                    verify blocks skip them, so their instruction sequence is
-//                    the one a call with all gates 0 runs, and their results
-//                    are bitwise identical to it.
+//                    (BM/2) x (BN/2).  Operands go straight from global memory
+//                    into LDS (buffer loads with the LDS-DMA bit; out-of-range
+//                    offsets write zeros, which pads rows, N and K without
+//                    branches), double-buffered in XOR-swizzled 16-byte chunks;
+//                    the copies of one stage are spread between the MFMAs of
+//                    the stage before.  Tiles holding draft rows run r/64
+//                    further K-steps with (T, B) after the W_AR K-loop, into
+//                    the same fp32 accumulators.  Verify rows of such a tile
+//                    read zero T rows and so add exact zeros to accumulators
+//                    that started at +0: their results are bitwise those of a
+//                    call with all gates 0.
 // Rows are gathered on load and scattered on store through the permutation.
 // Workgroups are ordered so that each XCD works on a contiguous band of
 // output columns (its L2 then holds that band's weights).
@@ -155,6 +157,16 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
     return r;
 }
 
+// The same value in every lane, held in scalar registers.
+__device__ __forceinline__ i32x4 uniform4(i32x4 v) {
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(v.x);
+    r.y = __builtin_amdgcn_readfirstlane(v.y);
+    r.z = __builtin_amdgcn_readfirstlane(v.z);
+    r.w = __builtin_amdgcn_readfirstlane(v.w);
+    return r;
+}
+
 // Direct global -> LDS copy of one 16-byte chunk per lane: lane l's chunk lands
 // at LDS byte lds_addr + 16 * l (lds_addr must be wave-uniform); an offset past
 // the buffer's range writes zeros.  Issued as inline assembly so that the
@@ -210,6 +222,7 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     using C = TileCfg<BM, BN>;
     constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
+    __shared__ int32_t s_orow[BM];  // output row of each tile row (-1: none)
 
     // ---- workgroup -> (m tile, n tile, split), each XCD taking a contiguous band of tiles
     const int32_t total = a.m_tiles * a.n_tiles * a.splits;
@@ -235,22 +248,49 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     if (m0 >= rows_valid) return;  // uniform for the workgroup, before any barrier
 
     const int tid = threadIdx.x;
+    // Output rows are looked up once, here, so that the epilogue's stores do
+    // not wait on a global load each (the main loop's barriers publish them).
+    for (int i = tid; i < BM; i += kGemmThreads) {
+        const int64_t p = m0 + i;
+        int32_t o = -1;
+        if (p < rows_valid) {
+            if constexpr (TMODE) {
+                o = static_cast<int32_t>(p);
+            } else {
+                o = a.perm[p];
+            }
+        }
+        s_orow[i] = o;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
     const int lane = tid % kWave;
     const int wm = wave >> 1;
     const int wn = wave & 1;
 
-    const i32x4 rx = make_rsrc(a.x, a.x_bytes);
-    const i32x4 rw = make_rsrc(a.w, a.w_bytes);
+    const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
+    const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
+    const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
+    const bool tile_has_draft =
+        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
+    const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
+    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
+    const int nk = nk_main + nk_ext;
 
-    // DMA assignment: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the A
-    // tile (and likewise of B) in 8-row blocks; lane l takes row l/8 of a block
-    // and the logical chunk that belongs at physical position l%8.
+    // ---- copies.  Stage `it` goes to LDS buffer it & 1 as AQ + BQ DMA items
+    // per wavefront: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the A tile
+    // (and likewise of B) in 8-row blocks; lane l takes row l/8 of a block and
+    // the logical chunk that belongs at physical position l%8.  Main stages
+    // read x rows (through the row plan) and W_AR rows; extension stages read
+    // T rows and lora_b rows.  Nothing here branches: a row past the end of
+    // its operand lands past the descriptor's range (whose size is cut to the
+    // valid rows) and reads zeros, a chunk past the end of K is sent to kOOB
+    // (which stays out of range whatever in-range K offset is added), and a
+    // stage past the last is read through a zero-size descriptor.
     const int lrow = lane >> 3;
     const uint32_t kc0 = static_cast<uint32_t>(((lane & 7) ^ lrow) * 16);        // even blocks
     const uint32_t kc1 = static_cast<uint32_t>(((lane & 7) ^ lrow ^ 1) * 16);    // odd blocks
-    // per-lane byte offsets of each DMA block at K = 0 (row offset + chunk offset)
-    uint32_t xoff[AQ], woff[BQ];
+    const uint32_t kcol0 = kc0 >> 1, kcol1 = kc1 >> 1;  // K index of the chunk within a stage
+    uint32_t xoff[AQ];  // x row offsets (gathered through the plan) + chunk offset
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
         const int64_t p = m0 + wave * (BM / 4) + q * 8 + lrow;
@@ -262,74 +302,79 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
         }
         xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + ((q & 1) ? kc1 : kc0);
     }
-#pragma unroll
-    for (int q = 0; q < BQ; ++q) {
-        const int64_t n = n0 + wave * (BN / 4) + q * 8 + lrow;
-        woff[q] = (n < a.N ? static_cast<uint32_t>(n * a.ldw * 2) : kOOB) + ((q & 1) ? kc1 : kc0);
+    const uint32_t ldw2 = static_cast<uint32_t>(a.ldw * 2);
+    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / 4) + lrow) * ldw2;
+    uint32_t ldt2 = 0, ldb2 = 0, trow0 = 0, brow0 = 0;
+    if constexpr (!TMODE) {
+        ldt2 = static_cast<uint32_t>(a.ldt * 2);
+        ldb2 = static_cast<uint32_t>(a.ldb * 2);
+        // T row of this lane's first A block; verify rows give a negative
+        // row whose wrapped byte offset is far past the range
+        trow0 = static_cast<uint32_t>(m0 + wave * (BM / 4) + lrow - info.Pv) * ldt2;
+        brow0 = static_cast<uint32_t>(n0 + wave * (BN / 4) + lrow) * ldb2;
     }
+    // source bases and byte ranges (scalars; the descriptors are built per copy)
+    const uint64_t x_base = reinterpret_cast<uint64_t>(a.x), w_base = reinterpret_cast<uint64_t>(a.w);
+    const uint64_t t_base = reinterpret_cast<uint64_t>(a.t), b_base = reinterpret_cast<uint64_t>(a.lb);
+    // (every scalar the copy lambdas use is a plain value, never a field read
+    // through a captured reference, so the compiler keeps them in registers)
+    const uint32_t x_range = __builtin_amdgcn_readfirstlane(a.x_bytes);
+    const uint32_t w_range = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(std::min<int64_t>(a.w_bytes, a.N * a.ldw * 2)));
+    const uint32_t t_range = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(std::min<int64_t>(a.t_bytes, static_cast<int64_t>(info.Md_pad) * a.ldt * 2)));
+    const uint32_t b_range = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(std::min<int64_t>(a.b_bytes, a.N * a.ldb * 2)));
+    const int32_t r_s = __builtin_amdgcn_readfirstlane(a.r);
     const uint32_t lds_base = lds_addr_of(smem);
-    auto sA_addr = [&](int buf) __attribute__((always_inline)) {
-        return lds_base + static_cast<uint32_t>(buf * C::STAGE_ELEMS * 2);
-    };
-    auto sB_addr = [&](int buf) __attribute__((always_inline)) {
-        return lds_base + static_cast<uint32_t>((buf * C::STAGE_ELEMS + BM * kBK) * 2);
-    };
+    const int nk_main_s = __builtin_amdgcn_readfirstlane(nk_main);
+    const int nk_s = __builtin_amdgcn_readfirstlane(nk);
+    const int32_t kb_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(kb));
+    const int32_t ke_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(ke));
 
-    const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
-    const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
-    const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
-    const bool tile_has_draft =
-        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
-    const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
-    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
-    const int nk = nk_main + nk_ext;
-
-    // Copy K-stage `it` into LDS buffer `buf`.  Main stages read x / W_AR rows;
-    // extension stages read T / B rows.  A row offset of kOOB plus any in-range
-    // K offset stays out of range, so padding needs no select; chunks past the
-    // end of K are masked explicitly.
-    auto issue_stage = [&](int it, int buf) __attribute__((always_inline)) {
-        const uint32_t la = sA_addr(buf) + static_cast<uint32_t>(wave * (BM / 4) * kBK * 2);
-        const uint32_t lb = sB_addr(buf) + static_cast<uint32_t>(wave * (BN / 4) * kBK * 2);
-        if (it < nk_main) {
-            const int64_t k0 = kb + static_cast<int64_t>(it) * kBK;
-            const uint32_t kbytes = static_cast<uint32_t>(k0 * 2);
-            if (k0 + kBK <= ke) {
-#pragma unroll
-                for (int q = 0; q < AQ; ++q) dma16(la + q * 8 * kBK * 2, xoff[q] + kbytes, rx);
-#pragma unroll
-                for (int q = 0; q < BQ; ++q) dma16(lb + q * 8 * kBK * 2, woff[q] + kbytes, rw);
-            } else {  // last stage runs past the end of K: mask the trailing chunks
-#pragma unroll
-                for (int q = 0; q < AQ; ++q) {
-                    const uint32_t kc = (q & 1) ? kc1 : kc0;
-                    dma16(la + q * 8 * kBK * 2, (k0 + kc / 2 < ke) ? xoff[q] + kbytes : kOOB, rx);
-                }
-#pragma unroll
-                for (int q = 0; q < BQ; ++q) {
-                    const uint32_t kc = (q & 1) ? kc1 : kc0;
-                    dma16(lb + q * 8 * kBK * 2, (k0 + kc / 2 < ke) ? woff[q] + kbytes : kOOB, rw);
-                }
-            }
+    constexpr int NITEM = AQ + BQ;
+    struct StageSrc {
+        uint64_t abase, bbase;  // A and B source addresses
+        uint32_t arange, brange;  // their byte ranges (0 past the last stage)
+        uint32_t kbytes;  // byte offset of the stage's first K within a row
+        uint32_t krem;    // K columns left in the stage's source (>= kBK: none masked)
+        uint32_t lds;     // LDS byte address of the stage's buffer
+        uint32_t ext;     // 1 for an extension stage
+    };
+    auto stage_src = [=](int it) __attribute__((always_inline)) {
+        StageSrc ss;
+        const bool e = it >= nk_main_s;
+        const bool live = it < nk_s;
+        const int32_t kfirst = e ? (it - nk_main_s) * kBK : kb_s + it * kBK;
+        const int32_t klim = e ? r_s : ke_s;
+        ss.ext = __builtin_amdgcn_readfirstlane(e ? 1u : 0u);
+        ss.abase = e ? t_base : x_base;
+        ss.bbase = e ? b_base : w_base;
+        ss.arange = __builtin_amdgcn_readfirstlane(live ? (e ? t_range : x_range) : 0u);
+        ss.brange = __builtin_amdgcn_readfirstlane(live ? (e ? b_range : w_range) : 0u);
+        ss.kbytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kfirst * 2));
+        ss.krem = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(klim > kfirst ? klim - kfirst : 0));
+        ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it & 1) * C::STAGE_ELEMS * 2));
+        return ss;
+    };
+    auto dma_item = [&](const StageSrc& ss, int q) __attribute__((always_inline)) {
+        if (q < AQ) {
+            const bool odd = q & 1;
+            const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / 4) + q * 8) * kBK * 2);
+            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * 8) * ldt2 + (odd ? kc1 : kc0);
+            uint32_t off = (ss.ext ? ext_off : xoff[q]) + ss.kbytes;
+            if ((odd ? kcol1 : kcol0) >= ss.krem) off = kOOB;
+            dma16(la, off, make_rsrc(reinterpret_cast<const void*>(ss.abase), ss.arange));
         } else {
-            const int k0 = (it - nk_main) * kBK;
-            const i32x4 rt = make_rsrc(a.t, a.t_bytes);
-            const i32x4 rbb = make_rsrc(a.lb, a.b_bytes);
-#pragma unroll
-            for (int q = 0; q < AQ; ++q) {
-                const uint32_t kc = (q & 1) ? kc1 : kc0;
-                const int64_t trow = m0 + wave * (BM / 4) + q * 8 + lrow - info.Pv;
-                const bool ok = trow >= 0 && trow < info.Md_pad && k0 + static_cast<int>(kc / 2) < a.r;
-                dma16(la + q * 8 * kBK * 2,
-                      ok ? static_cast<uint32_t>(trow * a.ldt * 2 + k0 * 2) + kc : kOOB, rt);
-            }
-#pragma unroll
-            for (int q = 0; q < BQ; ++q) {
-                const uint32_t kc = (q & 1) ? kc1 : kc0;
-                const int64_t n = n0 + wave * (BN / 4) + q * 8 + lrow;
-                const bool ok = n < a.N && k0 + static_cast<int>(kc / 2) < a.r;
-                dma16(lb + q * 8 * kBK * 2, ok ? static_cast<uint32_t>(n * a.ldb * 2 + k0 * 2) + kc : kOOB, rbb);
-            }
+            const int qb = q - AQ;
+            const bool odd = qb & 1;
+            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / 4) + qb * 8) * kBK) * 2);
+            const uint32_t kc = odd ? kc1 : kc0;
+            const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * 8) * ldw2;
+            const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * 8) * ldb2;
+            uint32_t off = (ss.ext ? off_b : off_w) + kc + ss.kbytes;
+            if ((odd ? kcol1 : kcol0) >= ss.krem) off = kOOB;
+            dma16(lb, off, make_rsrc(reinterpret_cast<const void*>(ss.bbase), ss.brange));
         }
     };
 
@@ -341,12 +386,15 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // Fragments are double-buffered in registers (set 0 / set 1): the reads for
-    // sub-step kk+1 are issued before the MFMAs of sub-step kk (sched_barrier
-    // fences keep the compiler from sinking them to their uses).  The hand-off
-    // to the next stage -- wait for its copy, barrier, start the copy of the
-    // stage after it, first fragment reads -- sits before the last sub-step's
-    // MFMAs, so the MFMA pipe stays busy meanwhile.
+    // ---- schedule.  Fragments are double-buffered in registers (set 0 / 1):
+    // reads for sub-step kk+1 are issued before the MFMAs of sub-step kk, and
+    // sched_barrier fences keep the compiler from sinking them to their uses.
+    // The copy of stage s may start only after the barrier that retires stage
+    // s-2 from its buffer; its NITEM items are spread over the next three MFMA
+    // groups (the last sub-step of stage s-2, the first two of stage s-1), a
+    // few MFMAs apart, so the wavefront never stalls on a burst of copies with
+    // the MFMA pipe idle; the third sub-step of stage s-1 covers the copy
+    // latency before the wait and barrier that publish stage s.
     bf16x8 af[2][MI], bfr[2][NJ];
     auto read_frags = [&](int buf, int kk, int set) __attribute__((always_inline)) {
         const uint16_t* sa = smem + buf * C::STAGE_ELEMS;
@@ -367,48 +415,87 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     // (out-of-range copies write zeros), so their MFMAs add an exact zero to
     // accumulators that started at +0 and therefore can never be -0 (round to
     // nearest) -- the verify rows keep the bits of a call with all gates 0.
-    auto mfma_step = [&](int set, auto) __attribute__((always_inline)) {
+    //
+    // One MFMA group (all MI x NJ blocks of sub-step `set`) with copy items
+    // [q0, q0 + NQ) of `ss` interleaved after every (MI*NJ)/NQ MFMAs.
+    constexpr int GROUP = MI * NJ;
+    constexpr int NQ = (NITEM + 2) / 3;  // items per MFMA group
+    auto mfma_group = [&](int set, const StageSrc& ss, int q0) __attribute__((always_inline)) {
+        int m = 0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
-    };
-    // a stage followed by another: its copy was started one stage earlier
-    auto body_next = [&](int it, auto ext_c) __attribute__((always_inline)) {
-        const int buf = it & 1;
+                ++m;
+                if (m % (GROUP / NQ > 0 ? GROUP / NQ : 1) == 0) {
+                    const int q = q0 + m / (GROUP / NQ > 0 ? GROUP / NQ : 1) - 1;
+                    if (q < q0 + NQ && q < NITEM) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        dma_item(ss, q);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        // items left over when GROUP < NQ
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
-            read_frags(buf, kk + 1, (kk + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(kk & 1, ext_c);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int q = q0 + (GROUP / NQ > 0 ? GROUP / (GROUP / NQ) : GROUP); q < q0 + NQ && q < NITEM; ++q)
+            dma_item(ss, q);
+    };
+
+    // stage `it` (data already in LDS) followed by stage it+1 (copy in flight)
+    auto body_next = [&](int it) __attribute__((always_inline)) {
+        const int buf = it & 1;
+        const StageSrc next = stage_src(it + 1);  // items NQ.. of its copy remain
+        const StageSrc next2 = stage_src(it + 2);
+        read_frags(buf, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(0, next, NQ);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(1, next, 2 * NQ);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 3, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(0, next2, NITEM);  // no items: next2 starts after the barrier
+        __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();  // this wavefront's copy of stage it+1 has landed
         __syncthreads();  // ... every wavefront's; and buffer `buf` is no longer read
-        if (it + 2 < nk) issue_stage(it + 2, buf);
         read_frags(buf ^ 1, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step((kBK / 16 - 1) & 1, ext_c);
+        mfma_group(1, next2, 0);  // first items of the copy of stage it+2
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto body_last = [&](int it, auto ext_c) __attribute__((always_inline)) {
+    auto body_last = [&](int it) __attribute__((always_inline)) {
         const int buf = it & 1;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16 - 1; ++kk) {
-            read_frags(buf, kk + 1, (kk + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(kk & 1, ext_c);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_step((kBK / 16 - 1) & 1, ext_c);
+        const StageSrc none = stage_src(nk_s);
+        read_frags(buf, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(0, none, NITEM);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(1, none, NITEM);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 3, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(0, none, NITEM);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_group(1, none, NITEM);
     };
 
     if (nk > 0) {
-        issue_stage(0, 0);
+        {  // stage 0 whole, first items of stage 1
+            const StageSrc s0 = stage_src(0);
+#pragma unroll
+            for (int q = 0; q < NITEM; ++q) dma_item(s0, q);
+            const StageSrc s1 = stage_src(1);
+#pragma unroll
+            for (int q = 0; q < NQ && q < NITEM; ++q) dma_item(s1, q);
+        }
         if (nk > 1) {
-            issue_stage(1, 1);
-            wait_vmcnt<C::DMA_PER_STAGE>();  // stage 0 landed; stage 1 may still be in flight
+            wait_vmcnt<(NQ < NITEM ? NQ : NITEM)>();  // stage 0 landed; stage 1 items may be in flight
         } else {
             wait_vmcnt<0>();
         }
@@ -416,8 +503,11 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
         read_frags(0, 0, 0);
         // stage count is uniform; keep it scalar
         const int nks = __builtin_amdgcn_readfirstlane(nk);
-        for (int it = 0; it < nks - 1; ++it) body_next(it, std::false_type{});
-        body_last(nks - 1, std::false_type{});
+        for (int it = 0; it < nks - 1; ++it) body_next(it);
+        body_last(nks - 1);
+        // the copy of the stage past the last (zero-size source) writes zeros
+        // into a free buffer; let it land before the epilogue reuses LDS
+        wait_vmcnt<0>();
     }
 
     // ---- epilogue
@@ -442,21 +532,15 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
                 }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's staging writes are done
         constexpr int CPR = C::WN / 8;  // 16-byte chunks per wavefront row
-        for (int e = lane; e < C::WM * CPR; e += kWave) {
-            const int r = e / CPR;
-            const int c = e - r * CPR;
-            const int64_t p = m0 + wm * C::WM + r;
-            const int64_t n = n0 + wn * C::WN + c * 8;
-            if (p >= rows_valid || n >= a.N) continue;
-            int64_t orow;
-            if constexpr (TMODE) {
-                orow = p;
-            } else {
-                orow = a.perm[p];
-            }
-            if (orow < 0) continue;
+        constexpr int RPI = kWave / CPR;  // rows per store instruction
+        const int c = lane % CPR;
+        const int64_t n = n0 + wn * C::WN + c * 8;
+#pragma unroll 8
+        for (int r = lane / CPR; r < C::WM; r += RPI) {
+            const int32_t orow = s_orow[wm * C::WM + r];
+            if (orow < 0 || n >= a.N) continue;
             const int pc = c ^ (((r >> 2) & 1) << 2);
-            *reinterpret_cast<uint4*>(a.y + orow * a.ldy + n) =
+            *reinterpret_cast<uint4*>(a.y + static_cast<int64_t>(orow) * a.ldy + n) =
                 *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
         }
         return;
@@ -468,12 +552,7 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
             const int64_t p = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             if (p >= rows_valid) continue;
             if (a.splits == 1) {
-                int64_t orow;
-                if constexpr (TMODE) {
-                    orow = p;
-                } else {
-                    orow = a.perm[p];
-                }
+                const int64_t orow = s_orow[wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)];
                 if (orow < 0) continue;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {

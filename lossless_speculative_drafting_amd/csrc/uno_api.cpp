@@ -92,6 +92,10 @@ static uno_status check_gemm(int64_t M, int64_t N, int64_t K, int32_t r, int32_t
         const int64_t rows_cap = (M + 31) / 32 * 32 + 32;
         if (M * K >= (1LL << 30) || N * K >= (1LL << 30) || rows_cap * r >= (1LL << 30))
             return fail(UNO_ERR_UNSUPPORTED, "bf16 operands must stay under 2^30 elements each");
+        // byte offsets of the rows one tile reads past N (or past r) stay
+        // under 2^32, where the copy engine's range check still sees them
+        if ((N + 256) * K >= (1LL << 31) || (r + 256) * K >= (1LL << 31) || (N + 256) * r >= (1LL << 31))
+            return fail(UNO_ERR_UNSUPPORTED, "operand rows past a tile edge would overflow 32-bit offsets");
         if (((rows_cap + 63) / 64) * ((N + 127) / 128) > kMaxGridX)
             return fail(UNO_ERR_UNSUPPORTED, "problem too large for the tile grid");
     } else {
