@@ -135,7 +135,10 @@ uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size
 /* LoRA down-projection on draft rows (bf16): t receives scale * (x A) for the
  * draft rows in plan order, zero rows for padding; t is a device buffer of
  * uno_lora_t_size(M, r) bytes.  x [M, K], lora_a [r, K].  Same domain as
- * uno_gated_lora_fwd with UNO_BF16. */
+ * uno_gated_lora_fwd with UNO_BF16, except that r here is the width of T: a
+ * multiple of 8 up to 1024, so that the A matrices of several projections
+ * that read the same x can be stacked ([A_q; A_k; A_v]) and their T computed
+ * in one call, side by side. */
 size_t uno_lora_t_size(int64_t M, int32_t r);
 size_t uno_lora_down_workspace_size(int64_t M, int64_t K, int32_t r);
 uno_status uno_lora_down(const void* x, const void* lora_a, const void* row_plan, void* t, int64_t M,
@@ -149,6 +152,26 @@ size_t uno_gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r)
 uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const void* lora_b,
                           const void* row_plan, void* y, int64_t M, int64_t N, int64_t K, int32_t r,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Grouped gated GEMM (bf16): several projections that read the same x (q, k
+ * and v of a layer; its gate and up) in one launch, each with its own LoRA
+ * adapter.  Group g has group_n[g] output columns; w [N, K] and lora_b [N, r]
+ * hold the groups' rows one after another (N = sum of group_n); t is the
+ * output of uno_lora_down over the stacked A matrices (width n_groups * r),
+ * whose columns [g*r, (g+1)*r) belong to group g; y is a host array of
+ * n_groups device pointers, y[g] a row-major [M, group_n[g]] output.  The
+ * result is that of uno_gated_gemm on each group alone up to the order of the
+ * fp32 sums (the launch plan, which may split K, depends on the total width);
+ * with the same plan it is bitwise the same.
+ * Domain: as uno_gated_gemm, with 1 <= n_groups <= 4 and every group but
+ * the last a multiple of 128 columns (UNO_ERR_UNSUPPORTED otherwise).
+ * group_n and y are read before the call returns. */
+size_t uno_gated_gemm_grouped_workspace_size(int64_t M, int64_t K, int32_t r, const int64_t* group_n,
+                                             int32_t n_groups);
+uno_status uno_gated_gemm_grouped(const void* x, const void* w, const void* t, const void* lora_b,
+                                  const void* row_plan, void* const* y, const int64_t* group_n,
+                                  int32_t n_groups, int64_t M, int64_t K, int32_t r, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Block verification ("The Psi-Spec Sampler" on the aifromscratch.in page:

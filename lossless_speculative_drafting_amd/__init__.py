@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     draft_sample,
     draft_sample_workspace_size,
     gated_gemm,
+    gated_gemm_grouped,
     gated_lora_fwd,
     gated_lora_workspace_size,
     header_symbols,

@@ -40,6 +40,9 @@ SIGNATURES = {
     "uno_gated_gemm_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32]),
     "uno_gated_gemm": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int64,
                                   _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_gated_gemm_grouped_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int32, _c_ptr, _c_int32]),
+    "uno_gated_gemm_grouped": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int32,
+                                          _c_int64, _c_int64, _c_int32, _c_ptr, _c_size, _c_ptr]),
     "uno_block_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int32]),
     "uno_block_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
                                     _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -231,6 +234,36 @@ def gated_gemm(x, w, t, lora_b, plan, out=None, workspace=None, stream=None):
     _check(_lib.uno_gated_gemm(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), _ptr(out), M, N, K, r,
                                _ptr(ws), need, _stream(stream)))
     return out
+
+
+def gated_gemm_grouped(x, w, t, lora_b, plan, group_n, outs=None, workspace=None, stream=None):
+    """Several projections of the same x in one launch (uno_gated_gemm_grouped).
+
+    w [N, K] and lora_b [N, r] stack the groups' rows (N = sum(group_n)); t is
+    lora_down over the stacked A matrices (width len(group_n) * r).  Returns
+    one [M, group_n[g]] output per group (outs, if given).
+    """
+    _need_cuda(x, w, t, lora_b)
+    M, K = x.shape
+    group_n = [int(n) for n in group_n]
+    G = len(group_n)
+    N = sum(group_n)
+    r = lora_b.shape[1]
+    if w.shape != (N, K) or lora_b.shape != (N, r) or plan.M != M:
+        raise ValueError("shape mismatch: x [M,K], w [N,K], lora_b [N,r] with N = sum(group_n), plan over M rows")
+    if t.numel() * t.element_size() < lora_t_size(M, r * G):
+        raise ValueError("t buffer too small")
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=x.dtype, device=x.device) for n in group_n]
+    if len(outs) != G or any(o.shape != (M, n) or not o.is_contiguous() for o, n in zip(outs, group_n)):
+        raise ValueError("outs must be contiguous [M, group_n[g]] tensors")
+    ns = (ctypes.c_int64 * G)(*group_n)
+    ys = (ctypes.c_void_p * G)(*[_ptr(o) for o in outs])
+    need = int(_lib.uno_gated_gemm_grouped_workspace_size(M, K, r, ns, G))  # 0 also on bad shapes: the call reports those
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_gated_gemm_grouped(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), ys, ns, G, M, K, r,
+                                       _ptr(ws), need, _stream(stream)))
+    return outs
 
 
 # ------------------------------------------------------------------ verification

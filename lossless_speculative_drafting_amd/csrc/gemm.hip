@@ -48,6 +48,7 @@ namespace {
 constexpr int kBK = 64;        // K per pipeline stage
 constexpr int kRowAlign = 32;  // segment padding = MFMA block height
 constexpr int kGemmThreads = 256;
+constexpr int kMaxGroups = 4;  // output column groups of one launch
 constexpr uint32_t kOOB = 0x80000000u;       // buffer offset past every range: loads return 0
 constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
@@ -117,6 +118,41 @@ __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t
 }
 
 // ------------------------------------------------------------ MFMA GEMM
+// Output columns split into groups (say q | k | v of one fused projection):
+// group g holds columns [end[g-1], end[g]) of the product, written to its own
+// row-major buffer y[g] with row stride ldy[g], and its draft rows use T
+// columns [g*r, (g+1)*r).  end[n-1] is the full width N; every other end
+// falls on a tile edge.
+struct OutGroups {
+    int32_t n;
+    int64_t end[kMaxGroups];
+    uint16_t* y[kMaxGroups];
+    int64_t ldy[kMaxGroups];
+};
+
+// Group of output column n (n below the last end); every result is uniform
+// when n is.
+struct GroupRef {
+    int32_t g;
+    int64_t start, end;
+    uint16_t* y;
+    int64_t ldy;
+};
+__device__ __forceinline__ GroupRef find_group(const OutGroups& o, int64_t n) {
+    GroupRef r{0, 0, o.end[0], o.y[0], o.ldy[0]};
+#pragma unroll
+    for (int i = 1; i < kMaxGroups; ++i) {
+        if (i < o.n && n >= o.end[i - 1]) {
+            r.g = i;
+            r.start = o.end[i - 1];
+            r.end = o.end[i];
+            r.y = o.y[i];
+            r.ldy = o.ldy[i];
+        }
+    }
+    return r;
+}
+
 struct GemmKArgs {
     const uint16_t* x;    // activations, rows gathered through perm
     int64_t ldx;
@@ -132,8 +168,7 @@ struct GemmKArgs {
     uint32_t b_bytes;
     const int32_t* perm;
     const SegInfo* info;
-    uint16_t* y;          // output rows (scattered through perm in main mode)
-    int64_t ldy;
+    OutGroups out;        // output column groups (rows scattered through perm in main mode)
     float* partial;       // [splits][rows_cap][N] when splits > 1
     int64_t rows_cap;
     int64_t N, K;
@@ -315,14 +350,19 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     }
     // source bases and byte ranges (scalars; the descriptors are built per copy)
     const uint64_t x_base = reinterpret_cast<uint64_t>(a.x), w_base = reinterpret_cast<uint64_t>(a.w);
-    const uint64_t t_base = reinterpret_cast<uint64_t>(a.t), b_base = reinterpret_cast<uint64_t>(a.lb);
+    // output group of this tile (tiles never straddle groups); its draft rows
+    // read T from column grp.g * r on
+    const GroupRef grp = find_group(a.out, n0);
+    const int32_t g_s = __builtin_amdgcn_readfirstlane(grp.g);
+    const uint32_t t_skip = static_cast<uint32_t>(g_s) * static_cast<uint32_t>(a.r) * 2u;  // bytes
+    const uint64_t t_base = reinterpret_cast<uint64_t>(a.t) + t_skip, b_base = reinterpret_cast<uint64_t>(a.lb);
     // (every scalar the copy lambdas use is a plain value, never a field read
     // through a captured reference, so the compiler keeps them in registers)
     const uint32_t x_range = __builtin_amdgcn_readfirstlane(a.x_bytes);
     const uint32_t w_range = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(std::min<int64_t>(a.w_bytes, a.N * a.ldw * 2)));
-    const uint32_t t_range = __builtin_amdgcn_readfirstlane(
-        static_cast<uint32_t>(std::min<int64_t>(a.t_bytes, static_cast<int64_t>(info.Md_pad) * a.ldt * 2)));
+    const uint32_t t_range = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(std::max<int64_t>(
+        std::min<int64_t>(a.t_bytes, static_cast<int64_t>(info.Md_pad) * a.ldt * 2) - t_skip, 0)));
     const uint32_t b_range = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(std::min<int64_t>(a.b_bytes, a.N * a.ldb * 2)));
     const int32_t r_s = __builtin_amdgcn_readfirstlane(a.r);
@@ -513,7 +553,11 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     // ---- epilogue
     // lane holds D[row][col] of each 32x32 block with col = lane % 32 and
     // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4, v = 0..15.
-    if (a.splits == 1 && (a.N % 8) == 0) {
+    const int64_t gend = grp.end;  // end of this tile's group
+    uint16_t* const gy = grp.y;
+    const int64_t gldy = grp.ldy;
+    const int64_t gstart = grp.start;
+    if (a.splits == 1 && (gend % 8) == 0 && (gstart % 8) == 0) {
         // Stage the wavefront's bf16 tile through LDS, then write whole 16-byte
         // row segments (coalesced), scattering rows through the permutation.
         __syncthreads();  // all stage buffers are free
@@ -538,9 +582,9 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
 #pragma unroll 8
         for (int r = lane / CPR; r < C::WM; r += RPI) {
             const int32_t orow = s_orow[wm * C::WM + r];
-            if (orow < 0 || n >= a.N) continue;
+            if (orow < 0 || n >= gend) continue;
             const int pc = c ^ (((r >> 2) & 1) << 2);
-            *reinterpret_cast<uint4*>(a.y + static_cast<int64_t>(orow) * a.ldy + n) =
+            *reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + (n - gstart)) =
                 *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
         }
         return;
@@ -557,7 +601,8 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
-                    if (n < a.N) a.y[orow * a.ldy + n] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
+                    if (n < gend)
+                        gy[orow * gldy + (n - gstart)] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
                 }
             } else {
                 float* prow = a.partial + (static_cast<int64_t>(z) * a.rows_cap + p) * a.N;
@@ -577,7 +622,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                            int64_t rows_cap, int64_t N,
                                                            const SegInfo* __restrict__ info,
                                                            const int32_t* __restrict__ perm, float alpha,
-                                                           uint16_t* __restrict__ y, int64_t ldy) {
+                                                           const OutGroups out) {
     const SegInfo si = *info;
     const int64_t rows_valid = TMODE ? si.Md_pad : static_cast<int64_t>(si.Pv) + si.Md_pad;
     const int64_t total = rows_valid * N;
@@ -589,7 +634,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         if (orow < 0) continue;
         float s = 0.f;
         for (int32_t zz = 0; zz < splits; ++zz) s += partial[(static_cast<int64_t>(zz) * rows_cap + p) * N + n];
-        y[orow * ldy + n] = static_cast<uint16_t>(f32_to_bf16_bits(s * alpha));
+        const GroupRef g = find_group(out, n);
+        g.y[orow * g.ldy + (n - g.start)] = static_cast<uint16_t>(f32_to_bf16_bits(s * alpha));
     }
 }
 
@@ -656,13 +702,33 @@ bool tile_supported(Tile t) {
            (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
 }
 
-Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K) {
+// Output groups: every group end but the last must fall on a tile edge.
+struct GroupSpec {
+    int32_t n;
+    int64_t end[kMaxGroups];
+};
+
+GroupSpec one_group(int64_t N) {
+    GroupSpec g{};
+    g.n = 1;
+    g.end[0] = N;
+    return g;
+}
+
+bool tile_fits(Tile t, const GroupSpec& gs) {
+    for (int i = 0; i + 1 < gs.n; ++i)
+        if (gs.end[i] % t.bn != 0) return false;
+    return true;
+}
+
+Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs) {
     const Tile forced = env_tile();
-    if (tile_supported(forced)) return forced;
+    if (tile_supported(forced) && tile_fits(forced, gs)) return forced;
     const Tile cands[] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}, {64, 128}};
     Tile best{64, 128};
     double best_t = 1e300;
     for (const Tile& t : cands) {
+        if (!tile_fits(t, gs)) continue;
         const int64_t tiles = ((rows_cap + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
         const int64_t slots = static_cast<int64_t>(kNumCUs) * occupancy(t);
         const int64_t waves = (tiles + slots - 1) / slots;
@@ -695,10 +761,10 @@ struct GemmPlan {
     size_t partial_bytes;
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs) {
     GemmPlan p{};
     p.rows_cap = rows_cap_for(M);
-    p.tile = tmode ? Tile{128, 128} : choose_tile(p.rows_cap, N, K);
+    p.tile = tmode ? Tile{128, 128} : choose_tile(p.rows_cap, N, K, gs);
     if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128};
     if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
@@ -739,7 +805,7 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         const int64_t elems = p.rows_cap * ka.N;
         const uint32_t rg = static_cast<uint32_t>(std::min<int64_t>(4096, (elems + 255) / 256));
         hipLaunchKernelGGL((splitk_reduce_kernel<TMODE>), dim3(rg), dim3(256), 0, stream, ka.partial, p.splits,
-                           p.rows_cap, ka.N, ka.info, ka.perm, ka.alpha, ka.y, ka.ldy);
+                           p.rows_cap, ka.N, ka.info, ka.perm, ka.alpha, ka.out);
     }
 }
 
@@ -767,11 +833,13 @@ size_t lora_t_bytes(int64_t M, int32_t r) {
     return align_up(static_cast<size_t>(rows_cap_for(M)) * r * sizeof(uint16_t), kWorkspaceAlign);
 }
 
-size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r) { return plan_gemm(M, r, K, true).partial_bytes; }
+size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r) {
+    return plan_gemm(M, r, K, true, one_group(r)).partial_bytes;
+}
 
 hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan, void* t, int64_t M, int64_t K,
                             int32_t r, float scale, void* ws, hipStream_t stream) {
-    const GemmPlan p = plan_gemm(M, r, K, true);
+    const GemmPlan p = plan_gemm(M, r, K, true, one_group(r));
     GemmKArgs ka{};
     ka.x = static_cast<const uint16_t*>(x);
     ka.ldx = K;
@@ -781,8 +849,10 @@ hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan,
     ka.w_bytes = static_cast<uint32_t>(static_cast<int64_t>(r) * K * 2);
     ka.perm = plan_perm(plan);
     ka.info = plan_info(plan);
-    ka.y = static_cast<uint16_t*>(t);
-    ka.ldy = r;
+    ka.out.n = 1;
+    ka.out.end[0] = r;
+    ka.out.y[0] = static_cast<uint16_t*>(t);
+    ka.out.ldy[0] = r;
     ka.partial = static_cast<float*>(ws);
     ka.N = r;
     ka.K = K;
@@ -793,11 +863,34 @@ hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan,
 }
 
 // ---------------------------------------------------------------- a3: gated GEMM
-size_t gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K) { return plan_gemm(M, N, K, false).partial_bytes; }
+namespace {
+GroupSpec group_spec(const int64_t* group_n, int32_t n_groups) {
+    GroupSpec gs{};
+    gs.n = n_groups;
+    int64_t e = 0;
+    for (int i = 0; i < n_groups; ++i) gs.end[i] = (e += group_n[i]);
+    return gs;
+}
+}  // namespace
+
+bool gated_gemm_groups_ok(const int64_t* group_n, int32_t n_groups) {
+    if (n_groups < 1 || n_groups > kMaxGroups) return false;
+    for (int i = 0; i < n_groups; ++i)
+        if (group_n[i] < 1 || (i + 1 < n_groups && group_n[i] % 128 != 0)) return false;
+    return true;
+}
+
+size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups) {
+    const GroupSpec gs = group_spec(group_n, n_groups);
+    return plan_gemm(M, gs.end[n_groups - 1], K, false, gs).partial_bytes;
+}
 
 hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
-                             void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* ws, hipStream_t stream) {
-    const GemmPlan p = plan_gemm(M, N, K, false);
+                             void* const* ys, const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K,
+                             int32_t r, void* ws, hipStream_t stream) {
+    const GroupSpec gs = group_spec(group_n, n_groups);
+    const int64_t N = gs.end[n_groups - 1];
+    const GemmPlan p = plan_gemm(M, N, K, false, gs);
     GemmKArgs ka{};
     ka.x = static_cast<const uint16_t*>(x);
     ka.ldx = K;
@@ -806,15 +899,19 @@ hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const 
     ka.ldw = K;
     ka.w_bytes = static_cast<uint32_t>(N * K * 2);
     ka.t = static_cast<const uint16_t*>(t);
-    ka.ldt = r;
-    ka.t_bytes = static_cast<uint32_t>(rows_cap_for(M) * r * 2);
+    ka.ldt = static_cast<int64_t>(r) * n_groups;
+    ka.t_bytes = static_cast<uint32_t>(rows_cap_for(M) * ka.ldt * 2);
     ka.lb = static_cast<const uint16_t*>(lora_b);
     ka.ldb = r;
     ka.b_bytes = static_cast<uint32_t>(N * r * 2);
     ka.perm = plan_perm(plan);
     ka.info = plan_info(plan);
-    ka.y = static_cast<uint16_t*>(y);
-    ka.ldy = N;
+    ka.out.n = n_groups;
+    for (int i = 0; i < n_groups; ++i) {
+        ka.out.end[i] = gs.end[i];
+        ka.out.y[i] = static_cast<uint16_t*>(ys[i]);
+        ka.out.ldy[i] = group_n[i];
+    }
     ka.partial = static_cast<float*>(ws);
     ka.N = N;
     ka.K = K;
@@ -839,7 +936,7 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     l.down_ws = off;
     off += align_up(lora_down_workspace_size(M, K, r), kWorkspaceAlign);
     l.gemm_ws = off;
-    off += align_up(gated_gemm_workspace_size(M, N, K), kWorkspaceAlign);
+    off += align_up(gated_gemm_workspace_size(M, K, &N, 1), kWorkspaceAlign);
     l.total = off;
     return l;
 }
@@ -873,7 +970,8 @@ hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, h
     if (e != hipSuccess) return e;
     e = lora_down_launch(pr.x, pr.a, base + l.plan, base + l.t, pr.M, pr.K, pr.r, pr.scale, base + l.down_ws, stream);
     if (e != hipSuccess) return e;
-    return gated_gemm_launch(pr.x, pr.w, base + l.t, pr.b, base + l.plan, pr.y, pr.M, pr.N, pr.K, pr.r,
+    void* ys[1] = {pr.y};
+    return gated_gemm_launch(pr.x, pr.w, base + l.t, pr.b, base + l.plan, ys, &pr.N, 1, pr.M, pr.K, pr.r,
                              base + l.gemm_ws, stream);
 }
 

@@ -153,21 +153,33 @@ uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size
     return from_hip(uno::segment_rows_launch(gate, M, row_plan, stream), "segment rows launch");
 }
 
+// T may hold several adapters side by side (their A rows stacked): its width
+// is the sum of their ranks.
+static uno_status check_lora_t(int64_t M, int64_t K, int32_t rt) {
+    if (rt < 8 || rt > 1024 || rt % 8 != 0)
+        return fail(UNO_ERR_UNSUPPORTED, "T width must be a multiple of 8 in [8, 1024] (got %d)", rt);
+    const uno_status st = check_gemm(M, rt, K, 8, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (((M + 31) / 32 * 32 + 32) * rt >= (1LL << 30))
+        return fail(UNO_ERR_UNSUPPORTED, "T must stay under 2^30 elements");
+    return UNO_OK;
+}
+
 size_t uno_lora_t_size(int64_t M, int32_t r) {
-    if (check_gemm(M, 8, 8, r, UNO_BF16) != UNO_OK) return 0;
+    if (check_lora_t(M, 8, r) != UNO_OK) return 0;
     ok();
     return uno::lora_t_bytes(M, r);
 }
 
 size_t uno_lora_down_workspace_size(int64_t M, int64_t K, int32_t r) {
-    if (check_gemm(M, 8, K, r, UNO_BF16) != UNO_OK) return 0;
+    if (check_lora_t(M, K, r) != UNO_OK) return 0;
     ok();
     return uno::lora_down_workspace_size(M, K, r);
 }
 
 uno_status uno_lora_down(const void* x, const void* lora_a, const void* row_plan, void* t, int64_t M, int64_t K,
                          int32_t r, float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    uno_status st = check_gemm(M, 8, K, r, UNO_BF16);
+    uno_status st = check_lora_t(M, K, r);
     if (st != UNO_OK) return st;
     if (!std::isfinite(scale)) return fail(UNO_ERR_INVALID_ARG, "scale must be finite");
     if (M == 0) return ok();
@@ -183,22 +195,64 @@ uno_status uno_lora_down(const void* x, const void* lora_a, const void* row_plan
 size_t uno_gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
     if (check_gemm(M, N, K, r, UNO_BF16) != UNO_OK) return 0;
     ok();
-    return uno::gated_gemm_workspace_size(M, N, K);
+    return uno::gated_gemm_workspace_size(M, K, &N, 1);
 }
 
 uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const void* lora_b, const void* row_plan,
                           void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* workspace,
                           size_t workspace_bytes, hipStream_t stream) {
+    return uno_gated_gemm_grouped(x, w, t, lora_b, row_plan, &y, &N, 1, M, K, r, workspace, workspace_bytes, stream);
+}
+
+static uno_status check_groups(const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K, int32_t r,
+                               int64_t* N_out) {
+    if (group_n == nullptr) return fail(UNO_ERR_INVALID_ARG, "group_n is null");
+    if (n_groups < 1 || n_groups > 4) return fail(UNO_ERR_UNSUPPORTED, "n_groups must be in [1, 4] (got %d)", n_groups);
+    int64_t N = 0;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        if (group_n[g] < 1 || group_n[g] > 2147483647LL) return fail(UNO_ERR_INVALID_ARG, "group %d has %lld columns", g,
+                                                                    static_cast<long long>(group_n[g]));
+        N += group_n[g];
+    }
+    if (!uno::gated_gemm_groups_ok(group_n, n_groups))
+        return fail(UNO_ERR_UNSUPPORTED, "every group but the last must have a multiple of 128 columns");
     uno_status st = check_gemm(M, N, K, r, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (n_groups > 1) {
+        st = check_lora_t(M, K, r * n_groups);
+        if (st != UNO_OK) return st;
+    }
+    *N_out = N;
+    return UNO_OK;
+}
+
+size_t uno_gated_gemm_grouped_workspace_size(int64_t M, int64_t K, int32_t r, const int64_t* group_n,
+                                             int32_t n_groups) {
+    int64_t N = 0;
+    if (check_groups(group_n, n_groups, M, K, r, &N) != UNO_OK) return 0;
+    ok();
+    return uno::gated_gemm_workspace_size(M, K, group_n, n_groups);
+}
+
+uno_status uno_gated_gemm_grouped(const void* x, const void* w, const void* t, const void* lora_b,
+                                  const void* row_plan, void* const* y, const int64_t* group_n, int32_t n_groups,
+                                  int64_t M, int64_t K, int32_t r, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    int64_t N = 0;
+    uno_status st = check_groups(group_n, n_groups, M, K, r, &N);
     if (st != UNO_OK) return st;
     if (M == 0) return ok();
     if (!x || !w || !t || !lora_b || !row_plan || !y) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
-    if (!aligned16(x) || !aligned16(w) || !aligned16(t) || !aligned16(lora_b) || !aligned16(y) ||
-        !aligned256(row_plan))
+    if (!aligned16(x) || !aligned16(w) || !aligned16(t) || !aligned16(lora_b) || !aligned256(row_plan))
         return fail(UNO_ERR_INVALID_ARG, "tensors must be 16-byte aligned, row_plan 256-byte aligned");
-    st = check_workspace(workspace, workspace_bytes, uno::gated_gemm_workspace_size(M, N, K));
+    for (int32_t g = 0; g < n_groups; ++g) {
+        if (y[g] == nullptr) return fail(UNO_ERR_INVALID_ARG, "output %d is null", g);
+        if (!aligned16(y[g])) return fail(UNO_ERR_INVALID_ARG, "output %d must be 16-byte aligned", g);
+    }
+    st = check_workspace(workspace, workspace_bytes, uno::gated_gemm_workspace_size(M, K, group_n, n_groups));
     if (st != UNO_OK) return st;
-    return from_hip(uno::gated_gemm_launch(x, w, t, lora_b, row_plan, y, M, N, K, r, workspace, stream),
+    return from_hip(uno::gated_gemm_launch(x, w, t, lora_b, row_plan, y, group_n, n_groups, M, K, r, workspace,
+                                           stream),
                     "gated gemm launch");
 }
 

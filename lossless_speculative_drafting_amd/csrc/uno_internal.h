@@ -66,9 +66,13 @@ size_t lora_t_bytes(int64_t M, int32_t r);
 size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r);
 hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan, void* t, int64_t M, int64_t K,
                             int32_t r, float scale, void* ws, hipStream_t stream);
-size_t gated_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+// Output column groups: n_groups in [1, 4], group_n[g] >= 1, every group but
+// the last a multiple of 128 columns.
+bool gated_gemm_groups_ok(const int64_t* group_n, int32_t n_groups);
+size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups);
 hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
-                             void* y, int64_t M, int64_t N, int64_t K, int32_t r, void* ws, hipStream_t stream);
+                             void* const* ys, const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K,
+                             int32_t r, void* ws, hipStream_t stream);
 
 // ---- layer glue ----------------------------------------------------------------
 hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps,

@@ -11,10 +11,17 @@ mixed batch of verify and draft rows:
     h = rmsnorm(x); x = x + P_down(silu(P_gate(h)) * P_up(h))
 
 All intermediates live in buffers allocated once.  The rows are planned
-once (uno_segment_rows) and every projection reuses the plan: one LoRA
-down-projection and one gated GEMM per projection.  After the first call a
-forward pass launches only library kernels on the current stream.
+once (uno_segment_rows) and every projection reuses the plan.  Projections
+that read the same input run as one grouped launch (q, k, v; gate, up): their
+W_AR and lora_b rows are stacked once at construction, their A matrices too,
+so one LoRA down-projection yields T for the whole group and one grouped
+gated GEMM writes each projection to its own buffer.  A layer is then four
+down-projections and four gated GEMMs.  With grouped=False every projection
+runs on its own.  After the first call a forward pass launches only library
+kernels on the current stream.
 """
+
+import ctypes
 
 import torch
 
@@ -23,10 +30,44 @@ from . import _lib
 PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
 
 
+GROUPS = (("q", "k", "v"), ("gate", "up"))
+
+
+def _stack_group(layer, names):
+    """Stacked (w, lora_a, lora_b) of the named projections, and views of each one's slices."""
+    w = torch.cat([layer[n][0] for n in names], 0)
+    a = torch.cat([layer[n][1] for n in names], 0)
+    b = torch.cat([layer[n][2] for n in names], 0)
+    views, n0, j0 = {}, 0, 0
+    for n in names:
+        N, r = layer[n][0].shape[0], layer[n][1].shape[0]
+        views[n] = (w[n0:n0 + N], a[j0:j0 + r], b[n0:n0 + N])
+        n0, j0 = n0 + N, j0 + r
+    return (w, a, b, [layer[n][0].shape[0] for n in names]), views
+
+
 class GatedLoraStack:
-    def __init__(self, layers, gate, scale=2.0, eps=1e-5):
+    def __init__(self, layers, gate, scale=2.0, eps=1e-5, grouped=True):
         """layers: list of dicts name -> (w [N,K], lora_a [r,K], lora_b [N,r]) bf16 CUDA tensors.
-        gate: uint8 CUDA tensor [M] (1 = draft row)."""
+        gate: uint8 CUDA tensor [M] (1 = draft row).
+
+        With grouped=True the q/k/v and gate/up weights are copied once into
+        stacked tensors; self.layers then holds views of those copies (the
+        caller may drop its own)."""
+        self.grouped = bool(grouped)
+        self.groups = []
+        if self.grouped:
+            new_layers = []
+            for layer in layers:
+                lay = dict(layer)
+                gl = {}
+                for names in GROUPS:
+                    stacked, views = _stack_group(layer, names)
+                    gl[names] = stacked
+                    lay.update(views)
+                new_layers.append(lay)
+                self.groups.append(gl)
+            layers = new_layers
         self.layers = layers
         self.gate = gate
         self.scale = float(scale)
@@ -50,21 +91,46 @@ class GatedLoraStack:
         self.act = torch.empty((M, ffn), dtype=bf, device=dev)
         self.dn = torch.empty((M, hidden), dtype=bf, device=dev)
         self.x = torch.empty((M, hidden), dtype=bf, device=dev)
+        lib = _lib.library()
         need = 0
         for name in PROJECTIONS:
             w = l0[name][0]
             N, K = w.shape
-            need = max(need, int(_lib.library().uno_lora_down_workspace_size(M, K, r)),
-                       int(_lib.library().uno_gated_gemm_workspace_size(M, N, K, r)))
+            need = max(need, int(lib.uno_lora_down_workspace_size(M, K, r)),
+                       int(lib.uno_gated_gemm_workspace_size(M, N, K, r)))
+        t_width = r
+        if self.grouped:
+            for names, (w, a, b, ns) in self.groups[0].items():
+                K = w.shape[1]
+                arr = (ctypes.c_int64 * len(ns))(*ns)
+                need = max(need, int(lib.uno_lora_down_workspace_size(M, K, a.shape[0])),
+                           int(lib.uno_gated_gemm_grouped_workspace_size(M, K, r, arr, len(ns))))
+                t_width = max(t_width, a.shape[0])
         self.ws = _lib.Workspace(dev)
         self.ws.get(need)
-        self.t = torch.empty(_lib.lora_t_size(M, r) // 2, dtype=bf, device=dev)
+        self.t = torch.empty(_lib.lora_t_size(M, t_width) // 2, dtype=bf, device=dev)
         self.plan = None
 
     def _proj(self, layer, name, inp, out):
         w, a, b = layer[name]
         _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
         _lib.gated_gemm(inp, w, self.t, b, self.plan, out=out, workspace=self.ws)
+
+    def _group(self, li, names, inp, outs):
+        w, a, b, ns = self.groups[li][names]
+        _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+        _lib.gated_gemm_grouped(inp, w, self.t, b, self.plan, ns, outs=outs, workspace=self.ws)
+
+    def _projections(self, li, layer, items, trace_into):
+        """items: [(name, input, output)] sharing one input when grouped."""
+        if self.grouped and len(items) > 1:
+            self._group(li, tuple(n for n, _, _ in items), items[0][1], [o for _, _, o in items])
+        else:
+            for name, inp, out in items:
+                self._proj(layer, name, inp, out)
+        if trace_into is not None:
+            for name, inp, out in items:
+                trace_into[name] = (inp.clone(), out.clone())
 
     def forward(self, x_in, trace_layer=None, trace=None):
         """Run every layer on x_in [M, hidden] (not modified); returns the final hidden state.
@@ -75,22 +141,14 @@ class GatedLoraStack:
         self.x.copy_(x_in)
         self.plan = _lib.RowPlan(self.gate) if self.plan is None else self.plan
         for li, layer in enumerate(self.layers):
-            rec = trace is not None and li == trace_layer
+            rec = trace if (trace is not None and li == trace_layer) else None
             _lib.rmsnorm(self.x, self.eps, out=self.h)
-            for name, inp, out in (("q", self.h, self.q), ("k", self.h, self.k), ("v", self.h, self.v),
-                                   ("o", self.q, self.o)):
-                self._proj(layer, name, inp, out)
-                if rec:
-                    trace[name] = (inp.clone(), out.clone())
+            self._projections(li, layer, [("q", self.h, self.q), ("k", self.h, self.k), ("v", self.h, self.v)], rec)
+            self._projections(li, layer, [("o", self.q, self.o)], rec)
             _lib.residual_add(self.x, self.o, out=self.x)
             _lib.rmsnorm(self.x, self.eps, out=self.h)
-            for name, inp, out in (("gate", self.h, self.g), ("up", self.h, self.u)):
-                self._proj(layer, name, inp, out)
-                if rec:
-                    trace[name] = (inp.clone(), out.clone())
+            self._projections(li, layer, [("gate", self.h, self.g), ("up", self.h, self.u)], rec)
             _lib.silu_mul(self.g, self.u, out=self.act)
-            self._proj(layer, "down", self.act, self.dn)
-            if rec:
-                trace["down"] = (self.act.clone(), self.dn.clone())
+            self._projections(li, layer, [("down", self.act, self.dn)], rec)
             _lib.residual_add(self.x, self.dn, out=self.x)
         return self.x

@@ -76,6 +76,31 @@ def test_gated_lora_validation(lib):
     assert lib.uno_gated_lora_workspace_size(24, 512, 512, 128, 1) == 24 * 128 * 4 + (256 - (24 * 128 * 4) % 256) % 256
 
 
+def test_grouped_gemm_and_lora_t_validation(lib):
+    def call(groups=(4096, 1024, 1024), M=64, K=256, r=128, ys=None, ws=FAKE, wsb=1 << 30):
+        ns = (ctypes.c_int64 * max(1, len(groups)))(*groups)
+        y = ys if ys is not None else (ctypes.c_void_p * max(1, len(groups)))(*([0x100000] * len(groups)))
+        return lib.uno_gated_gemm_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, y, ns, len(groups), M, K, r, ws, wsb, STREAM)
+    assert call(groups=()) == UNSUPPORTED
+    assert call(groups=(128, 128, 128, 128, 128)) == UNSUPPORTED
+    assert call(groups=(4000, 96)) == UNSUPPORTED and "multiple of 128" in _msg(lib)
+    assert call(groups=(128, 0)) == INVALID
+    assert call(r=12) == UNSUPPORTED
+    assert call(groups=(256, 256, 256, 256), r=256, M=1 << 20) == UNSUPPORTED  # T too wide for 2^30 elements
+    assert call(ys=(ctypes.c_void_p * 3)(0x100000, 0, 0x100000)) == INVALID
+    assert call(ys=(ctypes.c_void_p * 3)(0x100000, 0x100008, 0x100000)) == INVALID  # misaligned output
+    assert call(M=0) == OK                                      # empty batch: no launch
+    # a ragged last group is accepted (the size query succeeds and clears the error)
+    ns = (ctypes.c_int64 * 2)(4096, 1000)
+    lib.uno_gated_gemm_grouped_workspace_size(1024, 4096, 128, ns, 2)
+    assert lib.uno_last_error_message() == b""
+    # T may stack several adapters: width up to 1024
+    assert lib.uno_lora_t_size(1024, 384) == 1024 * 0 + ((1024 + 31) // 32 * 32 + 32) * 384 * 2
+    assert lib.uno_lora_t_size(1024, 1032) == 0
+    assert lib.uno_lora_down(FAKE, FAKE, FAKE, FAKE, 64, 256, 1032, 2.0, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_lora_down(FAKE, FAKE, FAKE, FAKE, 64, 256, 20, 2.0, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+
+
 def test_block_verify_validation(lib):
     def call(B=2, L=4, V=64, nb=0, T=1.0, dt=0, tok=FAKE, ws=FAKE, wsb=1 << 30, ts=256, ds=256):
         return lib.uno_block_verify(FAKE, FAKE, ts, ds, tok, FAKE, B, L, V, nb, T, dt, FAKE, FAKE, FAKE, ws, wsb,

@@ -140,3 +140,49 @@ def test_every_tile_shape_ragged(tile, monkeypatch):
     assert err <= BF16_TOL, err
     y_full = _run(inp, "bf16")
     assert np.array_equal(y, y_full), "split steps and the one-call projection must agree bitwise"
+
+
+GROUPED = [  # (M, K, group sizes, r)
+    (75, 256, (256, 128, 72), 64),          # ragged M and last group; K = 256 never splits
+    (300, 1000, (384, 256), 128),           # ragged K
+    (64, 4096, (4096, 1024, 1024), 128),    # q | k | v of the 8B layer, 2 x [16 | 16] rows
+    (96, 512, (128, 128, 128, 128), 16),    # four groups
+]
+
+
+def _group_inputs(M, K, group_n, r, seed, gate):
+    parts = [gemm_inputs(M, K, n, r, seed=seed + g, dtype="bf16", gate=gate) for g, n in enumerate(group_n)]
+    x = parts[0]["x"]
+    return x, [(p["w"], p["a"], p["b"]) for p in parts]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,group_n,r", GROUPED)
+def test_grouped_gemm_vs_oracle(M, K, group_n, r):
+    rng = np.random.default_rng(M + K)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    x, groups = _group_inputs(M, K, group_n, r, 40 + M, gate)
+    say("gemm grouped", M, K, group_n, r)
+    xd = to_dev(x, "bf16")
+    w = torch.cat([to_dev(g[0], "bf16") for g in groups])
+    a = torch.cat([to_dev(g[1], "bf16") for g in groups])
+    b = torch.cat([to_dev(g[2], "bf16") for g in groups])
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(xd, a, plan, 2.0)
+    outs = [to_host(o) for o in uno.gated_gemm_grouped(xd, w, t, b, plan, group_n)]
+    for g, (wg, ag, bg) in enumerate(groups):
+        ref = oracle.gated_lora(x, wg, ag, bg, gate, 2.0)
+        err = floored_rel_err(outs[g], ref)
+        assert err <= BF16_TOL, (g, err)
+    # verify rows are those of the same grouped call with every gate 0
+    plan0 = uno.RowPlan(to_dev(np.zeros_like(gate), "u8"))
+    t0 = uno.lora_down(xd, a, plan0, 2.0)
+    outs0 = [to_host(o) for o in uno.gated_gemm_grouped(xd, w, t0, b, plan0, group_n)]
+    for g in range(len(group_n)):
+        assert np.array_equal(outs[g][gate == 0], outs0[g][gate == 0])
+    if K == 256:
+        # no split anywhere: each group equals its own ungrouped call bitwise
+        for g, (wg, ag, bg) in enumerate(groups):
+            tg = uno.lora_down(xd, to_dev(ag, "bf16"), plan, 2.0)
+            yg = to_host(uno.gated_gemm(xd, to_dev(wg, "bf16"), tg, to_dev(bg, "bf16"), plan))
+            assert np.array_equal(yg, outs[g]), g

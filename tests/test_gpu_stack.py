@@ -49,20 +49,36 @@ def _check_trace(layer, trace, gate, rows):
 
 
 @pytest.mark.gpu
-def test_small_stack_teacher_forced():
+@pytest.mark.parametrize("grouped", [True, False])
+def test_small_stack_teacher_forced(grouped):
     shapes = (("q", 512, 512), ("k", 512, 128), ("v", 512, 128), ("o", 512, 512),
               ("gate", 512, 1024), ("up", 512, 1024), ("down", 1024, 512))
     layers = [sdev.layer_weights(shapes, 100 + 100 * i) for i in range(3)]
     gate = gate_vector(4, 16, 16)
-    st = uno.GatedLoraStack(layers, to_dev(gate, "u8"))
+    st = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=grouped)
     x0 = sdev.randn((gate.size, 512), 1.0, 7)
-    say("small stack")
+    say("small stack, grouped" if grouped else "small stack, one launch per projection")
     for li in range(3):
         trace = {}
         out = st.forward(x0, trace_layer=li, trace=trace)
         torch.cuda.synchronize()
         assert torch.isfinite(out.float()).all()
         _check_trace(layers[li], trace, gate, np.arange(gate.size))
+
+
+@pytest.mark.gpu
+def test_grouped_stack_matches_ungrouped():
+    """K = 512 runs unsplit in both modes, so stacking changes no sum: bitwise equal."""
+    shapes = (("q", 512, 512), ("k", 512, 128), ("v", 512, 128), ("o", 512, 512),
+              ("gate", 512, 1024), ("up", 512, 1024), ("down", 1024, 512))
+    layers = [sdev.layer_weights(shapes, 300 + 100 * i) for i in range(2)]
+    gate = gate_vector(4, 16, 16)
+    x0 = sdev.randn((gate.size, 512), 1.0, 9)
+    say("grouped vs ungrouped stack")
+    a = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=True).forward(x0).clone()
+    b = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=False).forward(x0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.gpu
