@@ -45,9 +45,9 @@
 namespace uno {
 namespace {
 
-constexpr int kBK = 64;        // K per pipeline stage
+constexpr int kBK = 32;        // K per pipeline stage
+constexpr int kNBUF = 4;       // LDS stage buffers: up to three stages of copies in flight
 constexpr int kRowAlign = 32;  // segment padding = MFMA block height
-constexpr int kGemmThreads = 256;
 constexpr int kMaxGroups = 4;  // output column groups of one launch
 constexpr uint32_t kOOB = 0x80000000u;       // buffer offset past every range: loads return 0
 constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
@@ -226,35 +226,38 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(p)));
 }
 
-// LDS tile rows hold 64 bf16 (eight 16-byte chunks); chunk c of row r lives at
-// chunk position c ^ s(r) with s(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
-// read has lanes 0..31 on 32 consecutive rows at one chunk; gfx950 serves a
-// 16-byte-per-lane LDS read 16 lanes at a time across 64 banks, and over any
-// 16 consecutive rows the pairs (r & 1, c ^ s(r)) are all distinct, so each
-// 16-lane group touches every bank once (measured: 4 LDS cycles per wave-wide
-// read, against 8 for the plain r & 7 swizzle).
+// LDS tile rows hold 32 bf16 (four 16-byte chunks); chunk c of row r lives at
+// chunk position c ^ ((r >> 2) & 3).  A fragment read has lanes 0..31 on 32
+// consecutive rows at one chunk; gfx950 serves a 16-byte-per-lane LDS read 16
+// lanes at a time across 64 four-byte banks (four 64-byte rows), and over any
+// 16 consecutive rows the pairs (r & 3, c ^ ((r >> 2) & 3)) are all distinct,
+// so each 16-lane group touches every bank once.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kBK + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 3);
+    return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 struct TileCfg {
-    static constexpr int WM = BM / 2;          // 2 x 2 wavefronts
-    static constexpr int WN = BN / 2;
+    static constexpr int NWAVES = WGM * WGN;   // WGM x WGN wavefronts
+    static constexpr int THREADS = NWAVES * kWave;
+    static constexpr int WM = BM / WGM;
+    static constexpr int WN = BN / WGN;
     static constexpr int MI = WM / 32;         // 32x32 MFMA blocks per wavefront
     static constexpr int NJ = WN / 32;
-    static constexpr int AQ = BM / 32;         // 8-row DMA blocks per wavefront per stage (A)
-    static constexpr int BQ = BN / 32;         // (B)
-    static constexpr int DMA_PER_STAGE = AQ + BQ;
+    static constexpr int AQ = BM / (16 * NWAVES);  // 16-row DMA blocks per wavefront per stage (A)
+    static constexpr int BQ = BN / (16 * NWAVES);  // (B)
+    static_assert(AQ >= 1 && BQ >= 1 && AQ * 16 * NWAVES == BM && BQ * 16 * NWAVES == BN, "copy split");
+    static_assert(MI >= 1 && NJ >= 1 && WN >= 64, "wavefront tile");
     static constexpr int STAGE_ELEMS = (BM + BN) * kBK;
-    static constexpr int LDS_ELEMS = 2 * STAGE_ELEMS;
+    static constexpr int LDS_ELEMS = kNBUF * STAGE_ELEMS;
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
     static_assert(4 * WM * WN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
-template <int BM, int BN, bool TMODE>
-__global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_gemm_kernel(const GemmKArgs a) {
-    using C = TileCfg<BM, BN>;
+template <int BM, int BN, int WGM, int WGN, bool TMODE>
+__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN>::THREADS), (TileCfg<BM, BN, WGM, WGN>::OCC))
+void gated_gemm_kernel(const GemmKArgs a) {
+    using C = TileCfg<BM, BN, WGM, WGN>;
     constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
     __shared__ int32_t s_orow[BM];  // output row of each tile row (-1: none)
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     const int tid = threadIdx.x;
     // Output rows are looked up once, here, so that the epilogue's stores do
     // not wait on a global load each (the main loop's barriers publish them).
-    for (int i = tid; i < BM; i += kGemmThreads) {
+    for (int i = tid; i < BM; i += C::THREADS) {
         const int64_t p = m0 + i;
         int32_t o = -1;
         if (p < rows_valid) {
@@ -299,65 +302,48 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
     const int lane = tid % kWave;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave / WGN;
+    const int wn = wave % WGN;
 
-    const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
-    const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
-    const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
-    const bool tile_has_draft =
-        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
-    const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
-    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
-    const int nk = nk_main + nk_ext;
-
-    // ---- copies.  Stage `it` goes to LDS buffer it & 1 as AQ + BQ DMA items
-    // per wavefront: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the A tile
-    // (and likewise of B) in 8-row blocks; lane l takes row l/8 of a block and
-    // the logical chunk that belongs at physical position l%8.  Main stages
-    // read x rows (through the row plan) and W_AR rows; extension stages read
-    // T rows and lora_b rows.  Nothing here branches: a row past the end of
-    // its operand lands past the descriptor's range (whose size is cut to the
-    // valid rows) and reads zeros, a chunk past the end of K is sent to kOOB
-    // (which stays out of range whatever in-range K offset is added), and a
-    // stage past the last is read through a zero-size descriptor.
-    const int lrow = lane >> 3;
-    const uint32_t kc0 = static_cast<uint32_t>(((lane & 7) ^ lrow) * 16);        // even blocks
-    const uint32_t kc1 = static_cast<uint32_t>(((lane & 7) ^ lrow ^ 1) * 16);    // odd blocks
-    const uint32_t kcol0 = kc0 >> 1, kcol1 = kc1 >> 1;  // K index of the chunk within a stage
+    const int lrow = lane >> 2;  // row within a 16-row DMA block
+    // byte offset within a row of the chunk this lane copies: the logical chunk
+    // stored at physical position lane & 3 of row lrow (blocks start at
+    // multiples of 16 rows, so (row >> 2) & 3 = lane >> 4)
+    const uint32_t kc = static_cast<uint32_t>(((lane & 3) ^ (lane >> 4)) * 16);
+    const uint32_t kcol = kc >> 1;  // its K index within the stage
     uint32_t xoff[AQ];  // x row offsets (gathered through the plan) + chunk offset
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-        const int64_t p = m0 + wave * (BM / 4) + q * 8 + lrow;
+        const int64_t p = m0 + wave * (BM / C::NWAVES) + q * 16 + lrow;
         int64_t src;
         if constexpr (TMODE) {
             src = (p < info.Md) ? a.perm[info.Pv + p] : -1;
         } else {
             src = (p < rows_valid) ? a.perm[p] : -1;
         }
-        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + ((q & 1) ? kc1 : kc0);
+        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kc;
     }
     const uint32_t ldw2 = static_cast<uint32_t>(a.ldw * 2);
-    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / 4) + lrow) * ldw2;
+    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldw2 + kc;
     uint32_t ldt2 = 0, ldb2 = 0, trow0 = 0, brow0 = 0;
     if constexpr (!TMODE) {
         ldt2 = static_cast<uint32_t>(a.ldt * 2);
         ldb2 = static_cast<uint32_t>(a.ldb * 2);
         // T row of this lane's first A block; verify rows give a negative
         // row whose wrapped byte offset is far past the range
-        trow0 = static_cast<uint32_t>(m0 + wave * (BM / 4) + lrow - info.Pv) * ldt2;
-        brow0 = static_cast<uint32_t>(n0 + wave * (BN / 4) + lrow) * ldb2;
+        trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - info.Pv) * ldt2 + kc;
+        brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2 + kc;
     }
-    // source bases and byte ranges (scalars; the descriptors are built per copy)
-    const uint64_t x_base = reinterpret_cast<uint64_t>(a.x), w_base = reinterpret_cast<uint64_t>(a.w);
     // output group of this tile (tiles never straddle groups); its draft rows
     // read T from column grp.g * r on
     const GroupRef grp = find_group(a.out, n0);
     const int32_t g_s = __builtin_amdgcn_readfirstlane(grp.g);
     const uint32_t t_skip = static_cast<uint32_t>(g_s) * static_cast<uint32_t>(a.r) * 2u;  // bytes
-    const uint64_t t_base = reinterpret_cast<uint64_t>(a.t) + t_skip, b_base = reinterpret_cast<uint64_t>(a.lb);
+    // source bases and byte ranges (scalars; the descriptors are built per copy)
     // (every scalar the copy lambdas use is a plain value, never a field read
     // through a captured reference, so the compiler keeps them in registers)
+    const uint64_t x_base = reinterpret_cast<uint64_t>(a.x), w_base = reinterpret_cast<uint64_t>(a.w);
+    const uint64_t t_base = reinterpret_cast<uint64_t>(a.t) + t_skip, b_base = reinterpret_cast<uint64_t>(a.lb);
     const uint32_t x_range = __builtin_amdgcn_readfirstlane(a.x_bytes);
     const uint32_t w_range = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(std::min<int64_t>(a.w_bytes, a.N * a.ldw * 2)));
@@ -367,19 +353,36 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
         static_cast<uint32_t>(std::min<int64_t>(a.b_bytes, a.N * a.ldb * 2)));
     const int32_t r_s = __builtin_amdgcn_readfirstlane(a.r);
     const uint32_t lds_base = lds_addr_of(smem);
+
+    const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
+    const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
+    const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
+    const bool tile_has_draft =
+        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
+    const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
+    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
     const int nk_main_s = __builtin_amdgcn_readfirstlane(nk_main);
-    const int nk_s = __builtin_amdgcn_readfirstlane(nk);
+    const int nk_s = __builtin_amdgcn_readfirstlane(nk_main + nk_ext);
     const int32_t kb_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(kb));
     const int32_t ke_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(ke));
 
+    // ---- copies.  Stage `it` goes to LDS buffer it % kNBUF as AQ + BQ DMA
+    // items per wavefront: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the
+    // A tile (and likewise of B) in 16-row blocks, lane l taking row l/4 of a
+    // block.  Main stages read x rows (through the row plan) and W_AR rows;
+    // extension stages read T rows and lora_b rows.  Nothing here branches: a
+    // row past the end of its operand lands past the descriptor's range (whose
+    // size is cut to the valid rows) and reads zeros, a chunk past the end of K
+    // is sent to kOOB (which stays out of range whatever in-range K offset is
+    // added), and a stage past the last is read through a zero-size descriptor.
     constexpr int NITEM = AQ + BQ;
     struct StageSrc {
-        uint64_t abase, bbase;  // A and B source addresses
+        uint64_t abase, bbase;    // A and B source addresses
         uint32_t arange, brange;  // their byte ranges (0 past the last stage)
-        uint32_t kbytes;  // byte offset of the stage's first K within a row
-        uint32_t krem;    // K columns left in the stage's source (>= kBK: none masked)
-        uint32_t lds;     // LDS byte address of the stage's buffer
-        uint32_t ext;     // 1 for an extension stage
+        uint32_t kbytes;          // byte offset of the stage's first K within a row
+        uint32_t krem;            // K columns left in the stage's source (>= kBK: none masked)
+        uint32_t lds;             // LDS byte address of the stage's buffer
+        uint32_t ext;             // 1 for an extension stage
     };
     auto stage_src = [=](int it) __attribute__((always_inline)) {
         StageSrc ss;
@@ -394,26 +397,23 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
         ss.brange = __builtin_amdgcn_readfirstlane(live ? (e ? b_range : w_range) : 0u);
         ss.kbytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kfirst * 2));
         ss.krem = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(klim > kfirst ? klim - kfirst : 0));
-        ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it & 1) * C::STAGE_ELEMS * 2));
+        ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * C::STAGE_ELEMS * 2));
         return ss;
     };
     auto dma_item = [&](const StageSrc& ss, int q) __attribute__((always_inline)) {
         if (q < AQ) {
-            const bool odd = q & 1;
-            const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / 4) + q * 8) * kBK * 2);
-            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * 8) * ldt2 + (odd ? kc1 : kc0);
+            const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / C::NWAVES) + q * 16) * kBK * 2);
+            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * 16) * ldt2;
             uint32_t off = (ss.ext ? ext_off : xoff[q]) + ss.kbytes;
-            if ((odd ? kcol1 : kcol0) >= ss.krem) off = kOOB;
+            if (kcol >= ss.krem) off = kOOB;
             dma16(la, off, make_rsrc(reinterpret_cast<const void*>(ss.abase), ss.arange));
         } else {
             const int qb = q - AQ;
-            const bool odd = qb & 1;
-            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / 4) + qb * 8) * kBK) * 2);
-            const uint32_t kc = odd ? kc1 : kc0;
-            const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * 8) * ldw2;
-            const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * 8) * ldb2;
-            uint32_t off = (ss.ext ? off_b : off_w) + kc + ss.kbytes;
-            if ((odd ? kcol1 : kcol0) >= ss.krem) off = kOOB;
+            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / C::NWAVES) + qb * 16) * kBK) * 2);
+            const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * 16) * ldw2;
+            const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * 16) * ldb2;
+            uint32_t off = (ss.ext ? off_b : off_w) + ss.kbytes;
+            if (kcol >= ss.krem) off = kOOB;
             dma16(lb, off, make_rsrc(reinterpret_cast<const void*>(ss.bbase), ss.brange));
         }
     };
@@ -426,15 +426,15 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // ---- schedule.  Fragments are double-buffered in registers (set 0 / 1):
-    // reads for sub-step kk+1 are issued before the MFMAs of sub-step kk, and
+    // ---- schedule.  A stage is two MFMA sub-steps (K = 16 each).  Fragments
+    // are double-buffered in registers (set 0 / 1): reads for the next
+    // sub-step are issued before the MFMAs of the current one, and
     // sched_barrier fences keep the compiler from sinking them to their uses.
-    // The copy of stage s may start only after the barrier that retires stage
-    // s-2 from its buffer; its NITEM items are spread over the next three MFMA
-    // groups (the last sub-step of stage s-2, the first two of stage s-1), a
-    // few MFMAs apart, so the wavefront never stalls on a burst of copies with
-    // the MFMA pipe idle; the third sub-step of stage s-1 covers the copy
-    // latency before the wait and barrier that publish stage s.
+    // Stage s+3 is copied while stage s is computed (its buffer held stage
+    // s-1, retired by the barrier that opens stage s), its items spread
+    // between the MFMAs of the first sub-step; before the barrier that opens
+    // stage s+1 each wavefront waits until at most two stages of its copies
+    // are outstanding, i.e. until stage s+1 has landed.
     bf16x8 af[2][MI], bfr[2][NJ];
     auto read_frags = [&](int buf, int kk, int set) __attribute__((always_inline)) {
         const uint16_t* sa = smem + buf * C::STAGE_ELEMS;
@@ -456,11 +456,12 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
     // accumulators that started at +0 and therefore can never be -0 (round to
     // nearest) -- the verify rows keep the bits of a call with all gates 0.
     //
-    // One MFMA group (all MI x NJ blocks of sub-step `set`) with copy items
-    // [q0, q0 + NQ) of `ss` interleaved after every (MI*NJ)/NQ MFMAs.
+    // One MFMA group (all MI x NJ blocks of fragment set `set`), with the
+    // copy items of `ss` (when given) spread evenly between its MFMAs.
     constexpr int GROUP = MI * NJ;
-    constexpr int NQ = (NITEM + 2) / 3;  // items per MFMA group
-    auto mfma_group = [&](int set, const StageSrc& ss, int q0) __attribute__((always_inline)) {
+    constexpr int SPACING = GROUP / NITEM > 0 ? GROUP / NITEM : 1;
+    constexpr int IN_GROUP = GROUP / SPACING < NITEM ? GROUP / SPACING : NITEM;
+    auto mfma_group = [&](int set, const StageSrc* ss) __attribute__((always_inline)) {
         int m = 0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -468,85 +469,58 @@ __global__ __launch_bounds__(kGemmThreads, (TileCfg<BM, BN>::OCC)) void gated_ge
             for (int j = 0; j < NJ; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
                 ++m;
-                if (m % (GROUP / NQ > 0 ? GROUP / NQ : 1) == 0) {
-                    const int q = q0 + m / (GROUP / NQ > 0 ? GROUP / NQ : 1) - 1;
-                    if (q < q0 + NQ && q < NITEM) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        dma_item(ss, q);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                if (ss != nullptr && m % SPACING == 0 && m / SPACING <= IN_GROUP) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_item(*ss, m / SPACING - 1);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        // items left over when GROUP < NQ
+        if (ss != nullptr) {
 #pragma unroll
-        for (int q = q0 + (GROUP / NQ > 0 ? GROUP / (GROUP / NQ) : GROUP); q < q0 + NQ && q < NITEM; ++q)
-            dma_item(ss, q);
+            for (int q = IN_GROUP; q < NITEM; ++q) dma_item(*ss, q);
+        }
     };
 
-    // stage `it` (data already in LDS) followed by stage it+1 (copy in flight)
+    // stage `it` (its first fragments already read), then open stage it+1
     auto body_next = [&](int it) __attribute__((always_inline)) {
-        const int buf = it & 1;
-        const StageSrc next = stage_src(it + 1);  // items NQ.. of its copy remain
-        const StageSrc next2 = stage_src(it + 2);
+        const int buf = it % kNBUF;
+        const StageSrc ahead = stage_src(it + 3);
         read_frags(buf, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, next, NQ);
+        mfma_group(0, &ahead);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 2, 0);
+        wait_vmcnt<2 * NITEM>();  // this wavefront's copy of stage it+1 has landed
+        __syncthreads();          // ... every wavefront's; and buffer `buf` is no longer read
+        read_frags((it + 1) % kNBUF, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, next, 2 * NQ);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 3, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, next2, NITEM);  // no items: next2 starts after the barrier
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<0>();  // this wavefront's copy of stage it+1 has landed
-        __syncthreads();  // ... every wavefront's; and buffer `buf` is no longer read
-        read_frags(buf ^ 1, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, next2, 0);  // first items of the copy of stage it+2
+        mfma_group(1, nullptr);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto body_last = [&](int it) __attribute__((always_inline)) {
-        const int buf = it & 1;
-        const StageSrc none = stage_src(nk_s);
-        read_frags(buf, 1, 1);
+        read_frags(it % kNBUF, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, none, NITEM);
+        mfma_group(0, nullptr);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, none, NITEM);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 3, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, none, NITEM);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, none, NITEM);
+        mfma_group(1, nullptr);
     };
 
-    if (nk > 0) {
-        {  // stage 0 whole, first items of stage 1
-            const StageSrc s0 = stage_src(0);
+    if (nk_s > 0) {
+        {  // stages 0, 1 and 2 (stages past the last copy zeros into free buffers)
+            const StageSrc s0 = stage_src(0), s1 = stage_src(1), s2 = stage_src(2);
 #pragma unroll
             for (int q = 0; q < NITEM; ++q) dma_item(s0, q);
-            const StageSrc s1 = stage_src(1);
 #pragma unroll
-            for (int q = 0; q < NQ && q < NITEM; ++q) dma_item(s1, q);
+            for (int q = 0; q < NITEM; ++q) dma_item(s1, q);
+#pragma unroll
+            for (int q = 0; q < NITEM; ++q) dma_item(s2, q);
         }
-        if (nk > 1) {
-            wait_vmcnt<(NQ < NITEM ? NQ : NITEM)>();  // stage 0 landed; stage 1 items may be in flight
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_vmcnt<2 * NITEM>();  // stage 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
-        // stage count is uniform; keep it scalar
-        const int nks = __builtin_amdgcn_readfirstlane(nk);
-        for (int it = 0; it < nks - 1; ++it) body_next(it);
-        body_last(nks - 1);
-        // the copy of the stage past the last (zero-size source) writes zeros
-        // into a free buffer; let it land before the epilogue reuses LDS
+        for (int it = 0; it < nk_s - 1; ++it) body_next(it);
+        body_last(nk_s - 1);
+        // copies of stages past the last write zeros into free buffers; let
+        // them land before the epilogue reuses LDS
         wait_vmcnt<0>();
     }
 
@@ -673,31 +647,42 @@ __global__ __launch_bounds__(256) void gated_gemm_f32_kernel(const float* __rest
 // ------------------------------------------------------------ planning
 struct Tile {
     int bm, bn;
+    int waves;  // 4 (2 x 2) or 8 (2 x 4, two wavefronts per SIMD)
 };
 
 constexpr int kNumCUs = 256;
 
 // Workgroups that run at once per CU for a tile shape (LDS-limited).
-int occupancy(Tile t) { return (2 * (t.bm + t.bn) * kBK * 2 > 80 * 1024) ? 1 : 2; }
+int occupancy(Tile t) { return (kNBUF * (t.bm + t.bn) * kBK * 2 > 80 * 1024) ? 1 : 2; }
 
-// Relative MFMA efficiency of a workgroup tile (wave tile size sets the LDS
-// traffic per MFMA); used only to rank tile shapes.
-double tile_eff(Tile t) {
-    const int wt = (t.bm / 2) * (t.bn / 2);
-    if (wt >= 128 * 128) return 1.0;
-    if (wt >= 128 * 64) return 0.85;
-    if (wt >= 64 * 64) return 0.7;
-    return 0.45;
+// Launch-time model used to rank (tile, split) plans: a workgroup costs a
+// fixed time (launch share, prologue, epilogue) plus its MFMA work at a
+// per-workgroup rate, workgroups run in waves of 256 x occupancy, and a split
+// of K adds the fp32 partial round trip and one more launch.  The rates and
+// fixed times were measured on MI355X for this kernel (M = 1024, K = 4096 and
+// 14336 projections); they only need to rank plans, not predict them.
+struct TileModel {
+    double rate;      // flop/s of one workgroup at its occupancy
+    double fixed_us;
+};
+TileModel tile_model(Tile t) {
+    if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.4e12, 9.0} : TileModel{4.6e12, 15.0};
+    if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
+    if (t.bm == 128) return {1.7e12, 10.0};
+    return {0.9e12, 8.0};
 }
 
+// UNO_GEMM_TILE=BMxBN or BMxBNwW forces a tile (tests and tuning).
 Tile env_tile() {
     const char* s = getenv("UNO_GEMM_TILE");
-    Tile t{0, 0};
-    if (s && sscanf(s, "%dx%d", &t.bm, &t.bn) == 2) return t;
-    return Tile{0, 0};
+    Tile t{0, 0, 4};
+    if (s && sscanf(s, "%dx%dw%d", &t.bm, &t.bn, &t.waves) >= 2) return t;
+    return Tile{0, 0, 4};
 }
 
 bool tile_supported(Tile t) {
+    if (t.waves == 8) return t.bm == 256 && t.bn == 256;
+    if (t.waves != 4) return false;
     return (t.bm == 64 && t.bn == 128) || (t.bm == 128 && t.bn == 128) || (t.bm == 128 && t.bn == 256) ||
            (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
 }
@@ -721,36 +706,50 @@ bool tile_fits(Tile t, const GroupSpec& gs) {
     return true;
 }
 
+int64_t split_k(int64_t K, int64_t s) { return ((K + s - 1) / s + kBK - 1) / kBK * kBK; }
+
+double plan_time_us(Tile t, int64_t rows_cap, int64_t N, int64_t K, int64_t s) {
+    const TileModel m = tile_model(t);
+    const int64_t tiles = ((rows_cap + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t slots = static_cast<int64_t>(kNumCUs) * occupancy(t);
+    const int64_t waves = (tiles * s + slots - 1) / slots;
+    const double per = m.fixed_us + 2.0 * t.bm * t.bn * static_cast<double>(split_k(K, s)) / m.rate * 1e6;
+    double us = static_cast<double>(waves) * per;
+    if (s > 1) us += static_cast<double>(s) * rows_cap * N * 8.0 / 6e12 * 1e6 + 4.0;
+    return us;
+}
+
+// Best split of K for a tile: 1..8 ways, at least 256 K per split.
+int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double* us_out) {
+    int64_t best = 1;
+    double best_us = plan_time_us(t, rows_cap, N, K, 1);
+    for (int64_t s = 2; s <= 8 && K / s >= 256; ++s) {
+        const double us = plan_time_us(t, rows_cap, N, K, s);
+        if (us < best_us * 0.97) {  // a split must pay for itself clearly
+            best_us = us;
+            best = s;
+        }
+    }
+    if (us_out) *us_out = best_us;
+    return best;
+}
+
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs)) return forced;
-    const Tile cands[] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}, {64, 128}};
-    Tile best{64, 128};
-    double best_t = 1e300;
+    const Tile cands[] = {{256, 256, 4}, {256, 256, 8}, {256, 128, 4}, {128, 256, 4}, {128, 128, 4}, {64, 128, 4}};
+    Tile best{64, 128, 4};
+    double best_us = 1e300;
     for (const Tile& t : cands) {
         if (!tile_fits(t, gs)) continue;
-        const int64_t tiles = ((rows_cap + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-        const int64_t slots = static_cast<int64_t>(kNumCUs) * occupancy(t);
-        const int64_t waves = (tiles + slots - 1) / slots;
-        // time ~ waves x (tile work / efficiency / occupancy share)
-        const double est = static_cast<double>(waves) * t.bm * t.bn * static_cast<double>(K) /
-                           (tile_eff(t) * occupancy(t));
-        if (est < best_t * 0.999) {
-            best_t = est;
+        double us = 0;
+        choose_split_for(t, rows_cap, N, K, &us);
+        if (us < best_us * 0.999) {
+            best_us = us;
             best = t;
         }
     }
     return best;
-}
-
-void choose_split(int64_t tiles, int64_t K, int32_t& splits, int64_t& kps) {
-    int64_t s = 1;
-    if (tiles < kNumCUs / 2) {
-        s = (kNumCUs + tiles - 1) / tiles;
-        s = std::min<int64_t>(s, std::max<int64_t>(1, K / (4 * kBK)));
-    }
-    kps = ((K + s - 1) / s + kBK - 1) / kBK * kBK;
-    splits = static_cast<int32_t>((K + kps - 1) / kps);
 }
 
 struct GemmPlan {
@@ -764,22 +763,29 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs) {
     GemmPlan p{};
     p.rows_cap = rows_cap_for(M);
-    p.tile = tmode ? Tile{128, 128} : choose_tile(p.rows_cap, N, K, gs);
-    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128};
-    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128};
+    // The plan covers rows_cap rows (room for both segments' padding), but in
+    // the usual case (segments of whole 32-row blocks) the last 32 are empty
+    // and their tiles exit at once: rank plans on the rows that hold work.
+    const int64_t rows_model = std::max<int64_t>(p.rows_cap - kRowAlign, kRowAlign);
+    p.tile = tmode ? Tile{128, 128, 4} : choose_tile(rows_model, N, K, gs);
+    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128, 4};
+    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
-    choose_split(p.m_tiles * p.n_tiles, K, p.splits, p.kps);
+    // T mode works on the draft rows only (at most rows_cap of them)
+    const int64_t s = choose_split_for(p.tile, rows_model, N, K, nullptr);
+    p.kps = split_k(K, s);
+    p.splits = static_cast<int32_t>((K + p.kps - 1) / p.kps);
     p.partial_bytes = p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float),
                                               kWorkspaceAlign)
                                    : 0;
     return p;
 }
 
-template <int BM, int BN, bool TMODE>
+template <int BM, int BN, int WGM, int WGN, bool TMODE>
 void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, TMODE>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kGemmThreads), 0, stream, ka);
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, TMODE>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(TileCfg<BM, BN, WGM, WGN>::THREADS), 0, stream, ka);
 }
 
 template <bool TMODE>
@@ -792,14 +798,15 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
     const int64_t blocks = p.m_tiles * p.n_tiles * p.splits;
     const Tile t = p.tile;
     if constexpr (TMODE) {
-        if (t.bm == 128) launch_tile<128, 128, true>(ka, blocks, stream);
-        else launch_tile<64, 128, true>(ka, blocks, stream);
+        if (t.bm == 128) launch_tile<128, 128, 2, 2, true>(ka, blocks, stream);
+        else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
-        if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, false>(ka, blocks, stream);
-        else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, false>(ka, blocks, stream);
-        else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, false>(ka, blocks, stream);
-        else if (t.bm == 128 && t.bn == 128) launch_tile<128, 128, false>(ka, blocks, stream);
-        else launch_tile<64, 128, false>(ka, blocks, stream);
+        if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128) launch_tile<128, 128, 2, 2, false>(ka, blocks, stream);
+        else launch_tile<64, 128, 2, 2, false>(ka, blocks, stream);
     }
     if (p.splits > 1) {
         const int64_t elems = p.rows_cap * ka.N;
