@@ -15,8 +15,10 @@ alpha 256), 32 sequences x [16 verify | 16 draft] rows, verification of a
 sigma = 1, T = 1).  Weights are random-initialised bf16; data is synthetic.
 
 Prints one JSON line: verified tokens/s (emitted tokens summed over the timed
-steps / elapsed time), the roofline of the dominant kernel (the gated-LoRA
-GEMM, bf16 MFMA), and the oracle timed on the host cores on a bounded sample.
+steps / elapsed time), the roofline of the dominant kernel (the gated GEMM,
+bf16 MFMA: algorithmic flops 2MKN + 2 Md r N per launch over its HIP-event
+time, every launch of the timed steps), block verification's HBM rate, and
+the oracle timed on the host cores on a bounded sample.
 """
 
 import argparse
@@ -31,7 +33,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-RANK = 128
 SCALE = 2.0                   # alpha / r = 256 / 128
 
 
@@ -42,13 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack32_b32", choices=["stack32_b32", "layer_b1", "layer_b64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
-
-
-def gemm_flops(M, Md, K, N, r=RANK):
-    """Algorithmic flops of one gated projection: 2MKN + 2 Md r (K + N)."""
-    return 2.0 * M * K * N + 2.0 * Md * r * (K + N)
 
 
 def verify_bytes(B, L, V, esz=2, redraws=None):
@@ -107,6 +102,7 @@ def main():
     gate_np = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
     gate = torch.from_numpy(gate_np).to(dev)
     stack = uno.GatedLoraStack(layers, gate, SCALE)
+    del layers  # the stack holds its own (stacked) copies
     x0 = sdev.randn((M, wl.projections[0][1]), 1.0, wl.seed)
     z, d = sdev.verify_logits(B, L, V, wl.seed, kind=wl.logits, target_sigma=wl.target_sigma,
                               draft_sigma=sigma)
@@ -119,63 +115,51 @@ def main():
     vws = uno.Workspace(dev)
     torch.cuda.synchronize()
 
-    def step(i):
+    verify_events = []
+
+    def step(i, timed):
+        stack.timer = gemm_events if timed else None
         stack.forward(x0)
         uno.philox_uniforms(0, 0, i * B * (L + 1), B * (L + 1), out=u)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
         uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[i], out_tok[i], n_emit[i]), workspace=vws)
+        if timed:
+            e1.record()
+            verify_events.append((e0, e1, i))
 
     for i in range(args.warmup):
-        step(i)
+        step(i, False)
     torch.cuda.synchronize()
+    # The dominant kernel (the gated GEMM) and block verification are timed
+    # per launch with HIP events recorded on the stream they run on, inside
+    # the timed steps themselves.
+    gemm_events = []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.warmup, total_steps):
-        step(i)
+        step(i, True)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    stack.timer = None
     gpu_ms = ev0.elapsed_time(ev1)
     elapsed = max(wall, gpu_ms / 1e3)
     tokens = int(n_emit[args.warmup:].sum().item())
     ms_per_step = elapsed * 1e3 / args.steps
     value = tokens / elapsed
 
-    # ---------------- dominant kernel: the gated-LoRA projection, timed per launch with HIP events
-    trace = {}
-    stack.forward(x0, trace_layer=0, trace=trace)
-    torch.cuda.synchronize()
-    layer0 = layers[0]
-    durations, flops = [], []
-    for name, K, N in wl.projections:
-        inp, _ = trace[name]
-        w, a, b = layer0[name]
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            uno.gated_lora_fwd(inp, w, a, b, gate, SCALE, out=out, workspace=stack.ws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.kernel_reps):
-            uno.gated_lora_fwd(inp, w, a, b, gate, SCALE, out=out, workspace=stack.ws)
-        e1.record()
-        torch.cuda.synchronize()
-        durations.append(e0.elapsed_time(e1) / args.kernel_reps / 1e3)
-        flops.append(gemm_flops(M, Md, K, N))
-    gemm_achieved = sum(flops) / sum(durations) / 1e12
+    gemm_s = sum(a.elapsed_time(b) for a, b, _ in gemm_events) / 1e3
+    gemm_flop = sum(f for _, _, f in gemm_events)
+    n_gemm = len(gemm_events)
+    gemm_achieved = gemm_flop / gemm_s / 1e12
     digest = source_digest("gemm.hip")
     traffic = committed_traffic("gated_gemm", digest)
 
-    # verify kernel chain, timed alone
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(3):
-        uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[0], out_tok[0], n_emit[0]), workspace=vws)
-    e0.record()
-    for _ in range(args.kernel_reps):
-        uno.block_verify(z, d, drafts, u, T, False, outputs=(n_acc[0], out_tok[0], n_emit[0]), workspace=vws)
-    e1.record()
-    torch.cuda.synchronize()
-    vt = e0.elapsed_time(e1) / args.kernel_reps / 1e3
-    redraws = int((n_acc[0] < L).sum().item())
+    vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
+    redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
     v_gbs = verify_bytes(B, L, V, 2, redraws) / vt / 1e9
 
     result = {
@@ -204,14 +188,16 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "gated-LoRA projection (uno_gated_lora_fwd), 7 shapes of one layer",
+            "kernel": "gated GEMM (gated_gemm_kernel, main mode, with its split-K reduction where planned): "
+                      "every launch of the timed steps",
             "achieved": round(gemm_achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "avg_launch_us": round(sum(durations) / len(durations) * 1e6, 3),
-            "algorithmic_gflop_per_launch": round(sum(flops) / len(flops) / 1e9, 4),
+            "launches": n_gemm,
+            "avg_launch_us": round(gemm_s / n_gemm * 1e6, 3),
+            "algorithmic_gflop_per_launch": round(gemm_flop / n_gemm / 1e9, 4),
         },
         "verify_roofline": {
             "bound": "hbm",
@@ -220,16 +206,16 @@ def main():
             "unit": "GB/s",
             "frac": round(v_gbs / PEAK_HBM_GBS, 4),
             "us_per_call": round(vt * 1e6, 3),
+            "redraws_per_call": redraws,
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, layers, trace, x0, z, d, drafts, u, gate_np, T, L,
-                                              tokens / args.steps)
+        result["cpu_baseline"] = cpu_baseline(wl, stack.layers, x0, z, d, drafts, u, gate_np, T, L)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, layers, trace, x0, z, d, drafts, u, gate_np, T, L, gpu_tokens_per_step):
+def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):
     """The fp64 oracle on the host cores: one layer of the stack and verification of a few sequences,
     scaled to a full step (layers x layer time + sequences x per-sequence verify time)."""
     import numpy as np

@@ -1,0 +1,175 @@
+"""Summaries of rocprofv3 output for the profiles/ folder (host-side text processing).
+
+    python -m lossless_speculative_drafting_amd.rocprof_summary stats KERNEL_STATS_CSV \\
+        --title TITLE --command CMD [--top N] [--group NAME=SUBSTRING ...]
+        Markdown table of a `--kernel-trace --stats` run, plus named groups of
+        kernels with their combined time per launch of the group's first member.
+
+    python -m lossless_speculative_drafting_amd.rocprof_summary copy-probe [--mib N]
+        Run one plain device copy of N MiB (torch copy_ of a bf16 tensor): the
+        known-size reference whose FETCH_SIZE / WRITE_SIZE calibrate the counters.
+
+    python -m lossless_speculative_drafting_amd.rocprof_summary traffic \\
+        --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib N \\
+        --key NAME --launch SUBSTRING [--also SUBSTRING] --source FILE ...
+        HBM bytes per launch of a kernel from two `--pmc` runs (FETCH_SIZE, then
+        WRITE_SIZE; KiB per dispatch), each scaled by the factor that makes the
+        copy probe's reading equal its known size.  A launch is one dispatch of
+        a kernel whose name contains --launch; dispatches matching --also
+        (a split-K reduction, say) are counted into the launch they follow.
+        Prints JSON with the digest of the named sources, so that a reader can
+        tell whether the numbers still describe the current code.
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name, width=96):
+    name = name.replace("uno::(anonymous namespace)::", "")
+    cut = name.find("(")
+    if cut > 0 and not name.startswith("void at::"):
+        name = name[:cut]
+    return name if len(name) <= width else name[:width - 3] + "..."
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = [f"# {args.title}", "", "Command (run from the repository root on one MI355X):", "", "```",
+           args.command, "```", "", "| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows[:args.top]:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    if args.group:
+        out += ["", "| group | launches | total ms | avg us per launch |", "|---|---:|---:|---:|"]
+        for spec in args.group:
+            gname, _, subs = spec.partition("=")
+            parts = subs.split("|")
+            launches = sum(int(r["Calls"]) for r in rows if parts[0] in r["Name"])
+            tot = sum(float(r["TotalDurationNs"]) for r in rows if any(p in r["Name"] for p in parts))
+            if launches:
+                out.append(f"| {gname} | {launches} | {tot / 1e6:.3f} | {tot / launches / 1e3:.2f} |")
+    out += ["", f"All kernels: {total / 1e6:.3f} ms."]
+    print("\n".join(out))
+
+
+def copy_probe(args):
+    import torch
+    n = args.mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {args.mib} MiB", flush=True)
+
+
+def _per_dispatch(path, counter):
+    """[(dispatch id, kernel name, value)] in dispatch order for one counter."""
+    acc = defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        acc[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(d, names[d], acc[d]) for d in sorted(acc)]
+
+
+def _copy_kib(path, counter):
+    vals = [v for _, n, v in _per_dispatch(path, counter) if "copy" in n.lower()]
+    if not vals:
+        raise SystemExit(f"no copy kernel with {counter} in {path}")
+    return max(vals)
+
+
+def _launch_kib(path, counter, launch, also):
+    per_launch, cur = [], None
+    for _, name, v in _per_dispatch(path, counter):
+        if launch in name:
+            if cur is not None:
+                per_launch.append(cur)
+            cur = v
+        elif also and any(a in name for a in also) and cur is not None:
+            cur += v
+    if cur is not None:
+        per_launch.append(cur)
+    if not per_launch:
+        raise SystemExit(f"no dispatch of {launch!r} in {path}")
+    return sum(per_launch) / len(per_launch), len(per_launch)
+
+
+def traffic(args):
+    known = args.copy_mib * float(1 << 20)
+    f_fac = known / (_copy_kib(args.copy_fetch, "FETCH_SIZE") * 1024.0)
+    w_fac = known / (_copy_kib(args.copy_write, "WRITE_SIZE") * 1024.0)
+    f_kib, n_f = _launch_kib(args.fetch, "FETCH_SIZE", args.launch, args.also)
+    w_kib, n_w = _launch_kib(args.write, "WRITE_SIZE", args.launch, args.also)
+    rec = {
+        "source_digest": source_digest(args.source),
+        "sources": args.source,
+        "launch_kernel": args.launch,
+        "counted_with_it": args.also,
+        "launches": [n_f, n_w],
+        "fetch_kib_per_launch_raw": round(f_kib, 1),
+        "write_kib_per_launch_raw": round(w_kib, 1),
+        "fetch_scale": round(f_fac, 4),
+        "write_scale": round(w_fac, 4),
+        "bytes_per_launch": round(f_kib * 1024.0 * f_fac + w_kib * 1024.0 * w_fac),
+    }
+    path = args.out
+    data = {}
+    if path and os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[args.key] = rec
+    text = json.dumps(data, indent=1, sort_keys=True)
+    if path:
+        with open(path, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--top", type=int, default=16)
+    s.add_argument("--group", action="append", default=[])
+    c = sub.add_parser("copy-probe")
+    c.add_argument("--mib", type=int, default=1024)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--key", required=True)
+    t.add_argument("--launch", required=True)
+    t.add_argument("--also", action="append", default=[])
+    t.add_argument("--source", action="append", required=True)
+    t.add_argument("--out", default=None)
+    args = ap.parse_args(argv)
+    {"stats": stats, "copy-probe": copy_probe, "traffic": traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

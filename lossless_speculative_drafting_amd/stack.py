@@ -81,6 +81,8 @@ class GatedLoraStack:
         r = l0["q"][1].shape[0]
         bf = torch.bfloat16
         self.M, self.hidden, self.kv, self.ffn, self.r = M, hidden, kv, ffn, r
+        self.Md = int(gate.to(torch.int64).sum().item())  # draft rows (one host sync, here)
+        self.timer = None
         self.h = torch.empty((M, hidden), dtype=bf, device=dev)
         self.q = torch.empty((M, hidden), dtype=bf, device=dev)
         self.k = torch.empty((M, kv), dtype=bf, device=dev)
@@ -111,15 +113,31 @@ class GatedLoraStack:
         self.t = torch.empty(_lib.lora_t_size(M, t_width) // 2, dtype=bf, device=dev)
         self.plan = None
 
+    def _timed(self, K, N, launch):
+        """Run one gated-GEMM launch; with a timer list set, bracket it with
+        HIP events on the current stream and record its algorithmic flops
+        (2 M K N for the product, 2 Md r N for the adapter extension)."""
+        if self.timer is None:
+            launch()
+            return
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        self.timer.append((e0, e1, 2.0 * self.M * K * N + 2.0 * self.Md * self.r * N))
+
     def _proj(self, layer, name, inp, out):
         w, a, b = layer[name]
         _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
-        _lib.gated_gemm(inp, w, self.t, b, self.plan, out=out, workspace=self.ws)
+        self._timed(w.shape[1], w.shape[0],
+                    lambda: _lib.gated_gemm(inp, w, self.t, b, self.plan, out=out, workspace=self.ws))
 
     def _group(self, li, names, inp, outs):
         w, a, b, ns = self.groups[li][names]
         _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
-        _lib.gated_gemm_grouped(inp, w, self.t, b, self.plan, ns, outs=outs, workspace=self.ws)
+        self._timed(w.shape[1], w.shape[0],
+                    lambda: _lib.gated_gemm_grouped(inp, w, self.t, b, self.plan, ns, outs=outs,
+                                                    workspace=self.ws))
 
     def _projections(self, li, layer, items, trace_into):
         """items: [(name, input, output)] sharing one input when grouped."""
