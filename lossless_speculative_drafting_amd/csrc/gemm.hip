@@ -35,6 +35,7 @@
 // fp32 path (correctness path for small problems): plain FMA loops, T kept
 // in fp32.
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <type_traits>
@@ -45,8 +46,7 @@
 namespace uno {
 namespace {
 
-constexpr int kBK = 32;        // K per pipeline stage
-constexpr int kNBUF = 4;       // LDS stage buffers: up to three stages of copies in flight
+constexpr int kStageK = 64;    // K granularity of split-K plans (a multiple of every stage depth)
 constexpr int kRowAlign = 32;  // segment padding = MFMA block height
 constexpr int kMaxGroups = 4;  // output column groups of one launch
 constexpr uint32_t kOOB = 0x80000000u;       // buffer offset past every range: loads return 0
@@ -226,38 +226,59 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(p)));
 }
 
-// LDS tile rows hold 32 bf16 (four 16-byte chunks); chunk c of row r lives at
-// chunk position c ^ ((r >> 2) & 3).  A fragment read has lanes 0..31 on 32
-// consecutive rows at one chunk; gfx950 serves a 16-byte-per-lane LDS read 16
-// lanes at a time across 64 four-byte banks (four 64-byte rows), and over any
-// 16 consecutive rows the pairs (r & 3, c ^ ((r >> 2) & 3)) are all distinct,
-// so each 16-lane group touches every bank once.
+// LDS stage layout: row-major [rows][KB] bf16 in 16-byte chunks, chunk c of
+// row r stored at chunk position c ^ s(r).  A fragment read has lanes 0..31
+// on 32 consecutive rows at one chunk; gfx950 serves a 16-byte-per-lane LDS
+// read 16 lanes at a time across 64 four-byte banks (256 bytes), so a read is
+// conflict-free when the 16 rows of each 16-lane group cover every bank once:
+//   KB = 64 (128-byte rows, two per 256 bytes): s(r) = (r & 7) ^ ((r >> 3) & 1)
+//     makes (r & 1, c ^ s(r)) distinct over 16 consecutive rows;
+//   KB = 32 (64-byte rows, four per 256 bytes): s(r) = (r >> 2) & 3 makes
+//     (r & 3, c ^ s(r)) distinct.
+template <int KB>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * kBK + ((chunk ^ ((row >> 2) & 3)) << 3);
+    if constexpr (KB == 64) return row * KB + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 3);
+    else return row * KB + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-template <int BM, int BN, int WGM, int WGN>
+// KB: K per pipeline stage (64 or 32); NBUF LDS stage buffers, NBUF * KB =
+// 128 (two 64-deep stages or four 32-deep ones).  A copy instruction moves
+// 1 KB: RB rows of 2*KB bytes.  Rows of 128 bytes move at about twice the
+// rate of rows of 64 bytes (L2-resident sources, measured on MI355X: 110 vs
+// 59 GB/s per CU), so KB = 64 is the default; KB = 32 keeps three stages in
+// flight where LDS would otherwise hold only two.
+template <int BM, int BN, int WGM, int WGN, int KB>
 struct TileCfg {
+    static_assert(KB == 64 || KB == 32, "stage depth");
+    static constexpr int NBUF = 128 / KB;
+    static constexpr int KSUB = KB / 16;       // MFMA sub-steps per stage
+    static constexpr int RB = 512 / KB;        // rows per copy instruction
     static constexpr int NWAVES = WGM * WGN;   // WGM x WGN wavefronts
     static constexpr int THREADS = NWAVES * kWave;
     static constexpr int WM = BM / WGM;
     static constexpr int WN = BN / WGN;
     static constexpr int MI = WM / 32;         // 32x32 MFMA blocks per wavefront
     static constexpr int NJ = WN / 32;
-    static constexpr int AQ = BM / (16 * NWAVES);  // 16-row DMA blocks per wavefront per stage (A)
-    static constexpr int BQ = BN / (16 * NWAVES);  // (B)
-    static_assert(AQ >= 1 && BQ >= 1 && AQ * 16 * NWAVES == BM && BQ * 16 * NWAVES == BN, "copy split");
+    static constexpr int AQ = BM / (RB * NWAVES);  // copy instructions per wavefront per stage (A)
+    static constexpr int BQ = BN / (RB * NWAVES);  // (B)
+    static_assert(AQ >= 1 && BQ >= 1 && AQ * RB * NWAVES == BM && BQ * RB * NWAVES == BN, "copy split");
+    static_assert(KB == 32 || ((BM / NWAVES) % (2 * RB) == 0 && (BN / NWAVES) % (2 * RB) == 0),
+                  "with KB 64 each wavefront's copy blocks start on an even block (the swizzle parity is q & 1)");
     static_assert(MI >= 1 && NJ >= 1 && WN >= 64, "wavefront tile");
-    static constexpr int STAGE_ELEMS = (BM + BN) * kBK;
-    static constexpr int LDS_ELEMS = kNBUF * STAGE_ELEMS;
+    static constexpr int STAGE_ELEMS = (BM + BN) * KB;
+    static constexpr int LDS_ELEMS = NBUF * STAGE_ELEMS;
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
-    static_assert(4 * WM * WN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
+    static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
-template <int BM, int BN, int WGM, int WGN, bool TMODE>
-__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN>::THREADS), (TileCfg<BM, BN, WGM, WGN>::OCC))
+template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP>
+__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB>::THREADS), (TileCfg<BM, BN, WGM, WGN, KB>::OCC))
 void gated_gemm_kernel(const GemmKArgs a) {
-    using C = TileCfg<BM, BN, WGM, WGN>;
+    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32), "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32");
+    using C = TileCfg<BM, BN, WGM, WGN, KB>;
+    constexpr int kBK = KB;
+    constexpr int kNBUF = C::NBUF;
+    constexpr int RB = C::RB;
     constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
     __shared__ int32_t s_orow[BM];  // output row of each tile row (-1: none)
@@ -305,34 +326,44 @@ void gated_gemm_kernel(const GemmKArgs a) {
     const int wm = wave / WGN;
     const int wn = wave % WGN;
 
-    const int lrow = lane >> 2;  // row within a 16-row DMA block
-    // byte offset within a row of the chunk this lane copies: the logical chunk
-    // stored at physical position lane & 3 of row lrow (blocks start at
-    // multiples of 16 rows, so (row >> 2) & 3 = lane >> 4)
-    const uint32_t kc = static_cast<uint32_t>(((lane & 3) ^ (lane >> 4)) * 16);
-    const uint32_t kcol = kc >> 1;  // its K index within the stage
+    // Copy lane mapping: lane l takes row lrow of an RB-row block and the
+    // logical chunk stored at physical chunk position pc of that row, so the
+    // instruction's 1 KB lands in LDS exactly in the swizzled layout.  Blocks
+    // start on multiples of RB rows; with KB = 64 the swizzle also depends on
+    // the block's parity (row bit 3), with KB = 32 only on lane bits.
+    constexpr int LPR = 64 / RB;  // lanes per row
+    const int lrow = lane / LPR;
+    const int pc = lane % LPR;
+    uint32_t kc_par[2];
+    if constexpr (KB == 64) {
+        kc_par[0] = static_cast<uint32_t>((pc ^ lrow) * 16);
+        kc_par[1] = static_cast<uint32_t>((pc ^ lrow ^ 1) * 16);
+    } else {
+        kc_par[0] = kc_par[1] = static_cast<uint32_t>((pc ^ (lrow >> 2)) * 16);
+    }
+    const uint32_t kcol_par[2] = {kc_par[0] >> 1, kc_par[1] >> 1};  // K index within the stage
     uint32_t xoff[AQ];  // x row offsets (gathered through the plan) + chunk offset
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-        const int64_t p = m0 + wave * (BM / C::NWAVES) + q * 16 + lrow;
+        const int64_t p = m0 + wave * (BM / C::NWAVES) + q * RB + lrow;
         int64_t src;
         if constexpr (TMODE) {
             src = (p < info.Md) ? a.perm[info.Pv + p] : -1;
         } else {
             src = (p < rows_valid) ? a.perm[p] : -1;
         }
-        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kc;
+        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kc_par[q & 1];
     }
     const uint32_t ldw2 = static_cast<uint32_t>(a.ldw * 2);
-    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldw2 + kc;
+    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldw2;
     uint32_t ldt2 = 0, ldb2 = 0, trow0 = 0, brow0 = 0;
     if constexpr (!TMODE) {
         ldt2 = static_cast<uint32_t>(a.ldt * 2);
         ldb2 = static_cast<uint32_t>(a.ldb * 2);
         // T row of this lane's first A block; verify rows give a negative
         // row whose wrapped byte offset is far past the range
-        trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - info.Pv) * ldt2 + kc;
-        brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2 + kc;
+        trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - info.Pv) * ldt2;
+        brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2;
     }
     // output group of this tile (tiles never straddle groups); its draft rows
     // read T from column grp.g * r on
@@ -366,10 +397,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
     const int32_t kb_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(kb));
     const int32_t ke_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(ke));
 
-    // ---- copies.  Stage `it` goes to LDS buffer it % kNBUF as AQ + BQ DMA
-    // items per wavefront: wavefront w copies rows [w*BM/4, (w+1)*BM/4) of the
-    // A tile (and likewise of B) in 16-row blocks, lane l taking row l/4 of a
-    // block.  Main stages read x rows (through the row plan) and W_AR rows;
+    // ---- copies.  Stage `it` goes to LDS buffer it % NBUF as AQ + BQ copy
+    // items per wavefront: wavefront w copies rows [w*BM/W, (w+1)*BM/W) of
+    // the A tile (W wavefronts; likewise for B) in RB-row blocks.  Main stages read x rows (through the row plan) and W_AR rows;
     // extension stages read T rows and lora_b rows.  Nothing here branches: a
     // row past the end of its operand lands past the descriptor's range (whose
     // size is cut to the valid rows) and reads zeros, a chunk past the end of K
@@ -402,18 +432,18 @@ void gated_gemm_kernel(const GemmKArgs a) {
     };
     auto dma_item = [&](const StageSrc& ss, int q) __attribute__((always_inline)) {
         if (q < AQ) {
-            const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / C::NWAVES) + q * 16) * kBK * 2);
-            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * 16) * ldt2;
+            const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / C::NWAVES) + q * RB) * kBK * 2);
+            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * RB) * ldt2 + kc_par[q & 1];
             uint32_t off = (ss.ext ? ext_off : xoff[q]) + ss.kbytes;
-            if (kcol >= ss.krem) off = kOOB;
+            if (kcol_par[q & 1] >= ss.krem) off = kOOB;
             dma16(la, off, make_rsrc(reinterpret_cast<const void*>(ss.abase), ss.arange));
         } else {
             const int qb = q - AQ;
-            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / C::NWAVES) + qb * 16) * kBK) * 2);
-            const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * 16) * ldw2;
-            const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * 16) * ldb2;
-            uint32_t off = (ss.ext ? off_b : off_w) + ss.kbytes;
-            if (kcol >= ss.krem) off = kOOB;
+            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / C::NWAVES) + qb * RB) * kBK) * 2);
+            const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * RB) * ldw2;
+            const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * RB) * ldb2;
+            uint32_t off = (ss.ext ? off_b : off_w) + kc_par[qb & 1] + ss.kbytes;
+            if (kcol_par[qb & 1] >= ss.krem) off = kOOB;
             dma16(lb, off, make_rsrc(reinterpret_cast<const void*>(ss.bbase), ss.brange));
         }
     };
@@ -426,15 +456,19 @@ void gated_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // ---- schedule.  A stage is two MFMA sub-steps (K = 16 each).  Fragments
-    // are double-buffered in registers (set 0 / 1): reads for the next
-    // sub-step are issued before the MFMAs of the current one, and
+    // ---- schedule.  A stage is KSUB MFMA sub-steps (K = 16 each).
+    // Fragments are double-buffered in registers (set 0 / 1): reads for the
+    // next sub-step are issued before the MFMAs of the current one, and
     // sched_barrier fences keep the compiler from sinking them to their uses.
-    // Stage s+3 is copied while stage s is computed (its buffer held stage
-    // s-1, retired by the barrier that opens stage s), its items spread
-    // between the MFMAs of the first sub-step; before the barrier that opens
-    // stage s+1 each wavefront waits until at most two stages of its copies
-    // are outstanding, i.e. until stage s+1 has landed.
+    // Stage s + NBUF - 1 is copied while stage s is computed (its buffer held
+    // stage s - 1, retired by the barrier that opens stage s), its items
+    // spread between the MFMAs of all sub-steps but the last; before the
+    // barrier that opens stage s + 1 each wavefront waits until at most
+    // NBUF - 2 stages of its copies are outstanding, i.e. until stage s + 1
+    // has landed.  The last sub-step's MFMAs run after that barrier, while
+    // the first fragments of stage s + 1 are read.
+    constexpr int KSUB = C::KSUB;
+    constexpr int AHEAD = kNBUF - 1;
     bf16x8 af[2][MI], bfr[2][NJ];
     auto read_frags = [&](int buf, int kk, int set) __attribute__((always_inline)) {
         const uint16_t* sa = smem + buf * C::STAGE_ELEMS;
@@ -443,12 +477,12 @@ void gated_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int row = wm * C::WM + i * 32 + (lane & 31);
-            af[set][i] = *reinterpret_cast<const bf16x8*>(&sa[lds_off(row, chunk)]);
+            af[set][i] = *reinterpret_cast<const bf16x8*>(&sa[lds_off<KB>(row, chunk)]);
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int row = wn * C::WN + j * 32 + (lane & 31);
-            bfr[set][j] = *reinterpret_cast<const bf16x8*>(&sb[lds_off(row, chunk)]);
+            bfr[set][j] = *reinterpret_cast<const bf16x8*>(&sb[lds_off<KB>(row, chunk)]);
         }
     };
     // Extension stages need no per-block test: verify rows read zero T rows
@@ -456,71 +490,138 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // accumulators that started at +0 and therefore can never be -0 (round to
     // nearest) -- the verify rows keep the bits of a call with all gates 0.
     //
-    // One MFMA group (all MI x NJ blocks of fragment set `set`), with the
-    // copy items of `ss` (when given) spread evenly between its MFMAs.
+    // One MFMA group (all MI x NJ blocks of fragment set `set`), with copy
+    // items [q0, q1) of `ss` (when given) spread evenly between its MFMAs.
     constexpr int GROUP = MI * NJ;
-    constexpr int SPACING = GROUP / NITEM > 0 ? GROUP / NITEM : 1;
-    constexpr int IN_GROUP = GROUP / SPACING < NITEM ? GROUP / SPACING : NITEM;
-    auto mfma_group = [&](int set, const StageSrc* ss) __attribute__((always_inline)) {
-        int m = 0;
+    auto mfma_group = [&](int set, const StageSrc* ss, int q0, int q1) __attribute__((always_inline)) {
+        const int nq = ss != nullptr ? q1 - q0 : 0;
+        const int spacing = nq > 0 && GROUP / nq > 0 ? GROUP / nq : 1;
+        int m = 0, q = q0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
                 ++m;
-                if (ss != nullptr && m % SPACING == 0 && m / SPACING <= IN_GROUP) {
+                if (ss != nullptr && m % spacing == 0 && q < q1) {
                     __builtin_amdgcn_sched_barrier(0);
-                    dma_item(*ss, m / SPACING - 1);
+                    dma_item(*ss, q);
+                    ++q;
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         if (ss != nullptr) {
 #pragma unroll
-            for (int q = IN_GROUP; q < NITEM; ++q) dma_item(*ss, q);
+            for (int qq = q0 + GROUP / spacing; qq < q1; ++qq) dma_item(*ss, qq);
         }
     };
+    // copy items per sub-step window (all sub-steps but the last carry items)
+    constexpr int WIN = KSUB - 1;
+    constexpr int PER_WIN = (NITEM + WIN - 1) / WIN;
 
     // stage `it` (its first fragments already read), then open stage it+1
     auto body_next = [&](int it) __attribute__((always_inline)) {
         const int buf = it % kNBUF;
-        const StageSrc ahead = stage_src(it + 3);
-        read_frags(buf, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, &ahead);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<2 * NITEM>();  // this wavefront's copy of stage it+1 has landed
-        __syncthreads();          // ... every wavefront's; and buffer `buf` is no longer read
+        const StageSrc ahead = stage_src(it + AHEAD);
+#pragma unroll
+        for (int kk = 0; kk < KSUB - 1; ++kk) {
+            read_frags(buf, kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_group(kk & 1, &ahead, kk * PER_WIN, (kk + 1) * PER_WIN < NITEM ? (kk + 1) * PER_WIN : NITEM);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt<(kNBUF - 2) * NITEM>();  // this wavefront's copy of stage it+1 has landed
+        __syncthreads();                    // ... every wavefront's; and buffer `buf` is no longer read
         read_frags((it + 1) % kNBUF, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, nullptr);
+        mfma_group((KSUB - 1) & 1, nullptr, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto body_last = [&](int it) __attribute__((always_inline)) {
-        read_frags(it % kNBUF, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(0, nullptr);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_group(1, nullptr);
+        const int buf = it % kNBUF;
+#pragma unroll
+        for (int kk = 0; kk < KSUB - 1; ++kk) {
+            read_frags(buf, kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_group(kk & 1, nullptr, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_group((KSUB - 1) & 1, nullptr, 0, 0);
     };
 
-    if (nk_s > 0) {
-        {  // stages 0, 1 and 2 (stages past the last copy zeros into free buffers)
-            const StageSrc s0 = stage_src(0), s1 = stage_src(1), s2 = stage_src(2);
+    if (!PP && nk_s > 0) {
+        // stages 0 .. NBUF-2 (stages past the last copy zeros into free buffers)
 #pragma unroll
-            for (int q = 0; q < NITEM; ++q) dma_item(s0, q);
+        for (int st = 0; st < AHEAD; ++st) {
+            const StageSrc ss = stage_src(st);
 #pragma unroll
-            for (int q = 0; q < NITEM; ++q) dma_item(s1, q);
-#pragma unroll
-            for (int q = 0; q < NITEM; ++q) dma_item(s2, q);
+            for (int q = 0; q < NITEM; ++q) dma_item(ss, q);
         }
-        wait_vmcnt<2 * NITEM>();  // stage 0 landed
+        wait_vmcnt<(kNBUF - 2) * NITEM>();  // stage 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
         for (int it = 0; it < nk_s - 1; ++it) body_next(it);
         body_last(nk_s - 1);
         // copies of stages past the last write zeros into free buffers; let
         // them land before the epilogue reuses LDS
+        wait_vmcnt<0>();
+    }
+
+    if (PP && nk_s > 0) {
+        // Ping-pong.  Wavefronts 0-3 (team 0) own tile rows [0, BM/2), 4-7
+        // (team 1) the rest, one wavefront of each team per SIMD.  Phases
+        // alternate: in even phases team 0 issues its MFMAs back to back while
+        // team 1 reads the fragments of its next stage and copies its rows of
+        // a later stage, in odd phases the other way round; one workgroup
+        // barrier closes each phase.  Team 0 computes stage s in phase 2s,
+        // team 1 in phase 2s + 1, each from fragments read in its phase before.
+        // Team 0 copies its rows of stage t in phase 2t - 7, team 1 in phase
+        // 2t - 6: the buffer last held stage t - 4, whose last reader (team 1,
+        // phase 2t - 8) is done.  A memory phase ends once at most two later
+        // stages of the wavefront's own copies are in flight, so stage s is
+        // whole by the barrier before phase 2s - 1, where team 0 reads it.
+        const int team = wave >> 2;  // scalar
+        auto load_stage = [&](int st) __attribute__((always_inline)) {
+            read_frags(st % kNBUF, 0, 0);
+            read_frags(st % kNBUF, 1, 1);
+        };
+        auto copy_stage = [&](int st) __attribute__((always_inline)) {
+            const StageSrc ss = stage_src(st);
+#pragma unroll
+            for (int q = 0; q < NITEM; ++q) dma_item(ss, q);
+        };
+        copy_stage(0);
+        copy_stage(1);
+        copy_stage(2);
+        if (team == 0) {
+            copy_stage(3);
+            wait_vmcnt<3 * NITEM>();
+        } else {
+            wait_vmcnt<2 * NITEM>();
+        }
+        __syncthreads();  // stage 0 whole
+        if (team == 0) {
+            load_stage(0);
+            wait_vmcnt<2 * NITEM>();  // own rows of stage 1 landed
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        const int nph = 2 * nk_s;
+        for (int p = 0; p < nph; ++p) {
+            if ((p & 1) == team) {
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_group(0, nullptr, 0, 0);
+                mfma_group(1, nullptr, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // the stage this team computes next (past the last stage the
+                // fragments are read from a free buffer and never used)
+                load_stage((p + 1) >> 1);
+                copy_stage((p + 7) >> 1);
+                wait_vmcnt<2 * NITEM>();
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+        }
         wait_vmcnt<0>();
     }
 
@@ -648,12 +749,14 @@ __global__ __launch_bounds__(256) void gated_gemm_f32_kernel(const float* __rest
 struct Tile {
     int bm, bn;
     int waves;  // 4 (2 x 2) or 8 (2 x 4, two wavefronts per SIMD)
+    bool pp;    // 8 wavefronts in two ping-pong teams (256 x 256 only, 32-deep stages)
+    int kb;     // K per stage: 64 (two LDS buffers) or 32 (four)
 };
 
 constexpr int kNumCUs = 256;
 
 // Workgroups that run at once per CU for a tile shape (LDS-limited).
-int occupancy(Tile t) { return (kNBUF * (t.bm + t.bn) * kBK * 2 > 80 * 1024) ? 1 : 2; }
+int occupancy(Tile t) { return (128 * (t.bm + t.bn) * 2 > 80 * 1024) ? 1 : 2; }
 
 // Launch-time model used to rank (tile, split) plans: a workgroup costs a
 // fixed time (launch share, prologue, epilogue) plus its MFMA work at a
@@ -666,23 +769,39 @@ struct TileModel {
     double fixed_us;
 };
 TileModel tile_model(Tile t) {
-    if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.4e12, 9.0} : TileModel{4.6e12, 15.0};
+    if (t.bm == 256 && t.bn == 256 && t.pp) return {4.2e12, 10.0};
+    if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.8e12, 9.0} : TileModel{4.3e12, 15.0};
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
     if (t.bm == 128) return {1.7e12, 10.0};
     return {0.9e12, 8.0};
 }
 
-// UNO_GEMM_TILE=BMxBN or BMxBNwW forces a tile (tests and tuning).
+// Stage depth measured best per tile: 32 for the large tiles (four buffers,
+// three stages in flight), 64 for the 128-row ones.
+int default_kb(int bm, int bn) { return bm * bn >= 256 * 128 ? 32 : 64; }
+
+// UNO_GEMM_TILE forces a tile (tests and tuning): "BMxBN" with optional
+// suffixes "w8" (eight wavefronts), "pp" (ping-pong), "k32" / "k64" (stage depth).
 Tile env_tile() {
     const char* s = getenv("UNO_GEMM_TILE");
-    Tile t{0, 0, 4};
-    if (s && sscanf(s, "%dx%dw%d", &t.bm, &t.bn, &t.waves) >= 2) return t;
-    return Tile{0, 0, 4};
+    Tile t{0, 0, 4, false, 64};
+    if (!s || sscanf(s, "%dx%d", &t.bm, &t.bn) != 2) return Tile{0, 0, 4, false, 64};
+    t.kb = default_kb(t.bm, t.bn);
+    if (strstr(s, "w8")) t.waves = 8;
+    if (strstr(s, "k64")) t.kb = 64;
+    if (strstr(s, "pp")) {
+        t.waves = 8;
+        t.pp = true;
+        t.kb = 32;
+    }
+    if (strstr(s, "k32")) t.kb = 32;
+    return t;
 }
 
 bool tile_supported(Tile t) {
-    if (t.waves == 8) return t.bm == 256 && t.bn == 256;
-    if (t.waves != 4) return false;
+    if (t.pp) return t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 32;
+    if (t.waves == 8) return t.bm == 256 && t.bn == 256 && (t.kb == 32 || t.kb == 64);
+    if (t.waves != 4 || t.kb != default_kb(t.bm, t.bn)) return false;
     return (t.bm == 64 && t.bn == 128) || (t.bm == 128 && t.bn == 128) || (t.bm == 128 && t.bn == 256) ||
            (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
 }
@@ -706,7 +825,7 @@ bool tile_fits(Tile t, const GroupSpec& gs) {
     return true;
 }
 
-int64_t split_k(int64_t K, int64_t s) { return ((K + s - 1) / s + kBK - 1) / kBK * kBK; }
+int64_t split_k(int64_t K, int64_t s) { return ((K + s - 1) / s + kStageK - 1) / kStageK * kStageK; }
 
 double plan_time_us(Tile t, int64_t rows_cap, int64_t N, int64_t K, int64_t s) {
     const TileModel m = tile_model(t);
@@ -737,8 +856,9 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs)) return forced;
-    const Tile cands[] = {{256, 256, 4}, {256, 256, 8}, {256, 128, 4}, {128, 256, 4}, {128, 128, 4}, {64, 128, 4}};
-    Tile best{64, 128, 4};
+    const Tile cands[] = {{256, 256, 8, false, 32}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
+                          {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
+    Tile best{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
         if (!tile_fits(t, gs)) continue;
@@ -767,9 +887,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     // the usual case (segments of whole 32-row blocks) the last 32 are empty
     // and their tiles exit at once: rank plans on the rows that hold work.
     const int64_t rows_model = std::max<int64_t>(p.rows_cap - kRowAlign, kRowAlign);
-    p.tile = tmode ? Tile{128, 128, 4} : choose_tile(rows_model, N, K, gs);
-    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128, 4};
-    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4};
+    p.tile = tmode ? Tile{128, 128, 4, false, 64} : choose_tile(rows_model, N, K, gs);
+    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128, 4, false, 64};
+    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4, false, 64};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
     // T mode works on the draft rows only (at most rows_cap of them)
@@ -782,10 +902,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     return p;
 }
 
-template <int BM, int BN, int WGM, int WGN, bool TMODE>
+template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false>
 void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, TMODE>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(TileCfg<BM, BN, WGM, WGN>::THREADS), 0, stream, ka);
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(TileCfg<BM, BN, WGM, WGN, KB>::THREADS), 0, stream, ka);
 }
 
 template <bool TMODE>
@@ -801,10 +921,13 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         if (t.bm == 128) launch_tile<128, 128, 2, 2, true>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
-        if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false>(ka, blocks, stream);
-        else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false>(ka, blocks, stream);
-        else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false>(ka, blocks, stream);
-        else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false>(ka, blocks, stream);
+        if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 64)
+            launch_tile<256, 256, 2, 4, false, 64>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 32>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false, 32>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false, 32>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 128) launch_tile<128, 128, 2, 2, false>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, false>(ka, blocks, stream);
     }
