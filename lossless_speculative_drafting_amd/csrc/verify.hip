@@ -71,12 +71,19 @@ struct Online {
     double s;
 };
 
+// Logit rows live in global memory; saying so lets the compiler use global
+// loads (counted by vmcnt alone) even for row pointers read from memory.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gptr(const void* p) {
+    return (const __attribute__((address_space(1))) T*)(p);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load_one(const void* row, int64_t k) {
     if constexpr (BF16) {
-        return bf16_bits_to_f32(static_cast<const uint16_t*>(row)[k]);
+        return bf16_bits_to_f32(gptr<uint16_t>(row)[k]);
     } else {
-        return static_cast<const float*>(row)[k];
+        return gptr<float>(row)[k];
     }
 }
 
@@ -84,12 +91,16 @@ __device__ __forceinline__ float load_one(const void* row, int64_t k) {
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void load8(const void* row, int64_t k, int64_t V, float* f) {
     if constexpr (VEC) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
         if constexpr (BF16) {
-            const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k);
+            const u32x4_t r = gptr<u32x4_t>(static_cast<const uint16_t*>(row) + k)[0];
+            uint4 v;
+            v.x = r.x; v.y = r.y; v.z = r.z; v.w = r.w;
             unpack8(v, f);
         } else {
-            const float4 v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k);
-            const float4 v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + k + 4);
+            const f32x4_t v0 = gptr<f32x4_t>(static_cast<const float*>(row) + k)[0];
+            const f32x4_t v1 = gptr<f32x4_t>(static_cast<const float*>(row) + k + 4)[0];
             f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
             f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
         }
@@ -208,10 +219,13 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
 // Merge the chunk statistics of one row in fp64: M = max, S = sum s_c e^{(m_c - M)/T}.
 __device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, bool use_b,
                                              double invT, float& M, double& S) {
+    // (unrolled so that the chunk loads of a pass are in flight together)
     float m = -INFINITY;
+#pragma unroll 8
     for (int32_t c = 0; c < n; ++c) m = fmaxf(m, use_b ? st[c].mB : st[c].mA);
     double s = 0.0;
     if (m != -INFINITY) {
+#pragma unroll 8
         for (int32_t c = 0; c < n; ++c) {
             const float mc = use_b ? st[c].mB : st[c].mA;
             if (mc == -INFINITY) continue;
@@ -242,14 +256,33 @@ struct DecideArgs {
     int32_t* n_emitted;
 };
 
+// Decision for sequence s by one wavefront (lane = lane index): acceptance of
+// every drafted position, the first rejection, the emitted prefix, and the
+// redraw job (written by lane 0 to *job_out).
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
-    const int lane = threadIdx.x % kWave;
-    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
-    if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
+__device__ __forceinline__ void decide_sequence(const DecideArgs& a, int64_t s, int lane, RedrawJob* job_out,
+                                                bool write_outputs = true) {
     const int32_t L = a.L;
     const int32_t rows = L + a.nb;
     const size_t esz = BF16 ? 2 : 4;
+    // The drafted token, its uniform and its two logits do not depend on the
+    // row statistics: their loads go out first, so that the memory round
+    // trips overlap the statistics merge.
+    int32_t x = 0;
+    bool valid = true;
+    bool acc = true;
+    float ux = 0.f, zx = 0.f, dx = 0.f;
+    if (lane < L) {
+        x = a.tokens[s * L + lane];
+        ux = a.uniforms[s * (L + 1) + lane];
+        valid = (x >= 0) && (static_cast<int64_t>(x) < a.V);
+        if (valid) {
+            const char* zrow = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(lane) * a.V) * esz;
+            const char* drow = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(lane) * a.V) * esz;
+            zx = load_one<BF16>(zrow, x);
+            dx = load_one<BF16>(drow, x);
+        }
+    }
 
     float Mz = -INFINITY, Md = -INFINITY;
     double Sz = 0.0, Sd = 0.0;
@@ -259,18 +292,9 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
         if (lane < L) merge_chunks(st, a.n_chunks, true, a.invT, Md, Sd);
     }
 
-    int32_t x = 0;
-    bool valid = true;
-    bool acc = true;
     if (lane < L) {
-        x = a.tokens[s * L + lane];
-        valid = (x >= 0) && (static_cast<int64_t>(x) < a.V);
         acc = false;
         if (valid) {
-            const char* zrow = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(lane) * a.V) * esz;
-            const char* drow = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(lane) * a.V) * esz;
-            const float zx = load_one<BF16>(zrow, x);
-            const float dx = load_one<BF16>(drow, x);
             double prob;
             if (zx == -INFINITY) {
                 prob = 0.0;
@@ -281,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
                 const double lq = (static_cast<double>(dx) - static_cast<double>(Md)) * a.invT - log(Sd);
                 prob = exp(fmin(0.0, lp - lq));
             }
-            acc = static_cast<double>(a.uniforms[s * (L + 1) + lane]) < prob;
+            acc = static_cast<double>(ux) < prob;
         }
     }
     const uint64_t bad = __ballot(!valid);
@@ -295,9 +319,9 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
     const double Sd_j = __shfl(Sd, j);
 
     int32_t* out = a.out_tokens + s * (L + 1);
-    if (lane < L) out[lane] = (!bad && lane < n_acc) ? x : -1;
+    if (write_outputs && lane < L) out[lane] = (!bad && lane < n_acc) ? x : -1;
     if (lane == 0) {
-        out[L] = -1;  // slot L: filled later only by a bonus draw
+        if (write_outputs) out[L] = -1;  // slot L: filled later only by a bonus draw
         RedrawJob job;
         job.a = nullptr;
         job.b = nullptr;
@@ -309,25 +333,33 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
         job.u = a.uniforms[s * (L + 1) + L];
         job.mode = kJobNone;
         if (bad) {
-            a.n_accepted[s] = -1;
-            a.n_emitted[s] = 0;
+            if (write_outputs) a.n_accepted[s] = -1;
+            if (write_outputs) a.n_emitted[s] = 0;
         } else {
-            a.n_accepted[s] = n_acc;
+            if (write_outputs) a.n_accepted[s] = n_acc;
             if (n_acc < L) {
                 job.mode = kJobResidual;
                 job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
                 job.b = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
-                a.n_emitted[s] = n_acc + 1;
+                if (write_outputs) a.n_emitted[s] = n_acc + 1;
             } else if (a.nb) {
                 job.mode = kJobSingle;
                 job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(L) * a.V) * esz;
-                a.n_emitted[s] = L + 1;
+                if (write_outputs) a.n_emitted[s] = L + 1;
             } else {
-                a.n_emitted[s] = L;
+                if (write_outputs) a.n_emitted[s] = L;
             }
         }
-        a.jobs[s] = job;
+        *job_out = job;
     }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
+    decide_sequence<BF16>(a, s, lane, a.jobs + s);
 }
 
 // ---------------------------------------------------------------- draft_decide
@@ -394,7 +426,8 @@ __device__ __forceinline__ void segment_weights(const RedrawJob& job, int64_t g,
 }
 
 // ---------------------------------------------------------------- redraw_mass
-// seg layout: [job][n_arr][nseg]; array 0 = drawn weights, array 1 = p (residual jobs).
+// seg layout: [job][n_arr][nseg]; array 0 = drawn weights, array 1 = p for
+// residual jobs, filled by redraw_select only when the residual has no mass.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void redraw_mass_kernel(const RedrawJob* __restrict__ jobs,
                                                               int32_t n_chunks, int64_t seg_per_chunk,
@@ -407,26 +440,31 @@ __global__ __launch_bounds__(kThreads) void redraw_mass_kernel(const RedrawJob* 
     float* out0 = seg + jid * n_arr * nseg;
     const int64_t g0 = static_cast<int64_t>(c) * seg_per_chunk;
     const int64_t g1 = min(nseg, g0 + seg_per_chunk);
-    for (int64_t g = g0 + threadIdx.x; g < g1; g += kThreads) {
-        float w[kSeg];
-        segment_weights<BF16, VEC>(job, g, V, c2, false, w);
-        float sr = 0.f;
+    // four segments per thread per round, their loads issued together
+    constexpr int kBatch = 4;
+    for (int64_t base = g0 + threadIdx.x; base < g1; base += kBatch * kThreads) {
+        float w[kBatch][kSeg];
 #pragma unroll
-        for (int j = 0; j < kSeg; ++j) sr += w[j];
-        out0[g] = sr;
-        if (job.mode == kJobResidual && n_arr > 1) {
-            float wp[kSeg];
-            segment_weights<BF16, VEC>(job, g, V, c2, true, wp);
-            float sp = 0.f;
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * kThreads;
+            if (g < g1) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
+        }
 #pragma unroll
-            for (int j = 0; j < kSeg; ++j) sp += wp[j];
-            out0[nseg + g] = sp;
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * kThreads;
+            if (g < g1) {
+                float sr = 0.f;
+#pragma unroll
+                for (int j = 0; j < kSeg; ++j) sr += w[u][j];
+                out0[g] = sr;
+            }
         }
     }
 }
 
 // Exclusive block scan of one double per thread (fixed order); returns the
 // exclusive prefix and writes the block total to *total.
+template <int NT = kThreads>
 __device__ __forceinline__ double block_excl_scan(double v, double* sh, double* total) {
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
@@ -441,48 +479,89 @@ __device__ __forceinline__ double block_excl_scan(double v, double* sh, double* 
     double base = 0.0;
     for (int w = 0; w < wave; ++w) base += sh[w];
     double tot = 0.0;
-    for (int w = 0; w < kThreads / kWave; ++w) tot += sh[w];
+    for (int w = 0; w < NT / kWave; ++w) tot += sh[w];
     __syncthreads();
     *total = tot;
     return base + (incl - v);
 }
 
 // ---------------------------------------------------------------- redraw_select
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob* __restrict__ jobs,
-                                                                int64_t nseg, int32_t n_arr,
-                                                                int64_t V, float c2,
-                                                                const float* __restrict__ seg) {
-    const RedrawJob job = jobs[blockIdx.x];
-    if (job.mode == kJobNone) return;
-    __shared__ double sh[kThreads / kWave];
-    __shared__ int32_t first_wave_lane[kThreads / kWave];
+// Segment sums staged in LDS by redraw_select (up to this many; longer rows
+// read them from global memory).  Index g is stored at g + g / 32: a lane's
+// run of 32 consecutive segments then starts 33 words after its neighbour's,
+// so the 64 lanes of a wavefront read 64 different banks.
+constexpr int64_t kSelectLdsSegs = 15360;  // (n + n/32 + 1) floats stay within 64 KB
+inline size_t select_lds_bytes(int64_t nseg) {
+    return nseg <= kSelectLdsSegs ? static_cast<size_t>(nseg + nseg / 32 + 1) * sizeof(float) : 0;
+}
+
+// Inverse-CDF draw for one job by a workgroup of NT threads: sg holds the
+// job's segment masses (array 0) and room for p's (array 1, filled here only
+// if the residual has no mass); s_seg, when given, is LDS for staging them.
+template <bool BF16, bool VEC, int NT>
+__device__ __forceinline__ void select_job(const RedrawJob& job, int64_t nseg, int32_t n_arr, int64_t V, float c2,
+                                           float* sg, float* s_seg, bool preloaded = false) {
+    __shared__ double sh[NT / kWave];
+    __shared__ int32_t first_wave_lane[NT / kWave];
     __shared__ int32_t chosen;
 
-    const int64_t per = (nseg + kThreads - 1) / kThreads;
+    const int64_t per = (nseg + NT - 1) / NT;
     const int64_t g0 = min(nseg, static_cast<int64_t>(threadIdx.x) * per);
     const int64_t g1 = min(nseg, g0 + per);
 
     bool use_p = false;
-    const float* sg = seg + static_cast<int64_t>(blockIdx.x) * n_arr * nseg;
+    // one coalesced pass brings the drawn array's sums into LDS
+    bool staged = s_seg != nullptr && nseg <= kSelectLdsSegs;
+    if (staged && !preloaded) {
+        // batches of 16 independent loads per thread, so that one memory
+        // latency covers a batch instead of every element
+        constexpr int kBatch = 16;
+        for (int64_t base = threadIdx.x; base < nseg; base += kBatch * NT) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t g = base + static_cast<int64_t>(u) * NT;
+                v[u] = g < nseg ? sg[g] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t g = base + static_cast<int64_t>(u) * NT;
+                if (g < nseg) s_seg[g + (g >> 5)] = v[u];
+            }
+        }
+        __syncthreads();
+    }
+    auto seg_at = [&](int64_t g) __attribute__((always_inline)) {
+        return staged ? s_seg[g + (g >> 5)] : sg[g];
+    };
     double tot = 0.0;
-    for (int64_t g = g0; g < g1; ++g) tot += static_cast<double>(sg[g]);
+    for (int64_t g = g0; g < g1; ++g) tot += static_cast<double>(seg_at(g));
     double R;
-    double excl = block_excl_scan(tot, sh, &R);
+    double excl = block_excl_scan<NT>(tot, sh, &R);
     if (job.mode == kJobResidual && R == 0.0 && n_arr > 1) {
-        // The residual lost all mass to rounding: draw from p instead.
+        // The residual lost all mass to rounding: draw from p instead (read
+        // from global memory: this branch is taken only in that event).
         use_p = true;
+        staged = false;
         sg += nseg;
         tot = 0.0;
-        for (int64_t g = g0; g < g1; ++g) tot += static_cast<double>(sg[g]);
-        excl = block_excl_scan(tot, sh, &R);
+        for (int64_t g = g0; g < g1; ++g) {
+            float w[kSeg];
+            segment_weights<BF16, VEC>(job, g, V, c2, true, w);
+            float sp = 0.f;
+#pragma unroll
+            for (int j = 0; j < kSeg; ++j) sp += w[j];
+            sg[g] = sp;
+            tot += static_cast<double>(sp);
+        }
+        excl = block_excl_scan<NT>(tot, sh, &R);  // (its barriers also publish sg to the block)
     }
     const double target = static_cast<double>(job.u) * R;
 
     // Walk this lane's segments in order; the running value at the end is the
     // lane's inclusive prefix as the select walk below will see it.
     double run = excl;
-    for (int64_t g = g0; g < g1; ++g) run += static_cast<double>(sg[g]);
+    for (int64_t g = g0; g < g1; ++g) run += static_cast<double>(seg_at(g));
     const bool cand = (g1 > g0) && (run > target);
     const uint64_t m = __ballot(cand);
     const int lane = threadIdx.x % kWave;
@@ -491,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
     __syncthreads();
     if (threadIdx.x == 0) {
         int32_t ch = -1;
-        for (int w = 0; w < kThreads / kWave; ++w) {
+        for (int w = 0; w < NT / kWave; ++w) {
             if (first_wave_lane[w] >= 0) {
                 ch = w * kWave + first_wave_lane[w];
                 break;
@@ -505,8 +584,9 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
         int64_t token = -1;
         double r = excl;
         for (int64_t g = g0; g < g1 && token < 0; ++g) {
-            const double next = r + static_cast<double>(sg[g]);
-            if (next > target && sg[g] > 0.f) {
+            const float sgg = seg_at(g);
+            const double next = r + static_cast<double>(sgg);
+            if (next > target && sgg > 0.f) {
                 float w[kSeg];
                 segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
                 float run32 = 0.f;
@@ -523,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
         if (token < 0) {
             // Rounding left no crossing: take the last token with weight.
             for (int64_t g = nseg - 1; g >= 0 && token < 0; --g) {
-                if (sg[g] > 0.f) {
+                if (seg_at(g) > 0.f) {
                     float w[kSeg];
                     segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
                     for (int j = kSeg - 1; j >= 0; --j) {
@@ -542,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
         // end of the row): take the last token with weight.
         int64_t token = -1;
         for (int64_t g = nseg - 1; g >= 0 && token < 0; --g) {
-            if (sg[g] > 0.f) {
+            if (seg_at(g) > 0.f) {
                 float w[kSeg];
                 segment_weights<BF16, VEC>(job, g, V, c2, use_p, w);
                 for (int j = kSeg - 1; j >= 0; --j) {
@@ -555,6 +635,61 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
         }
         *job.out = static_cast<int32_t>(token < 0 ? 0 : token);
     }
+}
+
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob* __restrict__ jobs,
+                                                                int64_t nseg, int32_t n_arr,
+                                                                int64_t V, float c2,
+                                                                float* __restrict__ seg) {
+    extern __shared__ float s_seg[];
+    const RedrawJob job = jobs[blockIdx.x];
+    if (job.mode == kJobNone) return;
+    select_job<BF16, VEC, kThreads>(job, nseg, n_arr, V, c2, seg + static_cast<int64_t>(blockIdx.x) * n_arr * nseg,
+                                    nseg <= kSelectLdsSegs ? s_seg : nullptr);
+}
+
+// ---------------------------------------------------------------- verify_tail
+// The sequence-level tail of verification in one launch, one workgroup per
+// sequence: the decision (wavefront 0), then the 16-token segment masses of
+// the row to draw from, computed as redraw_mass does but kept in LDS, and
+// the draw of redraw_select on them.  Used when the masses fit in LDS.
+constexpr int kTailThreads = 1024;
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTailThreads) void verify_tail_kernel(DecideArgs a, int64_t nseg, float c2,
+                                                                  float* __restrict__ seg) {
+    constexpr int NT = kTailThreads;
+    extern __shared__ float s_seg[];  // segment g at g + g / 32
+    __shared__ RedrawJob s_job;
+    const int64_t s = blockIdx.x;
+    if (threadIdx.x < kWave) decide_sequence<BF16>(a, s, static_cast<int>(threadIdx.x), &s_job);
+    __syncthreads();
+    const RedrawJob job = s_job;
+    if (job.mode == kJobNone) return;  // uniform for the workgroup
+    const int64_t V = a.V;
+    constexpr int kBatch = 4;
+    for (int64_t base = threadIdx.x; base < nseg; base += kBatch * NT) {
+        float w[kBatch][kSeg];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * NT;
+            if (g < nseg) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * NT;
+            if (g < nseg) {
+                float sr = 0.f;
+#pragma unroll
+                for (int j = 0; j < kSeg; ++j) sr += w[u][j];
+                s_seg[g + (g >> 5)] = sr;
+            }
+        }
+    }
+    __syncthreads();
+    select_job<BF16, VEC, NT>(job, nseg, 2, V, c2, seg + s * 2 * nseg, s_seg, true);
 }
 
 // ---------------------------------------------------------------- planning
@@ -586,7 +721,7 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     p.nseg = (V + kSeg - 1) / kSeg;
     p.n_jobs = n_jobs;
     const int64_t max_c3 = (p.nseg + kThreads - 1) / kThreads;
-    int64_t c3 = n_jobs > 0 ? (kTargetBlocks / 2 + n_jobs - 1) / n_jobs : 1;
+    int64_t c3 = n_jobs > 0 ? (kTargetBlocks / 8 + n_jobs - 1) / n_jobs : 1;
     c3 = std::max<int64_t>(1, std::min(c3, max_c3));
     int64_t spc = (p.nseg + c3 - 1) / c3;
     spc = (spc + kThreads - 1) / kThreads * kThreads;
@@ -642,12 +777,18 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     da.n_accepted = pr.n_accepted;
     da.out_tokens = pr.out_tokens;
     da.n_emitted = pr.n_emitted;
+    const size_t tail_lds = select_lds_bytes(p.nseg);
+    if (tail_lds > 0) {
+        hipLaunchKernelGGL((verify_tail_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kTailThreads),
+                           tail_lds, stream, da, p.nseg, c2, seg);
+        return hipGetLastError();
+    }
     const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
     hipLaunchKernelGGL((verify_decide_kernel<BF16>), dim3(dblocks), dim3(kThreads), 0, stream, da);
     hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * p.c3)), dim3(kThreads), 0,
                        stream, jobs, p.c3, p.spc3, p.nseg, p.n_arr, pr.V, c2, seg);
-    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kThreads), 0, stream,
-                       jobs, p.nseg, p.n_arr, pr.V, c2, seg);
+    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kThreads),
+                       select_lds_bytes(p.nseg), stream, jobs, p.nseg, p.n_arr, pr.V, c2, seg);
     return hipGetLastError();
 }
 
@@ -669,8 +810,8 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
                        pr.uniforms, pr.sampled, jobs);
     hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows * p.c3)), dim3(kThreads), 0,
                        stream, jobs, p.c3, p.spc3, p.nseg, 1, pr.V, c2, seg);
-    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows)), dim3(kThreads), 0, stream,
-                       jobs, p.nseg, 1, pr.V, c2, seg);
+    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows)), dim3(kThreads),
+                       select_lds_bytes(p.nseg), stream, jobs, p.nseg, 1, pr.V, c2, seg);
     return hipGetLastError();
 }
 
