@@ -887,13 +887,28 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     // the usual case (segments of whole 32-row blocks) the last 32 are empty
     // and their tiles exit at once: rank plans on the rows that hold work.
     const int64_t rows_model = std::max<int64_t>(p.rows_cap - kRowAlign, kRowAlign);
-    p.tile = tmode ? Tile{128, 128, 4, false, 64} : choose_tile(rows_model, N, K, gs);
-    if (tmode && p.rows_cap <= 128) p.tile = Tile{64, 128, 4, false, 64};
+    // T mode (the LoRA down-projection: few rows, N = r or a few r) runs
+    // 64 x 128 tiles, measured faster there than 128 x 128 by 10-30%.
+    p.tile = tmode ? Tile{64, 128, 4, false, 64} : choose_tile(rows_model, N, K, gs);
+    if (tmode && getenv("UNO_T_TILE") && atoi(getenv("UNO_T_TILE")) == 128) p.tile = Tile{128, 128, 4, false, 64};
     if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4, false, 64};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
-    // T mode works on the draft rows only (at most rows_cap of them)
-    const int64_t s = choose_split_for(p.tile, rows_model, N, K, nullptr);
+    int64_t s;
+    if (tmode) {
+        // T mode works on the draft rows only; its work is tiny and its time
+        // is latency: about 512 K per split measured best (K = 4096: 8 ways,
+        // K = 14336: 16), capped so that the grid stays near 4 waves
+        s = std::min<int64_t>(16, std::max<int64_t>(1, K / 512));
+        while (s > 1 && p.m_tiles * p.n_tiles * s > 4 * kNumCUs) s /= 2;
+    } else {
+        s = choose_split_for(p.tile, rows_model, N, K, nullptr);
+    }
+    // UNO_GEMM_SPLIT (T mode: UNO_T_SPLIT) forces the split count (tuning)
+    if (const char* e = getenv(tmode ? "UNO_T_SPLIT" : "UNO_GEMM_SPLIT")) {
+        const long v = strtol(e, nullptr, 10);
+        if (v >= 1 && v <= 64) s = v;
+    }
     p.kps = split_k(K, s);
     p.splits = static_cast<int32_t>((K + p.kps - 1) / p.kps);
     p.partial_bytes = p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float),
