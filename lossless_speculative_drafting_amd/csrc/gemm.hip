@@ -493,20 +493,22 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // One MFMA group (all MI x NJ blocks of fragment set `set`), with copy
     // items [q0, q1) of `ss` (when given) spread evenly between its MFMAs.
     constexpr int GROUP = MI * NJ;
+    // (item indices are derived from the unrolled MFMA index, so that they
+    // stay compile-time constants: a counter would make the per-item offset
+    // arrays dynamically indexed and push them to scratch)
     auto mfma_group = [&](int set, const StageSrc* ss, int q0, int q1) __attribute__((always_inline)) {
         const int nq = ss != nullptr ? q1 - q0 : 0;
         const int spacing = nq > 0 && GROUP / nq > 0 ? GROUP / nq : 1;
-        int m = 0, q = q0;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
-                ++m;
+                const int m = i * NJ + j + 1;
+                const int q = q0 + m / spacing - 1;
                 if (ss != nullptr && m % spacing == 0 && q < q1) {
                     __builtin_amdgcn_sched_barrier(0);
                     dma_item(*ss, q);
-                    ++q;
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
