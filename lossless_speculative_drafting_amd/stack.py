@@ -116,7 +116,8 @@ class GatedLoraStack:
     def _timed(self, K, N, launch):
         """Run one gated-GEMM launch; with a timer list set, bracket it with
         HIP events on the current stream and record its algorithmic flops
-        (2 M K N for the product, 2 Md r N for the adapter extension)."""
+        (2 M K N for the product, 2 Md r N for the adapter extension) and
+        bytes (W and B once, x and y once, the draft rows of T once)."""
         if self.timer is None:
             launch()
             return
@@ -124,7 +125,10 @@ class GatedLoraStack:
         e0.record()
         launch()
         e1.record()
-        self.timer.append((e0, e1, 2.0 * self.M * K * N + 2.0 * self.Md * self.r * N))
+        M, Md, r = self.M, self.Md, self.r
+        flops = 2.0 * M * K * N + 2.0 * Md * r * N
+        nbytes = 2.0 * (N * K + N * r + M * K + M * N + Md * r)
+        self.timer.append((e0, e1, flops, nbytes))
 
     def _proj(self, layer, name, inp, out):
         w, a, b = layer[name]
