@@ -250,7 +250,12 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
  * uno_rmsnorm      : y[m, :] = x[m, :] / sqrt(mean_k x[m, k]^2 + eps), x, y [M, K]
  * uno_silu_mul     : out = silu(gate) * up elementwise, silu(t) = t / (1 + e^-t)
  * uno_residual_add : out = a + b elementwise (out may alias a or b)
- * Domain: sizes >= 0; K <= 65536 for uno_rmsnorm; eps >= 0; only UNO_BF16.
+ * uno_residual_rmsnorm : s = x + y (rounded to bf16) into s_out, then h = rmsnorm(s);
+ *                    x, y, s_out, h [M, K]; s_out may alias x (the residual stream
+ *                    updated in place), h must not alias any of them.  Both outputs
+ *                    are bitwise those of uno_residual_add followed by uno_rmsnorm.
+ * Domain: sizes >= 0; K % 8 == 0 and K <= 65536 for the two norms; eps >= 0; only UNO_BF16;
+ * every pointer 16-byte aligned.
  * ------------------------------------------------------------------------ */
 uno_status uno_rmsnorm(const void* x, void* y, int64_t M, int64_t K, float eps, int32_t dtype,
                        hipStream_t stream);
@@ -258,6 +263,8 @@ uno_status uno_silu_mul(const void* gate, const void* up, void* out, int64_t n, 
                         hipStream_t stream);
 uno_status uno_residual_add(const void* a, const void* b, void* out, int64_t n, int32_t dtype,
                             hipStream_t stream);
+uno_status uno_residual_rmsnorm(const void* x, const void* y, void* s_out, void* h, int64_t M, int64_t K,
+                                float eps, int32_t dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

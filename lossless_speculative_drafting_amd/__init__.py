@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     lora_t_size,
     philox_uniforms,
     residual_add,
+    residual_rmsnorm,
     rmsnorm,
     silu_mul,
     status_string,

@@ -53,6 +53,8 @@ SIGNATURES = {
     "uno_rmsnorm": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_float, _c_int32, _c_ptr]),
     "uno_silu_mul": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
     "uno_residual_add": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
+    "uno_residual_rmsnorm": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_float, _c_int32,
+                                        _c_ptr]),
 }
 
 
@@ -66,7 +68,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libuno.so not found at {LIB_PATH}; build it with "
-            "`python -m lossless_speculative_drafting_amd.build` (there is no CPU fallback)")
+            "`python lossless_speculative_drafting_amd/build.py` (there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -365,6 +367,17 @@ def residual_add(a, b, out=None, stream=None):
     out = torch.empty_like(a) if out is None else out
     _check(_lib.uno_residual_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _dtype_code(a.dtype), _stream(stream)))
     return out
+
+
+def residual_rmsnorm(x, y, eps=1e-5, s_out=None, h_out=None, stream=None):
+    """s = x + y and h = rmsnorm(s) in one launch; returns (s, h).  s_out may be x."""
+    _need_cuda(x, y)
+    M, K = x.shape
+    s_out = torch.empty_like(x) if s_out is None else s_out
+    h_out = torch.empty_like(x) if h_out is None else h_out
+    _check(_lib.uno_residual_rmsnorm(_ptr(x), _ptr(y), _ptr(s_out), _ptr(h_out), M, K, float(eps),
+                                     _dtype_code(x.dtype), _stream(stream)))
+    return s_out, h_out
 
 
 def header_symbols(header_path):

@@ -1,6 +1,8 @@
 """Build libuno.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m lossless_speculative_drafting_amd.build [--jobs N] [--verbose]
+    python lossless_speculative_drafting_amd/build.py [--jobs N] [--verbose]
+
+(run as a script: importing the package first would load the library it rebuilds)
 
 Every source under csrc/ is compiled to an object in _build/ and linked into
 lossless_speculative_drafting_amd/libuno.so.  Packed-fp32 instructions are

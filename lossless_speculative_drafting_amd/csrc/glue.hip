@@ -50,6 +50,71 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(const uint16_t* __res
     }
 }
 
+// Residual add followed by RMSNorm of the sum, one workgroup per row:
+// s = bf16(x + y) is stored to s_out (which may be x itself) and
+// h = bf16(s / rms(s)).  Each thread handles the same 8-element vectors, sums
+// the same squares in the same order and reduces them the same way as
+// eltwise_kernel<1> followed by rmsnorm_kernel, so both outputs are bitwise
+// those of the two separate launches.  Rows of up to kThreads * CACHE
+// vectors keep their sums in registers; longer rows re-read s_out, which this
+// thread wrote itself.
+template <int CACHE>
+__global__ __launch_bounds__(kThreads) void residual_rmsnorm_kernel(const uint16_t* x,
+                                                                   const uint16_t* __restrict__ y,
+                                                                   uint16_t* s_out,
+                                                                   uint16_t* __restrict__ h, int64_t K,
+                                                                   float eps) {
+    const int64_t row = blockIdx.x;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+    const uint4* yr = reinterpret_cast<const uint4*>(y + row * K);
+    uint4* sr = reinterpret_cast<uint4*>(s_out + row * K);
+    uint4* hr = reinterpret_cast<uint4*>(h + row * K);
+    const int64_t nv = K / 8;
+    uint4 keep[CACHE > 0 ? CACHE : 1];
+    float ss = 0.f;
+    int c = 0;
+    for (int64_t v = threadIdx.x; v < nv; v += kThreads, ++c) {
+        float fa[8], fb[8];
+        unpack8(xr[v], fa);
+        unpack8(yr[v], fb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fa[j] = fa[j] + fb[j];
+        const uint4 packed = pack8(fa);
+        sr[v] = packed;
+        if constexpr (CACHE > 0) {
+#pragma unroll
+            for (int i = 0; i < CACHE; ++i)
+                if (i == c) keep[i] = packed;
+        }
+        unpack8(packed, fa);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += fa[j] * fa[j];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    __shared__ float sh[kThreads / kWave];
+    if ((threadIdx.x % kWave) == 0) sh[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    const float tot = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    const float inv = 1.0f / sqrtf(tot / static_cast<float>(K) + eps);
+    c = 0;
+    for (int64_t v = threadIdx.x; v < nv; v += kThreads, ++c) {
+        uint4 packed = keep[0];
+        if constexpr (CACHE > 0) {
+#pragma unroll
+            for (int i = 0; i < CACHE; ++i)
+                if (i == c) packed = keep[i];
+        } else {
+            packed = sr[v];
+        }
+        float f[8];
+        unpack8(packed, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] *= inv;
+        hr[v] = pack8(f);
+    }
+}
+
 template <int OP>  // 0: silu(a) * b, 1: a + b
 __global__ __launch_bounds__(kThreads) void eltwise_kernel(const uint16_t* __restrict__ a,
                                                           const uint16_t* __restrict__ b,
@@ -94,6 +159,23 @@ hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float ep
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), K, eps);
+    return hipGetLastError();
+}
+
+hipError_t residual_rmsnorm_launch(const void* x, const void* y, void* s_out, void* h, int64_t M, int64_t K,
+                                  float eps, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    const int64_t per_thread = (K / 8 + kThreads - 1) / kThreads;
+    const auto* xs = static_cast<const uint16_t*>(x);
+    const auto* ys = static_cast<const uint16_t*>(y);
+    auto* so = static_cast<uint16_t*>(s_out);
+    auto* hs = static_cast<uint16_t*>(h);
+    if (per_thread <= 4)
+        hipLaunchKernelGGL(residual_rmsnorm_kernel<4>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0, stream,
+                           xs, ys, so, hs, K, eps);
+    else
+        hipLaunchKernelGGL(residual_rmsnorm_kernel<0>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0, stream,
+                           xs, ys, so, hs, K, eps);
     return hipGetLastError();
 }
 

@@ -363,6 +363,21 @@ uno_status uno_rmsnorm(const void* x, void* y, int64_t M, int64_t K, float eps, 
     return from_hip(uno::rmsnorm_launch(x, y, M, K, eps, stream), "rmsnorm launch");
 }
 
+uno_status uno_residual_rmsnorm(const void* x, const void* y, void* s_out, void* h, int64_t M, int64_t K, float eps,
+                                int32_t dtype, hipStream_t stream) {
+    if (dtype != UNO_BF16) return fail(UNO_ERR_UNSUPPORTED, "residual_rmsnorm supports bf16 only");
+    if (M < 0 || K < 0) return fail(UNO_ERR_INVALID_ARG, "sizes must be >= 0");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(UNO_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (M == 0 || K == 0) return ok();
+    if (K % 8 != 0 || K > 65536)
+        return fail(UNO_ERR_UNSUPPORTED, "residual_rmsnorm needs K %% 8 == 0 and K <= 65536");
+    if (M > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "too many rows");
+    if (!x || !y || !s_out || !h) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(s_out) || !aligned16(h))
+        return fail(UNO_ERR_INVALID_ARG, "residual_rmsnorm tensors must be 16-byte aligned");
+    return from_hip(uno::residual_rmsnorm_launch(x, y, s_out, h, M, K, eps, stream), "residual_rmsnorm launch");
+}
+
 static uno_status check_eltwise(const void* a, const void* b, void* out, int64_t n, int32_t dtype) {
     if (dtype != UNO_BF16) return fail(UNO_ERR_UNSUPPORTED, "elementwise glue supports bf16 only");
     if (n < 0) return fail(UNO_ERR_INVALID_ARG, "n must be >= 0");

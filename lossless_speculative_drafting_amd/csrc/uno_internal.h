@@ -81,5 +81,7 @@ hipError_t silu_mul_launch(const void* gate, const void* up, void* out, int64_t 
                            hipStream_t stream);
 hipError_t residual_add_launch(const void* a, const void* b, void* out, int64_t n,
                                hipStream_t stream);
+hipError_t residual_rmsnorm_launch(const void* x, const void* y, void* s_out, void* h, int64_t M, int64_t K,
+                                  float eps, hipStream_t stream);
 
 }  // namespace uno

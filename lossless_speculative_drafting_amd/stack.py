@@ -162,15 +162,20 @@ class GatedLoraStack:
         """
         self.x.copy_(x_in)
         self.plan = _lib.RowPlan(self.gate) if self.plan is None else self.plan
+        # Each residual add that is followed by a norm runs as one fused launch
+        # (bitwise the same as the two separate ones).
+        _lib.rmsnorm(self.x, self.eps, out=self.h)
+        last = len(self.layers) - 1
         for li, layer in enumerate(self.layers):
             rec = trace if (trace is not None and li == trace_layer) else None
-            _lib.rmsnorm(self.x, self.eps, out=self.h)
             self._projections(li, layer, [("q", self.h, self.q), ("k", self.h, self.k), ("v", self.h, self.v)], rec)
             self._projections(li, layer, [("o", self.q, self.o)], rec)
-            _lib.residual_add(self.x, self.o, out=self.x)
-            _lib.rmsnorm(self.x, self.eps, out=self.h)
+            _lib.residual_rmsnorm(self.x, self.o, self.eps, s_out=self.x, h_out=self.h)
             self._projections(li, layer, [("gate", self.h, self.g), ("up", self.h, self.u)], rec)
             _lib.silu_mul(self.g, self.u, out=self.act)
             self._projections(li, layer, [("down", self.act, self.dn)], rec)
-            _lib.residual_add(self.x, self.dn, out=self.x)
+            if li < last:
+                _lib.residual_rmsnorm(self.x, self.dn, self.eps, s_out=self.x, h_out=self.h)
+            else:
+                _lib.residual_add(self.x, self.dn, out=self.x)
         return self.x

@@ -131,3 +131,9 @@ def test_draft_sample_and_glue_validation(lib):
     assert lib.uno_silu_mul(FAKE, NULL, FAKE, 16, 0, STREAM) == INVALID
     assert lib.uno_residual_add(FAKE, FAKE, ctypes.c_void_p(0x100004), 16, 0, STREAM) == INVALID
     assert lib.uno_silu_mul(NULL, NULL, NULL, 0, 0, STREAM) == OK
+    assert lib.uno_residual_rmsnorm(FAKE, FAKE, FAKE, FAKE, 4, 12, 1e-5, 0, STREAM) == UNSUPPORTED
+    assert lib.uno_residual_rmsnorm(FAKE, FAKE, FAKE, FAKE, 4, 16, 1e-5, 1, STREAM) == UNSUPPORTED
+    assert lib.uno_residual_rmsnorm(FAKE, FAKE, FAKE, FAKE, 4, 16, float("nan"), 0, STREAM) == INVALID
+    assert lib.uno_residual_rmsnorm(FAKE, NULL, FAKE, FAKE, 4, 16, 1e-5, 0, STREAM) == INVALID
+    assert lib.uno_residual_rmsnorm(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), 4, 16, 1e-5, 0, STREAM) == INVALID
+    assert lib.uno_residual_rmsnorm(NULL, NULL, NULL, NULL, 0, 16, 1e-5, 0, STREAM) == OK

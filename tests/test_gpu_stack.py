@@ -38,6 +38,29 @@ def test_glue_kernels():
     assert floored_rel_err(ro[None], oracle.stack.residual_add(xo, yo)[None]) <= 1e-2
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("K", [4096, 8, 1032, 16384])
+def test_residual_rmsnorm_fused(K):
+    """The fused launch equals residual_add then rmsnorm bit for bit, in place too,
+    and stays within the oracle's bound.  K = 16384 takes the re-read path."""
+    rng = np.random.default_rng(K)
+    M = 37
+    x = bf16_round(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    y = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    say(f"residual_rmsnorm K={K}")
+    xd, yd = to_dev(x, "bf16"), to_dev(y, "bf16")
+    s_ref = uno.residual_add(xd, yd)
+    h_ref = uno.rmsnorm(s_ref, 1e-5)
+    s, h = uno.residual_rmsnorm(xd, yd, 1e-5)
+    assert torch.equal(s, s_ref) and torch.equal(h, h_ref)
+    xin = xd.clone()
+    s2, h2 = uno.residual_rmsnorm(xin, yd, 1e-5, s_out=xin)
+    assert s2.data_ptr() == xin.data_ptr()
+    assert torch.equal(xin, s_ref) and torch.equal(h2, h_ref)
+    ref = oracle.stack.rmsnorm(oracle.stack.residual_add(x, y), 1e-5)
+    assert floored_rel_err(to_host(h), ref) <= 2e-2
+
+
 def _check_trace(layer, trace, gate, rows):
     for name in PROJECTIONS:
         inp, out = trace[name]
