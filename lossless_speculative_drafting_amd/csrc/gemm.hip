@@ -241,16 +241,19 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     else return row * KB + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-// KB: K per pipeline stage (64 or 32); NBUF LDS stage buffers, NBUF * KB =
-// 128 (two 64-deep stages or four 32-deep ones).  A copy instruction moves
+// KB: K per pipeline stage (64 or 32); NBUF LDS stage buffers (NB, or by
+// default NBUF * KB = 128: two 64-deep stages or four 32-deep ones; small
+// tiles that run one workgroup per CU take more buffers, so that more copies
+// are in flight).  A copy instruction moves
 // 1 KB: RB rows of 2*KB bytes.  Rows of 128 bytes move at about twice the
 // rate of rows of 64 bytes (L2-resident sources, measured on MI355X: 110 vs
 // 59 GB/s per CU), so KB = 64 is the default; KB = 32 keeps three stages in
 // flight where LDS would otherwise hold only two.
-template <int BM, int BN, int WGM, int WGN, int KB>
+template <int BM, int BN, int WGM, int WGN, int KB, int NB = 0>
 struct TileCfg {
     static_assert(KB == 64 || KB == 32, "stage depth");
-    static constexpr int NBUF = 128 / KB;
+    static constexpr int NBUF = NB > 0 ? NB : 128 / KB;
+    static_assert(NBUF >= 2 && NBUF <= 8, "stage buffers");
     static constexpr int KSUB = KB / 16;       // MFMA sub-steps per stage
     static constexpr int RB = 512 / KB;        // rows per copy instruction
     static constexpr int NWAVES = WGM * WGN;   // WGM x WGN wavefronts
@@ -268,14 +271,16 @@ struct TileCfg {
     static constexpr int STAGE_ELEMS = (BM + BN) * KB;
     static constexpr int LDS_ELEMS = NBUF * STAGE_ELEMS;
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
+    static_assert(LDS_ELEMS * 2 + BM * 4 <= 160 * 1024, "LDS");
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
-template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP>
-__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB>::THREADS), (TileCfg<BM, BN, WGM, WGN, KB>::OCC))
+template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB>
+__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB>::THREADS), (TileCfg<BM, BN, WGM, WGN, KB, NB>::OCC))
 void gated_gemm_kernel(const GemmKArgs a) {
-    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32), "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32");
-    using C = TileCfg<BM, BN, WGM, WGN, KB>;
+    using C = TileCfg<BM, BN, WGM, WGN, KB, NB>;
+    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4),
+                  "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32, four buffers");
     constexpr int kBK = KB;
     constexpr int kNBUF = C::NBUF;
     constexpr int RB = C::RB;
@@ -430,7 +435,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
         ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * C::STAGE_ELEMS * 2));
         return ss;
     };
-    auto dma_item = [&](const StageSrc& ss, int q) __attribute__((always_inline)) {
+    auto dma_item = [&](const StageSrc ss, int q) __attribute__((always_inline)) {
         if (q < AQ) {
             const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / C::NWAVES) + q * RB) * kBK * 2);
             const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * RB) * ldt2 + kc_par[q & 1];
@@ -495,9 +500,11 @@ void gated_gemm_kernel(const GemmKArgs a) {
     constexpr int GROUP = MI * NJ;
     // (item indices are derived from the unrolled MFMA index, so that they
     // stay compile-time constants: a counter would make the per-item offset
-    // arrays dynamically indexed and push them to scratch)
-    auto mfma_group = [&](int set, const StageSrc* ss, int q0, int q1) __attribute__((always_inline)) {
-        const int nq = ss != nullptr ? q1 - q0 : 0;
+    // arrays dynamically indexed and push them to scratch; the stage source
+    // is passed by value for the same reason -- through a pointer it is kept
+    // in memory)
+    auto mfma_group = [&](int set, bool has_ss, const StageSrc ss, int q0, int q1) __attribute__((always_inline)) {
+        const int nq = has_ss ? q1 - q0 : 0;
         const int spacing = nq > 0 && GROUP / nq > 0 ? GROUP / nq : 1;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -506,19 +513,21 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
                 const int m = i * NJ + j + 1;
                 const int q = q0 + m / spacing - 1;
-                if (ss != nullptr && m % spacing == 0 && q < q1) {
+                if (has_ss && m % spacing == 0 && q < q1) {
                     __builtin_amdgcn_sched_barrier(0);
-                    dma_item(*ss, q);
+                    dma_item(ss, q);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        if (ss != nullptr) {
+        if (has_ss) {
 #pragma unroll
-            for (int qq = q0 + GROUP / spacing; qq < q1; ++qq) dma_item(*ss, qq);
+            for (int qq = q0 + GROUP / spacing; qq < q1; ++qq) dma_item(ss, qq);
         }
     };
-    // copy items per sub-step window (all sub-steps but the last carry items)
-    constexpr int WIN = KSUB - 1;
+    // copy items per sub-step window (all sub-steps but the last carry items;
+    // with two buffers the copies of stage s + 1 have only stage s to land in,
+    // so they all go out in its first sub-step)
+    constexpr int WIN = kNBUF == 2 ? 1 : KSUB - 1;
     constexpr int PER_WIN = (NITEM + WIN - 1) / WIN;
 
     // stage `it` (its first fragments already read), then open stage it+1
@@ -529,14 +538,14 @@ void gated_gemm_kernel(const GemmKArgs a) {
         for (int kk = 0; kk < KSUB - 1; ++kk) {
             read_frags(buf, kk + 1, (kk + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_group(kk & 1, &ahead, kk * PER_WIN, (kk + 1) * PER_WIN < NITEM ? (kk + 1) * PER_WIN : NITEM);
+            mfma_group(kk & 1, true, ahead, kk * PER_WIN, (kk + 1) * PER_WIN < NITEM ? (kk + 1) * PER_WIN : NITEM);
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmcnt<(kNBUF - 2) * NITEM>();  // this wavefront's copy of stage it+1 has landed
         __syncthreads();                    // ... every wavefront's; and buffer `buf` is no longer read
         read_frags((it + 1) % kNBUF, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group((KSUB - 1) & 1, nullptr, 0, 0);
+        mfma_group((KSUB - 1) & 1, false, StageSrc{}, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto body_last = [&](int it) __attribute__((always_inline)) {
@@ -545,10 +554,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
         for (int kk = 0; kk < KSUB - 1; ++kk) {
             read_frags(buf, kk + 1, (kk + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_group(kk & 1, nullptr, 0, 0);
+            mfma_group(kk & 1, false, StageSrc{}, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_group((KSUB - 1) & 1, nullptr, 0, 0);
+        mfma_group((KSUB - 1) & 1, false, StageSrc{}, 0, 0);
     };
 
     if (!PP && nk_s > 0) {
@@ -611,8 +620,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
         for (int p = 0; p < nph; ++p) {
             if ((p & 1) == team) {
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_group(0, nullptr, 0, 0);
-                mfma_group(1, nullptr, 0, 0);
+                mfma_group(0, false, StageSrc{}, 0, 0);
+                mfma_group(1, false, StageSrc{}, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 // the stage this team computes next (past the last stage the
@@ -752,13 +761,16 @@ struct Tile {
     int bm, bn;
     int waves;  // 4 (2 x 2) or 8 (2 x 4, two wavefronts per SIMD)
     bool pp;    // 8 wavefronts in two ping-pong teams (256 x 256 only, 32-deep stages)
-    int kb;     // K per stage: 64 (two LDS buffers) or 32 (four)
+    int kb;     // K per stage: 64 (two LDS buffers by default) or 32 (four)
+    int nb = 0; // LDS stage buffers when not the default 128 / kb
 };
+
+int stage_buffers(Tile t) { return t.nb > 0 ? t.nb : 128 / t.kb; }
 
 constexpr int kNumCUs = 256;
 
 // Workgroups that run at once per CU for a tile shape (LDS-limited).
-int occupancy(Tile t) { return (128 * (t.bm + t.bn) * 2 > 80 * 1024) ? 1 : 2; }
+int occupancy(Tile t) { return (stage_buffers(t) * t.kb * (t.bm + t.bn) * 2 > 80 * 1024) ? 1 : 2; }
 
 // Launch-time model used to rank (tile, split) plans: a workgroup costs a
 // fixed time (launch share, prologue, epilogue) plus its MFMA work at a
@@ -774,7 +786,8 @@ TileModel tile_model(Tile t) {
     if (t.bm == 256 && t.bn == 256 && t.pp) return {4.2e12, 10.0};
     if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.8e12, 9.0} : TileModel{4.3e12, 15.0};
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
-    if (t.bm == 128) return {1.7e12, 10.0};
+    if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {4.1e12, 8.0};  // one per CU
+    if (t.bm == 128) return {2.2e12, 8.0};
     return {0.9e12, 8.0};
 }
 
@@ -783,7 +796,8 @@ TileModel tile_model(Tile t) {
 int default_kb(int bm, int bn) { return bm * bn >= 256 * 128 ? 32 : 64; }
 
 // UNO_GEMM_TILE forces a tile (tests and tuning): "BMxBN" with optional
-// suffixes "w8" (eight wavefronts), "pp" (ping-pong), "k32" / "k64" (stage depth).
+// suffixes "w8" (eight wavefronts), "pp" (ping-pong), "k32" / "k64" (stage
+// depth), "bN" (N LDS stage buffers).
 Tile env_tile() {
     const char* s = getenv("UNO_GEMM_TILE");
     Tile t{0, 0, 4, false, 64};
@@ -797,12 +811,18 @@ Tile env_tile() {
         t.kb = 32;
     }
     if (strstr(s, "k32")) t.kb = 32;
+    if (const char* b = strchr(s, 'b')) {
+        if (b[1] >= '2' && b[1] <= '8') t.nb = b[1] - '0';
+    }
     return t;
 }
 
 bool tile_supported(Tile t) {
+    if (t.nb > 0 && t.nb != 128 / t.kb)  // extra stage buffers: the one-workgroup-per-CU 128 x 128 tile
+        return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && (t.nb == 3 || t.nb == 4);
     if (t.pp) return t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 32;
     if (t.waves == 8) return t.bm == 256 && t.bn == 256 && (t.kb == 32 || t.kb == 64);
+    if (t.bm == 256 && t.bn == 256 && t.waves == 4 && t.kb == 64) return true;
     if (t.waves != 4 || t.kb != default_kb(t.bm, t.bn)) return false;
     return (t.bm == 64 && t.bn == 128) || (t.bm == 128 && t.bn == 128) || (t.bm == 128 && t.bn == 256) ||
            (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
@@ -859,7 +879,7 @@ Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs)) return forced;
     const Tile cands[] = {{256, 256, 8, false, 32}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
-                          {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
+                          {128, 128, 4, false, 64, 4}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
     Tile best{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
@@ -891,8 +911,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     const int64_t rows_model = std::max<int64_t>(p.rows_cap - kRowAlign, kRowAlign);
     // T mode (the LoRA down-projection: few rows, N = r or a few r) runs
     // 64 x 128 tiles, measured faster there than 128 x 128 by 10-30%.
-    p.tile = tmode ? Tile{64, 128, 4, false, 64} : choose_tile(rows_model, N, K, gs);
-    if (tmode && getenv("UNO_T_TILE") && atoi(getenv("UNO_T_TILE")) == 128) p.tile = Tile{128, 128, 4, false, 64};
+    // (four stage buffers: the prologue puts three stages in flight at once,
+    // measured 3-10% faster than two)
+    p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs);
+    if (const char* e = tmode ? getenv("UNO_T_TILE") : nullptr) {  // tuning: "128" (two buffers) or "64b2"
+        if (atoi(e) == 128) p.tile = Tile{128, 128, 4, false, 64};
+        if (strstr(e, "b2")) p.tile.nb = 2;
+    }
     if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4, false, 64};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
@@ -919,10 +944,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     return p;
 }
 
-template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false>
+template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false, int NB = 0>
 void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(TileCfg<BM, BN, WGM, WGN, KB>::THREADS), 0, stream, ka);
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP, NB>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(TileCfg<BM, BN, WGM, WGN, KB, NB>::THREADS), 0, stream, ka);
 }
 
 template <bool TMODE>
@@ -936,15 +961,21 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
     const Tile t = p.tile;
     if constexpr (TMODE) {
         if (t.bm == 128) launch_tile<128, 128, 2, 2, true>(ka, blocks, stream);
+        else if (stage_buffers(t) == 4) launch_tile<64, 128, 2, 2, true, 64, false, 4>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 64)
             launch_tile<256, 256, 2, 4, false, 64>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 32>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 256 && t.kb == 64) launch_tile<256, 256, 2, 2, false, 64>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false, 32>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128 && stage_buffers(t) == 4)
+            launch_tile<128, 128, 2, 2, false, 64, false, 4>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128 && stage_buffers(t) == 3)
+            launch_tile<128, 128, 2, 2, false, 64, false, 3>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 128) launch_tile<128, 128, 2, 2, false>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, false>(ka, blocks, stream);
     }

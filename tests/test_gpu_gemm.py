@@ -121,7 +121,8 @@ def test_deterministic_repeat():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("tile", ["64x128", "128x128", "128x256", "256x128", "256x256", "256x256w8", "256x256w8k64", "256x256pp"])
+@pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x256", "256x128", "256x256",
+                                  "256x256k64", "256x256w8", "256x256w8k64", "256x256pp"])
 def test_every_tile_shape_ragged(tile, monkeypatch):
     """Each workgroup tile on a problem ragged in M, N and K, through the split steps."""
     monkeypatch.setenv("UNO_GEMM_TILE", tile)
@@ -140,6 +141,24 @@ def test_every_tile_shape_ragged(tile, monkeypatch):
     assert err <= BF16_TOL, err
     y_full = _run(inp, "bf16")
     assert np.array_equal(y, y_full), "split steps and the one-call projection must agree bitwise"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("t_tile", ["64b2", "128"])
+def test_lora_down_tiles_agree(t_tile, monkeypatch):
+    """The LoRA down-projection gives the same T bits with every tile and buffer count
+    (each output sums the same K slices in the same order)."""
+    M, K, r = 300, 2048, 128  # K = 2048: four K splits for every tile
+    rng = np.random.default_rng(12)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    inp = gemm_inputs(M, K, 256, r, seed=22, dtype="bf16", gate=gate)
+    say("lora_down tile", t_tile)
+    x, a = to_dev(inp["x"], "bf16"), to_dev(inp["a"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t_default = uno.lora_down(x, a, plan, 2.0).clone()
+    monkeypatch.setenv("UNO_T_TILE", t_tile)
+    t_forced = uno.lora_down(x, a, plan, 2.0)
+    assert torch.equal(t_default, t_forced)
 
 
 GROUPED = [  # (M, K, group sizes, r)
