@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 SCALE = 2.0                   # alpha / r = 256 / 128
+EARLY_CHUNK = 4  # positions per chunk of the early-exit verifier
 
 
 def parse():
@@ -166,6 +167,27 @@ def main():
     digest = source_digest("gemm.hip")
     traffic = committed_traffic("gated_gemm", digest)
 
+    # The early-exit verifier on the last step's inputs (outside the timed
+    # region): its time per call, the share of logit rows it streams, and a
+    # check that its outputs are the one-pass verifier's.
+    last = total_steps - 1
+    uno.philox_uniforms(0, 0, last * B * (L + 1), B * (L + 1), out=u)
+    e_out = (torch.empty_like(n_acc[0]), torch.empty_like(out_tok[0]), torch.empty_like(n_emit[0]))
+    ews = uno.Workspace(dev)
+    for _ in range(3):
+        uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
+    ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ee0.record()
+    for _ in range(20):
+        uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
+    ee1.record()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(e_out, (n_acc[last], out_tok[last], n_emit[last])))
+    chunks_read = torch.clamp((n_acc[last].long() + EARLY_CHUNK) // EARLY_CHUNK, max=(L + EARLY_CHUNK - 1) // EARLY_CHUNK)
+    rows_read = torch.clamp(chunks_read * EARLY_CHUNK, max=L).sum().item() / (B * L)
+    verify_early = {"chunk": EARLY_CHUNK, "us_per_call": round(ee0.elapsed_time(ee1) / 20 * 1e3, 3),
+                    "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
+
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
     v_gbs = verify_bytes(B, L, V, 2, redraws) / vt / 1e9
@@ -216,6 +238,7 @@ def main():
             "frac": round(v_gbs / PEAK_HBM_GBS, 4),
             "us_per_call": round(vt * 1e6, 3),
             "redraws_per_call": redraws,
+            "early_exit": verify_early,
         },
         "cpu_baseline": None,
     }

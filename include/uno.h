@@ -221,6 +221,33 @@ uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Block verification with early exit.  Only the prefix up to the first
+ * rejection decides the output ("The Psi-Spec Sampler" on the
+ * aifromscratch.in page: the longest valid prefix is kept), so positions are
+ * taken in chunks of `chunk`: the logit rows of a chunk are streamed only for
+ * sequences with no rejection in earlier chunks, and a sequence stops at the
+ * chunk holding its first rejection (the bonus row, if any, streams with the
+ * last chunk).  Rows read per sequence fall from L (+1) to about
+ * chunk * ceil((n_acc + 1) / chunk).
+ *
+ * Arguments, arithmetic, domain and outputs are those of uno_block_verify,
+ * plus chunk in [1, 64]; every output equals uno_block_verify's bit for bit
+ * (a row's statistics are formed with the same chunking of V, and every
+ * position is decided by the same code).  Launches 2 * ceil(L / chunk) + 2
+ * kernels instead of 2, so it pays where rejections come early and rows
+ * are long.
+ * workspace: at least uno_block_verify_early_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+size_t uno_block_verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
+uno_status uno_block_verify_early(const void* target_logits, const void* draft_logits,
+                                  int64_t target_seq_stride, int64_t draft_seq_stride,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  int64_t B, int32_t L, int64_t V, int32_t has_bonus,
+                                  float temperature, int32_t logits_dtype, int32_t chunk,
+                                  int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Draft proposal: one token per drafted position, drawn in parallel from the
  * diffusion pathway's distribution q_i = softmax(d_i / T) by inverse CDF
  * ("The Psi-Spec Sampler" on the aifromscratch.in page: the diffusion

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     UnoError,
     Workspace,
     block_verify,
+    block_verify_early_workspace_size,
     block_verify_workspace_size,
     draft_sample,
     draft_sample_workspace_size,

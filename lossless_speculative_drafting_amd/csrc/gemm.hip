@@ -271,7 +271,11 @@ struct TileCfg {
     static constexpr int STAGE_ELEMS = (BM + BN) * KB;
     static constexpr int LDS_ELEMS = NBUF * STAGE_ELEMS;
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
-    static_assert(LDS_ELEMS * 2 + BM * 4 <= 160 * 1024, "LDS");
+    // The output-row table (BM int32) goes behind the epilogue's staging area
+    // in the stage buffers when they have room for it, else into LDS of its own.
+    static constexpr bool OROW_IN_STAGE = LDS_ELEMS * 2 >= BM * BN * 2 + BM * 4;
+    static_assert(LDS_ELEMS * 2 + (OROW_IN_STAGE ? 0 : BM * 4) <= 160 * 1024, "LDS");
+    static_assert(THREADS >= BM, "one output row per thread");
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
@@ -286,7 +290,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
     constexpr int RB = C::RB;
     constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
-    __shared__ int32_t s_orow[BM];  // output row of each tile row (-1: none)
+    __shared__ int32_t s_orow_own[C::OROW_IN_STAGE ? 1 : BM];
+    // output row of each tile row (-1: none)
+    int32_t* const s_orow = C::OROW_IN_STAGE ? reinterpret_cast<int32_t*>(smem + BM * BN) : s_orow_own;
 
     // ---- workgroup -> (m tile, n tile, split), each XCD taking a contiguous band of tiles
     const int32_t total = a.m_tiles * a.n_tiles * a.splits;
@@ -313,19 +319,19 @@ void gated_gemm_kernel(const GemmKArgs a) {
 
     const int tid = threadIdx.x;
     // Output rows are looked up once, here, so that the epilogue's stores do
-    // not wait on a global load each (the main loop's barriers publish them).
-    for (int i = tid; i < BM; i += C::THREADS) {
-        const int64_t p = m0 + i;
-        int32_t o = -1;
-        if (p < rows_valid) {
-            if constexpr (TMODE) {
-                o = static_cast<int32_t>(p);
-            } else {
-                o = a.perm[p];
-            }
+    // not wait on a global load each: thread t holds row t's in a register
+    // and publishes it to LDS (at once when the table has LDS of its own, the
+    // main loop's barriers publishing it; else after the main loop, when the
+    // stage buffers are free).
+    int32_t my_orow = -1;
+    if (tid < BM && m0 + tid < rows_valid) {
+        if constexpr (TMODE) {
+            my_orow = static_cast<int32_t>(m0 + tid);
+        } else {
+            my_orow = a.perm[m0 + tid];
         }
-        s_orow[i] = o;
     }
+    if (!C::OROW_IN_STAGE && tid < BM) s_orow[tid] = my_orow;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
     const int lane = tid % kWave;
     const int wm = wave / WGN;
@@ -637,6 +643,11 @@ void gated_gemm_kernel(const GemmKArgs a) {
     }
 
     // ---- epilogue
+    if constexpr (C::OROW_IN_STAGE) {
+        __syncthreads();  // every wavefront is done with the stage buffers
+        if (tid < BM) s_orow[tid] = my_orow;
+        __syncthreads();
+    }
     // lane holds D[row][col] of each 32x32 block with col = lane % 32 and
     // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4, v = 0..15.
     const int64_t gend = grp.end;  // end of this tile's group

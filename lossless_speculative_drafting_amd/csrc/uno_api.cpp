@@ -272,11 +272,12 @@ size_t uno_block_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t 
     return uno::verify_workspace_size(B, L, V, has_bonus ? 1 : 0);
 }
 
-uno_status uno_block_verify(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
-                            int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms, int64_t B,
-                            int32_t L, int64_t V, int32_t has_bonus, float temperature, int32_t logits_dtype,
-                            int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+static uno_status block_verify_common(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
+                                      int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms,
+                                      int64_t B, int32_t L, int64_t V, int32_t has_bonus, float temperature,
+                                      int32_t logits_dtype, int32_t* n_accepted, int32_t* out_tokens,
+                                      int32_t* n_emitted, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream, int32_t chunk) {
     uno_status st = check_logits(B, L, V, temperature, logits_dtype);
     if (st != UNO_OK) return st;
     if (has_bonus != 0 && has_bonus != 1) return fail(UNO_ERR_INVALID_ARG, "has_bonus must be 0 or 1");
@@ -292,7 +293,8 @@ uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
     const int64_t rows = B * (L + has_bonus);
     const int64_t max_chunks = (V + 2047) / 2048;
     if (rows * max_chunks > kMaxGridX || B > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "problem too large for one launch");
-    const size_t need = uno::verify_workspace_size(B, L, V, has_bonus);
+    const size_t need = chunk > 0 ? uno::verify_early_workspace_size(B, L, V, has_bonus)
+                                  : uno::verify_workspace_size(B, L, V, has_bonus);
     st = check_workspace(workspace, workspace_bytes, need);
     if (st != UNO_OK) return st;
     uno::VerifyProblem p{};
@@ -311,7 +313,34 @@ uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
     p.n_accepted = n_accepted;
     p.out_tokens = out_tokens;
     p.n_emitted = n_emitted;
-    return from_hip(uno::block_verify_launch(p, workspace, stream), "block verify launch");
+    return from_hip(uno::block_verify_launch(p, workspace, stream, chunk), "block verify launch");
+}
+
+uno_status uno_block_verify(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
+                            int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms, int64_t B,
+                            int32_t L, int64_t V, int32_t has_bonus, float temperature, int32_t logits_dtype,
+                            int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    return block_verify_common(target_logits, draft_logits, target_seq_stride, draft_seq_stride, draft_tokens,
+                               uniforms, B, L, V, has_bonus, temperature, logits_dtype, n_accepted, out_tokens,
+                               n_emitted, workspace, workspace_bytes, stream, 0);
+}
+
+size_t uno_block_verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
+    if (B < 0 || L < 1 || L > 64 || V < 1) return 0;
+    ok();
+    return uno::verify_early_workspace_size(B, L, V, has_bonus ? 1 : 0);
+}
+
+uno_status uno_block_verify_early(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
+                                  int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms,
+                                  int64_t B, int32_t L, int64_t V, int32_t has_bonus, float temperature,
+                                  int32_t logits_dtype, int32_t chunk, int32_t* n_accepted, int32_t* out_tokens,
+                                  int32_t* n_emitted, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (chunk < 1 || chunk > 64) return fail(UNO_ERR_INVALID_ARG, "chunk must be in [1, 64] (got %d)", chunk);
+    return block_verify_common(target_logits, draft_logits, target_seq_stride, draft_seq_stride, draft_tokens,
+                               uniforms, B, L, V, has_bonus, temperature, logits_dtype, n_accepted, out_tokens,
+                               n_emitted, workspace, workspace_bytes, stream, chunk);
 }
 
 size_t uno_draft_sample_workspace_size(int64_t B, int32_t L, int64_t V) {

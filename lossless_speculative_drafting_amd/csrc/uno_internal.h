@@ -38,8 +38,10 @@ struct VerifyProblem {
 };
 
 size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
+size_t verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
 size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V);
-hipError_t block_verify_launch(const VerifyProblem& p, void* ws, hipStream_t stream);
+// chunk = 0: one pass over every row; chunk > 0: early exit in chunks of positions
+hipError_t block_verify_launch(const VerifyProblem& p, void* ws, hipStream_t stream, int32_t chunk = 0);
 hipError_t draft_sample_launch(const VerifyProblem& p, void* ws, hipStream_t stream);
 
 // ---- gated-LoRA projection ----------------------------------------------------

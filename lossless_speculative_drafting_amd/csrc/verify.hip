@@ -144,17 +144,21 @@ __device__ __forceinline__ Online wave_merge(Online o, float c2) {
 }
 
 // ---------------------------------------------------------------- row_stats
-// Rows are (s, i) with i < rows_per_seq; array B exists for i < rows_with_b.
+// Rows are (s, i) with i in [i0, i0 + rows_per_seq) of rows_full rows per
+// sequence; array B exists for i < rows_with_b.  With live flags, sequences
+// whose flag is 0 are skipped (their statistics are not written).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(
     const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
     int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
-    ChunkStat* __restrict__ stats) {
+    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full, const int32_t* __restrict__ live) {
     const int64_t blk = blockIdx.x;
-    const int64_t row = blk / n_chunks;
+    const int64_t lrow = blk / n_chunks;
     const int32_t c = static_cast<int32_t>(blk % n_chunks);
-    const int64_t s = row / rows_per_seq;
-    const int32_t i = static_cast<int32_t>(row % rows_per_seq);
+    const int64_t s = lrow / rows_per_seq;
+    const int32_t i = i0 + static_cast<int32_t>(lrow % rows_per_seq);
+    const int64_t row = s * rows_full + i;
+    if (live != nullptr && live[s] == 0) return;  // uniform for the workgroup
     const size_t esz = BF16 ? 2 : 4;
     const char* arow = static_cast<const char*>(A) + (s * a_stride + static_cast<int64_t>(i) * V) * esz;
     const bool has_b = (B != nullptr) && (i < rows_with_b);
@@ -256,58 +260,78 @@ struct DecideArgs {
     int32_t* n_emitted;
 };
 
-// Decision for sequence s by one wavefront (lane = lane index): acceptance of
-// every drafted position, the first rejection, the emitted prefix, and the
-// redraw job (written by lane 0 to *job_out).
+// Position `lane` of sequence s: its drafted token, whether it is in range,
+// the merged statistics of its target (and draft) row, and whether it is
+// accepted.  `drafted`: a drafted position (lane < L); `stat_row`: a row with
+// statistics (lane < L + bonus).  Every verifier decides a position through
+// this one function, so that all of them take the same decision.
+struct LaneDecision {
+    int32_t x;
+    bool valid, acc;
+    float Mz, Md;
+    double Sz, Sd;
+};
+
 template <bool BF16>
-__device__ __forceinline__ void decide_sequence(const DecideArgs& a, int64_t s, int lane, RedrawJob* job_out,
-                                                bool write_outputs = true) {
+__device__ __forceinline__ LaneDecision lane_decision(const DecideArgs& a, int64_t s, int lane, bool drafted,
+                                                      bool stat_row) {
     const int32_t L = a.L;
     const int32_t rows = L + a.nb;
     const size_t esz = BF16 ? 2 : 4;
+    LaneDecision d{0, true, true, -INFINITY, -INFINITY, 0.0, 0.0};
     // The drafted token, its uniform and its two logits do not depend on the
     // row statistics: their loads go out first, so that the memory round
     // trips overlap the statistics merge.
-    int32_t x = 0;
-    bool valid = true;
-    bool acc = true;
     float ux = 0.f, zx = 0.f, dx = 0.f;
-    if (lane < L) {
-        x = a.tokens[s * L + lane];
+    if (drafted) {
+        d.x = a.tokens[s * L + lane];
         ux = a.uniforms[s * (L + 1) + lane];
-        valid = (x >= 0) && (static_cast<int64_t>(x) < a.V);
-        if (valid) {
+        d.valid = (d.x >= 0) && (static_cast<int64_t>(d.x) < a.V);
+        if (d.valid) {
             const char* zrow = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(lane) * a.V) * esz;
             const char* drow = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(lane) * a.V) * esz;
-            zx = load_one<BF16>(zrow, x);
-            dx = load_one<BF16>(drow, x);
+            zx = load_one<BF16>(zrow, d.x);
+            dx = load_one<BF16>(drow, d.x);
         }
     }
-
-    float Mz = -INFINITY, Md = -INFINITY;
-    double Sz = 0.0, Sd = 0.0;
-    if (lane < rows) {
+    if (stat_row) {
         const ChunkStat* st = a.stats + (s * rows + lane) * a.n_chunks;
-        merge_chunks(st, a.n_chunks, false, a.invT, Mz, Sz);
-        if (lane < L) merge_chunks(st, a.n_chunks, true, a.invT, Md, Sd);
+        merge_chunks(st, a.n_chunks, false, a.invT, d.Mz, d.Sz);
+        if (drafted) merge_chunks(st, a.n_chunks, true, a.invT, d.Md, d.Sd);
     }
-
-    if (lane < L) {
-        acc = false;
-        if (valid) {
+    if (drafted) {
+        d.acc = false;
+        if (d.valid) {
             double prob;
             if (zx == -INFINITY) {
                 prob = 0.0;
             } else if (dx == -INFINITY) {
                 prob = 1.0;
             } else {
-                const double lp = (static_cast<double>(zx) - static_cast<double>(Mz)) * a.invT - log(Sz);
-                const double lq = (static_cast<double>(dx) - static_cast<double>(Md)) * a.invT - log(Sd);
+                const double lp = (static_cast<double>(zx) - static_cast<double>(d.Mz)) * a.invT - log(d.Sz);
+                const double lq = (static_cast<double>(dx) - static_cast<double>(d.Md)) * a.invT - log(d.Sd);
                 prob = exp(fmin(0.0, lp - lq));
             }
-            acc = static_cast<double>(ux) < prob;
+            d.acc = static_cast<double>(ux) < prob;
         }
     }
+    return d;
+}
+
+// Decision for sequence s by one wavefront (lane = lane index): acceptance of
+// every drafted position, the first rejection, the emitted prefix, and the
+// redraw job (written by lane 0 to *job_out).  Positions past the first
+// rejection do not change any output, so their statistics may be stale.
+template <bool BF16>
+__device__ __forceinline__ void decide_sequence(const DecideArgs& a, int64_t s, int lane, RedrawJob* job_out,
+                                                bool write_outputs = true) {
+    const int32_t L = a.L;
+    const size_t esz = BF16 ? 2 : 4;
+    const LaneDecision d = lane_decision<BF16>(a, s, lane, lane < L, lane < L + a.nb);
+    const int32_t x = d.x;
+    const bool valid = d.valid, acc = d.acc;
+    const float Mz = d.Mz, Md = d.Md;
+    const double Sz = d.Sz, Sd = d.Sd;
     const uint64_t bad = __ballot(!valid);
     const uint64_t rej = __ballot(!acc);
     const int32_t n_acc = rej ? static_cast<int32_t>(__builtin_ctzll(rej)) : L;
@@ -360,6 +384,29 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
     const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
     decide_sequence<BF16>(a, s, lane, a.jobs + s);
+}
+
+// ---------------------------------------------------------------- early exit
+// Verification in chunks of positions: the statistics of positions [i0, i1)
+// are streamed only for sequences with no rejection before i0, and this
+// kernel (one wavefront per sequence) clears a sequence's live flag at its
+// first rejection (or out-of-range token) in [i0, i1).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void chunk_decide_kernel(DecideArgs a, int32_t i0, int32_t i1,
+                                                                int32_t* __restrict__ live) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
+    if (live[s] == 0) return;
+    const bool in = lane >= i0 && lane < i1;
+    const LaneDecision d = lane_decision<BF16>(a, s, lane, in, in);
+    const uint64_t stop = __ballot(in && (!d.valid || !d.acc));
+    if (lane == 0 && stop != 0) live[s] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void live_init_kernel(int32_t* __restrict__ live, int64_t B) {
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (s < B) live[s] = 1;
 }
 
 // ---------------------------------------------------------------- draft_decide
@@ -745,8 +792,10 @@ bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
     return (V % kVec == 0) && (s0 % kVec == 0) && (s1 % kVec == 0) && al(p0) && (p1 == nullptr || al(p1));
 }
 
+// chunk = 0: one pass over every row; chunk > 0: early exit, positions in
+// chunks of `chunk` (the live flags follow the plan's workspace).
 template <bool BF16, bool VEC>
-hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const int32_t nb = pr.has_bonus ? 1 : 0;
     const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2);
     char* base = static_cast<char*>(ws);
@@ -756,9 +805,6 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     const double invT = 1.0 / static_cast<double>(pr.temperature);
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
 
-    hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
-                       stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
-                       p.chunk1, p.c1, c2, stats);
     DecideArgs da;
     da.target = pr.target;
     da.draft = pr.draft;
@@ -777,6 +823,27 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     da.n_accepted = pr.n_accepted;
     da.out_tokens = pr.out_tokens;
     da.n_emitted = pr.n_emitted;
+    if (chunk <= 0) {
+        hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
+                           0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
+                           p.chunk1, p.c1, c2, stats, 0, pr.L + nb, nullptr);
+    } else {
+        // The statistics of a row are the same bits as in the one-pass plan
+        // (same chunking of V), so every decision is the one-pass decision.
+        int32_t* live = reinterpret_cast<int32_t*>(base + p.total);
+        const uint32_t sblocks = static_cast<uint32_t>((pr.B + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(live_init_kernel, dim3(sblocks), dim3(kThreads), 0, stream, live, pr.B);
+        const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
+        for (int32_t i0 = 0; i0 < pr.L; i0 += chunk) {
+            const int32_t i1 = std::min(pr.L, i0 + chunk);
+            const int32_t nrows = (i1 - i0) + (i1 == pr.L ? nb : 0);  // the bonus row rides with the last chunk
+            hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * nrows * p.c1)),
+                               dim3(kThreads), 0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, nrows,
+                               pr.L, pr.V, p.chunk1, p.c1, c2, stats, i0, pr.L + nb, live);
+            hipLaunchKernelGGL((chunk_decide_kernel<BF16>), dim3(dblocks), dim3(kThreads), 0, stream, da, i0, i1,
+                               live);
+        }
+    }
     const size_t tail_lds = select_lds_bytes(p.nseg);
     if (tail_lds > 0) {
         hipLaunchKernelGGL((verify_tail_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kTailThreads),
@@ -804,7 +871,7 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
     hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
                        stream, pr.draft, pr.d_stride, nullptr, int64_t(0), pr.L, 0, pr.V, p.chunk1, p.c1, c2,
-                       stats);
+                       stats, 0, pr.L, nullptr);
     hipLaunchKernelGGL((draft_decide_kernel<BF16>), dim3(static_cast<uint32_t>((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, invT, stats, p.c1,
                        pr.uniforms, pr.sampled, jobs);
@@ -822,14 +889,19 @@ size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus)
     return make_plan(B, L, V, L + nb, B, 2).total;
 }
 
+size_t verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
+    return verify_workspace_size(B, L, V, has_bonus) + align_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign);
+}
+
 size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V) {
     return make_plan(B, L, V, L, B * L, 1).total;
 }
 
-hipError_t block_verify_launch(const VerifyProblem& pr, void* ws, hipStream_t stream) {
+hipError_t block_verify_launch(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const bool vec = vec_ok(pr.target, pr.draft, pr.V, pr.t_stride, pr.d_stride);
-    if (pr.bf16) return vec ? verify_impl<true, true>(pr, ws, stream) : verify_impl<true, false>(pr, ws, stream);
-    return vec ? verify_impl<false, true>(pr, ws, stream) : verify_impl<false, false>(pr, ws, stream);
+    if (pr.bf16)
+        return vec ? verify_impl<true, true>(pr, ws, stream, chunk) : verify_impl<true, false>(pr, ws, stream, chunk);
+    return vec ? verify_impl<false, true>(pr, ws, stream, chunk) : verify_impl<false, false>(pr, ws, stream, chunk);
 }
 
 hipError_t draft_sample_launch(const VerifyProblem& pr, void* ws, hipStream_t stream) {

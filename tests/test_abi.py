@@ -121,6 +121,20 @@ def test_block_verify_validation(lib):
     assert lib.uno_block_verify_workspace_size(64, 65, 128256, 0) == 0
 
 
+def test_block_verify_early_validation(lib):
+    assert lib.uno_block_verify_early_workspace_size(64, 16, 128256, 0) >= lib.uno_block_verify_workspace_size(64, 16, 128256, 0) > 0
+    assert lib.uno_block_verify_early_workspace_size(64, 65, 128256, 0) == 0
+    args = (FAKE, FAKE, 0, 0, FAKE, FAKE, 4, 8, 64, 0, 1.0, 0)
+    tail = (FAKE, FAKE, FAKE, FAKE, 1 << 30, STREAM)
+    assert lib.uno_block_verify_early(*args, 0, *tail) == INVALID        # chunk < 1
+    assert lib.uno_block_verify_early(*args, 65, *tail) == INVALID       # chunk > 64
+    assert lib.uno_block_verify_early(FAKE, FAKE, 0, 0, FAKE, FAKE, 4, 8, 64, 0, -1.0, 0, 4, *tail) != OK
+    assert lib.uno_block_verify_early(FAKE, FAKE, 0, 0, FAKE, FAKE, 4, 8, 64, 0, 1.0, 0, 4,
+                                      FAKE, FAKE, FAKE, FAKE, 4, STREAM) == WORKSPACE
+    assert lib.uno_block_verify_early(NULL, NULL, 0, 0, NULL, NULL, 0, 8, 64, 0, 1.0, 0, 4,
+                                      NULL, NULL, NULL, NULL, 0, STREAM) == OK
+
+
 def test_draft_sample_and_glue_validation(lib):
     assert lib.uno_draft_sample(FAKE, 0, FAKE, 2, 0, 64, 1.0, 0, FAKE, FAKE, 1 << 30, STREAM) == INVALID
     assert lib.uno_draft_sample(FAKE, 0, FAKE, 2, 4, 64, -1.0, 0, FAKE, FAKE, 1 << 30, STREAM) == UNSUPPORTED

@@ -176,3 +176,76 @@ def test_serve_b256_full_size(T):
 def test_stack32_b32_full_size():
     wl = WORKLOADS["stack32_b32"]
     _full_vocab_case(32, wl.block, wl.vocab, "normal", 1.0, 1.0, wl.seed, np.arange(32))
+
+
+# ---------------------------------------------------------------- early exit
+EARLY = [  # B, L, V, dtype, kind, sigma, T, bonus, chunk
+    (37, 7, 1000, "bf16", "normal", 1.0, 1.0, False, 3),    # ragged last chunk
+    (37, 7, 999, "bf16", "normal", 0.25, 0.6, True, 2),     # bonus row with the last chunk
+    (16, 64, 4096, "bf16", "normal", 1.0, 1.0, False, 4),
+    (9, 63, 520, "f32", "normal", 4.0, 1.0, True, 16),
+    (64, 16, 2048, "bf16", "zipf", 0.5, 0.6, False, 1),     # one position per chunk
+    (64, 16, 2048, "bf16", "zipf", 0.5, 0.6, True, 64),     # one chunk: the one-pass schedule
+    (300, 2, 17, "f32", "normal", 1.0, 2.0, False, 1),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,L,V,dtype,kind,sigma,T,bonus,chunk", EARLY)
+def test_early_exit_matches_one_pass_and_oracle(B, L, V, dtype, kind, sigma, T, bonus, chunk):
+    """Early-exit verification: the same bits as the one-pass verifier, and the oracle's tokens."""
+    z, d = verify_inputs(B, L, V, seed=B * 37 + L + V, kind=kind, target_sigma=3.0, draft_sigma=sigma,
+                         has_bonus=bonus, dtype=dtype)
+    x = _drafts(d, T)
+    u = oracle.philox_uniforms(0, 0, 0, B * (L + 1)).reshape(B, L + 1)
+    args = (to_dev(z, dtype), to_dev(d, dtype), to_dev(x, "i32"), to_dev(u, "f32"), T, bonus)
+    say(f"verify early B={B} L={L} V={V} chunk={chunk} bonus={bonus}")
+    one = [to_host(t) for t in uno.block_verify(*args)]
+    early = [to_host(t) for t in uno.block_verify(*args, early_chunk=chunk)]
+    for a, b in zip(one, early):
+        np.testing.assert_array_equal(a, b)
+    ref = oracle.block_verify(z, d, x, u, T, bonus)
+    exact, excused, fails = compare_verify(tuple(early), ref, z, d, u, T, bonus)
+    assert not fails, fails[:5]
+    assert excused <= max(1, 0.01 * B)
+
+
+@pytest.mark.gpu
+def test_early_exit_invalid_tokens_and_accept_all():
+    """Out-of-range tokens past a rejection still give -1; q == p accepts every chunk."""
+    B, L, V = 12, 9, 300
+    z, d = verify_inputs(B, L, V, seed=5, kind="normal", target_sigma=2.0, draft_sigma=1.0, dtype="bf16")
+    x = _drafts(d, 1.0)
+    x[1, 8] = V          # invalid token in the last chunk
+    x[2, 0] = -1         # invalid token in the first chunk
+    u = oracle.philox_uniforms(1, 0, 0, B * (L + 1)).reshape(B, L + 1)
+    args = (to_dev(z, "bf16"), to_dev(d, "bf16"), to_dev(x, "i32"), to_dev(u, "f32"), 1.0, False)
+    say("verify early: invalid tokens")
+    one = [to_host(t) for t in uno.block_verify(*args)]
+    early = [to_host(t) for t in uno.block_verify(*args, early_chunk=2)]
+    for a, b in zip(one, early):
+        np.testing.assert_array_equal(a, b)
+    assert early[0][1] == -1 and early[0][2] == -1
+    zt = to_dev(z, "bf16")
+    xs = _drafts(z, 1.0)
+    say("verify early: q == p")
+    n_acc, tok, n_emit = uno.block_verify(zt, zt, to_dev(xs, "i32"), to_dev(u, "f32"), 1.0, False, early_chunk=4)
+    assert np.all(to_host(n_acc) == L) and np.all(to_host(n_emit) == L)
+    np.testing.assert_array_equal(to_host(tok)[:, :L], xs)
+
+
+@pytest.mark.gpu
+def test_early_exit_full_size():
+    """Full vocabulary (V = 128256) at 32 x 16 positions: early exit equals one pass."""
+    wl = WORKLOADS["stack32_b32"]
+    B, L, V = 32, wl.block, wl.vocab
+    say(f"verify early full-size B={B} L={L} V={V}")
+    zt, dt = sdev.verify_logits(B, L, V, wl.seed, kind="normal", target_sigma=3.0, draft_sigma=1.0)
+    d = to_host(dt).astype(np.float32)
+    xt = to_dev(_drafts(d, 1.0, seed=wl.seed), "i32")
+    u = to_dev(oracle.philox_uniforms(wl.seed, 0, 0, B * (L + 1)).reshape(B, L + 1), "f32")
+    one = [to_host(t) for t in uno.block_verify(zt, dt, xt, u, 1.0, False)]
+    for chunk in (2, 4):
+        early = [to_host(t) for t in uno.block_verify(zt, dt, xt, u, 1.0, False, early_chunk=chunk)]
+        for a, b in zip(one, early):
+            np.testing.assert_array_equal(a, b)
