@@ -173,6 +173,43 @@ uno_status uno_gated_gemm_grouped(const void* x, const void* w, const void* t, c
                                   int32_t n_groups, int64_t M, int64_t K, int32_t r, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* Gated GEMM with the residual add in its epilogue: y <- y + P, P the
+ * uno_gated_gemm result, for a projection that feeds the residual stream of
+ * its layer (the pages put the LoRA pathway into each transformer layer --
+ * "How It Works: The 'Uno' Architecture" on the aifromscratch.in page).  P is
+ * rounded to bf16 first and the sum is rounded again, so y is bitwise
+ * uno_residual_add(y, P).  y [M, N] is read and written in place (it must
+ * not alias x, w, t or lora_b); other arguments and the domain as
+ * uno_gated_gemm. */
+size_t uno_gated_gemm_residual_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
+uno_status uno_gated_gemm_residual(const void* x, const void* w, const void* t, const void* lora_b,
+                                   const void* row_plan, void* y, int64_t M, int64_t N, int64_t K, int32_t r,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gate and up projections of a layer with silu(g) * u in the epilogue (the
+ * layer structure as for uno_gated_gemm_residual).  The weights come
+ * interleaved by uno_swiglu_pack: w_packed [2 N_half, K] holds 128-row blocks
+ * of W_gate and W_up in turn, b_packed [2 N_half, rt] the block-diagonal
+ * LoRA B (gate rows use T columns [0, rt/2), up rows [rt/2, rt)); t is
+ * uno_lora_down over the stacked [A_gate; A_up] (width rt = 2 r).  Output
+ * act [M, N_half] = bf16(silu(g) * u) with g, u the bf16 gate and up
+ * projections, bitwise the result of uno_gated_gemm_grouped for gate and up
+ * under the same plan followed by uno_silu_mul.
+ * Domain: N_half a positive multiple of 128, rt a multiple of 8 in [8, 256],
+ * otherwise as uno_gated_gemm; act must not alias the inputs. */
+size_t uno_gated_gemm_swiglu_workspace_size(int64_t M, int64_t N_half, int64_t K, int32_t rt);
+uno_status uno_gated_gemm_swiglu(const void* x, const void* w_packed, const void* t, const void* b_packed,
+                                 const void* row_plan, void* act, int64_t M, int64_t N_half, int64_t K, int32_t rt,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Packing for uno_gated_gemm_swiglu: w_gate, w_up [N_half, K] and b_gate,
+ * b_up [N_half, r] (bf16) into w_packed [2 N_half, K] and b_packed
+ * [2 N_half, 2 r] as described there.  Domain: N_half a positive multiple of
+ * 128; K, r multiples of 8, r <= 512; outputs must not alias inputs. */
+uno_status uno_swiglu_pack(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
+                           int64_t N_half, int64_t K, int32_t r, void* w_packed, void* b_packed,
+                           hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Block verification ("The Psi-Spec Sampler" on the aifromscratch.in page:
  * rejection-sample the drafted block against the AR model and keep the

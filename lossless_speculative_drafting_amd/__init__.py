@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     draft_sample_workspace_size,
     gated_gemm,
     gated_gemm_grouped,
+    gated_gemm_residual,
+    gated_gemm_swiglu,
     gated_lora_fwd,
     gated_lora_workspace_size,
     header_symbols,
@@ -37,5 +39,6 @@ from ._lib import (  # noqa: F401
     rmsnorm,
     silu_mul,
     status_string,
+    swiglu_pack,
 )
 from .stack import GatedLoraStack  # noqa: F401

@@ -40,6 +40,14 @@ SIGNATURES = {
     "uno_gated_gemm_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32]),
     "uno_gated_gemm": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int64,
                                   _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_gated_gemm_residual_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32]),
+    "uno_gated_gemm_residual": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64,
+                                           _c_int64, _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_gated_gemm_swiglu_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int64, _c_int32]),
+    "uno_gated_gemm_swiglu": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64,
+                                         _c_int64, _c_int32, _c_ptr, _c_size, _c_ptr]),
+    "uno_swiglu_pack": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int32, _c_ptr, _c_ptr,
+                                   _c_ptr]),
     "uno_gated_gemm_grouped_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int32, _c_ptr, _c_int32]),
     "uno_gated_gemm_grouped": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int32,
                                           _c_int64, _c_int64, _c_int32, _c_ptr, _c_size, _c_ptr]),
@@ -270,6 +278,59 @@ def gated_gemm_grouped(x, w, t, lora_b, plan, group_n, outs=None, workspace=None
     _check(_lib.uno_gated_gemm_grouped(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), ys, ns, G, M, K, r,
                                        _ptr(ws), need, _stream(stream)))
     return outs
+
+
+def gated_gemm_residual(x, w, t, lora_b, plan, y, workspace=None, stream=None):
+    """y += x W_AR + T B on the plan's draft rows (uno_gated_gemm_residual); returns y."""
+    _need_cuda(x, w, t, lora_b, y)
+    M, K = x.shape
+    N = w.shape[0]
+    r = lora_b.shape[1]
+    if w.shape != (N, K) or lora_b.shape != (N, r) or y.shape != (M, N) or plan.M != M or not y.is_contiguous():
+        raise ValueError("shape mismatch: x [M,K], w [N,K], lora_b [N,r], y [M,N] contiguous, plan over M rows")
+    if t.numel() * t.element_size() < lora_t_size(M, r):
+        raise ValueError("t buffer too small")
+    need = int(_lib.uno_gated_gemm_residual_workspace_size(M, N, K, r))
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_gated_gemm_residual(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), _ptr(y), M, N, K,
+                                        r, _ptr(ws), need, _stream(stream)))
+    return y
+
+
+def swiglu_pack(w_gate, w_up, b_gate, b_up, stream=None):
+    """(w_packed [2N, K], b_packed [2N, 2r]) for gated_gemm_swiglu (uno_swiglu_pack)."""
+    _need_cuda(w_gate, w_up, b_gate, b_up)
+    N, K = w_gate.shape
+    r = b_gate.shape[1]
+    if w_up.shape != (N, K) or b_gate.shape != (N, r) or b_up.shape != (N, r):
+        raise ValueError("shape mismatch: w_gate, w_up [N,K]; b_gate, b_up [N,r]")
+    w_p = torch.empty((2 * N, K), dtype=w_gate.dtype, device=w_gate.device)
+    b_p = torch.empty((2 * N, 2 * r), dtype=w_gate.dtype, device=w_gate.device)
+    _check(_lib.uno_swiglu_pack(_ptr(w_gate), _ptr(w_up), _ptr(b_gate), _ptr(b_up), N, K, r, _ptr(w_p), _ptr(b_p),
+                                _stream(stream)))
+    return w_p, b_p
+
+
+def gated_gemm_swiglu(x, w_packed, t, b_packed, plan, out=None, workspace=None, stream=None):
+    """act = silu(x W_gate + ...) * (x W_up + ...) from swiglu_pack weights (uno_gated_gemm_swiglu)."""
+    _need_cuda(x, w_packed, t, b_packed)
+    M, K = x.shape
+    N2 = w_packed.shape[0]
+    rt = b_packed.shape[1]
+    if w_packed.shape != (N2, K) or b_packed.shape != (N2, rt) or N2 % 2 or plan.M != M:
+        raise ValueError("shape mismatch: x [M,K], w_packed [2N,K], b_packed [2N,rt], plan over M rows")
+    if t.numel() * t.element_size() < lora_t_size(M, rt):
+        raise ValueError("t buffer too small")
+    Nh = N2 // 2
+    if out is None:
+        out = torch.empty((M, Nh), dtype=x.dtype, device=x.device)
+    if out.shape != (M, Nh) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] tensor")
+    need = int(_lib.uno_gated_gemm_swiglu_workspace_size(M, Nh, K, rt))
+    ws = _workspace(workspace, need, x.device)
+    _check(_lib.uno_gated_gemm_swiglu(_ptr(x), _ptr(w_packed), _ptr(t), _ptr(b_packed), _ptr(plan.buf), _ptr(out), M,
+                                      Nh, K, rt, _ptr(ws), need, _stream(stream)))
+    return out
 
 
 # ------------------------------------------------------------------ verification

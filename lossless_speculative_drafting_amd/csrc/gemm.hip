@@ -123,6 +123,39 @@ __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t
 // row-major buffer y[g] with row stride ldy[g], and its draft rows use T
 // columns [g*r, (g+1)*r).  end[n-1] is the full width N; every other end
 // falls on a tile edge.
+// Epilogues of the main mode.  Store: y = bf16(result).  Accumulate:
+// y = bf16(y + bf16(result)) (the residual add, rounded as a separate add
+// would).  SwiGLU: the weights interleave 128-row blocks of W_gate and W_up,
+// so that columns [256 i, 256 i + 128) of the result are gate columns
+// [128 i, 128 i + 128) and the next 128 the matching up columns; the output
+// is act[:, 128 i + c] = bf16(silu(bf16(g)) * bf16(u)), rounded as the
+// separate GEMM and silu_mul launches would.
+constexpr int32_t kEpiStore = 0, kEpiAccumulate = 1, kEpiSwiglu = 2;
+constexpr int kSwigluBlock = 128;
+
+__device__ __forceinline__ uint4 add8_bf16(const uint4 a, const uint4 b) {
+    float fa[8], fb[8];
+    unpack8(a, fa);
+    unpack8(b, fb);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = f32_to_bf16_bits(fa[2 * j] + fb[2 * j]) | (f32_to_bf16_bits(fa[2 * j + 1] + fb[2 * j + 1]) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ uint4 swiglu8_bf16(const uint4 g, const uint4 u) {
+    float fg[8], fu[8];
+    unpack8(g, fg);
+    unpack8(u, fu);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = f32_to_bf16_bits(silu_mul_f32(fg[2 * j], fu[2 * j])) |
+               (f32_to_bf16_bits(silu_mul_f32(fg[2 * j + 1], fu[2 * j + 1])) << 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 struct OutGroups {
     int32_t n;
     int64_t end[kMaxGroups];
@@ -177,6 +210,7 @@ struct GemmKArgs {
     int64_t k_per_split;
     int32_t m_tiles, n_tiles;
     float alpha;
+    int32_t epi;          // Epilogue (main mode): kEpiStore, kEpiAccumulate, kEpiSwiglu
 };
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -676,13 +710,38 @@ void gated_gemm_kernel(const GemmKArgs a) {
         constexpr int RPI = kWave / CPR;  // rows per store instruction
         const int c = lane % CPR;
         const int64_t n = n0 + wn * C::WN + c * 8;
+        if constexpr (!TMODE && BN == 2 * kSwigluBlock && WGN % 2 == 0) {
+            if (a.epi == kEpiSwiglu) {
+                // Wavefront (wm, pw) holds gate columns [pw WN, pw WN + WN) of the
+                // tile and (wm, pw + WGN / 2) the matching up columns; the two
+                // share the output rows of the pair, each taking half of them.
+                __syncthreads();
+                const int pw = wn % (WGN / 2), half = wn / (WGN / 2);
+                const uint16_t* sg = smem + (wm * WGN + pw) * C::WM * C::WN;
+                const uint16_t* su = smem + (wm * WGN + pw + WGN / 2) * C::WM * C::WN;
+                const int64_t ng = n0 + pw * C::WN + c * 8;          // gate column
+                const int64_t na = (n0 >> 1) + pw * C::WN + c * 8;   // act column
+#pragma unroll 4
+                for (int r = half * (C::WM / 2) + lane / CPR; r < (half + 1) * (C::WM / 2); r += RPI) {
+                    const int32_t orow = s_orow[wm * C::WM + r];
+                    if (orow < 0 || ng >= gend) continue;
+                    const int pc = c ^ (((r >> 2) & 1) << 2);
+                    *reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + na) =
+                        swiglu8_bf16(*reinterpret_cast<const uint4*>(&sg[r * C::WN + pc * 8]),
+                                     *reinterpret_cast<const uint4*>(&su[r * C::WN + pc * 8]));
+                }
+                return;
+            }
+        }
+        const bool accumulate = a.epi == kEpiAccumulate;
 #pragma unroll 8
         for (int r = lane / CPR; r < C::WM; r += RPI) {
             const int32_t orow = s_orow[wm * C::WM + r];
             if (orow < 0 || n >= gend) continue;
             const int pc = c ^ (((r >> 2) & 1) << 2);
-            *reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + (n - gstart)) =
-                *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
+            uint4* dst = reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + (n - gstart));
+            const uint4 v = *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
+            *dst = accumulate ? add8_bf16(*dst, v) : v;
         }
         return;
     }
@@ -698,8 +757,13 @@ void gated_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
-                    if (n < gend)
-                        gy[orow * gldy + (n - gstart)] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
+                    if (n < gend) {
+                        uint16_t* dst = gy + orow * gldy + (n - gstart);
+                        const uint32_t yb = f32_to_bf16_bits(acc[i][j][v] * a.alpha);
+                        *dst = static_cast<uint16_t>(
+                            a.epi == kEpiAccumulate ? f32_to_bf16_bits(bf16_bits_to_f32(*dst) + bf16_bits_to_f32(yb))
+                                                    : yb);
+                    }
                 }
             } else {
                 float* prow = a.partial + (static_cast<int64_t>(z) * a.rows_cap + p) * a.N;
@@ -713,26 +777,41 @@ void gated_gemm_kernel(const GemmKArgs a) {
     }
 }
 
-// Sum split-K partials in split order, scale, round to bf16 and scatter.
+// Sum split-K partials in split order, scale, round to bf16 and scatter
+// through the epilogue (SwiGLU: one output per gate / up column pair).
 template <bool TMODE>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int32_t splits,
                                                            int64_t rows_cap, int64_t N,
                                                            const SegInfo* __restrict__ info,
                                                            const int32_t* __restrict__ perm, float alpha,
-                                                           const OutGroups out) {
+                                                           const OutGroups out, int32_t epi) {
     const SegInfo si = *info;
     const int64_t rows_valid = TMODE ? si.Md_pad : static_cast<int64_t>(si.Pv) + si.Md_pad;
-    const int64_t total = rows_valid * N;
+    const bool swiglu = !TMODE && epi == kEpiSwiglu;
+    const int64_t ncols = swiglu ? N / 2 : N;
+    const int64_t total = rows_valid * ncols;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += stride) {
-        const int64_t p = e / N;
-        const int64_t n = e - p * N;
-        const int64_t orow = TMODE ? p : perm[p];
-        if (orow < 0) continue;
+    auto sum = [&](int64_t p, int64_t n) {
         float s = 0.f;
         for (int32_t zz = 0; zz < splits; ++zz) s += partial[(static_cast<int64_t>(zz) * rows_cap + p) * N + n];
+        return f32_to_bf16_bits(s * alpha);
+    };
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += stride) {
+        const int64_t p = e / ncols;
+        const int64_t n = e - p * ncols;
+        const int64_t orow = TMODE ? p : perm[p];
+        if (orow < 0) continue;
+        if (swiglu) {
+            const int64_t ng = (n / kSwigluBlock) * 2 * kSwigluBlock + n % kSwigluBlock;
+            const float g = bf16_bits_to_f32(sum(p, ng)), u = bf16_bits_to_f32(sum(p, ng + kSwigluBlock));
+            out.y[0][orow * out.ldy[0] + n] = static_cast<uint16_t>(f32_to_bf16_bits(silu_mul_f32(g, u)));
+            continue;
+        }
         const GroupRef g = find_group(out, n);
-        g.y[orow * g.ldy + (n - g.start)] = static_cast<uint16_t>(f32_to_bf16_bits(s * alpha));
+        uint16_t* dst = g.y + orow * g.ldy + (n - g.start);
+        const uint32_t yb = sum(p, n);
+        *dst = static_cast<uint16_t>(
+            (!TMODE && epi == kEpiAccumulate) ? f32_to_bf16_bits(bf16_bits_to_f32(*dst) + bf16_bits_to_f32(yb)) : yb);
     }
 }
 
@@ -886,15 +965,17 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
     return best;
 }
 
-Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs) {
+// bn256: only tiles 256 columns wide (the SwiGLU epilogue pairs columns c and
+// c + 128 of a tile).
+Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256) {
     const Tile forced = env_tile();
-    if (tile_supported(forced) && tile_fits(forced, gs)) return forced;
+    if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256)) return forced;
     const Tile cands[] = {{256, 256, 8, false, 32}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
                           {128, 128, 4, false, 64, 4}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
-    Tile best{64, 128, 4, false, 64};
+    Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
-        if (!tile_fits(t, gs)) continue;
+        if (!tile_fits(t, gs) || (bn256 && t.bn != 256)) continue;
         double us = 0;
         choose_split_for(t, rows_cap, N, K, &us);
         if (us < best_us * 0.999) {
@@ -913,7 +994,7 @@ struct GemmPlan {
     size_t partial_bytes;
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs, bool bn256 = false) {
     GemmPlan p{};
     p.rows_cap = rows_cap_for(M);
     // The plan covers rows_cap rows (room for both segments' padding), but in
@@ -924,12 +1005,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     // 64 x 128 tiles, measured faster there than 128 x 128 by 10-30%.
     // (four stage buffers: the prologue puts three stages in flight at once,
     // measured 3-10% faster than two)
-    p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs);
+    p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs, bn256);
     if (const char* e = tmode ? getenv("UNO_T_TILE") : nullptr) {  // tuning: "128" (two buffers) or "64b2"
         if (atoi(e) == 128) p.tile = Tile{128, 128, 4, false, 64};
         if (strstr(e, "b2")) p.tile.nb = 2;
     }
-    if (!tmode && p.rows_cap <= 64) p.tile = Tile{64, 128, 4, false, 64};
+    if (!tmode && p.rows_cap <= 64) p.tile = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
     int64_t s;
@@ -994,7 +1075,7 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         const int64_t elems = p.rows_cap * ka.N;
         const uint32_t rg = static_cast<uint32_t>(std::min<int64_t>(4096, (elems + 255) / 256));
         hipLaunchKernelGGL((splitk_reduce_kernel<TMODE>), dim3(rg), dim3(256), 0, stream, ka.partial, p.splits,
-                           p.rows_cap, ka.N, ka.info, ka.perm, ka.alpha, ka.out);
+                           p.rows_cap, ka.N, ka.info, ka.perm, ka.alpha, ka.out, ka.epi);
     }
 }
 
@@ -1069,17 +1150,17 @@ bool gated_gemm_groups_ok(const int64_t* group_n, int32_t n_groups) {
     return true;
 }
 
-size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups) {
+size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups, int32_t epi) {
     const GroupSpec gs = group_spec(group_n, n_groups);
-    return plan_gemm(M, gs.end[n_groups - 1], K, false, gs).partial_bytes;
+    return plan_gemm(M, gs.end[n_groups - 1], K, false, gs, epi == kEpiSwiglu).partial_bytes;
 }
 
 hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
                              void* const* ys, const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K,
-                             int32_t r, void* ws, hipStream_t stream) {
+                             int32_t r, void* ws, hipStream_t stream, int32_t epi) {
     const GroupSpec gs = group_spec(group_n, n_groups);
     const int64_t N = gs.end[n_groups - 1];
-    const GemmPlan p = plan_gemm(M, N, K, false, gs);
+    const GemmPlan p = plan_gemm(M, N, K, false, gs, epi == kEpiSwiglu);
     GemmKArgs ka{};
     ka.x = static_cast<const uint16_t*>(x);
     ka.ldx = K;
@@ -1099,13 +1180,14 @@ hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const 
     for (int i = 0; i < n_groups; ++i) {
         ka.out.end[i] = gs.end[i];
         ka.out.y[i] = static_cast<uint16_t*>(ys[i]);
-        ka.out.ldy[i] = group_n[i];
+        ka.out.ldy[i] = epi == kEpiSwiglu ? group_n[i] / 2 : group_n[i];
     }
     ka.partial = static_cast<float*>(ws);
     ka.N = N;
     ka.K = K;
     ka.r = r;
     ka.alpha = 1.0f;
+    ka.epi = epi;
     launch_gemm<false>(p, ka, stream);
     return hipGetLastError();
 }

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void eltwise_kernel(const uint16_t* __res
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if constexpr (OP == 0) {
-                fa[j] = fa[j] / (1.0f + __expf(-fa[j])) * fb[j];
+                fa[j] = silu_mul_f32(fa[j], fb[j]);
             } else {
                 fa[j] = fa[j] + fb[j];
             }
@@ -140,8 +140,44 @@ __global__ __launch_bounds__(kThreads) void eltwise_kernel(const uint16_t* __res
     if (t < n && t >= nv * 8) {
         const float fa = bf16_bits_to_f32(a[t]);
         const float fb = bf16_bits_to_f32(b[t]);
-        const float r = (OP == 0) ? fa / (1.0f + __expf(-fa)) * fb : fa + fb;
+        const float r = (OP == 0) ? silu_mul_f32(fa, fb) : fa + fb;
         out[t] = static_cast<uint16_t>(f32_to_bf16_bits(r));
+    }
+}
+
+// One thread per 16-byte chunk of the packed outputs: row R of W_out is row
+// (R / 256) * 128 + R % 128 of W_gate (R % 256 < 128) or of W_up; row R of
+// B_out holds that row of B_gate in columns [0, r) or of B_up in [r, 2 r),
+// zeros elsewhere.  K % 8 == 0 and r % 8 == 0 (checked by the host).
+__global__ __launch_bounds__(kThreads) void swiglu_pack_kernel(const uint16_t* __restrict__ wg,
+                                                              const uint16_t* __restrict__ wu,
+                                                              const uint16_t* __restrict__ bg,
+                                                              const uint16_t* __restrict__ bu, int64_t N_half,
+                                                              int64_t K, int32_t r, uint16_t* __restrict__ w_out,
+                                                              uint16_t* __restrict__ b_out) {
+    const int64_t wv = K / 8, bv = 2 * static_cast<int64_t>(r) / 8;
+    const int64_t rows = 2 * N_half;
+    const int64_t total = rows * (wv + bv);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < total; e += stride) {
+        const int64_t R = e / (wv + bv);
+        const int64_t v = e - R * (wv + bv);
+        const bool up = (R % 256) >= 128;
+        const int64_t src = (R / 256) * 128 + R % 128;
+        if (v < wv) {
+            const uint16_t* w = up ? wu : wg;
+            reinterpret_cast<uint4*>(w_out + R * K)[v] = reinterpret_cast<const uint4*>(w + src * K)[v];
+        } else {
+            const int64_t bvv = v - wv;               // chunk of the 2 r output columns
+            const bool in_half = up ? (bvv * 8 >= r) : (bvv * 8 < r);
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (in_half) {
+                const uint16_t* b = up ? bu : bg;
+                const int64_t cv = up ? bvv - r / 8 : bvv;
+                val = reinterpret_cast<const uint4*>(b + src * r)[cv];
+            }
+            reinterpret_cast<uint4*>(b_out + R * 2 * r)[bvv] = val;
+        }
     }
 }
 
@@ -176,6 +212,17 @@ hipError_t residual_rmsnorm_launch(const void* x, const void* y, void* s_out, vo
     else
         hipLaunchKernelGGL(residual_rmsnorm_kernel<0>, dim3(static_cast<uint32_t>(M)), dim3(kThreads), 0, stream,
                            xs, ys, so, hs, K, eps);
+    return hipGetLastError();
+}
+
+hipError_t swiglu_pack_launch(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
+                              int64_t N_half, int64_t K, int32_t r, void* w_out, void* b_out, hipStream_t stream) {
+    if (N_half <= 0) return hipSuccess;
+    const int64_t total = 2 * N_half * (K / 8 + 2 * static_cast<int64_t>(r) / 8);
+    hipLaunchKernelGGL(swiglu_pack_kernel, dim3(eltwise_grid(total * 8)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                       static_cast<const uint16_t*>(b_gate), static_cast<const uint16_t*>(b_up), N_half, K, r,
+                       static_cast<uint16_t*>(w_out), static_cast<uint16_t*>(b_out));
     return hipGetLastError();
 }
 

@@ -204,6 +204,82 @@ uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const voi
     return uno_gated_gemm_grouped(x, w, t, lora_b, row_plan, &y, &N, 1, M, K, r, workspace, workspace_bytes, stream);
 }
 
+size_t uno_gated_gemm_residual_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r) {
+    if (check_gemm(M, N, K, r, UNO_BF16) != UNO_OK) return 0;
+    ok();
+    return uno::gated_gemm_workspace_size(M, K, &N, 1, 1);
+}
+
+uno_status uno_gated_gemm_residual(const void* x, const void* w, const void* t, const void* lora_b,
+                                   const void* row_plan, void* y, int64_t M, int64_t N, int64_t K, int32_t r,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_gemm(M, N, K, r, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (M == 0) return ok();
+    if (!x || !w || !t || !lora_b || !row_plan || !y) return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(t) || !aligned16(lora_b) || !aligned16(y) ||
+        !aligned256(row_plan))
+        return fail(UNO_ERR_INVALID_ARG, "tensors must be 16-byte aligned, row_plan 256-byte aligned");
+    st = check_workspace(workspace, workspace_bytes, uno::gated_gemm_workspace_size(M, K, &N, 1, 1));
+    if (st != UNO_OK) return st;
+    void* ys[1] = {y};
+    return from_hip(uno::gated_gemm_launch(x, w, t, lora_b, row_plan, ys, &N, 1, M, K, r, workspace, stream, 1),
+                    "gated gemm (residual) launch");
+}
+
+static uno_status check_swiglu(int64_t M, int64_t N_half, int64_t K, int32_t rt) {
+    if (N_half < 128 || N_half % 128 != 0)
+        return fail(UNO_ERR_UNSUPPORTED, "N_half must be a positive multiple of 128 (got %lld)",
+                    static_cast<long long>(N_half));
+    if (N_half > (1LL << 30)) return fail(UNO_ERR_UNSUPPORTED, "N_half too large");
+    uno_status st = check_gemm(M, 2 * N_half, K, rt, UNO_BF16);
+    if (st != UNO_OK) return st;
+    return check_lora_t(M, K, rt);
+}
+
+size_t uno_gated_gemm_swiglu_workspace_size(int64_t M, int64_t N_half, int64_t K, int32_t rt) {
+    if (check_swiglu(M, N_half, K, rt) != UNO_OK) return 0;
+    ok();
+    const int64_t N = 2 * N_half;
+    return uno::gated_gemm_workspace_size(M, K, &N, 1, 2);
+}
+
+uno_status uno_gated_gemm_swiglu(const void* x, const void* w_packed, const void* t, const void* b_packed,
+                                 const void* row_plan, void* act, int64_t M, int64_t N_half, int64_t K, int32_t rt,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_swiglu(M, N_half, K, rt);
+    if (st != UNO_OK) return st;
+    if (M == 0) return ok();
+    if (!x || !w_packed || !t || !b_packed || !row_plan || !act)
+        return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(x) || !aligned16(w_packed) || !aligned16(t) || !aligned16(b_packed) || !aligned16(act) ||
+        !aligned256(row_plan))
+        return fail(UNO_ERR_INVALID_ARG, "tensors must be 16-byte aligned, row_plan 256-byte aligned");
+    int64_t N = 2 * N_half;
+    st = check_workspace(workspace, workspace_bytes, uno::gated_gemm_workspace_size(M, K, &N, 1, 2));
+    if (st != UNO_OK) return st;
+    void* ys[1] = {act};
+    return from_hip(uno::gated_gemm_launch(x, w_packed, t, b_packed, row_plan, ys, &N, 1, M, K, rt, workspace,
+                                           stream, 2),
+                    "gated gemm (SwiGLU) launch");
+}
+
+uno_status uno_swiglu_pack(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
+                           int64_t N_half, int64_t K, int32_t r, void* w_packed, void* b_packed, hipStream_t stream) {
+    if (N_half < 128 || N_half % 128 != 0)
+        return fail(UNO_ERR_UNSUPPORTED, "N_half must be a positive multiple of 128");
+    if (K < 8 || K % 8 != 0 || r < 8 || r % 8 != 0 || r > 512)
+        return fail(UNO_ERR_UNSUPPORTED, "need K and r multiples of 8, r in [8, 512]");
+    if (N_half > (1LL << 30) || K > (1LL << 30)) return fail(UNO_ERR_UNSUPPORTED, "sizes too large");
+    if (!w_gate || !w_up || !b_gate || !b_up || !w_packed || !b_packed)
+        return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(b_gate) || !aligned16(b_up) || !aligned16(w_packed) ||
+        !aligned16(b_packed))
+        return fail(UNO_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    return from_hip(uno::swiglu_pack_launch(w_gate, w_up, b_gate, b_up, N_half, K, r, w_packed, b_packed, stream),
+                    "swiglu pack launch");
+}
+
 static uno_status check_groups(const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K, int32_t r,
                                int64_t* N_out) {
     if (group_n == nullptr) return fail(UNO_ERR_INVALID_ARG, "group_n is null");

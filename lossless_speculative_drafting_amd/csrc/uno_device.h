@@ -37,6 +37,14 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
     f[7] = __uint_as_float(v.w & 0xFFFF0000u);
 }
 
+// silu(g) * u = g * (1 / (1 + e^-g)) * u with the hardware exp and
+// reciprocal (each within about 1 ulp of fp32, far below the bf16 rounding of
+// the result): the one spelling every kernel uses, so that the fused and the
+// separate SwiGLU paths round identically.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Raw hardware 2^x (v_exp_f32).  Results below the normal range flush to 0,
 // which only drops terms far below one part in 2^126 of a softmax sum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -70,11 +70,17 @@ hipError_t lora_down_launch(const void* x, const void* lora_a, const void* plan,
                             int32_t r, float scale, void* ws, hipStream_t stream);
 // Output column groups: n_groups in [1, 4], group_n[g] >= 1, every group but
 // the last a multiple of 128 columns.
+// epi: 0 store, 1 accumulate into y, 2 SwiGLU over 128-column gate / up
+// blocks (one group of 2 * N_half interleaved columns; y is [M, N_half]).
 bool gated_gemm_groups_ok(const int64_t* group_n, int32_t n_groups);
-size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups);
+size_t gated_gemm_workspace_size(int64_t M, int64_t K, const int64_t* group_n, int32_t n_groups, int32_t epi = 0);
 hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const void* lora_b, const void* plan,
                              void* const* ys, const int64_t* group_n, int32_t n_groups, int64_t M, int64_t K,
-                             int32_t r, void* ws, hipStream_t stream);
+                             int32_t r, void* ws, hipStream_t stream, int32_t epi = 0);
+// Interleave W_gate / W_up [N_half, K] into [2 N_half, K] in 128-row blocks and
+// B_gate / B_up [N_half, r] into the block-diagonal [2 N_half, 2 r].
+hipError_t swiglu_pack_launch(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
+                              int64_t N_half, int64_t K, int32_t r, void* w_out, void* b_out, hipStream_t stream);
 
 // ---- layer glue ----------------------------------------------------------------
 hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps,

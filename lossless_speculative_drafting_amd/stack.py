@@ -16,9 +16,14 @@ that read the same input run as one grouped launch (q, k, v; gate, up): their
 W_AR and lora_b rows are stacked once at construction, their A matrices too,
 so one LoRA down-projection yields T for the whole group and one grouped
 gated GEMM writes each projection to its own buffer.  A layer is then four
-down-projections and four gated GEMMs.  With grouped=False every projection
-runs on its own.  After the first call a forward pass launches only library
-kernels on the current stream.
+down-projections and four gated GEMMs.  With fused=True (the default) gate
+and up run with silu(g) * u in the GEMM epilogue (uno_gated_gemm_swiglu,
+weights interleaved once at construction), bitwise the unfused chain under
+the same plan.  (The residual add is not fused into o and down: their tiles
+run one per CU, where the epilogue's read of the residual is not hidden, and
+the separate add + norm launch costs less.)  With grouped=False every
+projection runs on its own.  After the first call a forward pass launches only library kernels on
+the current stream.
 """
 
 import ctypes
@@ -47,7 +52,7 @@ def _stack_group(layer, names):
 
 
 class GatedLoraStack:
-    def __init__(self, layers, gate, scale=2.0, eps=1e-5, grouped=True):
+    def __init__(self, layers, gate, scale=2.0, eps=1e-5, grouped=True, fused=True):
         """layers: list of dicts name -> (w [N,K], lora_a [r,K], lora_b [N,r]) bf16 CUDA tensors.
         gate: uint8 CUDA tensor [M] (1 = draft row).
 
@@ -69,6 +74,14 @@ class GatedLoraStack:
                 self.groups.append(gl)
             layers = new_layers
         self.layers = layers
+        self.fused = self.grouped and bool(fused)
+        self.swiglu = []
+        if self.fused:
+            for li, layer in enumerate(layers):
+                wg, _, bg = layer["gate"]
+                wu, _, bu = layer["up"]
+                w_p, b_p = _lib.swiglu_pack(wg, wu, bg, bu)
+                self.swiglu.append((w_p, self.groups[li][GROUPS[1]][1], b_p))
         self.gate = gate
         self.scale = float(scale)
         self.eps = float(eps)
@@ -108,16 +121,21 @@ class GatedLoraStack:
                 need = max(need, int(lib.uno_lora_down_workspace_size(M, K, a.shape[0])),
                            int(lib.uno_gated_gemm_grouped_workspace_size(M, K, r, arr, len(ns))))
                 t_width = max(t_width, a.shape[0])
+        if self.fused:
+            w_p, a_st, b_p = self.swiglu[0]
+            need = max(need, int(lib.uno_gated_gemm_swiglu_workspace_size(M, w_p.shape[0] // 2, w_p.shape[1],
+                                                                          b_p.shape[1])))
         self.ws = _lib.Workspace(dev)
         self.ws.get(need)
         self.t = torch.empty(_lib.lora_t_size(M, t_width) // 2, dtype=bf, device=dev)
         self.plan = None
 
-    def _timed(self, K, N, launch):
+    def _timed(self, K, N, launch, out_cols=None, t_cols=None):
         """Run one gated-GEMM launch; with a timer list set, bracket it with
         HIP events on the current stream and record its algorithmic flops
         (2 M K N for the product, 2 Md r N for the adapter extension) and
-        bytes (W and B once, x and y once, the draft rows of T once)."""
+        bytes (W and B once, x and y once, the draft rows of T once; y is
+        out_cols wide and T t_cols wide when given)."""
         if self.timer is None:
             launch()
             return
@@ -126,8 +144,10 @@ class GatedLoraStack:
         launch()
         e1.record()
         M, Md, r = self.M, self.Md, self.r
+        out_cols = N if out_cols is None else out_cols
+        t_cols = r if t_cols is None else t_cols
         flops = 2.0 * M * K * N + 2.0 * Md * r * N
-        nbytes = 2.0 * (N * K + N * r + M * K + M * N + Md * r)
+        nbytes = 2.0 * (N * K + N * r + M * K + M * out_cols + Md * t_cols)
         self.timer.append((e0, e1, flops, nbytes))
 
     def _proj(self, layer, name, inp, out):
@@ -142,6 +162,15 @@ class GatedLoraStack:
         self._timed(w.shape[1], w.shape[0],
                     lambda: _lib.gated_gemm_grouped(inp, w, self.t, b, self.plan, ns, outs=outs,
                                                     workspace=self.ws))
+
+    def _swiglu(self, li, inp):
+        """act = silu(P_gate(inp)) * P_up(inp) in one launch."""
+        w_p, a_st, b_p = self.swiglu[li]
+        _lib.lora_down(inp, a_st, self.plan, self.scale, t=self.t, workspace=self.ws)
+        self._timed(w_p.shape[1], w_p.shape[0],
+                    lambda: _lib.gated_gemm_swiglu(inp, w_p, self.t, b_p, self.plan, out=self.act,
+                                                   workspace=self.ws),
+                    out_cols=w_p.shape[0] // 2, t_cols=a_st.shape[0])
 
     def _projections(self, li, layer, items, trace_into):
         """items: [(name, input, output)] sharing one input when grouped."""
@@ -162,8 +191,8 @@ class GatedLoraStack:
         """
         self.x.copy_(x_in)
         self.plan = _lib.RowPlan(self.gate) if self.plan is None else self.plan
-        # Each residual add that is followed by a norm runs as one fused launch
-        # (bitwise the same as the two separate ones).
+        # (unfused layers: each residual add followed by a norm is one launch,
+        # bitwise the two separate ones)
         _lib.rmsnorm(self.x, self.eps, out=self.h)
         last = len(self.layers) - 1
         for li, layer in enumerate(self.layers):
@@ -171,8 +200,11 @@ class GatedLoraStack:
             self._projections(li, layer, [("q", self.h, self.q), ("k", self.h, self.k), ("v", self.h, self.v)], rec)
             self._projections(li, layer, [("o", self.q, self.o)], rec)
             _lib.residual_rmsnorm(self.x, self.o, self.eps, s_out=self.x, h_out=self.h)
-            self._projections(li, layer, [("gate", self.h, self.g), ("up", self.h, self.u)], rec)
-            _lib.silu_mul(self.g, self.u, out=self.act)
+            if self.fused and rec is None:  # (a traced layer runs unfused: its g and u then exist)
+                self._swiglu(li, self.h)
+            else:
+                self._projections(li, layer, [("gate", self.h, self.g), ("up", self.h, self.u)], rec)
+                _lib.silu_mul(self.g, self.u, out=self.act)
             self._projections(li, layer, [("down", self.act, self.dn)], rec)
             if li < last:
                 _lib.residual_rmsnorm(self.x, self.dn, self.eps, s_out=self.x, h_out=self.h)

@@ -15,6 +15,7 @@ import lossless_speculative_drafting_amd as uno
 import oracle
 from gpu_util import say, to_dev, to_host
 from parity import BF16_TOL, F32_TOL, floored_rel_err
+from synthetic import device as sdev
 from synthetic import WORKLOADS, gate_vector, gemm_inputs
 
 
@@ -159,6 +160,90 @@ def test_lora_down_tiles_agree(t_tile, monkeypatch):
     monkeypatch.setenv("UNO_T_TILE", t_tile)
     t_forced = uno.lora_down(x, a, plan, 2.0)
     assert torch.equal(t_default, t_forced)
+
+
+EPILOGUE = [  # M, K, N (per projection), forced tile or None, forced split or None
+    (1024, 512, 512, None, None),       # planner's tiles, one K pass
+    (300, 1000, 512, "256x256w8", "2"),  # ragged M and K, split-K: the reduction applies the epilogue
+    (32, 256, 256, None, None),          # few rows: the 128 x 256 tile (SwiGLU) / 64 x 128 (residual)
+    (96, 512, 768, "128x256", None),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,tile,split", EPILOGUE)
+def test_residual_epilogue_is_separate_add(M, K, N, tile, split, monkeypatch):
+    """uno_gated_gemm_residual == uno_residual_add(y, uno_gated_gemm(...)), bit for bit."""
+    if tile:
+        monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    if split:
+        monkeypatch.setenv("UNO_GEMM_SPLIT", split)
+    rng = np.random.default_rng(M + N)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    inp = gemm_inputs(M, K, N, 128, seed=M + K, dtype="bf16", gate=gate)
+    say("residual epilogue", M, K, N, tile, split)
+    x, w = to_dev(inp["x"], "bf16"), to_dev(inp["w"], "bf16")
+    a, b = to_dev(inp["a"], "bf16"), to_dev(inp["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, a, plan, 2.0)
+    y0 = sdev.randn((M, N), 2.0, M + 5)
+    ref = uno.residual_add(y0, uno.gated_gemm(x, w, t, b, plan))
+    y = y0.clone()
+    uno.gated_gemm_residual(x, w, t, b, plan, y)
+    assert torch.equal(y, ref)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,tile,split", EPILOGUE)
+def test_swiglu_epilogue_is_separate_silu_mul(M, K, N, tile, split, monkeypatch):
+    """uno_gated_gemm_swiglu on packed weights == silu_mul of the gate and up projections, bit for
+    bit (same tile family and split), and within the bf16 bound of the fp64 oracle."""
+    if tile:
+        monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    # the same K split on both sides (the two plans may otherwise split differently)
+    monkeypatch.setenv("UNO_GEMM_SPLIT", split or "1")
+    rng = np.random.default_rng(M + 3 * N)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    g_in = gemm_inputs(M, K, N, 128, seed=M + 1, dtype="bf16", gate=gate)
+    u_in = gemm_inputs(M, K, N, 128, seed=M + 2, dtype="bf16", gate=gate)
+    say("swiglu epilogue", M, K, N, tile, split)
+    x = to_dev(g_in["x"], "bf16")
+    wg, wu = to_dev(g_in["w"], "bf16"), to_dev(u_in["w"], "bf16")
+    ag, au = to_dev(g_in["a"], "bf16"), to_dev(u_in["a"], "bf16")
+    bg, bu = to_dev(g_in["b"], "bf16"), to_dev(u_in["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, torch.cat([ag, au], 0), plan, 2.0)       # [T_gate | T_up]
+    w_p, b_p = uno.swiglu_pack(wg, wu, bg, bu)
+    act = uno.gated_gemm_swiglu(x, w_p, t, b_p, plan)
+    g, u = uno.gated_gemm_grouped(x, torch.cat([wg, wu], 0), t, torch.cat([bg, bu], 0), plan, [N, N])
+    assert torch.equal(act, uno.silu_mul(g, u))
+    ref = oracle.stack.silu_mul(oracle.gated_lora(g_in["x"], g_in["w"], g_in["a"], g_in["b"], gate, 2.0),
+                                oracle.gated_lora(g_in["x"], u_in["w"], u_in["a"], u_in["b"], gate, 2.0))
+    # silu(g) * u of two projections each within BF16_TOL: to first order their
+    # relative errors add (silu's own relative sensitivity is at most 1 where
+    # silu(g) is not small next to the row scale)
+    err = floored_rel_err(to_host(act), ref)
+    assert err <= 2 * BF16_TOL, err
+
+
+@pytest.mark.gpu
+def test_swiglu_pack_layout():
+    """Packed rows and the block-diagonal B, checked element by element on the host."""
+    N, K, r = 256, 64, 16
+    rng = np.random.default_rng(8)
+    mats = [rng.standard_normal(s).astype(np.float32) for s in ((N, K), (N, K), (N, r), (N, r))]
+    w_p, b_p = (to_host(t) for t in uno.swiglu_pack(*(to_dev(m, "bf16") for m in mats)))
+    wg, wu, bg, bu = (to_host(to_dev(m, "bf16")) for m in mats)
+    for R in range(2 * N):
+        src = (R // 256) * 128 + R % 128
+        up = R % 256 >= 128
+        np.testing.assert_array_equal(w_p[R], (wu if up else wg)[src])
+        want = np.zeros(2 * r, np.float32)
+        if up:
+            want[r:] = bu[src]
+        else:
+            want[:r] = bg[src]
+        np.testing.assert_array_equal(b_p[R], want)
 
 
 GROUPED = [  # (M, K, group sizes, r)

@@ -98,8 +98,23 @@ def test_grouped_stack_matches_ungrouped():
     gate = gate_vector(4, 16, 16)
     x0 = sdev.randn((gate.size, 512), 1.0, 9)
     say("grouped vs ungrouped stack")
-    a = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=True).forward(x0).clone()
+    a = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=True, fused=False).forward(x0).clone()
     b = uno.GatedLoraStack(layers, to_dev(gate, "u8"), grouped=False).forward(x0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.gpu
+def test_fused_stack_matches_unfused_8b_shapes():
+    """Residual adds and SwiGLU in the GEMM epilogues give the unfused chain's bits
+    (two layers of the 8B shapes at 32 x [16 | 16] rows, the bench's plans)."""
+    wl = WORKLOADS["stack32_b32"]
+    layers = [sdev.layer_weights(wl.projections, 77 + 100 * i) for i in range(2)]
+    gate = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
+    x0 = sdev.randn((wl.rows, 4096), 1.0, 3)
+    say("fused vs unfused stack, 8B shapes")
+    a = uno.GatedLoraStack(layers, to_dev(gate, "u8"), fused=True).forward(x0).clone()
+    b = uno.GatedLoraStack(layers, to_dev(gate, "u8"), fused=False).forward(x0).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
