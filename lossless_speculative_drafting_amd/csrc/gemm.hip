@@ -283,11 +283,17 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // rate of rows of 64 bytes (L2-resident sources, measured on MI355X: 110 vs
 // 59 GB/s per CU), so KB = 64 is the default; KB = 32 keeps three stages in
 // flight where LDS would otherwise hold only two.
-template <int BM, int BN, int WGM, int WGN, int KB, int NB = 0>
+// NBB > 0 splits the ring: A (x) stages then have NBUF buffers of their own
+// and B (weight) stages NBB, so that the weights, which come from HBM, can be
+// fetched further ahead than the activations, which the L2 holds.
+template <int BM, int BN, int WGM, int WGN, int KB, int NB = 0, int NBB = 0>
 struct TileCfg {
     static_assert(KB == 64 || KB == 32, "stage depth");
     static constexpr int NBUF = NB > 0 ? NB : 128 / KB;
-    static_assert(NBUF >= 2 && NBUF <= 8, "stage buffers");
+    static constexpr bool SPLIT = NBB > 0;
+    static constexpr int NBUF_B = SPLIT ? NBB : NBUF;
+    static_assert(NBUF >= 2 && NBUF <= 8 && NBUF_B >= 2 && NBUF_B <= 8, "stage buffers");
+    static_assert(!SPLIT || NBUF == 2, "a split ring keeps two A buffers");
     static constexpr int KSUB = KB / 16;       // MFMA sub-steps per stage
     static constexpr int RB = 512 / KB;        // rows per copy instruction
     static constexpr int NWAVES = WGM * WGN;   // WGM x WGN wavefronts
@@ -303,7 +309,7 @@ struct TileCfg {
                   "with KB 64 each wavefront's copy blocks start on an even block (the swizzle parity is q & 1)");
     static_assert(MI >= 1 && NJ >= 1 && WN >= 64, "wavefront tile");
     static constexpr int STAGE_ELEMS = (BM + BN) * KB;
-    static constexpr int LDS_ELEMS = NBUF * STAGE_ELEMS;
+    static constexpr int LDS_ELEMS = SPLIT ? NBUF * BM * KB + NBUF_B * BN * KB : NBUF * STAGE_ELEMS;
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
     // The output-row table (BM int32) goes behind the epilogue's staging area
     // in the stage buffers when they have room for it, else into LDS of its own.
@@ -313,11 +319,12 @@ struct TileCfg {
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
-template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB>
-__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB>::THREADS), (TileCfg<BM, BN, WGM, WGN, KB, NB>::OCC))
+template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB, int NBB = 0>
+__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::THREADS),
+                             (TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::OCC))
 void gated_gemm_kernel(const GemmKArgs a) {
-    using C = TileCfg<BM, BN, WGM, WGN, KB, NB>;
-    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4),
+    using C = TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>;
+    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4 && !C::SPLIT),
                   "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32, four buffers");
     constexpr int kBK = KB;
     constexpr int kNBUF = C::NBUF;
@@ -456,7 +463,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
         uint32_t arange, brange;  // their byte ranges (0 past the last stage)
         uint32_t kbytes;          // byte offset of the stage's first K within a row
         uint32_t krem;            // K columns left in the stage's source (>= kBK: none masked)
-        uint32_t lds;             // LDS byte address of the stage's buffer
+        uint32_t lds;             // LDS byte address of the stage's A buffer
+        uint32_t ldsb;            // ... and of its B buffer
         uint32_t ext;             // 1 for an extension stage
     };
     auto stage_src = [=](int it) __attribute__((always_inline)) {
@@ -472,7 +480,14 @@ void gated_gemm_kernel(const GemmKArgs a) {
         ss.brange = __builtin_amdgcn_readfirstlane(live ? (e ? b_range : w_range) : 0u);
         ss.kbytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kfirst * 2));
         ss.krem = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(klim > kfirst ? klim - kfirst : 0));
-        ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * C::STAGE_ELEMS * 2));
+        if constexpr (C::SPLIT) {
+            ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * BM * kBK * 2));
+            ss.ldsb = __builtin_amdgcn_readfirstlane(
+                lds_base + static_cast<uint32_t>((kNBUF * BM + (it % C::NBUF_B) * BN) * kBK * 2));
+        } else {
+            ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * C::STAGE_ELEMS * 2));
+            ss.ldsb = ss.lds + static_cast<uint32_t>(BM * kBK * 2);
+        }
         return ss;
     };
     auto dma_item = [&](const StageSrc ss, int q) __attribute__((always_inline)) {
@@ -484,7 +499,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
             dma16(la, off, make_rsrc(reinterpret_cast<const void*>(ss.abase), ss.arange));
         } else {
             const int qb = q - AQ;
-            const uint32_t lb = ss.lds + static_cast<uint32_t>((BM * kBK + (wave * (BN / C::NWAVES) + qb * RB) * kBK) * 2);
+            const uint32_t lb = ss.ldsb + static_cast<uint32_t>(((wave * (BN / C::NWAVES) + qb * RB) * kBK) * 2);
             const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * RB) * ldw2;
             const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * RB) * ldb2;
             uint32_t off = (ss.ext ? off_b : off_w) + kc_par[qb & 1] + ss.kbytes;
@@ -513,11 +528,21 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // has landed.  The last sub-step's MFMAs run after that barrier, while
     // the first fragments of stage s + 1 are read.
     constexpr int KSUB = C::KSUB;
-    constexpr int AHEAD = kNBUF - 1;
+    constexpr int AHEAD = kNBUF - 1;          // A stages copied ahead of the one computed
+    constexpr int AHEAD_B = C::NBUF_B - 1;    // B stages (the same unless the ring is split)
+    // vmcnt that leaves only later stages' copies in flight once stage it+1 has landed
+    constexpr int kLandedWait = C::SPLIT ? (C::NBUF_B - 2) * BQ : (kNBUF - 2) * NITEM;
     bf16x8 af[2][MI], bfr[2][NJ];
-    auto read_frags = [&](int buf, int kk, int set) __attribute__((always_inline)) {
-        const uint16_t* sa = smem + buf * C::STAGE_ELEMS;
-        const uint16_t* sb = sa + BM * kBK;
+    auto read_frags = [&](int st, int kk, int set) __attribute__((always_inline)) {
+        const uint16_t* sa;
+        const uint16_t* sb;
+        if constexpr (C::SPLIT) {
+            sa = smem + (st % kNBUF) * BM * kBK;
+            sb = smem + (kNBUF * BM + (st % C::NBUF_B) * BN) * kBK;
+        } else {
+            sa = smem + (st % kNBUF) * C::STAGE_ELEMS;
+            sb = sa + BM * kBK;
+        }
         const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -543,7 +568,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // arrays dynamically indexed and push them to scratch; the stage source
     // is passed by value for the same reason -- through a pointer it is kept
     // in memory)
-    auto mfma_group = [&](int set, bool has_ss, const StageSrc ss, int q0, int q1) __attribute__((always_inline)) {
+    auto mfma_group = [&](int set, bool has_ss, const StageSrc ssa, const StageSrc ssb, int q0, int q1)
+                          __attribute__((always_inline)) {
         const int nq = has_ss ? q1 - q0 : 0;
         const int spacing = nq > 0 && GROUP / nq > 0 ? GROUP / nq : 1;
 #pragma unroll
@@ -555,60 +581,65 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 const int q = q0 + m / spacing - 1;
                 if (has_ss && m % spacing == 0 && q < q1) {
                     __builtin_amdgcn_sched_barrier(0);
-                    dma_item(ss, q);
+                    dma_item(q < AQ ? ssa : ssb, q);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         if (has_ss) {
 #pragma unroll
-            for (int qq = q0 + GROUP / spacing; qq < q1; ++qq) dma_item(ss, qq);
+            for (int qq = q0 + GROUP / spacing; qq < q1; ++qq) dma_item(qq < AQ ? ssa : ssb, qq);
         }
     };
     // copy items per sub-step window (all sub-steps but the last carry items;
     // with two buffers the copies of stage s + 1 have only stage s to land in,
     // so they all go out in its first sub-step)
-    constexpr int WIN = kNBUF == 2 ? 1 : KSUB - 1;
+    // (a split ring: the A copies in the first sub-step, the B copies, which
+    // are not needed before the stage after next, in the second)
+    constexpr int WIN = C::SPLIT ? 2 : kNBUF == 2 ? 1 : KSUB - 1;
     constexpr int PER_WIN = (NITEM + WIN - 1) / WIN;
 
     // stage `it` (its first fragments already read), then open stage it+1
     auto body_next = [&](int it) __attribute__((always_inline)) {
-        const int buf = it % kNBUF;
         const StageSrc ahead = stage_src(it + AHEAD);
+        const StageSrc ahead_b = C::SPLIT ? stage_src(it + AHEAD_B) : ahead;
 #pragma unroll
         for (int kk = 0; kk < KSUB - 1; ++kk) {
-            read_frags(buf, kk + 1, (kk + 1) & 1);
+            read_frags(it, kk + 1, (kk + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_group(kk & 1, true, ahead, kk * PER_WIN, (kk + 1) * PER_WIN < NITEM ? (kk + 1) * PER_WIN : NITEM);
+            mfma_group(kk & 1, true, ahead, ahead_b, kk * PER_WIN,
+                       (kk + 1) * PER_WIN < NITEM ? (kk + 1) * PER_WIN : NITEM);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt<(kNBUF - 2) * NITEM>();  // this wavefront's copy of stage it+1 has landed
-        __syncthreads();                    // ... every wavefront's; and buffer `buf` is no longer read
-        read_frags((it + 1) % kNBUF, 0, 0);
+        wait_vmcnt<kLandedWait>();  // this wavefront's copy of stage it+1 has landed
+        __syncthreads();            // ... every wavefront's; and stage it's buffers are no longer read
+        read_frags(it + 1, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_group((KSUB - 1) & 1, false, StageSrc{}, 0, 0);
+        mfma_group((KSUB - 1) & 1, false, StageSrc{}, StageSrc{}, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto body_last = [&](int it) __attribute__((always_inline)) {
-        const int buf = it % kNBUF;
 #pragma unroll
         for (int kk = 0; kk < KSUB - 1; ++kk) {
-            read_frags(buf, kk + 1, (kk + 1) & 1);
+            read_frags(it, kk + 1, (kk + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_group(kk & 1, false, StageSrc{}, 0, 0);
+            mfma_group(kk & 1, false, StageSrc{}, StageSrc{}, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_group((KSUB - 1) & 1, false, StageSrc{}, 0, 0);
+        mfma_group((KSUB - 1) & 1, false, StageSrc{}, StageSrc{}, 0, 0);
     };
 
     if (!PP && nk_s > 0) {
-        // stages 0 .. NBUF-2 (stages past the last copy zeros into free buffers)
+        // A stages 0 .. AHEAD-1 and B stages 0 .. AHEAD_B-1, A before B within
+        // a stage (stages past the last copy zeros into free buffers)
+        constexpr int kPrologue = AHEAD > AHEAD_B ? AHEAD : AHEAD_B;
 #pragma unroll
-        for (int st = 0; st < AHEAD; ++st) {
+        for (int st = 0; st < kPrologue; ++st) {
             const StageSrc ss = stage_src(st);
 #pragma unroll
-            for (int q = 0; q < NITEM; ++q) dma_item(ss, q);
+            for (int q = 0; q < NITEM; ++q)
+                if ((q < AQ && st < AHEAD) || (q >= AQ && st < AHEAD_B)) dma_item(ss, q);
         }
-        wait_vmcnt<(kNBUF - 2) * NITEM>();  // stage 0 landed
+        wait_vmcnt<kLandedWait>();  // stage 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
         for (int it = 0; it < nk_s - 1; ++it) body_next(it);
@@ -660,8 +691,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
         for (int p = 0; p < nph; ++p) {
             if ((p & 1) == team) {
                 __builtin_amdgcn_sched_barrier(0);
-                mfma_group(0, false, StageSrc{}, 0, 0);
-                mfma_group(1, false, StageSrc{}, 0, 0);
+                mfma_group(0, false, StageSrc{}, StageSrc{}, 0, 0);
+                mfma_group(1, false, StageSrc{}, StageSrc{}, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             } else {
                 // the stage this team computes next (past the last stage the
@@ -853,14 +884,19 @@ struct Tile {
     bool pp;    // 8 wavefronts in two ping-pong teams (256 x 256 only, 32-deep stages)
     int kb;     // K per stage: 64 (two LDS buffers by default) or 32 (four)
     int nb = 0; // LDS stage buffers when not the default 128 / kb
+    int nbb = 0; // > 0: a split ring, two A buffers and nbb B buffers
 };
 
 int stage_buffers(Tile t) { return t.nb > 0 ? t.nb : 128 / t.kb; }
+int lds_bytes(Tile t) {
+    if (t.nbb > 0) return (2 * t.bm + t.nbb * t.bn) * t.kb * 2;
+    return stage_buffers(t) * t.kb * (t.bm + t.bn) * 2;
+}
 
 constexpr int kNumCUs = 256;
 
 // Workgroups that run at once per CU for a tile shape (LDS-limited).
-int occupancy(Tile t) { return (stage_buffers(t) * t.kb * (t.bm + t.bn) * 2 > 80 * 1024) ? 1 : 2; }
+int occupancy(Tile t) { return lds_bytes(t) > 80 * 1024 ? 1 : 2; }
 
 // Launch-time model used to rank (tile, split) plans: a workgroup costs a
 // fixed time (launch share, prologue, epilogue) plus its MFMA work at a
@@ -874,6 +910,7 @@ struct TileModel {
 };
 TileModel tile_model(Tile t) {
     if (t.bm == 256 && t.bn == 256 && t.pp) return {4.2e12, 10.0};
+    if (t.bm == 256 && t.bn == 256 && t.nbb > 0) return t.waves == 8 ? TileModel{5.05e12, 9.0} : TileModel{4.2e12, 15.0};
     if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.8e12, 9.0} : TileModel{4.3e12, 15.0};
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
     if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {4.1e12, 8.0};  // one per CU
@@ -881,8 +918,11 @@ TileModel tile_model(Tile t) {
     return {0.9e12, 8.0};
 }
 
-// Stage depth measured best per tile: 32 for the large tiles (four buffers,
-// three stages in flight), 64 for the 128-row ones.
+// Stage depth of a forced tile without a "k" suffix: 32 for the large tiles
+// (four buffers, three stages in flight), 64 for the 128-row ones.  (The
+// planner's 256 x 256 tile is the split ring with 64-deep stages: 128-byte
+// row segments move at twice the rate of 64-byte ones, and three B buffers
+// keep the weight stream two stages ahead.)
 int default_kb(int bm, int bn) { return bm * bn >= 256 * 128 ? 32 : 64; }
 
 // UNO_GEMM_TILE forces a tile (tests and tuning): "BMxBN" with optional
@@ -904,10 +944,16 @@ Tile env_tile() {
     if (const char* b = strchr(s, 'b')) {
         if (b[1] >= '2' && b[1] <= '8') t.nb = b[1] - '0';
     }
+    if (const char* b = strchr(s, 'r')) {
+        if (b[1] >= '2' && b[1] <= '8') t.nbb = b[1] - '0';
+    }
     return t;
 }
 
 bool tile_supported(Tile t) {
+    if (t.nbb > 0)  // split ring: 256 x 256, 64-deep stages, two A and three B buffers
+        return t.bm == 256 && t.bn == 256 && t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 &&
+               (t.waves == 8 || t.waves == 4);
     if (t.nb > 0 && t.nb != 128 / t.kb)  // extra stage buffers: the one-workgroup-per-CU 128 x 128 tile
         return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && (t.nb == 3 || t.nb == 4);
     if (t.pp) return t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 32;
@@ -970,7 +1016,7 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256)) return forced;
-    const Tile cands[] = {{256, 256, 8, false, 32}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
+    const Tile cands[] = {{256, 256, 8, false, 64, 0, 3}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
                           {128, 128, 4, false, 64, 4}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
     Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
@@ -1036,10 +1082,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     return p;
 }
 
-template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false, int NB = 0>
+template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false, int NB = 0, int NBB = 0>
 void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP, NB>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(TileCfg<BM, BN, WGM, WGN, KB, NB>::THREADS), 0, stream, ka);
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP, NB, NBB>),
+                       dim3(static_cast<uint32_t>(blocks)), dim3(TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::THREADS), 0,
+                       stream, ka);
 }
 
 template <bool TMODE>
@@ -1057,6 +1104,8 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
+        else if (t.nbb == 3 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 64, false, 0, 3>(ka, blocks, stream);
+        else if (t.nbb == 3) launch_tile<256, 256, 2, 2, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 64)
             launch_tile<256, 256, 2, 4, false, 64>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 32>(ka, blocks, stream);
