@@ -161,8 +161,9 @@ uno_status uno_gated_gemm(const void* x, const void* w, const void* t, const voi
  * whose columns [g*r, (g+1)*r) belong to group g; y is a host array of
  * n_groups device pointers, y[g] a row-major [M, group_n[g]] output.  The
  * result is that of uno_gated_gemm on each group alone up to the order of the
- * fp32 sums (the launch plan, which may split K, depends on the total width);
- * with the same plan it is bitwise the same.
+ * fp32 sums (the launch plan depends on the total width: it may split K, or
+ * use a tile whose two wavefront groups sum alternate K steps apart); with
+ * the same plan it is bitwise the same.
  * Domain: as uno_gated_gemm, with 1 <= n_groups <= 4 and every group but
  * the last a multiple of 128 columns (UNO_ERR_UNSUPPORTED otherwise).
  * group_n and y are read before the call returns. */

@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <type_traits>
 
 #include "uno_device.h"
@@ -286,17 +287,24 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // NBB > 0 splits the ring: A (x) stages then have NBUF buffers of their own
 // and B (weight) stages NBB, so that the weights, which come from HBM, can be
 // fetched further ahead than the activations, which the L2 holds.
-template <int BM, int BN, int WGM, int WGN, int KB, int NB = 0, int NBB = 0>
+// KG = 2 doubles the wavefronts of a tile: two groups of WGM x WGN
+// wavefronts take alternate MFMA sub-steps of every stage (each group its own
+// half of K) and add up at the end, so that each SIMD holds two wavefronts of
+// the tile and one can compute while the other waits on LDS or copies.
+template <int BM, int BN, int WGM, int WGN, int KB, int NB = 0, int NBB = 0, int KG = 1>
 struct TileCfg {
     static_assert(KB == 64 || KB == 32, "stage depth");
     static constexpr int NBUF = NB > 0 ? NB : 128 / KB;
     static constexpr bool SPLIT = NBB > 0;
     static constexpr int NBUF_B = SPLIT ? NBB : NBUF;
     static_assert(NBUF >= 2 && NBUF <= 8 && NBUF_B >= 2 && NBUF_B <= 8, "stage buffers");
-    static_assert(!SPLIT || NBUF == 2, "a split ring keeps two A buffers");
+    static_assert(!SPLIT || (NBUF == 2 && NBUF_B == 3), "a split ring keeps two A and three B buffers");
     static constexpr int KSUB = KB / 16;       // MFMA sub-steps per stage
+    static_assert(KG == 1 || (KG == 2 && !SPLIT), "K groups: 1, or 2 without a split ring");
+    static constexpr int KSUB_W = KSUB / KG;   // ... per wavefront
     static constexpr int RB = 512 / KB;        // rows per copy instruction
-    static constexpr int NWAVES = WGM * WGN;   // WGM x WGN wavefronts
+    static constexpr int NWAVES_T = WGM * WGN;  // WGM x WGN wavefronts per K group
+    static constexpr int NWAVES = NWAVES_T * KG;
     static constexpr int THREADS = NWAVES * kWave;
     static constexpr int WM = BM / WGM;
     static constexpr int WN = BN / WGN;
@@ -314,17 +322,21 @@ struct TileCfg {
     // The output-row table (BM int32) goes behind the epilogue's staging area
     // in the stage buffers when they have room for it, else into LDS of its own.
     static constexpr bool OROW_IN_STAGE = LDS_ELEMS * 2 >= BM * BN * 2 + BM * 4;
+    // K groups hand accumulators over behind the staging area and the row table
+    static constexpr int XCH_BYTE = (BM * BN * 2 + BM * 4 + 1023) / 1024 * 1024;
+    static_assert(KG == 1 || (OROW_IN_STAGE && XCH_BYTE + NWAVES_T * BM / WGM * BN / WGN * 4 <= LDS_ELEMS * 2),
+                  "K-group exchange must fit in the stage buffers");
     static_assert(LDS_ELEMS * 2 + (OROW_IN_STAGE ? 0 : BM * 4) <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one output row per thread");
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
 
-template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB, int NBB = 0>
-__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::THREADS),
-                             (TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::OCC))
+template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB, int NBB = 0, int KG = 1>
+__global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::THREADS),
+                             (TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::OCC))
 void gated_gemm_kernel(const GemmKArgs a) {
-    using C = TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>;
-    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4 && !C::SPLIT),
+    using C = TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>;
+    static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4 && !C::SPLIT && KG == 1),
                   "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32, four buffers");
     constexpr int kBK = KB;
     constexpr int kNBUF = C::NBUF;
@@ -375,8 +387,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
     if (!C::OROW_IN_STAGE && tid < BM) s_orow[tid] = my_orow;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
     const int lane = tid % kWave;
-    const int wm = wave / WGN;
-    const int wn = wave % WGN;
+    const int kg = wave / C::NWAVES_T;  // K group (scalar)
+    const int wt = wave % C::NWAVES_T;  // wavefront within its group
+    const int wm = wt / WGN;
+    const int wn = wt % WGN;
 
     // Copy lane mapping: lane l takes row lrow of an RB-row block and the
     // logical chunk stored at physical chunk position pc of that row, so the
@@ -527,11 +541,15 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // NBUF - 2 stages of its copies are outstanding, i.e. until stage s + 1
     // has landed.  The last sub-step's MFMAs run after that barrier, while
     // the first fragments of stage s + 1 are read.
-    constexpr int KSUB = C::KSUB;
+    constexpr int KSUB = C::KSUB_W;  // sub-steps this wavefront computes per stage
     constexpr int AHEAD = kNBUF - 1;          // A stages copied ahead of the one computed
     constexpr int AHEAD_B = C::NBUF_B - 1;    // B stages (the same unless the ring is split)
-    // vmcnt that leaves only later stages' copies in flight once stage it+1 has landed
-    constexpr int kLandedWait = C::SPLIT ? (C::NBUF_B - 2) * BQ : (kNBUF - 2) * NITEM;
+    // vmcnt that leaves only later stages' copies in flight once stage it+1
+    // has landed.  Copies complete in issue order, and with a split ring the
+    // last copies issued before the wait are A(it+1) then B(it+NBUF_B-1):
+    // only those BQ may remain, so B runs at most two stages ahead whatever
+    // NBUF_B is (three B buffers are all a split ring can use).
+    constexpr int kLandedWait = C::SPLIT ? BQ : (kNBUF - 2) * NITEM;
     bf16x8 af[2][MI], bfr[2][NJ];
     auto read_frags = [&](int st, int kk, int set) __attribute__((always_inline)) {
         const uint16_t* sa;
@@ -543,7 +561,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
             sa = smem + (st % kNBUF) * C::STAGE_ELEMS;
             sb = sa + BM * kBK;
         }
-        const int chunk = kk * 2 + (lane >> 5);
+        const int chunk = (kk * KG + kg) * 2 + (lane >> 5);  // K group kg takes sub-steps kg, kg + KG, ...
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
             const int row = wm * C::WM + i * 32 + (lane & 31);
@@ -708,6 +726,35 @@ void gated_gemm_kernel(const GemmKArgs a) {
     }
 
     // ---- epilogue
+    if constexpr (KG == 2) {
+        // group 1 hands its sums to group 0 (even sub-steps + odd sub-steps)
+        __syncthreads();  // every wavefront is done with the stage buffers
+        f32x4* xch = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(smem) + C::XCH_BYTE) + wt * (MI * NJ * 4 * kWave);
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        f32x4 t;
+                        for (int e = 0; e < 4; ++e) t[e] = acc[i][j][v4 * 4 + e];
+                        xch[((i * NJ + j) * 4 + v4) * kWave + lane] = t;
+                    }
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        const f32x4 t = xch[((i * NJ + j) * 4 + v4) * kWave + lane];
+                        for (int e = 0; e < 4; ++e) acc[i][j][v4 * 4 + e] += t[e];
+                    }
+        }
+    }
     if constexpr (C::OROW_IN_STAGE) {
         __syncthreads();  // every wavefront is done with the stage buffers
         if (tid < BM) s_orow[tid] = my_orow;
@@ -723,9 +770,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
         // Stage the wavefront's bf16 tile through LDS, then write whole 16-byte
         // row segments (coalesced), scattering rows through the permutation.
         __syncthreads();  // all stage buffers are free
+        if (kg != 0) return;  // (K group 1's sums are in group 0's accumulators)
         // staging layout: [WM rows][WN cols] bf16; rows r and r+4 (written by one
         // instruction) are offset by 32 columns (XOR) to land in different banks
-        uint16_t* st = smem + wave * C::WM * C::WN;
+        uint16_t* st = smem + wt * C::WM * C::WN;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -748,7 +796,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 // share the output rows of the pair, each taking half of them.
                 __syncthreads();
                 const int pw = wn % (WGN / 2), half = wn / (WGN / 2);
-                const uint16_t* sg = smem + (wm * WGN + pw) * C::WM * C::WN;
+                const uint16_t* sg = smem + (wm * WGN + pw) * C::WM * C::WN;  // (K groups: KG == 1 here)
                 const uint16_t* su = smem + (wm * WGN + pw + WGN / 2) * C::WM * C::WN;
                 const int64_t ng = n0 + pw * C::WN + c * 8;          // gate column
                 const int64_t na = (n0 >> 1) + pw * C::WN + c * 8;   // act column
@@ -776,6 +824,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
         }
         return;
     }
+    if (kg != 0) return;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -885,6 +934,7 @@ struct Tile {
     int kb;     // K per stage: 64 (two LDS buffers by default) or 32 (four)
     int nb = 0; // LDS stage buffers when not the default 128 / kb
     int nbb = 0; // > 0: a split ring, two A buffers and nbb B buffers
+    int kg = 1;  // K groups of wavefronts (2: twice the wavefronts, alternate sub-steps)
 };
 
 int stage_buffers(Tile t) { return t.nb > 0 ? t.nb : 128 / t.kb; }
@@ -913,7 +963,7 @@ TileModel tile_model(Tile t) {
     if (t.bm == 256 && t.bn == 256 && t.nbb > 0) return t.waves == 8 ? TileModel{5.05e12, 9.0} : TileModel{4.2e12, 15.0};
     if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.8e12, 9.0} : TileModel{4.3e12, 15.0};
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
-    if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {4.1e12, 8.0};  // one per CU
+    if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {t.kg == 2 ? 4.3e12 : 4.1e12, 8.0};  // one per CU
     if (t.bm == 128) return {2.2e12, 8.0};
     return {0.9e12, 8.0};
 }
@@ -927,7 +977,7 @@ int default_kb(int bm, int bn) { return bm * bn >= 256 * 128 ? 32 : 64; }
 
 // UNO_GEMM_TILE forces a tile (tests and tuning): "BMxBN" with optional
 // suffixes "w8" (eight wavefronts), "pp" (ping-pong), "k32" / "k64" (stage
-// depth), "bN" (N LDS stage buffers).
+// depth), "bN" (N LDS stage buffers), "r3" (split ring), "kg2" (two K groups).
 Tile env_tile() {
     const char* s = getenv("UNO_GEMM_TILE");
     Tile t{0, 0, 4, false, 64};
@@ -947,15 +997,19 @@ Tile env_tile() {
     if (const char* b = strchr(s, 'r')) {
         if (b[1] >= '2' && b[1] <= '8') t.nbb = b[1] - '0';
     }
+    if (strstr(s, "kg2")) t.kg = 2;
     return t;
 }
 
 bool tile_supported(Tile t) {
-    if (t.nbb > 0)  // split ring: 256 x 256, 64-deep stages, two A and three B buffers
-        return t.bm == 256 && t.bn == 256 && t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 &&
+    if (t.kg == 2)  // two K groups: the 128 x 128 tile with four stage buffers
+        return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.nb == 4;
+    if (t.kg != 1) return false;
+    if (t.nbb > 0)  // split ring (two A and three B buffers): the 256 x 256 tile
+        return t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 && t.bm == 256 && t.bn == 256 &&
                (t.waves == 8 || t.waves == 4);
     if (t.nb > 0 && t.nb != 128 / t.kb)  // extra stage buffers: the one-workgroup-per-CU 128 x 128 tile
-        return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && (t.nb == 3 || t.nb == 4);
+        return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nb >= 3 && t.nb <= 5;
     if (t.pp) return t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 32;
     if (t.waves == 8) return t.bm == 256 && t.bn == 256 && (t.kb == 32 || t.kb == 64);
     if (t.bm == 256 && t.bn == 256 && t.waves == 4 && t.kb == 64) return true;
@@ -1016,8 +1070,14 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256)) return forced;
+    if (forced.bm > 0 && !tile_supported(forced)) {
+        static bool warned = false;  // (tuning aid: say once that the forced tile is not one of ours)
+        if (!warned) fprintf(stderr, "libuno: UNO_GEMM_TILE=%s is not a supported tile; planning instead\n",
+                             getenv("UNO_GEMM_TILE"));
+        warned = true;
+    }
     const Tile cands[] = {{256, 256, 8, false, 64, 0, 3}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
-                          {128, 128, 4, false, 64, 4}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
+                          {128, 128, 4, false, 64, 4, 0, 2}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
     Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
@@ -1082,11 +1142,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     return p;
 }
 
-template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false, int NB = 0, int NBB = 0>
+template <int BM, int BN, int WGM, int WGN, bool TMODE, int KB = 64, bool PP = false, int NB = 0, int NBB = 0,
+          int KG = 1>
 void launch_tile(const GemmKArgs& ka, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP, NB, NBB>),
-                       dim3(static_cast<uint32_t>(blocks)), dim3(TileCfg<BM, BN, WGM, WGN, KB, NB, NBB>::THREADS), 0,
-                       stream, ka);
+    hipLaunchKernelGGL((gated_gemm_kernel<BM, BN, WGM, WGN, KB, TMODE, PP, NB, NBB, KG>),
+                       dim3(static_cast<uint32_t>(blocks)),
+                       dim3(TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::THREADS), 0, stream, ka);
 }
 
 template <bool TMODE>
@@ -1113,6 +1174,10 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false, 32>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128 && t.kg == 2 && stage_buffers(t) == 4)
+            launch_tile<128, 128, 2, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 128 && stage_buffers(t) == 5)
+            launch_tile<128, 128, 2, 2, false, 64, false, 5>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 128 && stage_buffers(t) == 4)
             launch_tile<128, 128, 2, 2, false, 64, false, 4>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 128 && stage_buffers(t) == 3)

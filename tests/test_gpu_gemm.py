@@ -122,7 +122,8 @@ def test_deterministic_repeat():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x256", "256x128", "256x256",
+@pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x128b5", "128x128b4kg2", "128x256",
+                                  "256x128", "256x256",
                                   "256x256k64", "256x256k64r3", "256x256w8", "256x256w8k64", "256x256w8k64r3",
                                   "256x256pp"])
 def test_every_tile_shape_ragged(tile, monkeypatch):
@@ -168,6 +169,7 @@ EPILOGUE = [  # M, K, N (per projection), forced tile or None, forced split or N
     (300, 1000, 512, "256x256w8", "2"),  # ragged M and K, split-K: the reduction applies the epilogue
     (32, 256, 256, None, None),          # few rows: the 128 x 256 tile (SwiGLU) / 64 x 128 (residual)
     (96, 512, 768, "128x256", None),
+    (300, 1000, 512, "256x256w8k64r3", None),  # split ring, ragged
 ]
 
 
@@ -199,9 +201,9 @@ def test_residual_epilogue_is_separate_add(M, K, N, tile, split, monkeypatch):
 def test_swiglu_epilogue_is_separate_silu_mul(M, K, N, tile, split, monkeypatch):
     """uno_gated_gemm_swiglu on packed weights == silu_mul of the gate and up projections, bit for
     bit (same tile family and split), and within the bf16 bound of the fp64 oracle."""
-    if tile:
-        monkeypatch.setenv("UNO_GEMM_TILE", tile)
-    # the same K split on both sides (the two plans may otherwise split differently)
+    # the same tile family and K split on both sides (the two plans may
+    # otherwise differ, and K-group tiles sum alternate sub-steps apart)
+    monkeypatch.setenv("UNO_GEMM_TILE", tile or "256x256w8k64r3")
     monkeypatch.setenv("UNO_GEMM_SPLIT", split or "1")
     rng = np.random.default_rng(M + 3 * N)
     gate = (rng.random(M) < 0.5).astype(np.uint8)
