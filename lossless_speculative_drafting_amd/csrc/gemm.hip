@@ -313,8 +313,8 @@ struct TileCfg {
     static constexpr int AQ = BM / (RB * NWAVES);  // copy instructions per wavefront per stage (A)
     static constexpr int BQ = BN / (RB * NWAVES);  // (B)
     static_assert(AQ >= 1 && BQ >= 1 && AQ * RB * NWAVES == BM && BQ * RB * NWAVES == BN, "copy split");
-    static_assert(KB == 32 || ((BM / NWAVES) % (2 * RB) == 0 && (BN / NWAVES) % (2 * RB) == 0),
-                  "with KB 64 each wavefront's copy blocks start on an even block (the swizzle parity is q & 1)");
+    static_assert((BM / NWAVES) % RB == 0 && (BN / NWAVES) % RB == 0,
+                  "each wavefront's copies start on a block (the KB 64 swizzle parity is the block's)");
     static_assert(MI >= 1 && NJ >= 1 && WN >= 64, "wavefront tile");
     static constexpr int STAGE_ELEMS = (BM + BN) * KB;
     static constexpr int LDS_ELEMS = SPLIT ? NBUF * BM * KB + NBUF_B * BN * KB : NBUF * STAGE_ELEMS;
@@ -407,7 +407,14 @@ void gated_gemm_kernel(const GemmKArgs a) {
     } else {
         kc_par[0] = kc_par[1] = static_cast<uint32_t>((pc ^ (lrow >> 2)) * 16);
     }
-    const uint32_t kcol_par[2] = {kc_par[0] >> 1, kc_par[1] >> 1};  // K index within the stage
+    // (a wavefront that copies fewer than 2 RB rows -- K groups -- may start on
+    // an odd block: its items' parities are flipped)
+    const bool parA = (((wave * (BM / C::NWAVES)) / RB) & 1) != 0;
+    const bool parB = (((wave * (BN / C::NWAVES)) / RB) & 1) != 0;
+    const uint32_t kcA[2] = {parA ? kc_par[1] : kc_par[0], parA ? kc_par[0] : kc_par[1]};
+    const uint32_t kcB[2] = {parB ? kc_par[1] : kc_par[0], parB ? kc_par[0] : kc_par[1]};
+    const uint32_t kcolA[2] = {kcA[0] >> 1, kcA[1] >> 1};  // K index within the stage
+    const uint32_t kcolB[2] = {kcB[0] >> 1, kcB[1] >> 1};
     uint32_t xoff[AQ];  // x row offsets (gathered through the plan) + chunk offset
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
@@ -418,7 +425,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
         } else {
             src = (p < rows_valid) ? a.perm[p] : -1;
         }
-        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kc_par[q & 1];
+        xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kcA[q & 1];
     }
     const uint32_t ldw2 = static_cast<uint32_t>(a.ldw * 2);
     const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldw2;
@@ -507,17 +514,17 @@ void gated_gemm_kernel(const GemmKArgs a) {
     auto dma_item = [&](const StageSrc ss, int q) __attribute__((always_inline)) {
         if (q < AQ) {
             const uint32_t la = ss.lds + static_cast<uint32_t>((wave * (BM / C::NWAVES) + q * RB) * kBK * 2);
-            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * RB) * ldt2 + kc_par[q & 1];
+            const uint32_t ext_off = trow0 + static_cast<uint32_t>(q * RB) * ldt2 + kcA[q & 1];
             uint32_t off = (ss.ext ? ext_off : xoff[q]) + ss.kbytes;
-            if (kcol_par[q & 1] >= ss.krem) off = kOOB;
+            if (kcolA[q & 1] >= ss.krem) off = kOOB;
             dma16(la, off, make_rsrc(reinterpret_cast<const void*>(ss.abase), ss.arange));
         } else {
             const int qb = q - AQ;
             const uint32_t lb = ss.ldsb + static_cast<uint32_t>(((wave * (BN / C::NWAVES) + qb * RB) * kBK) * 2);
             const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * RB) * ldw2;
             const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * RB) * ldb2;
-            uint32_t off = (ss.ext ? off_b : off_w) + kc_par[qb & 1] + ss.kbytes;
-            if (kcol_par[qb & 1] >= ss.krem) off = kOOB;
+            uint32_t off = (ss.ext ? off_b : off_w) + kcB[qb & 1] + ss.kbytes;
+            if (kcolB[qb & 1] >= ss.krem) off = kOOB;
             dma16(lb, off, make_rsrc(reinterpret_cast<const void*>(ss.bbase), ss.brange));
         }
     };
@@ -1112,9 +1119,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     // (four stage buffers: the prologue puts three stages in flight at once,
     // measured 3-10% faster than two)
     p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs, bn256);
-    if (const char* e = tmode ? getenv("UNO_T_TILE") : nullptr) {  // tuning: "128" (two buffers) or "64b2"
+    if (const char* e = tmode ? getenv("UNO_T_TILE") : nullptr) {  // tuning: "128" (two buffers), "64b2", "64kg2"
         if (atoi(e) == 128) p.tile = Tile{128, 128, 4, false, 64};
         if (strstr(e, "b2")) p.tile.nb = 2;
+        if (strstr(e, "kg2")) p.tile.kg = 2;
     }
     if (!tmode && p.rows_cap <= 64) p.tile = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
@@ -1161,6 +1169,7 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
     const Tile t = p.tile;
     if constexpr (TMODE) {
         if (t.bm == 128) launch_tile<128, 128, 2, 2, true>(ka, blocks, stream);
+        else if (stage_buffers(t) == 4 && t.kg == 2) launch_tile<64, 128, 2, 2, true, 64, false, 4, 0, 2>(ka, blocks, stream);
         else if (stage_buffers(t) == 4) launch_tile<64, 128, 2, 2, true, 64, false, 4>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {

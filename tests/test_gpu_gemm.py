@@ -147,10 +147,12 @@ def test_every_tile_shape_ragged(tile, monkeypatch):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("t_tile", ["64b2", "128"])
+@pytest.mark.parametrize("t_tile", ["64b2", "128", "64kg2"])
 def test_lora_down_tiles_agree(t_tile, monkeypatch):
-    """The LoRA down-projection gives the same T bits with every tile and buffer count
-    (each output sums the same K slices in the same order)."""
+    """The LoRA down-projection gives the same T bits with every one-group tile and
+    buffer count (each output sums the same K slices in the same order).  Two K
+    groups sum the even and the odd K sub-steps apart and add the two sums, so
+    there T agrees to bf16 rounding instead."""
     M, K, r = 300, 2048, 128  # K = 2048: four K splits for every tile
     rng = np.random.default_rng(12)
     gate = (rng.random(M) < 0.5).astype(np.uint8)
@@ -161,7 +163,11 @@ def test_lora_down_tiles_agree(t_tile, monkeypatch):
     t_default = uno.lora_down(x, a, plan, 2.0).clone()
     monkeypatch.setenv("UNO_T_TILE", t_tile)
     t_forced = uno.lora_down(x, a, plan, 2.0)
-    assert torch.equal(t_default, t_forced)
+    if "kg2" in t_tile:
+        err = floored_rel_err(to_host(t_forced).astype(np.float64), to_host(t_default).astype(np.float64))
+        assert err <= BF16_TOL, err
+    else:
+        assert torch.equal(t_default, t_forced)
 
 
 EPILOGUE = [  # M, K, N (per projection), forced tile or None, forced split or None
