@@ -307,6 +307,48 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The LM head fused with the statistics of block verification.  The
+ * verifier ("The Psi-Spec Sampler" on the aifromscratch.in page) needs, per
+ * position, the softmax normalisers of the target and draft rows and their
+ * logits at the drafted token; only the redraw needs whole rows, and only
+ * one pair per sequence.  Here the LM-head GEMM (bf16 MFMA, fp32
+ * accumulation) forms those statistics in its epilogue, tile by tile, so the
+ * logits need never reach memory:
+ *
+ *   z = bf16(hidden_target W^T),  d = bf16(hidden_draft W^T)
+ *   then exactly what uno_block_verify computes on (z, d).
+ *
+ * hidden       : device bf16 [B (L + has_bonus) + B L, K], row-major: target
+ *                row (s, i) at row s (L + has_bonus) + i, then draft row (s, i)
+ *                at row B (L + has_bonus) + s L + i
+ * w_lm         : device bf16 [V, K] (the head's weight, nn.Linear layout)
+ * draft_tokens, uniforms, n_accepted, out_tokens, n_emitted, temperature,
+ * has_bonus    : as in uno_block_verify
+ * logits       : device bf16 [B (L + has_bonus) + B L, V] receiving z then d
+ *                (the same row order as hidden), or NULL.  With NULL no logit
+ *                row is written; the target and draft rows of each
+ *                sequence's redraw are recomputed after the decision (one
+ *                more pass over W for 2 B rows, the same bits).  Storing pays
+ *                while 2 rows V bytes of logits cost less than reading W once.
+ * Statistics are formed per 256-column tile of the head (the chunking
+ * uno_block_verify uses with 256-token chunks) and merged per row in fp64 in
+ * a fixed order; every output is bitwise that of uno_block_verify run on
+ * these logits with that chunking.
+ *
+ * Domain: B >= 0 (B = 0 is a no-op), 1 <= L <= 64 (L <= 63 with has_bonus),
+ * V >= 1, K % 8 == 0, V K < 2^30, rows K < 2^30, T > 0 and finite; hidden,
+ * w_lm, logits 16-byte aligned.  Every logit row must hold a finite value.
+ * workspace: at least uno_lm_head_verify_workspace_size() bytes (about
+ * 24 (B (L+1)) ceil(V / 256) + 4 B V bytes).
+ * ------------------------------------------------------------------------ */
+size_t uno_lm_head_verify_workspace_size(int64_t B, int32_t L, int64_t V, int64_t K, int32_t has_bonus);
+uno_status uno_lm_head_verify(const void* hidden, const void* w_lm, int64_t B, int32_t L, int64_t V, int64_t K,
+                              int32_t has_bonus, float temperature, const int32_t* draft_tokens,
+                              const float* uniforms, int32_t* n_accepted, int32_t* out_tokens,
+                              int32_t* n_emitted, void* logits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Glue between projections of a layer with the attention mixing left out
  * (the pages add the LoRA pathway to each transformer layer -- "How It Works:
  * The 'Uno' Architecture" on the aifromscratch.in page -- but describe no

@@ -5,6 +5,9 @@ Python binding over libuno.so (hand-written HIP for gfx950):
 * gated_lora_fwd  -- y = x W_AR + g * (alpha/r) * (x A) B on a mixed batch of
                      draft (g = 1) and verify (g = 0) rows;
 * block_verify    -- lossless speculative verification of drafted blocks;
+* lm_head_verify  -- the LM head with the verification statistics in its
+                     epilogue, then the same verification (no logit rows
+                     written unless asked for);
 * draft_sample    -- parallel inverse-CDF proposal of draft tokens;
 * philox_uniforms -- the counter-based uniforms both consume;
 * rmsnorm, silu_mul, residual_add -- glue of the synthetic layer stack.
@@ -31,6 +34,8 @@ from ._lib import (  # noqa: F401
     gated_lora_workspace_size,
     header_symbols,
     library,
+    lm_head_verify,
+    lm_head_verify_workspace_size,
     lora_down,
     lora_t_size,
     philox_uniforms,

@@ -62,6 +62,9 @@ SIGNATURES = {
     "uno_draft_sample_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64]),
     "uno_draft_sample": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_int64, _c_int32, _c_int64, _c_float,
                                     _c_int32, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "uno_lm_head_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int64, _c_int32]),
+    "uno_lm_head_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int32, _c_int64, _c_int64, _c_int32, _c_float,
+                                      _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "uno_rmsnorm": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_float, _c_int32, _c_ptr]),
     "uno_silu_mul": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
     "uno_residual_add": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_ptr]),
@@ -341,6 +344,50 @@ def block_verify_workspace_size(B, L, V, has_bonus=False):
 
 def block_verify_early_workspace_size(B, L, V, has_bonus=False):
     return int(_lib.uno_block_verify_early_workspace_size(B, L, V, int(bool(has_bonus))))
+
+
+def lm_head_verify_workspace_size(B, L, V, K, has_bonus=False):
+    return int(_lib.uno_lm_head_verify_workspace_size(B, L, V, K, int(bool(has_bonus))))
+
+
+def lm_head_verify(hidden, w_lm, draft_tokens, uniforms, temperature=1.0, has_bonus=False, logits=None,
+                   outputs=None, workspace=None, stream=None):
+    """The LM head with the verification statistics in its epilogue, then block verification.
+
+    hidden: bf16 [B*(L+has_bonus) + B*L, K] (target rows of every sequence,
+    then draft rows); w_lm: bf16 [V, K]; draft_tokens int32 [B, L]; uniforms
+    float32 [B, L+1].  logits: None (no logit row is stored; the redraw rows
+    are recomputed) or a bf16 [rows, V] tensor that receives the logits.
+    Returns (n_accepted [B], out_tokens [B, L+1], n_emitted [B]) int32 tensors.
+    """
+    _need_cuda(hidden, w_lm, draft_tokens, uniforms)
+    if hidden.dtype != torch.bfloat16 or w_lm.dtype != torch.bfloat16:
+        raise TypeError("hidden and w_lm must be bfloat16")
+    if draft_tokens.dtype != torch.int32 or uniforms.dtype != torch.float32:
+        raise TypeError("draft_tokens must be int32 and uniforms float32")
+    B, L = draft_tokens.shape
+    V, K = w_lm.shape
+    nb = 1 if has_bonus else 0
+    rows = B * (L + nb) + B * L
+    if hidden.shape != (rows, K) or not hidden.is_contiguous() or not w_lm.is_contiguous():
+        raise ValueError(f"hidden must be contiguous [{rows}, {K}] and w_lm contiguous [V, K]")
+    if uniforms.numel() < B * (L + 1) or not draft_tokens.is_contiguous() or not uniforms.is_contiguous():
+        raise ValueError("uniforms must hold B*(L+1) values; tokens and uniforms contiguous")
+    if logits is not None and (logits.dtype != torch.bfloat16 or logits.shape != (rows, V)
+                               or not logits.is_contiguous()):
+        raise ValueError(f"logits must be a contiguous bf16 [{rows}, {V}] tensor")
+    dev = hidden.device
+    if outputs is None:
+        outputs = (torch.empty(B, dtype=torch.int32, device=dev),
+                   torch.empty((B, L + 1), dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev))
+    n_acc, out_tok, n_emit = outputs
+    need = int(_lib.uno_lm_head_verify_workspace_size(B, L, V, K, nb))
+    ws = _workspace(workspace, need, dev)
+    _check(_lib.uno_lm_head_verify(_ptr(hidden), _ptr(w_lm), int(B), int(L), int(V), int(K), nb, float(temperature),
+                                   _ptr(draft_tokens), _ptr(uniforms), _ptr(n_acc), _ptr(out_tok), _ptr(n_emit),
+                                   _ptr(logits), _ptr(ws), need, _stream(stream)))
+    return n_acc, out_tok, n_emit
 
 
 def block_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature=1.0, has_bonus=False,

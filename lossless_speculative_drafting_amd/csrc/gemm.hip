@@ -131,8 +131,15 @@ __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t
 // [128 i, 128 i + 128) and the next 128 the matching up columns; the output
 // is act[:, 128 i + c] = bf16(silu(bf16(g)) * bf16(u)), rounded as the
 // separate GEMM and silu_mul launches would.
-constexpr int32_t kEpiStore = 0, kEpiAccumulate = 1, kEpiSwiglu = 2;
+// Statistics (the LM head fused with verification): the bf16-rounded result
+// is optionally stored, and for each row and each tile of kStatCols columns
+// the softmax statistics (max, sum of exp((v - max) / T)) of those columns
+// are written as one chunk of the row's ChunkStat, with the logit of the
+// row's token gathered on the way.  They are the same bits that
+// verification's row statistics give for a chunk of kStatCols columns.
+constexpr int32_t kEpiStore = 0, kEpiAccumulate = 1, kEpiSwiglu = 2, kEpiStats = 3;
 constexpr int kSwigluBlock = 128;
+constexpr int kStatCols = 256;
 
 __device__ __forceinline__ uint4 add8_bf16(const uint4 a, const uint4 b) {
     float fa[8], fb[8];
@@ -211,7 +218,15 @@ struct GemmKArgs {
     int64_t k_per_split;
     int32_t m_tiles, n_tiles;
     float alpha;
-    int32_t epi;          // Epilogue (main mode): kEpiStore, kEpiAccumulate, kEpiSwiglu
+    int32_t epi;          // Epilogue (main mode): kEpiStore, kEpiAccumulate, kEpiSwiglu, kEpiStats
+    int32_t out_compact;  // 1: output row = plan position (rows still gathered through perm)
+    // kEpiStats only (out.y[0] may be null: nothing stored)
+    ChunkStat* stats;           // [stat rows][stat_ld]
+    int32_t stat_ld;            // chunks per stat row (the column tiles)
+    const int32_t* stat_map;    // per output row: (stat row << 1) | 1 for a draft row, or -1
+    const int32_t* row_token;   // per output row: token whose logit is gathered, or -1
+    float* gathered;            // per output row
+    float c2;                   // log2(e) / T
 };
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -306,6 +321,7 @@ struct TileCfg {
     static constexpr int NWAVES_T = WGM * WGN;  // WGM x WGN wavefronts per K group
     static constexpr int NWAVES = NWAVES_T * KG;
     static constexpr int THREADS = NWAVES * kWave;
+    static constexpr int BM_ = BM;
     static constexpr int WM = BM / WGM;
     static constexpr int WN = BN / WGN;
     static constexpr int MI = WM / 32;         // 32x32 MFMA blocks per wavefront
@@ -330,6 +346,57 @@ struct TileCfg {
     static_assert(THREADS >= BM, "one output row per thread");
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
+
+// Statistics epilogue over a staged BM x kStatCols tile (bf16, staged per
+// wavefront as [WM][WN] with the column XOR of the store path).  Row R is
+// handled by one half-wavefront: lane h takes columns [8h, 8h + 8), exactly
+// the values thread h of verification's row statistics takes for a chunk of
+// kStatCols columns (the other threads there hold nothing, so their merges
+// are the identity), then the half-wave tree merges the 32 lanes.
+template <class C, int WGN>
+__device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_t* smem, const int32_t* s_orow,
+                                               int32_t nt, int64_t n0, int wave, int lane) {
+    const int h = lane & 31;
+    const int hc = 8 * h;  // tile column of this lane's eight values
+    const int wn_c = hc / C::WN, cc = hc % C::WN;
+    const int64_t ncol = n0 + hc;
+    for (int R = wave * 2 + (lane >> 5); R < C::BM_; R += 2 * C::NWAVES) {
+        const int32_t orow = s_orow[R];
+        const int wm_r = R / C::WM, rl = R % C::WM;
+        const uint16_t* src = smem + (wm_r * WGN + wn_c) * C::WM * C::WN + rl * C::WN + (cc ^ (((rl >> 2) & 1) << 5));
+        float v[8];
+        unpack8(*reinterpret_cast<const uint4*>(src), v);
+        Online o{-INFINITY, 0.0};
+        if (ncol < a.N) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (ncol + j >= a.N) v[j] = -INFINITY;
+            online_add8(o, v, a.c2);
+        }
+        o = half_wave_merge(o, a.c2);
+        if (orow < 0) continue;
+        const int32_t sm = a.stat_map[orow];
+        if (h == 0 && sm >= 0) {
+            ChunkStat* st = a.stats + static_cast<int64_t>(sm >> 1) * a.stat_ld + nt;
+            if (sm & 1) {
+                st->sB = o.s;
+                st->mB = o.m;
+            } else {
+                st->sA = o.s;
+                st->mA = o.m;
+            }
+        }
+        const int32_t tok = a.row_token[orow];
+        const int64_t dt = static_cast<int64_t>(tok) - ncol;
+        if (tok >= 0 && tok < a.N && dt >= 0 && dt < 8) {
+            float g = v[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j)
+                if (dt == j) g = v[j];
+            a.gathered[orow] = g;
+        }
+    }
+}
 
 template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB, int NBB = 0, int KG = 1>
 __global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::THREADS),
@@ -382,6 +449,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
             my_orow = static_cast<int32_t>(m0 + tid);
         } else {
             my_orow = a.perm[m0 + tid];
+            if (a.out_compact && my_orow >= 0) my_orow = static_cast<int32_t>(m0 + tid);
         }
     }
     if (!C::OROW_IN_STAGE && tid < BM) s_orow[tid] = my_orow;
@@ -773,7 +841,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
     uint16_t* const gy = grp.y;
     const int64_t gldy = grp.ldy;
     const int64_t gstart = grp.start;
-    if (a.splits == 1 && (gend % 8) == 0 && (gstart % 8) == 0) {
+    const bool stats_epi = !TMODE && BN == kStatCols && a.epi == kEpiStats;
+    if (a.splits == 1 && (((gend % 8) == 0 && (gstart % 8) == 0) || stats_epi)) {
         // Stage the wavefront's bf16 tile through LDS, then write whole 16-byte
         // row segments (coalesced), scattering rows through the permutation.
         __syncthreads();  // all stage buffers are free
@@ -816,6 +885,30 @@ void gated_gemm_kernel(const GemmKArgs a) {
                         swiglu8_bf16(*reinterpret_cast<const uint4*>(&sg[r * C::WN + pc * 8]),
                                      *reinterpret_cast<const uint4*>(&su[r * C::WN + pc * 8]));
                 }
+                return;
+            }
+        }
+        if constexpr (!TMODE && BN == kStatCols) {
+            if (stats_epi) {
+                if (gy != nullptr) {
+                    const bool vec = (gldy % 8) == 0 && (reinterpret_cast<uintptr_t>(gy) % 16) == 0;
+                    for (int r = lane / CPR; r < C::WM; r += RPI) {
+                        const int32_t orow = s_orow[wm * C::WM + r];
+                        if (orow < 0 || n >= gend) continue;
+                        const int pc = c ^ (((r >> 2) & 1) << 2);
+                        const uint4 v = *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
+                        uint16_t* dst = gy + static_cast<int64_t>(orow) * gldy + (n - gstart);
+                        if (vec && n + 8 <= gend) {
+                            *reinterpret_cast<uint4*>(dst) = v;
+                        } else {
+                            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                            for (int j = 0; j < 8 && n + j < gend; ++j)
+                                dst[j] = static_cast<uint16_t>(w4[j >> 1] >> (16 * (j & 1)));
+                        }
+                    }
+                }
+                __syncthreads();  // every wavefront's staged results are visible
+                stats_epilogue<C, WGN>(a, smem, s_orow, nt, n0, wave, lane);
                 return;
             }
         }
@@ -1107,7 +1200,9 @@ struct GemmPlan {
     size_t partial_bytes;
 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs, bool bn256 = false) {
+// one_pass: no split of K (the statistics epilogue needs whole sums).
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs, bool bn256 = false,
+                   bool one_pass = false) {
     GemmPlan p{};
     p.rows_cap = rows_cap_for(M);
     // The plan covers rows_cap rows (room for both segments' padding), but in
@@ -1142,6 +1237,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
         const long v = strtol(e, nullptr, 10);
         if (v >= 1 && v <= 64) s = v;
     }
+    if (one_pass) s = 1;
     p.kps = split_k(K, s);
     p.splits = static_cast<int32_t>((K + p.kps - 1) / p.kps);
     p.partial_bytes = p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float),
@@ -1367,6 +1463,103 @@ hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, h
     void* ys[1] = {pr.y};
     return gated_gemm_launch(pr.x, pr.w, base + l.t, pr.b, base + l.plan, ys, &pr.N, 1, pr.M, pr.K, pr.r,
                              base + l.gemm_ws, stream);
+}
+
+// ---------------------------------------------------------------- LM head with statistics
+namespace {
+// Plans and per-row maps of the LM head over the stacked hidden rows
+// [B (L + nb) target rows | B L draft rows]: identity order with every row
+// an AR row (the head has no adapter); row r's statistics go to the chunk
+// row of its position (field A for a target row, B for a draft row) and the
+// logit of its drafted token (none for the bonus row) is gathered.  The
+// redraw-row plan gets its segment info and an empty permutation, which the
+// decision fills.
+__global__ __launch_bounds__(256) void lm_rows_kernel(int64_t B, int32_t L, int32_t nb,
+                                                      const int32_t* __restrict__ tokens, int64_t rows,
+                                                      int64_t rows_cap, int32_t* __restrict__ perm,
+                                                      SegInfo* __restrict__ info, int32_t* __restrict__ stat_map,
+                                                      int32_t* __restrict__ row_token, int64_t rc_rows,
+                                                      int64_t rc_cap, int32_t* __restrict__ rc_perm,
+                                                      SegInfo* __restrict__ rc_info) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t nt = B * (L + nb);
+    if (r < rows_cap) perm[r] = r < rows ? static_cast<int32_t>(r) : -1;
+    if (r < rows) {
+        int64_t s, i, srow;
+        int32_t draft;
+        if (r < nt) {
+            s = r / (L + nb);
+            i = r - s * (L + nb);
+            draft = 0;
+        } else {
+            s = (r - nt) / L;
+            i = (r - nt) - s * L;
+            draft = 1;
+        }
+        srow = s * (L + nb) + i;
+        stat_map[r] = static_cast<int32_t>((srow << 1) | draft);
+        row_token[r] = i < L ? tokens[s * L + i] : -1;
+    }
+    if (r < rc_cap) rc_perm[r] = -1;
+    if (r == 0) {
+        const int32_t pv = static_cast<int32_t>((rows + kRowAlign - 1) / kRowAlign * kRowAlign);
+        *info = SegInfo{static_cast<int32_t>(rows), 0, pv, 0};
+        const int32_t rpv = static_cast<int32_t>((rc_rows + kRowAlign - 1) / kRowAlign * kRowAlign);
+        *rc_info = SegInfo{static_cast<int32_t>(rc_rows), 0, rpv, 0};
+    }
+}
+}  // namespace
+
+int32_t* row_plan_perm(void* plan) {
+    return reinterpret_cast<int32_t*>(static_cast<char*>(plan) + kPlanPermOffset);
+}
+
+hipError_t lm_rows_launch(int64_t B, int32_t L, int32_t nb, const int32_t* tokens, void* plan, int32_t* stat_map,
+                          int32_t* row_token, void* rc_plan, hipStream_t stream) {
+    const int64_t rows = B * (L + nb) + B * L;
+    const int64_t rc_rows = 2 * B;
+    const int64_t cap = std::max(rows_cap_for(rows), rows_cap_for(rc_rows));
+    hipLaunchKernelGGL(lm_rows_kernel, dim3(static_cast<uint32_t>((cap + 255) / 256)), dim3(256), 0, stream, B, L, nb,
+                       tokens, rows, rows_cap_for(rows), row_plan_perm(plan), static_cast<SegInfo*>(plan), stat_map,
+                       row_token, rc_rows, rows_cap_for(rc_rows), row_plan_perm(rc_plan),
+                       static_cast<SegInfo*>(rc_plan));
+    return hipGetLastError();
+}
+
+int64_t lm_head_stat_chunks(int64_t V) { return (V + kStatCols - 1) / kStatCols; }
+
+hipError_t lm_head_gemm_launch(const void* x, int64_t x_rows, const void* w, const void* plan, int64_t M, int64_t V,
+                               int64_t K, void* y, int32_t out_compact, void* stats, const int32_t* stat_map,
+                               const int32_t* row_token, float* gathered, float c2, hipStream_t stream) {
+    const GroupSpec gs = one_group(V);
+    const GemmPlan p = plan_gemm(M, V, K, false, gs, true, true);
+    GemmKArgs ka{};
+    ka.x = static_cast<const uint16_t*>(x);
+    ka.ldx = K;
+    ka.x_bytes = static_cast<uint32_t>(x_rows * K * 2);
+    ka.w = static_cast<const uint16_t*>(w);
+    ka.ldw = K;
+    ka.w_bytes = static_cast<uint32_t>(V * K * 2);
+    ka.perm = plan_perm(plan);
+    ka.info = plan_info(plan);
+    ka.out.n = 1;
+    ka.out.end[0] = V;
+    ka.out.y[0] = static_cast<uint16_t*>(y);
+    ka.out.ldy[0] = V;
+    ka.N = V;
+    ka.K = K;
+    ka.r = 0;
+    ka.alpha = 1.0f;
+    ka.epi = stats != nullptr ? kEpiStats : kEpiStore;
+    ka.out_compact = out_compact;
+    ka.stats = static_cast<ChunkStat*>(stats);
+    ka.stat_ld = static_cast<int32_t>(lm_head_stat_chunks(V));
+    ka.stat_map = stat_map;
+    ka.row_token = row_token;
+    ka.gathered = gathered;
+    ka.c2 = c2;
+    launch_gemm<false>(p, ka, stream);
+    return hipGetLastError();
 }
 
 }  // namespace uno

@@ -455,6 +455,56 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride, const 
     return from_hip(uno::draft_sample_launch(p, workspace, stream), "draft sample launch");
 }
 
+// ------------------------------------------------------------------ LM head + verification
+static uno_status check_lm_head(int64_t B, int32_t L, int64_t V, int64_t K, int32_t has_bonus, float temperature) {
+    uno_status st = check_logits(B, L, V, temperature, UNO_BF16);
+    if (st != UNO_OK) return st;
+    if (has_bonus != 0 && has_bonus != 1) return fail(UNO_ERR_INVALID_ARG, "has_bonus must be 0 or 1");
+    if (L > 64 || (has_bonus && L > 63))
+        return fail(UNO_ERR_UNSUPPORTED, "block length must be <= 64 (<= 63 with a bonus row)");
+    if (K < 1) return fail(UNO_ERR_INVALID_ARG, "K must be >= 1");
+    if (B > (1LL << 24)) return fail(UNO_ERR_UNSUPPORTED, "too many sequences");
+    const int64_t rows = B * (L + has_bonus) + B * L;
+    return check_gemm(rows, V, K, 8, UNO_BF16);
+}
+
+size_t uno_lm_head_verify_workspace_size(int64_t B, int32_t L, int64_t V, int64_t K, int32_t has_bonus) {
+    if (check_lm_head(B, L, V, K, has_bonus, 1.0f) != UNO_OK) return 0;
+    ok();
+    return uno::lm_head_verify_workspace_size(B, L, V, has_bonus);
+}
+
+uno_status uno_lm_head_verify(const void* hidden, const void* w_lm, int64_t B, int32_t L, int64_t V, int64_t K,
+                              int32_t has_bonus, float temperature, const int32_t* draft_tokens,
+                              const float* uniforms, int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted,
+                              void* logits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    uno_status st = check_lm_head(B, L, V, K, has_bonus, temperature);
+    if (st != UNO_OK) return st;
+    if (B == 0) return ok();
+    if (!hidden || !w_lm || !draft_tokens || !uniforms || !n_accepted || !out_tokens || !n_emitted)
+        return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(hidden) || !aligned16(w_lm) || (logits != nullptr && !aligned16(logits)))
+        return fail(UNO_ERR_INVALID_ARG, "hidden, w_lm and logits must be 16-byte aligned");
+    st = check_workspace(workspace, workspace_bytes, uno::lm_head_verify_workspace_size(B, L, V, has_bonus));
+    if (st != UNO_OK) return st;
+    uno::LmHeadProblem p{};
+    p.hidden = hidden;
+    p.w = w_lm;
+    p.B = B;
+    p.L = L;
+    p.V = V;
+    p.K = K;
+    p.has_bonus = has_bonus;
+    p.temperature = temperature;
+    p.tokens = draft_tokens;
+    p.uniforms = uniforms;
+    p.n_accepted = n_accepted;
+    p.out_tokens = out_tokens;
+    p.n_emitted = n_emitted;
+    p.logits = logits;
+    return from_hip(uno::lm_head_verify_launch(p, workspace, stream), "LM head verify launch");
+}
+
 // ------------------------------------------------------------------ glue
 uno_status uno_rmsnorm(const void* x, void* y, int64_t M, int64_t K, float eps, int32_t dtype, hipStream_t stream) {
     if (dtype != UNO_BF16) return fail(UNO_ERR_UNSUPPORTED, "rmsnorm supports bf16 only");

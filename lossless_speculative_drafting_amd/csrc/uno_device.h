@@ -49,4 +49,61 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
 // which only drops terms far below one part in 2^126 of a softmax sum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- softmax statistics of logit rows (verification and the LM head's
+// statistics epilogue form them with these functions, so that both give the
+// same bits for the same chunk of a row)
+
+// Statistics of one chunk of a row pair: the target row (A) and the draft
+// row (B) at the same position.
+struct ChunkStat {
+    double sA, sB;  // sum of exp((v - m) / T) over the chunk
+    float mA, mB;   // chunk maxima (raw logits)
+};
+
+// Running (max, sum of exp((v - max) / T)) of a set of logits; c2 = log2(e) / T.
+struct Online {
+    float m;
+    double s;
+};
+
+// Add eight logits: fp32 exponentials of the max-subtracted values, summed in
+// a fixed pairwise order in fp32, accumulated in fp64.
+__device__ __forceinline__ void online_add8(Online& o, const float* v, float c2) {
+#pragma clang fp contract(off)
+    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                           fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    if (vm > o.m) {
+        o.s *= static_cast<double>(fast_exp2((o.m - vm) * c2));
+        o.m = vm;
+    }
+    if (o.m != -INFINITY) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = fast_exp2((v[j] - o.m) * c2);
+        const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        o.s += static_cast<double>(t);
+    }
+}
+
+// Merge two running states (symmetric in its arguments, bit for bit).
+__device__ __forceinline__ Online online_merge(Online a, Online b, float c2) {
+#pragma clang fp contract(off)
+    const float m = fmaxf(a.m, b.m);
+    if (m == -INFINITY) return Online{m, 0.0};
+    const double s = a.s * static_cast<double>(fast_exp2((a.m - m) * c2)) +
+                     b.s * static_cast<double>(fast_exp2((b.m - m) * c2));
+    return Online{m, s};
+}
+
+// Merge the states of the 32 lanes of each half of a wavefront (xor tree,
+// offsets 16 .. 1): every lane of a half ends with the half's state.
+__device__ __forceinline__ Online half_wave_merge(Online o, float c2) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+        Online p{__shfl_xor(o.m, off), __shfl_xor(o.s, off)};
+        o = online_merge(o, p, c2);
+    }
+    return o;
+}
+
 }  // namespace uno

@@ -82,6 +82,39 @@ hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const 
 hipError_t swiglu_pack_launch(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
                               int64_t N_half, int64_t K, int32_t r, void* w_out, void* b_out, hipStream_t stream);
 
+// ---- LM head fused with the verification statistics ----------------------------
+// Row plan, statistics map and gathered tokens of the stacked hidden rows, and
+// the (empty) plan of the 2 B redraw rows.
+int32_t* row_plan_perm(void* plan);
+hipError_t lm_rows_launch(int64_t B, int32_t L, int32_t nb, const int32_t* tokens, void* plan, int32_t* stat_map,
+                          int32_t* row_token, void* rc_plan, hipStream_t stream);
+// Chunks per row of the statistics (one per 256 columns of the head).
+int64_t lm_head_stat_chunks(int64_t V);
+// y = x W^T over the M rows of the plan (x holds x_rows rows), bf16 (y may be
+// null with stats); with stats (ChunkStat [rows][chunks]) the statistics
+// epilogue; out_compact: the output row is the plan position.
+hipError_t lm_head_gemm_launch(const void* x, int64_t x_rows, const void* w, const void* plan, int64_t M, int64_t V,
+                               int64_t K, void* y, int32_t out_compact, void* stats, const int32_t* stat_map,
+                               const int32_t* row_token, float* gathered, float c2, hipStream_t stream);
+
+struct LmHeadProblem {
+    const void* hidden;      // bf16 [B (L + nb) + B L, K]: target rows, then draft rows
+    const void* w;           // bf16 [V, K]
+    int64_t B;
+    int32_t L;
+    int64_t V, K;
+    int32_t has_bonus;
+    float temperature;
+    const int32_t* tokens;   // [B, L]
+    const float* uniforms;   // [B, L + 1]
+    int32_t* n_accepted;
+    int32_t* out_tokens;
+    int32_t* n_emitted;
+    void* logits;            // bf16 [rows, V] or null (redraw rows recomputed)
+};
+size_t lm_head_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);
+hipError_t lm_head_verify_launch(const LmHeadProblem& p, void* ws, hipStream_t stream);
+
 // ---- layer glue ----------------------------------------------------------------
 hipError_t rmsnorm_launch(const void* x, void* y, int64_t M, int64_t K, float eps,
                           hipStream_t stream);

@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "uno_device.h"
@@ -50,11 +52,6 @@ constexpr int kVec = 8;    // tokens per 16-byte (bf16) vector
 constexpr int kSeg = 16;   // tokens per redraw segment
 constexpr int kStatTile = kThreads * kVec;
 
-struct ChunkStat {
-    double sA, sB;  // sum of exp((v - m) / T) for the target / draft row
-    float mA, mB;   // chunk maxima (raw logits)
-};
-
 enum : int32_t { kJobNone = 0, kJobResidual = 1, kJobSingle = 2 };
 
 struct RedrawJob {
@@ -64,11 +61,6 @@ struct RedrawJob {
     float Ma, invSa, Mb, invSb;
     float u;
     int32_t mode;
-};
-
-struct Online {
-    float m;
-    double s;
 };
 
 // Logit rows live in global memory; saying so lets the compiler use global
@@ -110,37 +102,11 @@ __device__ __forceinline__ void load8(const void* row, int64_t k, int64_t V, flo
     }
 }
 
-__device__ __forceinline__ void online_add8(Online& o, const float* v, float c2) {
-    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                           fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-    if (vm > o.m) {
-        o.s *= static_cast<double>(fast_exp2((o.m - vm) * c2));
-        o.m = vm;
-    }
-    if (o.m != -INFINITY) {
-        float e[kVec];
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) e[j] = fast_exp2((v[j] - o.m) * c2);
-        const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        o.s += static_cast<double>(t);
-    }
-}
-
-__device__ __forceinline__ Online online_merge(Online a, Online b, float c2) {
-    const float m = fmaxf(a.m, b.m);
-    if (m == -INFINITY) return Online{m, 0.0};
-    const double s = a.s * static_cast<double>(fast_exp2((a.m - m) * c2)) +
-                     b.s * static_cast<double>(fast_exp2((b.m - m) * c2));
-    return Online{m, s};
-}
-
+// Whole-wavefront merge: offset 32 first, then the half-wave tree.  (When
+// lanes 32..63 hold nothing, the first merge is the identity, bit for bit.)
 __device__ __forceinline__ Online wave_merge(Online o, float c2) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        Online p{__shfl_xor(o.m, off), __shfl_xor(o.s, off)};
-        o = online_merge(o, p, c2);
-    }
-    return o;
+    Online p{__shfl_xor(o.m, 32), __shfl_xor(o.s, 32)};
+    return half_wave_merge(online_merge(o, p, c2), c2);
 }
 
 // ---------------------------------------------------------------- row_stats
@@ -241,6 +207,58 @@ __device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, boo
     S = s;
 }
 
+// The chunk statistics of each row merged into one chunk: M = max_c m_c and
+// S = sum_c s_c e^{(m_c - M)/T} in fp64, as merge_chunks forms them but in a
+// fixed parallel order: lane l of the row's wavefront sums chunks l, l + 64,
+// ... in order, then the 64 lane sums add in an xor tree.  Rows with many
+// chunks (the LM head's 256-column tiles) are merged here once; the decision
+// then merges one chunk per row, which leaves the values unchanged
+// (e^0 = 1).  Array B is merged for rows i < rows_with_b of each sequence.
+__global__ __launch_bounds__(kThreads) void stat_merge_kernel(const ChunkStat* __restrict__ in, int32_t n_chunks,
+                                                             int64_t rows, int32_t rows_per_seq,
+                                                             int32_t rows_with_b, double invT,
+                                                             ChunkStat* __restrict__ out) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (row >= rows) return;  // whole wavefronts leave together
+    const bool has_b = (row % rows_per_seq) < rows_with_b;
+    const ChunkStat* st = in + row * n_chunks;
+    float ma = -INFINITY, mb = -INFINITY;
+    for (int32_t c = lane; c < n_chunks; c += kWave) {
+        ma = fmaxf(ma, st[c].mA);
+        if (has_b) mb = fmaxf(mb, st[c].mB);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        ma = fmaxf(ma, __shfl_xor(ma, off));
+        mb = fmaxf(mb, __shfl_xor(mb, off));
+    }
+    double sa = 0.0, sb = 0.0;
+    for (int32_t c = lane; c < n_chunks; c += kWave) {
+        const float mca = st[c].mA;
+        if (ma != -INFINITY && mca != -INFINITY)
+            sa += st[c].sA * exp((static_cast<double>(mca) - static_cast<double>(ma)) * invT);
+        if (has_b) {
+            const float mcb = st[c].mB;
+            if (mb != -INFINITY && mcb != -INFINITY)
+                sb += st[c].sB * exp((static_cast<double>(mcb) - static_cast<double>(mb)) * invT);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        sa += __shfl_xor(sa, off);
+        sb += __shfl_xor(sb, off);
+    }
+    if (lane == 0) {
+        ChunkStat r;
+        r.sA = sa;
+        r.mA = ma;
+        r.sB = has_b ? sb : 0.0;
+        r.mB = has_b ? mb : -INFINITY;
+        out[row] = r;
+    }
+}
+
 // ---------------------------------------------------------------- verify_decide
 struct DecideArgs {
     const void* target;
@@ -258,6 +276,18 @@ struct DecideArgs {
     int32_t* n_accepted;
     int32_t* out_tokens;
     int32_t* n_emitted;
+    // The LM head with statistics: the drafted tokens' logits come gathered
+    // (gz[s * gz_stride + i], gd[s * gd_stride + i]) instead of from the rows.
+    const float* gz;
+    const float* gd;
+    int64_t gz_stride, gd_stride;
+    // compact: a sequence's redraw rows sit at target + s * t_stride and
+    // draft + s * d_stride whatever their position; rc_perm (if set) receives
+    // the stacked hidden rows to recompute them from: plan row 2s <- the
+    // target row, 2s + 1 <- the draft row (draft rows start at rc_draft_base).
+    int32_t compact;
+    int32_t* rc_perm;
+    int64_t rc_draft_base;
 };
 
 // Position `lane` of sequence s: its drafted token, whether it is in range,
@@ -287,7 +317,10 @@ __device__ __forceinline__ LaneDecision lane_decision(const DecideArgs& a, int64
         d.x = a.tokens[s * L + lane];
         ux = a.uniforms[s * (L + 1) + lane];
         d.valid = (d.x >= 0) && (static_cast<int64_t>(d.x) < a.V);
-        if (d.valid) {
+        if (d.valid && a.gz != nullptr) {
+            zx = a.gz[s * a.gz_stride + lane];
+            dx = a.gd[s * a.gd_stride + lane];
+        } else if (d.valid) {
             const char* zrow = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(lane) * a.V) * esz;
             const char* drow = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(lane) * a.V) * esz;
             zx = load_one<BF16>(zrow, d.x);
@@ -361,18 +394,25 @@ __device__ __forceinline__ void decide_sequence(const DecideArgs& a, int64_t s, 
             if (write_outputs) a.n_emitted[s] = 0;
         } else {
             if (write_outputs) a.n_accepted[s] = n_acc;
+            const int64_t jz = a.compact ? 0 : n_acc;  // row of the redraw pair within its arrays
             if (n_acc < L) {
                 job.mode = kJobResidual;
-                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
-                job.b = static_cast<const char*>(a.draft) + (s * a.d_stride + static_cast<int64_t>(n_acc) * a.V) * esz;
+                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + jz * a.V) * esz;
+                job.b = static_cast<const char*>(a.draft) + (s * a.d_stride + jz * a.V) * esz;
                 if (write_outputs) a.n_emitted[s] = n_acc + 1;
             } else if (a.nb) {
                 job.mode = kJobSingle;
-                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + static_cast<int64_t>(L) * a.V) * esz;
+                job.a = static_cast<const char*>(a.target) + (s * a.t_stride + (a.compact ? 0 : L) * a.V) * esz;
                 if (write_outputs) a.n_emitted[s] = L + 1;
             } else {
                 if (write_outputs) a.n_emitted[s] = L;
             }
+        }
+        if (a.rc_perm != nullptr) {
+            const int64_t jrow = job.mode == kJobResidual ? n_acc : L;
+            a.rc_perm[2 * s] = job.mode != kJobNone ? static_cast<int32_t>(s * (L + a.nb) + jrow) : -1;
+            a.rc_perm[2 * s + 1] =
+                job.mode == kJobResidual ? static_cast<int32_t>(a.rc_draft_base + s * L + n_acc) : -1;
         }
         *job_out = job;
     }
@@ -704,14 +744,20 @@ __global__ __launch_bounds__(kThreads) void redraw_select_kernel(const RedrawJob
 // the draw of redraw_select on them.  Used when the masses fit in LDS.
 constexpr int kTailThreads = 1024;
 
-template <bool BF16, bool VEC>
+// DECIDE = false: the decision ran before (verify_decide_kernel) and its job
+// is read from a.jobs.
+template <bool BF16, bool VEC, bool DECIDE = true>
 __global__ __launch_bounds__(kTailThreads) void verify_tail_kernel(DecideArgs a, int64_t nseg, float c2,
                                                                   float* __restrict__ seg) {
     constexpr int NT = kTailThreads;
     extern __shared__ float s_seg[];  // segment g at g + g / 32
     __shared__ RedrawJob s_job;
     const int64_t s = blockIdx.x;
-    if (threadIdx.x < kWave) decide_sequence<BF16>(a, s, static_cast<int>(threadIdx.x), &s_job);
+    if constexpr (DECIDE) {
+        if (threadIdx.x < kWave) decide_sequence<BF16>(a, s, static_cast<int>(threadIdx.x), &s_job);
+    } else {
+        if (threadIdx.x == 0) s_job = a.jobs[s];
+    }
     __syncthreads();
     const RedrawJob job = s_job;
     if (job.mode == kJobNone) return;  // uniform for the workgroup
@@ -742,7 +788,7 @@ __global__ __launch_bounds__(kTailThreads) void verify_tail_kernel(DecideArgs a,
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-    int32_t c1;       // chunks per row in row_stats
+    int32_t c1;       // chunks per row in row_stats (past kMergeChunks: merged by stat_merge_kernel)
     int64_t chunk1;   // tokens per chunk
     int32_t c3;       // chunks per job in redraw_mass
     int64_t spc3;     // segments per chunk
@@ -750,12 +796,23 @@ struct Plan {
     int32_t n_arr;    // segment-sum arrays per job
     int64_t rows;     // rows streamed by row_stats
     int64_t n_jobs;
-    size_t off_stats, off_jobs, off_seg, total;
+    size_t off_stats, off_merged, off_jobs, off_seg, total;
 };
 
 constexpr int64_t kTargetBlocks = 2048;
+constexpr int32_t kMergeChunks = 64;
 
-Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
+// UNO_VERIFY_STAT_CHUNK (tests): tokens per row-statistics chunk of the
+// one-pass verifier, a multiple of 8 (256 gives the chunking of the LM head's
+// statistics epilogue).
+int64_t env_stat_chunk() {
+    const char* e = getenv("UNO_VERIFY_STAT_CHUNK");
+    const long v = e ? strtol(e, nullptr, 10) : 0;
+    return (v >= 8 && v % 8 == 0) ? v : 0;
+}
+
+Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr,
+               int64_t stat_chunk = 0) {
     Plan p{};
     p.rows = B * rows_per_seq;
     const int64_t max_c1 = (V + kStatTile - 1) / kStatTile;
@@ -763,6 +820,7 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     c1 = std::max<int64_t>(1, std::min(c1, max_c1));
     int64_t chunk = (V + c1 - 1) / c1;
     chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
+    if (stat_chunk > 0) chunk = stat_chunk;
     p.chunk1 = chunk;
     p.c1 = static_cast<int32_t>((V + chunk - 1) / chunk);
     p.nseg = (V + kSeg - 1) / kSeg;
@@ -778,6 +836,8 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     size_t off = 0;
     p.off_stats = off;
     off = align_up(off + static_cast<size_t>(p.rows) * p.c1 * sizeof(ChunkStat), kWorkspaceAlign);
+    p.off_merged = off;
+    off = align_up(off + static_cast<size_t>(p.rows) * sizeof(ChunkStat), kWorkspaceAlign);
     p.off_jobs = off;
     off = align_up(off + static_cast<size_t>(n_jobs) * sizeof(RedrawJob), kWorkspaceAlign);
     p.off_seg = off;
@@ -797,7 +857,7 @@ bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
 template <bool BF16, bool VEC>
 hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const int32_t nb = pr.has_bonus ? 1 : 0;
-    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2);
+    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2, chunk <= 0 ? env_stat_chunk() : 0);
     char* base = static_cast<char*>(ws);
     ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + p.off_stats);
     RedrawJob* jobs = reinterpret_cast<RedrawJob*>(base + p.off_jobs);
@@ -805,7 +865,7 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
     const double invT = 1.0 / static_cast<double>(pr.temperature);
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
 
-    DecideArgs da;
+    DecideArgs da{};
     da.target = pr.target;
     da.draft = pr.draft;
     da.t_stride = pr.t_stride;
@@ -827,6 +887,13 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
         hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
                            0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
                            p.chunk1, p.c1, c2, stats, 0, pr.L + nb, nullptr);
+        if (p.c1 > kMergeChunks) {
+            ChunkStat* merged = reinterpret_cast<ChunkStat*>(base + p.off_merged);
+            hipLaunchKernelGGL(stat_merge_kernel, dim3(static_cast<uint32_t>((p.rows + 3) / 4)), dim3(kThreads), 0,
+                               stream, stats, p.c1, p.rows, pr.L + nb, pr.L, invT, merged);
+            da.stats = merged;
+            da.n_chunks = 1;
+        }
     } else {
         // The statistics of a row are the same bits as in the one-pass plan
         // (same chunking of V), so every decision is the one-pass decision.
@@ -886,7 +953,7 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
 
 size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
     const int32_t nb = has_bonus ? 1 : 0;
-    return make_plan(B, L, V, L + nb, B, 2).total;
+    return std::max(make_plan(B, L, V, L + nb, B, 2).total, make_plan(B, L, V, L + nb, B, 2, env_stat_chunk()).total);
 }
 
 size_t verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
@@ -908,6 +975,145 @@ hipError_t draft_sample_launch(const VerifyProblem& pr, void* ws, hipStream_t st
     const bool vec = vec_ok(pr.draft, nullptr, pr.V, pr.d_stride, 0);
     if (pr.bf16) return vec ? draft_impl<true, true>(pr, ws, stream) : draft_impl<true, false>(pr, ws, stream);
     return vec ? draft_impl<false, true>(pr, ws, stream) : draft_impl<false, false>(pr, ws, stream);
+}
+
+// ---------------------------------------------------------------- LM head + verification
+namespace {
+struct LmLayout {
+    size_t plan, rc_plan, stat_map, row_token, gathered, stats, merged, jobs, seg, rc_logits, total;
+    int64_t rows, chunks;
+    Plan vp;  // redraw geometry
+};
+
+LmLayout lm_layout(int64_t B, int32_t L, int64_t V, int32_t nb) {
+    LmLayout l{};
+    l.rows = B * (L + nb) + B * L;
+    l.chunks = lm_head_stat_chunks(V);
+    l.vp = make_plan(B, L, V, L + nb, B, 2);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, kWorkspaceAlign);
+        return at;
+    };
+    l.plan = take(row_plan_bytes(l.rows));
+    l.rc_plan = take(row_plan_bytes(2 * B));
+    l.stat_map = take(static_cast<size_t>(l.rows) * sizeof(int32_t));
+    l.row_token = take(static_cast<size_t>(l.rows) * sizeof(int32_t));
+    l.gathered = take(static_cast<size_t>(l.rows) * sizeof(float));
+    l.stats = take(static_cast<size_t>(B) * (L + nb) * l.chunks * sizeof(ChunkStat));
+    l.merged = take(static_cast<size_t>(B) * (L + nb) * sizeof(ChunkStat));
+    l.jobs = take(static_cast<size_t>(B) * sizeof(RedrawJob));
+    l.seg = take(static_cast<size_t>(B) * 2 * l.vp.nseg * sizeof(float));
+    l.rc_logits = take(static_cast<size_t>(2 * B) * V * sizeof(uint16_t));
+    l.total = off;
+    return l;
+}
+
+template <bool VEC>
+void lm_tail(const DecideArgs& da, const Plan& p, bool decided, float c2, float* seg, hipStream_t stream) {
+    const size_t tail_lds = select_lds_bytes(p.nseg);
+    const uint32_t B = static_cast<uint32_t>(da.B);
+    if (tail_lds > 0) {
+        if (decided)
+            hipLaunchKernelGGL((verify_tail_kernel<true, VEC, false>), dim3(B), dim3(kTailThreads), tail_lds, stream,
+                               da, p.nseg, c2, seg);
+        else
+            hipLaunchKernelGGL((verify_tail_kernel<true, VEC, true>), dim3(B), dim3(kTailThreads), tail_lds, stream,
+                               da, p.nseg, c2, seg);
+        return;
+    }
+    if (!decided) {
+        const uint32_t dblocks = static_cast<uint32_t>((da.B + kThreads / kWave - 1) / (kThreads / kWave));
+        hipLaunchKernelGGL((verify_decide_kernel<true>), dim3(dblocks), dim3(kThreads), 0, stream, da);
+    }
+    hipLaunchKernelGGL((redraw_mass_kernel<true, VEC>), dim3(static_cast<uint32_t>(da.B * p.c3)), dim3(kThreads), 0,
+                       stream, da.jobs, p.c3, p.spc3, p.nseg, p.n_arr, da.V, c2, seg);
+    hipLaunchKernelGGL((redraw_select_kernel<true, VEC>), dim3(B), dim3(kThreads), select_lds_bytes(p.nseg), stream,
+                       da.jobs, p.nseg, p.n_arr, da.V, c2, seg);
+}
+}  // namespace
+
+size_t lm_head_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
+    return lm_layout(B, L, V, has_bonus ? 1 : 0).total;
+}
+
+// The LM head over every row with the statistics epilogue (no logits
+// written unless pr.logits is set), the per-row merge, the decision on the
+// gathered logits of the drafted tokens, and the redraw: on the stored
+// logits, or on the 2 B redraw rows recomputed by the same GEMM (same tile
+// family, one pass over K: the same bits as the first pass).
+hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t stream) {
+    const int32_t nb = pr.has_bonus ? 1 : 0;
+    const LmLayout l = lm_layout(pr.B, pr.L, pr.V, nb);
+    char* base = static_cast<char*>(ws);
+    int32_t* stat_map = reinterpret_cast<int32_t*>(base + l.stat_map);
+    int32_t* row_token = reinterpret_cast<int32_t*>(base + l.row_token);
+    float* gathered = reinterpret_cast<float*>(base + l.gathered);
+    ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + l.stats);
+    ChunkStat* merged = reinterpret_cast<ChunkStat*>(base + l.merged);
+    uint16_t* rc = reinterpret_cast<uint16_t*>(base + l.rc_logits);
+    const double invT = 1.0 / static_cast<double>(pr.temperature);
+    const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
+    const int64_t nt = pr.B * (pr.L + nb);
+
+    hipError_t e = lm_rows_launch(pr.B, pr.L, nb, pr.tokens, base + l.plan, stat_map, row_token, base + l.rc_plan,
+                                  stream);
+    if (e != hipSuccess) return e;
+    e = lm_head_gemm_launch(pr.hidden, l.rows, pr.w, base + l.plan, l.rows, pr.V, pr.K, pr.logits, 0, stats, stat_map,
+                            row_token, gathered, c2, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(stat_merge_kernel, dim3(static_cast<uint32_t>((nt + 3) / 4)), dim3(kThreads), 0, stream, stats,
+                       static_cast<int32_t>(l.chunks), nt, pr.L + nb, pr.L, invT, merged);
+
+    DecideArgs da{};
+    da.tokens = pr.tokens;
+    da.uniforms = pr.uniforms;
+    da.B = pr.B;
+    da.L = pr.L;
+    da.nb = nb;
+    da.V = pr.V;
+    da.invT = invT;
+    da.stats = merged;
+    da.n_chunks = 1;
+    da.jobs = reinterpret_cast<RedrawJob*>(base + l.jobs);
+    da.n_accepted = pr.n_accepted;
+    da.out_tokens = pr.out_tokens;
+    da.n_emitted = pr.n_emitted;
+    da.gz = gathered;
+    da.gz_stride = pr.L + nb;
+    da.gd = gathered + nt;
+    da.gd_stride = pr.L;
+    float* seg = reinterpret_cast<float*>(base + l.seg);
+    if (pr.logits != nullptr) {
+        const uint16_t* lg = static_cast<const uint16_t*>(pr.logits);
+        da.target = lg;
+        da.t_stride = (pr.L + nb) * pr.V;
+        da.draft = lg + nt * pr.V;
+        da.d_stride = static_cast<int64_t>(pr.L) * pr.V;
+        if (vec_ok(da.target, da.draft, pr.V, da.t_stride, da.d_stride))
+            lm_tail<true>(da, l.vp, false, c2, seg, stream);
+        else
+            lm_tail<false>(da, l.vp, false, c2, seg, stream);
+        return hipGetLastError();
+    }
+    da.target = rc;
+    da.t_stride = 2 * pr.V;
+    da.draft = rc + pr.V;
+    da.d_stride = 2 * pr.V;
+    da.compact = 1;
+    da.rc_perm = row_plan_perm(base + l.rc_plan);
+    da.rc_draft_base = nt;
+    const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((verify_decide_kernel<true>), dim3(dblocks), dim3(kThreads), 0, stream, da);
+    e = lm_head_gemm_launch(pr.hidden, l.rows, pr.w, base + l.rc_plan, 2 * pr.B, pr.V, pr.K, rc, 1, nullptr, nullptr,
+                            nullptr, nullptr, c2, stream);
+    if (e != hipSuccess) return e;
+    if (vec_ok(da.target, da.draft, pr.V, da.t_stride, da.d_stride))
+        lm_tail<true>(da, l.vp, true, c2, seg, stream);
+    else
+        lm_tail<false>(da, l.vp, true, c2, seg, stream);
+    return hipGetLastError();
 }
 
 }  // namespace uno

@@ -34,6 +34,7 @@ Modules
                 resampling, emit, and inverse-CDF draft sampling.
 ``stack``       the weightless RMSNorm / SiLU-gate glue used between the
                 projections of the synthetic layer stack.
+``lm_head``     bf16 logits of the LM head and block verification on them.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (a library special case, brute force,
@@ -51,6 +52,7 @@ from .verify import (
     draft_sample,
 )
 from . import stack
+from . import lm_head
 
 __all__ = [
     "philox4x32_10",
@@ -65,4 +67,5 @@ __all__ = [
     "residual_weights",
     "draft_sample",
     "stack",
+    "lm_head",
 ]

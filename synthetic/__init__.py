@@ -14,5 +14,6 @@ from .workloads import (  # noqa: F401
     gate_vector,
     gemm_inputs,
     verify_inputs,
+    lm_head_inputs,
     layer_shapes,
 )

@@ -11,7 +11,7 @@ import math
 
 import torch
 
-from .workloads import RANK
+from .workloads import RANK, _exact_scale
 
 
 def _gen(seed, device):
@@ -68,3 +68,25 @@ def random_tokens(B, L, V, seed, device="cuda"):
     """Uniformly random token ids (int32) -- filler drafts for rows a test does not inspect."""
     g = _gen(seed, device)
     return torch.randint(0, V, (B, L), generator=g, device=device, dtype=torch.int32)
+
+
+def lm_head_tensors(B, L, V, K, seed, has_bonus=False, kind="normal", logit_sigma=3.0, draft_noise=0.3,
+                    device="cuda"):
+    """The LM head's inputs on the device, same recipes as synthetic.workloads.lm_head_inputs:
+    (hidden [B (L+nb) + B L, K] bf16, w [V, K] bf16, tokens [B, L] int32, uniforms [B, L+1] float32)."""
+    g = _gen(seed, device)
+    nb = 1 if has_bonus else 0
+    if kind == "normal":
+        ht = torch.randn((B, L + nb, K), generator=g, device=device)
+        hd = ht[:, :L] + torch.randn((B, L, K), generator=g, device=device) * draft_noise
+        w = (torch.randn((V, K), generator=g, device=device) * (logit_sigma / math.sqrt(K))).to(torch.bfloat16)
+    elif kind == "exact":
+        ht = torch.randint(-3, 4, (B, L + nb, K), generator=g, device=device).float()
+        hd = ht[:, :L] + torch.randint(-1, 2, (B, L, K), generator=g, device=device).float()
+        w = (torch.randint(-2, 3, (V, K), generator=g, device=device).float() * _exact_scale(K)).to(torch.bfloat16)
+    else:
+        raise ValueError(kind)
+    hidden = torch.cat([ht.reshape(B * (L + nb), K), hd.reshape(B * L, K)]).to(torch.bfloat16).contiguous()
+    tokens = torch.randint(0, V, (B, L), generator=g, device=device, dtype=torch.int32)
+    uniforms = torch.rand((B, L + 1), generator=g, device=device, dtype=torch.float32)
+    return hidden, w.contiguous(), tokens, uniforms

@@ -161,3 +161,41 @@ def verify_inputs(B, L, V, seed, kind="normal", target_sigma=3.0, draft_sigma=1.
     elif dtype != "f32":
         raise ValueError(dtype)
     return np.ascontiguousarray(z, np.float32), np.ascontiguousarray(d, np.float32)
+
+
+def _exact_scale(K):
+    """2^-e with 2^e the power of two nearest sqrt(K)."""
+    return float(2.0 ** -round(0.5 * np.log2(max(K, 1))))
+
+
+def lm_head_inputs(B, L, V, K, seed, has_bonus=False, kind="normal", logit_sigma=3.0, draft_noise=0.3):
+    """Inputs of the LM head + verification: stacked hidden rows
+    [B (L + has_bonus) + B L, K] (target rows, then draft rows), the head
+    w [V, K], draft tokens [B, L] int32 and uniforms [B, L + 1] float32.
+
+    normal: target hidden ~ N(0, 1); each draft row is the target row of the
+            same position plus N(0, draft_noise^2); w ~ N(0, logit_sigma^2 / K),
+            so logits have a spread of about logit_sigma.  bf16 rounds hidden and w.
+    exact:  small integers, so that every fp32 sum of products is exact
+            whatever the order: target hidden in [-3, 3], draft = target plus
+            [-1, 1], w in [-2, 2] times 2^-e with 2^e near sqrt(K).
+    Tokens are uniform over [0, V); uniforms uniform on [0, 1).
+    """
+    g = _rng(seed)
+    nb = 1 if has_bonus else 0
+    if kind == "normal":
+        ht = g.standard_normal((B, L + nb, K), dtype=np.float32)
+        hd = ht[:, :L] + g.standard_normal((B, L, K), dtype=np.float32) * np.float32(draft_noise)
+        w = g.standard_normal((V, K), dtype=np.float32) * np.float32(logit_sigma / np.sqrt(K))
+        ht, hd, w = bf16_round(ht), bf16_round(hd), bf16_round(w)
+    elif kind == "exact":
+        ht = g.integers(-3, 4, (B, L + nb, K)).astype(np.float32)
+        hd = ht[:, :L] + g.integers(-1, 2, (B, L, K)).astype(np.float32)
+        w = g.integers(-2, 3, (V, K)).astype(np.float32) * np.float32(_exact_scale(K))
+    else:
+        raise ValueError(kind)
+    hidden = np.concatenate([ht.reshape(B * (L + nb), K), hd.reshape(B * L, K)])
+    tokens = g.integers(0, V, (B, L)).astype(np.int32)
+    uniforms = g.random((B, L + 1), dtype=np.float32)
+    return {"hidden": np.ascontiguousarray(hidden), "w": np.ascontiguousarray(w), "tokens": tokens,
+            "uniforms": uniforms}

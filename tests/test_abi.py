@@ -151,3 +151,22 @@ def test_draft_sample_and_glue_validation(lib):
     assert lib.uno_residual_rmsnorm(FAKE, NULL, FAKE, FAKE, 4, 16, 1e-5, 0, STREAM) == INVALID
     assert lib.uno_residual_rmsnorm(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), 4, 16, 1e-5, 0, STREAM) == INVALID
     assert lib.uno_residual_rmsnorm(NULL, NULL, NULL, NULL, 0, 16, 1e-5, 0, STREAM) == OK
+
+
+def test_lm_head_verify_validation(lib):
+    assert lib.uno_lm_head_verify_workspace_size(32, 16, 128256, 4096, 1) > 0
+    assert lib.uno_lm_head_verify_workspace_size(32, 65, 128256, 4096, 0) == 0   # L > 64
+    assert lib.uno_lm_head_verify_workspace_size(32, 16, 128256, 4100, 0) == 0   # K % 8 != 0
+    assert lib.uno_lm_head_verify_workspace_size(32, 16, 1 << 20, 4096, 0) == 0  # V K >= 2^30
+    args = (FAKE, FAKE, 4, 8, 1024, 256)
+    outs = (FAKE, FAKE, FAKE, FAKE, FAKE, NULL)   # tokens, uniforms, three outputs, logits
+    assert lib.uno_lm_head_verify(*args, 2, 1.0, *outs, FAKE, 1 << 30, STREAM) == INVALID       # has_bonus
+    assert lib.uno_lm_head_verify(*args, 0, 0.0, *outs, FAKE, 1 << 30, STREAM) == UNSUPPORTED   # T
+    assert lib.uno_lm_head_verify(FAKE, FAKE, 4, 64, 1024, 256, 1, 1.0, *outs, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_lm_head_verify(FAKE, FAKE, 4, 8, 1024, 12, 0, 1.0, *outs, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_lm_head_verify(NULL, FAKE, 4, 8, 1024, 256, 0, 1.0, *outs, FAKE, 1 << 30, STREAM) == INVALID
+    assert lib.uno_lm_head_verify(ctypes.c_void_p(0x100008), FAKE, 4, 8, 1024, 256, 0, 1.0, *outs, FAKE, 1 << 30,
+                                  STREAM) == INVALID                                        # alignment
+    assert lib.uno_lm_head_verify(*args, 0, 1.0, *outs, FAKE, 4, STREAM) == WORKSPACE
+    assert lib.uno_lm_head_verify(NULL, NULL, 0, 8, 1024, 256, 0, 1.0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
+                                  STREAM) == OK                                             # B = 0
