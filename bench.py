@@ -191,6 +191,8 @@ def main():
     verify_early = {"chunk": EARLY_CHUNK, "us_per_call": round(ee0.elapsed_time(ee1) / 20 * 1e3, 3),
                     "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
 
+    lm_head = lm_head_measure(uno, sdev, torch, B, L, V, wl.projections[0][1], T, wl.seed, dev)
+
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
     v_gbs = verify_bytes(B, L, V, 2, redraws) / vt / 1e9
@@ -243,11 +245,76 @@ def main():
             "redraws_per_call": redraws,
             "early_exit": verify_early,
         },
+        "lm_head": lm_head,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, stack.layers, x0, z, d, drafts, u, gate_np, T, L)
     print(json.dumps(result), flush=True)
+
+
+def lm_head_measure(uno, sdev, torch, B, L, V, K, T, seed, dev, reps=5):
+    """The LM head fused with the verification statistics, on this workload's
+    rows (B sequences x L drafted positions, target and draft rows: 2 B L rows
+    of K = hidden over V tokens), outside the timed region.  Per-call times
+    (HIP events, `reps` calls) of uno_lm_head_verify with the redraw rows
+    recomputed (no logit row written) and with the logits stored, and of the
+    unfused chain: the plain GEMM writing the logits, then uno_block_verify.
+    Drafts come from the draft rows' own distribution.  All three must give
+    the same outputs (up to the unfused verifier's different chunking of the
+    statistics, which can move a decision only on an exact tie)."""
+    bf = torch.bfloat16
+    hidden, w, x, u = sdev.lm_head_tensors(B, L, V, K, seed + 501, kind="normal", device=dev)
+    rows = hidden.shape[0]
+    logits = torch.empty((rows, V), dtype=bf, device=dev)
+    ws = uno.Workspace(dev)
+    uno.lm_head_verify(hidden, w, x, u, T, logits=logits, workspace=ws)
+    x = uno.draft_sample(logits[B * L:].view(B, L, V), uno.philox_uniforms(0, 7, 0, B * L, device=dev), T)
+    plan = uno.RowPlan(torch.zeros(rows, dtype=torch.uint8, device=dev))  # every row an AR row: no adapter
+    t0 = torch.zeros(uno.lora_t_size(rows, 8) // 2, dtype=bf, device=dev)
+    b0 = torch.zeros((V, 8), dtype=bf, device=dev)
+    gws, vws = uno.Workspace(dev), uno.Workspace(dev)
+
+    def outs():
+        return (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, L + 1), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+
+    def unfused(o):
+        uno.gated_gemm(hidden, w, t0, b0, plan, out=logits, workspace=gws)
+        uno.block_verify(logits[:B * L].view(B, L, V), logits[B * L:].view(B, L, V), x, u, T, False, outputs=o,
+                         workspace=vws)
+
+    calls = {
+        "fused_recompute": lambda o: uno.lm_head_verify(hidden, w, x, u, T, outputs=o, workspace=ws),
+        "fused_store": lambda o: uno.lm_head_verify(hidden, w, x, u, T, logits=logits, outputs=o, workspace=ws),
+        "unfused": unfused,
+    }
+    res, got = {}, {}
+    for name, fn in calls.items():
+        o = outs()
+        for _ in range(2):
+            fn(o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(o)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
+        got[name] = o
+    same = all(torch.equal(a, b) for a, b in zip(got["fused_recompute"], got["fused_store"]))
+    agree = sum(int(torch.equal(got["fused_store"][1][s], got["unfused"][1][s])) for s in range(B)) / B
+    flop = 2.0 * rows * V * K
+    res.update({
+        "rows": rows, "vocab": V, "hidden": K,
+        "gemm_gflop": round(flop / 1e9, 2),
+        "fused_store_tflops": round(flop / (res["fused_store_us"] * 1e-6) / 1e12, 1),
+        "logit_bytes_not_written_mb": round(rows * V * 2 / 1e6, 1),
+        "fused_modes_same_outputs": bool(same),
+        "seqs_same_as_unfused_frac": round(agree, 4),
+        "mean_accepted": round(float(got["fused_store"][0].float().mean().item()), 3),
+    })
+    return res
 
 
 def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):

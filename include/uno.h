@@ -330,10 +330,13 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
  *                sequence's redraw are recomputed after the decision (one
  *                more pass over W for 2 B rows, the same bits).  Storing pays
  *                while 2 rows V bytes of logits cost less than reading W once.
- * Statistics are formed per 256-column tile of the head (the chunking
- * uno_block_verify uses with 256-token chunks) and merged per row in fp64 in
- * a fixed order; every output is bitwise that of uno_block_verify run on
- * these logits with that chunking.
+ * Statistics are formed per 256-column tile of the head with the arithmetic
+ * of uno_block_verify (fp32 exponentials of max-subtracted logits, fp64
+ * sums) and merged per row in fp64 in a fixed order.  The sums run in
+ * another order than uno_block_verify's, so the two agree except where a
+ * uniform falls within rounding (about 1e-7 relative) of an acceptance
+ * probability or a CDF boundary.  Both modes (logits stored or not) give
+ * the same bits.
  *
  * Domain: B >= 0 (B = 0 is a no-op), 1 <= L <= 64 (L <= 63 with has_bonus),
  * V >= 1, K % 8 == 0, V K < 2^30, rows K < 2^30, T > 0 and finite; hidden,

@@ -135,8 +135,8 @@ __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t
 // is optionally stored, and for each row and each tile of kStatCols columns
 // the softmax statistics (max, sum of exp((v - max) / T)) of those columns
 // are written as one chunk of the row's ChunkStat, with the logit of the
-// row's token gathered on the way.  They are the same bits that
-// verification's row statistics give for a chunk of kStatCols columns.
+// row's token gathered on the way.  Same arithmetic as verification's row
+// statistics (fp32 exponentials, fp64 sums), summed in another order.
 constexpr int32_t kEpiStore = 0, kEpiAccumulate = 1, kEpiSwiglu = 2, kEpiStats = 3;
 constexpr int kSwigluBlock = 128;
 constexpr int kStatCols = 256;
@@ -348,35 +348,52 @@ struct TileCfg {
 };
 
 // Statistics epilogue over a staged BM x kStatCols tile (bf16, staged per
-// wavefront as [WM][WN] with the column XOR of the store path).  Row R is
-// handled by one half-wavefront: lane h takes columns [8h, 8h + 8), exactly
-// the values thread h of verification's row statistics takes for a chunk of
-// kStatCols columns (the other threads there hold nothing, so their merges
-// are the identity), then the half-wave tree merges the 32 lanes.
+// wavefront as [WM][WN] with the column XOR of the store path).  Eight lanes
+// take one row: lane p of the eight accumulates, in order, the 8-column
+// vectors p, p + 8, p + 16, p + 24 of the row (an online max / sum of exp),
+// then the eight states merge in an xor tree (offsets 4, 2, 1).  At each step
+// the eight lanes of a row read eight different 16-byte chunks of one staged
+// 64-column block, and two rows fill the 16 bank groups, so the reads are
+// free of bank conflicts.
 template <class C, int WGN>
 __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_t* smem, const int32_t* s_orow,
                                                int32_t nt, int64_t n0, int wave, int lane) {
-    const int h = lane & 31;
-    const int hc = 8 * h;  // tile column of this lane's eight values
-    const int wn_c = hc / C::WN, cc = hc % C::WN;
-    const int64_t ncol = n0 + hc;
-    for (int R = wave * 2 + (lane >> 5); R < C::BM_; R += 2 * C::NWAVES) {
+    static_assert(kStatCols == 256 && C::WN % 64 == 0, "32 vectors of 8 columns; 64-column staging blocks");
+    const int p = lane & 7;  // this lane's part of its row
+    constexpr int kRowsPerPass = 8 * C::NWAVES;
+    static_assert(C::BM_ % kRowsPerPass == 0, "whole passes over the tile rows");
+#pragma unroll
+    for (int it = 0; it < C::BM_ / kRowsPerPass; ++it) {
+        const int R = it * kRowsPerPass + wave * 8 + (lane >> 3);
         const int32_t orow = s_orow[R];
         const int wm_r = R / C::WM, rl = R % C::WM;
-        const uint16_t* src = smem + (wm_r * WGN + wn_c) * C::WM * C::WN + rl * C::WN + (cc ^ (((rl >> 2) & 1) << 5));
-        float v[8];
-        unpack8(*reinterpret_cast<const uint4*>(src), v);
+        const uint16_t* rowp = smem + wm_r * WGN * C::WM * C::WN + rl * C::WN;
+        const int sw = ((rl >> 2) & 1) << 5;
+        const int32_t tok = orow >= 0 ? a.row_token[orow] : -1;
+        const int64_t dt = static_cast<int64_t>(tok) - n0;  // token's column in the tile
         Online o{-INFINITY, 0.0};
-        if (ncol < a.N) {
+        float g = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (ncol + j >= a.N) v[j] = -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+            const int c = 64 * q + 8 * p;  // tile column of the vector
+            const int wn_c = c / C::WN, cc = c % C::WN;
+            float v[8];
+            unpack8(*reinterpret_cast<const uint4*>(rowp + wn_c * C::WM * C::WN + (cc ^ sw)), v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (n0 + c + j >= a.N) v[j] = -INFINITY;
+                if (dt == c + j) g = v[j];
+            }
             online_add8(o, v, a.c2);
         }
-        o = half_wave_merge(o, a.c2);
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) {
+            Online q{__shfl_xor(o.m, off), __shfl_xor(o.s, off)};
+            o = online_merge(o, q, a.c2);
+        }
         if (orow < 0) continue;
         const int32_t sm = a.stat_map[orow];
-        if (h == 0 && sm >= 0) {
+        if (p == 0 && sm >= 0) {
             ChunkStat* st = a.stats + static_cast<int64_t>(sm >> 1) * a.stat_ld + nt;
             if (sm & 1) {
                 st->sB = o.s;
@@ -386,15 +403,8 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
                 st->mA = o.m;
             }
         }
-        const int32_t tok = a.row_token[orow];
-        const int64_t dt = static_cast<int64_t>(tok) - ncol;
-        if (tok >= 0 && tok < a.N && dt >= 0 && dt < 8) {
-            float g = v[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j)
-                if (dt == j) g = v[j];
+        if (tok >= 0 && tok < a.N && dt >= 0 && dt < kStatCols && ((dt >> 3) & 7) == p)
             a.gathered[orow] = g;
-        }
     }
 }
 
@@ -890,26 +900,25 @@ void gated_gemm_kernel(const GemmKArgs a) {
         }
         if constexpr (!TMODE && BN == kStatCols) {
             if (stats_epi) {
-                if (gy != nullptr) {
-                    const bool vec = (gldy % 8) == 0 && (reinterpret_cast<uintptr_t>(gy) % 16) == 0;
-                    for (int r = lane / CPR; r < C::WM; r += RPI) {
+                // statistics first (they read every wavefront's staged results),
+                // then the optional store of the logits
+                __syncthreads();
+                stats_epilogue<C, WGN>(a, smem, s_orow, nt, n0, wave, lane);
+                if (gy == nullptr) return;
+                if ((gend % 8) != 0 || (gldy % 8) != 0 || (reinterpret_cast<uintptr_t>(gy) % 16) != 0) {
+                    for (int r = lane / CPR; r < C::WM; r += RPI) {  // rows not 16-byte aligned
                         const int32_t orow = s_orow[wm * C::WM + r];
                         if (orow < 0 || n >= gend) continue;
                         const int pc = c ^ (((r >> 2) & 1) << 2);
                         const uint4 v = *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
                         uint16_t* dst = gy + static_cast<int64_t>(orow) * gldy + (n - gstart);
-                        if (vec && n + 8 <= gend) {
-                            *reinterpret_cast<uint4*>(dst) = v;
-                        } else {
-                            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                            for (int j = 0; j < 8 && n + j < gend; ++j)
-                                dst[j] = static_cast<uint16_t>(w4[j >> 1] >> (16 * (j & 1)));
-                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            if (n + j < gend) dst[j] = static_cast<uint16_t>(w4[j >> 1] >> (16 * (j & 1)));
                     }
+                    return;
                 }
-                __syncthreads();  // every wavefront's staged results are visible
-                stats_epilogue<C, WGN>(a, smem, s_orow, nt, n0, wave, lane);
-                return;
             }
         }
         const bool accumulate = a.epi == kEpiAccumulate;
@@ -1532,7 +1541,9 @@ hipError_t lm_head_gemm_launch(const void* x, int64_t x_rows, const void* w, con
                                int64_t K, void* y, int32_t out_compact, void* stats, const int32_t* stat_map,
                                const int32_t* row_token, float* gathered, float c2, hipStream_t stream) {
     const GroupSpec gs = one_group(V);
-    const GemmPlan p = plan_gemm(M, V, K, false, gs, true, true);
+    // (the statistics take 256-column tiles; every tile family without a
+    // split of K gives the same bits, so a store-only pass may take any)
+    const GemmPlan p = plan_gemm(M, V, K, false, gs, stats != nullptr, true);
     GemmKArgs ka{};
     ka.x = static_cast<const uint16_t*>(x);
     ka.ldx = K;

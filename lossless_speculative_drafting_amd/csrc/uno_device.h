@@ -67,32 +67,39 @@ struct Online {
 };
 
 // Add eight logits: fp32 exponentials of the max-subtracted values, summed in
-// a fixed pairwise order in fp32, accumulated in fp64.
+// a fixed pairwise order in fp32, accumulated in fp64.  Written without
+// branches (selects keep the untaken side's value), so that a wavefront runs
+// it in lockstep: rescaling an empty state (s = 0) and adding a set that is
+// all -inf both leave the state as it was, bit for bit.
 __device__ __forceinline__ void online_add8(Online& o, const float* v, float c2) {
 #pragma clang fp contract(off)
     const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
                            fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-    if (vm > o.m) {
-        o.s *= static_cast<double>(fast_exp2((o.m - vm) * c2));
-        o.m = vm;
-    }
-    if (o.m != -INFINITY) {
-        float e[8];
+    const bool grow = vm > o.m;
+    const float f = fast_exp2((o.m - vm) * c2);
+    if (grow && o.s != 0.0) o.s *= static_cast<double>(f);
+    const float m = grow ? vm : o.m;
+    o.m = m;
+    float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fast_exp2((v[j] - o.m) * c2);
-        const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        o.s += static_cast<double>(t);
-    }
+    for (int j = 0; j < 8; ++j) e[j] = fast_exp2((v[j] - m) * c2);
+    const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if (m != -INFINITY) o.s += static_cast<double>(t);
 }
 
-// Merge two running states (symmetric in its arguments, bit for bit).
+// Merge two running states: s = s_a e^{(m_a - m)/T} + s_b e^{(m_b - m)/T}
+// with m the larger maximum.  The larger side's factor is 2^0 = 1 exactly,
+// so only the smaller side's is formed (the same bits as forming both);
+// symmetric in its arguments, bit for bit.  Two empty states give an empty
+// state.
 __device__ __forceinline__ Online online_merge(Online a, Online b, float c2) {
 #pragma clang fp contract(off)
-    const float m = fmaxf(a.m, b.m);
-    if (m == -INFINITY) return Online{m, 0.0};
-    const double s = a.s * static_cast<double>(fast_exp2((a.m - m) * c2)) +
-                     b.s * static_cast<double>(fast_exp2((b.m - m) * c2));
-    return Online{m, s};
+    const bool a_big = a.m >= b.m;
+    const float m = a_big ? a.m : b.m;
+    const float m_small = a_big ? b.m : a.m;
+    const double s_big = a_big ? a.s : b.s, s_small = a_big ? b.s : a.s;
+    const double s = s_big + s_small * static_cast<double>(fast_exp2((m_small - m) * c2));
+    return Online{m, m == -INFINITY ? 0.0 : s};
 }
 
 // Merge the states of the 32 lanes of each half of a wavefront (xor tree,
