@@ -307,6 +307,47 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Tree verification ("The Psi-Spec Sampler" on the aifromscratch.in page:
+ * the tree sampler takes several candidates per position -- the top K --
+ * and verifies them in a prefix tree, keeping the AR model's law).  The
+ * pages give no rule; with fixed candidates, rejection over a node's
+ * children is in law one draw from the node's AR distribution followed by a
+ * look-up among the children, which is what runs:
+ *
+ *   v = root; depth = 0
+ *   loop: y = smallest k with C_k > u[s, depth] R over p_v = softmax(z_v / T)
+ *         out_tokens[s, depth] = y
+ *         if a child c of v has token y (the lowest-numbered if several):
+ *             v = c, depth += 1
+ *         else stop
+ *   n_accepted[s] = depth (tree tokens kept), n_emitted[s] = depth + 1,
+ *   last_node[s] = v; out_tokens padded with -1.
+ *
+ * node_logits : device, dtype; the AR logits after node n's prefix (node 0:
+ *               after the committed context) at s * seq_stride + n * V
+ * parents     : device int32 [B, N]; parents[s, 0] = -1 and
+ *               0 <= parents[s, n] < n for n >= 1
+ * tokens      : device int32 [B, N]; the token of node n (node 0's unused),
+ *               in [0, V)
+ * uniforms    : device float [B, N]; slot d is the draw at depth d
+ * out_tokens  : device int32 [B, N]; n_accepted, n_emitted, last_node [B]
+ * A tree breaking the parent or token rule gives n_accepted = -1,
+ * n_emitted = 0, last_node = -1 and out_tokens all -1.  Arithmetic: that of
+ * uno_draft_sample (every node draws its token with its depth's uniform;
+ * only the walked path's draws are used).
+ *
+ * Domain: B >= 0 (B = 0 is a no-op), 1 <= N <= 4096, V >= 1, T > 0 and
+ * finite, logits UNO_BF16 or UNO_F32 with a finite value in every row.
+ * workspace: at least uno_tree_verify_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+size_t uno_tree_verify_workspace_size(int64_t B, int32_t N, int64_t V);
+uno_status uno_tree_verify(const void* node_logits, int64_t seq_stride, const int32_t* parents,
+                           const int32_t* tokens, const float* uniforms, int64_t B, int32_t N, int64_t V,
+                           float temperature, int32_t logits_dtype, int32_t* n_accepted, int32_t* out_tokens,
+                           int32_t* n_emitted, int32_t* last_node, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * The LM head fused with the statistics of block verification.  The
  * verifier ("The Psi-Spec Sampler" on the aifromscratch.in page) needs, per
  * position, the softmax normalisers of the target and draft rows and their

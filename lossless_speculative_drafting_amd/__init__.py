@@ -9,6 +9,7 @@ Python binding over libuno.so (hand-written HIP for gfx950):
                      epilogue, then the same verification (no logit rows
                      written unless asked for);
 * draft_sample    -- parallel inverse-CDF proposal of draft tokens;
+* tree_verify     -- verification of candidate prefix trees (the tree sampler);
 * philox_uniforms -- the counter-based uniforms both consume;
 * rmsnorm, silu_mul, residual_add -- glue of the synthetic layer stack.
 
@@ -45,5 +46,7 @@ from ._lib import (  # noqa: F401
     silu_mul,
     status_string,
     swiglu_pack,
+    tree_verify,
+    tree_verify_workspace_size,
 )
 from .stack import GatedLoraStack  # noqa: F401

@@ -62,6 +62,9 @@ SIGNATURES = {
     "uno_draft_sample_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64]),
     "uno_draft_sample": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_int64, _c_int32, _c_int64, _c_float,
                                     _c_int32, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "uno_tree_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64]),
+    "uno_tree_verify": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int32, _c_int64, _c_float,
+                                   _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "uno_lm_head_verify_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int64, _c_int32]),
     "uno_lm_head_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int32, _c_int64, _c_int64, _c_int32, _c_float,
                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
@@ -344,6 +347,39 @@ def block_verify_workspace_size(B, L, V, has_bonus=False):
 
 def block_verify_early_workspace_size(B, L, V, has_bonus=False):
     return int(_lib.uno_block_verify_early_workspace_size(B, L, V, int(bool(has_bonus))))
+
+
+def tree_verify_workspace_size(B, N, V):
+    return int(_lib.uno_tree_verify_workspace_size(B, N, V))
+
+
+def tree_verify(node_logits, parents, tokens, uniforms, temperature=1.0, outputs=None, workspace=None, stream=None):
+    """Verify B candidate trees of N nodes (uno_tree_verify).
+
+    node_logits [B, N, V] (bf16 or float32), parents / tokens int32 [B, N],
+    uniforms float32 [B, N].  Returns (n_accepted [B], out_tokens [B, N],
+    n_emitted [B], last_node [B]) int32 tensors.
+    """
+    _need_cuda(node_logits, parents, tokens, uniforms)
+    B, N, V = node_logits.shape
+    if parents.shape != (B, N) or tokens.shape != (B, N) or uniforms.shape != (B, N):
+        raise ValueError("parents, tokens and uniforms must be [B, N]")
+    if parents.dtype != torch.int32 or tokens.dtype != torch.int32 or uniforms.dtype != torch.float32:
+        raise TypeError("parents and tokens must be int32, uniforms float32")
+    for t in (node_logits, parents, tokens, uniforms):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = node_logits.device
+    if outputs is None:
+        outputs = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+    n_acc, out_tok, n_emit, last = outputs
+    need = int(_lib.uno_tree_verify_workspace_size(B, N, V))
+    ws = _workspace(workspace, need, dev)
+    _check(_lib.uno_tree_verify(_ptr(node_logits), N * V, _ptr(parents), _ptr(tokens), _ptr(uniforms), int(B), int(N),
+                                int(V), float(temperature), _dtype_code(node_logits.dtype), _ptr(n_acc), _ptr(out_tok),
+                                _ptr(n_emit), _ptr(last), _ptr(ws), need, _stream(stream)))
+    return n_acc, out_tok, n_emit, last
 
 
 def lm_head_verify_workspace_size(B, L, V, K, has_bonus=False):

@@ -455,6 +455,57 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride, const 
     return from_hip(uno::draft_sample_launch(p, workspace, stream), "draft sample launch");
 }
 
+// ------------------------------------------------------------------ tree verification
+static uno_status check_tree(int64_t B, int32_t N, int64_t V, float temperature, int32_t dtype) {
+    uno_status st = check_logits(B, 1, V, temperature, dtype);
+    if (st != UNO_OK) return st;
+    if (N < 1 || N > 4096) return fail(UNO_ERR_UNSUPPORTED, "nodes per tree must be in [1, 4096] (got %d)", N);
+    const int64_t max_chunks = (V + 2047) / 2048;
+    if (B * N * max_chunks > kMaxGridX || B * N > kMaxGridX)
+        return fail(UNO_ERR_UNSUPPORTED, "problem too large for one launch");
+    return UNO_OK;
+}
+
+size_t uno_tree_verify_workspace_size(int64_t B, int32_t N, int64_t V) {
+    if (B < 0 || N < 1 || N > 4096 || V < 1) return 0;
+    ok();
+    return uno::tree_verify_workspace_size(B, N, V);
+}
+
+uno_status uno_tree_verify(const void* node_logits, int64_t seq_stride, const int32_t* parents,
+                           const int32_t* tokens, const float* uniforms, int64_t B, int32_t N, int64_t V,
+                           float temperature, int32_t logits_dtype, int32_t* n_accepted, int32_t* out_tokens,
+                           int32_t* n_emitted, int32_t* last_node, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    uno_status st = check_tree(B, N, V, temperature, logits_dtype);
+    if (st != UNO_OK) return st;
+    if (seq_stride < 0) return fail(UNO_ERR_INVALID_ARG, "seq_stride must be >= 0");
+    if (B == 0) return ok();
+    if (!node_logits || !parents || !tokens || !uniforms || !n_accepted || !out_tokens || !n_emitted || !last_node)
+        return fail(UNO_ERR_INVALID_ARG, "null pointer argument");
+    const size_t esz = logits_dtype == UNO_BF16 ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(node_logits) % esz)
+        return fail(UNO_ERR_INVALID_ARG, "logits must be aligned to their element size");
+    st = check_workspace(workspace, workspace_bytes, uno::tree_verify_workspace_size(B, N, V));
+    if (st != UNO_OK) return st;
+    uno::TreeProblem p{};
+    p.logits = node_logits;
+    p.seq_stride = seq_stride;
+    p.parents = parents;
+    p.tokens = tokens;
+    p.uniforms = uniforms;
+    p.B = B;
+    p.N = N;
+    p.V = V;
+    p.temperature = temperature;
+    p.bf16 = logits_dtype == UNO_BF16;
+    p.n_accepted = n_accepted;
+    p.out_tokens = out_tokens;
+    p.n_emitted = n_emitted;
+    p.last_node = last_node;
+    return from_hip(uno::tree_verify_launch(p, workspace, stream), "tree verify launch");
+}
+
 // ------------------------------------------------------------------ LM head + verification
 static uno_status check_lm_head(int64_t B, int32_t L, int64_t V, int64_t K, int32_t has_bonus, float temperature) {
     uno_status st = check_logits(B, L, V, temperature, UNO_BF16);

@@ -82,6 +82,26 @@ hipError_t gated_gemm_launch(const void* x, const void* w, const void* t, const 
 hipError_t swiglu_pack_launch(const void* w_gate, const void* w_up, const void* b_gate, const void* b_up,
                               int64_t N_half, int64_t K, int32_t r, void* w_out, void* b_out, hipStream_t stream);
 
+// ---- tree verification ----------------------------------------------------------
+struct TreeProblem {
+    const void* logits;      // node (s, n) row at s * seq_stride + n * V
+    int64_t seq_stride;
+    const int32_t* parents;  // [B, N]
+    const int32_t* tokens;   // [B, N]
+    const float* uniforms;   // [B, N]: the draw at depth d uses slot d
+    int64_t B;
+    int32_t N;
+    int64_t V;
+    float temperature;
+    bool bf16;
+    int32_t* n_accepted;
+    int32_t* out_tokens;     // [B, N]
+    int32_t* n_emitted;
+    int32_t* last_node;
+};
+size_t tree_verify_workspace_size(int64_t B, int32_t N, int64_t V);
+hipError_t tree_verify_launch(const TreeProblem& p, void* ws, hipStream_t stream);
+
 // ---- LM head fused with the verification statistics ----------------------------
 // Row plan, statistics map and gathered tokens of the stacked hidden rows, and
 // the (empty) plan of the 2 B redraw rows.

@@ -977,6 +977,125 @@ hipError_t draft_sample_launch(const VerifyProblem& pr, void* ws, hipStream_t st
     return vec ? draft_impl<false, true>(pr, ws, stream) : draft_impl<false, false>(pr, ws, stream);
 }
 
+// ---------------------------------------------------------------- tree verification
+// The tree sampler ("The Psi-Spec Sampler" on the aifromscratch.in page:
+// several candidates per position, verified in a prefix tree, the AR law
+// kept).  With fixed candidates, rejection over a node's children is in law
+// one draw y ~ p_v followed by a look-up of y among the children, so: every
+// node draws its token with the uniform of its depth (the draft sampler's
+// kernels, one row per node), then one wavefront per tree walks from the
+// root while the drawn token names a child.  Only the drawn tokens of the
+// walked path are used; one uniform per depth serves every node of that
+// depth because the path holds one node per depth.
+
+namespace {
+
+// Uniform of each node: uniforms[s, depth(node)] (a malformed parent chain
+// stops the walk up; the tree is then rejected by tree_walk_kernel).
+__global__ __launch_bounds__(kThreads) void tree_prep_kernel(const int32_t* __restrict__ parents,
+                                                            const float* __restrict__ uniforms, int64_t B,
+                                                            int32_t N, float* __restrict__ u_node) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (e >= B * N) return;
+    const int64_t s = e / N;
+    const int32_t* par = parents + s * N;
+    int32_t c = static_cast<int32_t>(e - s * N), d = 0;
+    while (c > 0) {
+        const int32_t pc = par[c];
+        if (pc < 0 || pc >= c) break;  // malformed: rejected later
+        c = pc;
+        ++d;
+    }
+    u_node[e] = uniforms[s * N + d];
+}
+
+__global__ __launch_bounds__(kThreads) void tree_walk_kernel(const int32_t* __restrict__ parents,
+                                                            const int32_t* __restrict__ tokens,
+                                                            const int32_t* __restrict__ drawn, int64_t B,
+                                                            int32_t N, int64_t V, int32_t* __restrict__ n_accepted,
+                                                            int32_t* __restrict__ out_tokens,
+                                                            int32_t* __restrict__ n_emitted,
+                                                            int32_t* __restrict__ last_node) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+    if (s >= B) return;  // whole wavefronts leave together
+    const int32_t* par = parents + s * N;
+    const int32_t* tok = tokens + s * N;
+    int32_t* out = out_tokens + s * N;
+    bool bad = false;
+    for (int32_t c = lane; c < N; c += kWave) {
+        const int32_t pc = par[c];
+        const int32_t t = tok[c];
+        bad |= c == 0 ? pc != -1 : (pc < 0 || pc >= c || t < 0 || static_cast<int64_t>(t) >= V);
+    }
+    if (__ballot(bad) != 0) {
+        for (int32_t c = lane; c < N; c += kWave) out[c] = -1;
+        if (lane == 0) {
+            n_accepted[s] = -1;
+            n_emitted[s] = 0;
+            last_node[s] = -1;
+        }
+        return;
+    }
+    int32_t v = 0, depth = 0;
+    while (true) {  // v rises at every step (children are numbered above their parent)
+        const int32_t y = drawn[s * N + v];
+        if (lane == 0) out[depth] = y;
+        int32_t child = -1;
+        for (int32_t base = v + 1; base < N; base += kWave) {
+            const int32_t c = base + lane;
+            const uint64_t hit = __ballot(c < N && par[c] == v && tok[c] == y);
+            if (hit != 0) {
+                child = base + static_cast<int32_t>(__builtin_ctzll(hit));
+                break;
+            }
+        }
+        if (child < 0) break;
+        v = child;
+        ++depth;
+    }
+    for (int32_t c = depth + 1 + lane; c < N; c += kWave) out[c] = -1;
+    if (lane == 0) {
+        n_accepted[s] = depth;
+        n_emitted[s] = depth + 1;
+        last_node[s] = v;
+    }
+}
+
+}  // namespace
+
+size_t tree_verify_workspace_size(int64_t B, int32_t N, int64_t V) {
+    return draft_sample_workspace_size(B, N, V) +
+           2 * align_up(static_cast<size_t>(B) * N * sizeof(int32_t), kWorkspaceAlign);
+}
+
+hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t stream) {
+    char* base = static_cast<char*>(ws);
+    const size_t dws = draft_sample_workspace_size(tp.B, tp.N, tp.V);
+    float* u_node = reinterpret_cast<float*>(base + dws);
+    int32_t* drawn = reinterpret_cast<int32_t*>(base + dws + align_up(static_cast<size_t>(tp.B) * tp.N * 4,
+                                                                     kWorkspaceAlign));
+    const int64_t nodes = tp.B * tp.N;
+    hipLaunchKernelGGL(tree_prep_kernel, dim3(static_cast<uint32_t>((nodes + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, tp.parents, tp.uniforms, tp.B, tp.N, u_node);
+    VerifyProblem pr{};
+    pr.draft = tp.logits;
+    pr.d_stride = tp.seq_stride;
+    pr.uniforms = u_node;
+    pr.B = tp.B;
+    pr.L = tp.N;
+    pr.V = tp.V;
+    pr.temperature = tp.temperature;
+    pr.bf16 = tp.bf16;
+    pr.sampled = drawn;
+    hipError_t e = draft_sample_launch(pr, ws, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(tree_walk_kernel, dim3(static_cast<uint32_t>((tp.B + kThreads / kWave - 1) / (kThreads / kWave))),
+                       dim3(kThreads), 0, stream, tp.parents, tp.tokens, drawn, tp.B, tp.N, tp.V, tp.n_accepted,
+                       tp.out_tokens, tp.n_emitted, tp.last_node);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- LM head + verification
 namespace {
 struct LmLayout {

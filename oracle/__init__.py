@@ -35,6 +35,7 @@ Modules
 ``stack``       the weightless RMSNorm / SiLU-gate glue used between the
                 projections of the synthetic layer stack.
 ``lm_head``     bf16 logits of the LM head and block verification on them.
+``tree``        verification of a candidate prefix tree (the tree sampler).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (a library special case, brute force,
@@ -53,6 +54,7 @@ from .verify import (
 )
 from . import stack
 from . import lm_head
+from . import tree
 
 __all__ = [
     "philox4x32_10",
@@ -68,4 +70,5 @@ __all__ = [
     "draft_sample",
     "stack",
     "lm_head",
+    "tree",
 ]

@@ -170,3 +170,20 @@ def test_lm_head_verify_validation(lib):
     assert lib.uno_lm_head_verify(*args, 0, 1.0, *outs, FAKE, 4, STREAM) == WORKSPACE
     assert lib.uno_lm_head_verify(NULL, NULL, 0, 8, 1024, 256, 0, 1.0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
                                   STREAM) == OK                                             # B = 0
+
+
+def test_tree_verify_validation(lib):
+    assert lib.uno_tree_verify_workspace_size(32, 64, 128256) > 0
+    assert lib.uno_tree_verify_workspace_size(32, 0, 128256) == 0
+    assert lib.uno_tree_verify_workspace_size(32, 4097, 128256) == 0
+    outs = (FAKE, FAKE, FAKE, FAKE)
+    assert lib.uno_tree_verify(FAKE, 0, FAKE, FAKE, FAKE, 4, 0, 64, 1.0, 0, *outs, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_tree_verify(FAKE, 0, FAKE, FAKE, FAKE, 4, 8, 64, -1.0, 0, *outs, FAKE, 1 << 30, STREAM) == UNSUPPORTED
+    assert lib.uno_tree_verify(FAKE, 0, FAKE, FAKE, FAKE, 4, 8, 64, 1.0, 7, *outs, FAKE, 1 << 30, STREAM) == INVALID
+    assert lib.uno_tree_verify(FAKE, -1, FAKE, FAKE, FAKE, 4, 8, 64, 1.0, 0, *outs, FAKE, 1 << 30, STREAM) == INVALID
+    assert lib.uno_tree_verify(FAKE, 0, NULL, FAKE, FAKE, 4, 8, 64, 1.0, 0, *outs, FAKE, 1 << 30, STREAM) == INVALID
+    assert lib.uno_tree_verify(ctypes.c_void_p(0x100001), 0, FAKE, FAKE, FAKE, 4, 8, 64, 1.0, 0, *outs, FAKE, 1 << 30,
+                               STREAM) == INVALID
+    assert lib.uno_tree_verify(FAKE, 0, FAKE, FAKE, FAKE, 4, 8, 64, 1.0, 0, *outs, FAKE, 4, STREAM) == WORKSPACE
+    assert lib.uno_tree_verify(NULL, 0, NULL, NULL, NULL, 0, 8, 64, 1.0, 0, NULL, NULL, NULL, NULL, NULL, 0,
+                               STREAM) == OK
