@@ -192,6 +192,7 @@ def main():
                     "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
 
     lm_head = lm_head_measure(uno, sdev, torch, B, L, V, wl.projections[0][1], T, wl.seed, dev)
+    tree = tree_measure(uno, sdev, torch, B, V, T, wl.seed, dev)
 
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
@@ -246,6 +247,7 @@ def main():
             "early_exit": verify_early,
         },
         "lm_head": lm_head,
+        "tree_verify": tree,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -315,6 +317,47 @@ def lm_head_measure(uno, sdev, torch, B, L, V, K, T, seed, dev, reps=5):
         "mean_accepted": round(float(got["fused_store"][0].float().mean().item()), 3),
     })
     return res
+
+
+def tree_measure(uno, sdev, torch, B, V, T, seed, dev, K=2, D=5, reps=10):
+    """Tree verification (the tree sampler) outside the timed region: B
+    trees, each the K-ary prefix tree of depth D over per-depth top-K
+    candidates (2^(D+1) - 1 = 63 nodes for K = 2, D = 5), node logits the
+    depth's base logits plus noise, bf16 over V.  Per-call HIP-event time
+    and the algorithmic bytes it streams (every node row twice: statistics,
+    then segment masses)."""
+    N = (K ** (D + 1) - 1) // (K - 1)
+    parents, depth, frontier = [-1], [0], [0]
+    for d in range(D):
+        nxt = []
+        for v in frontier:
+            for _ in range(K):
+                parents.append(v)
+                depth.append(d + 1)
+                nxt.append(len(parents) - 1)
+        frontier = nxt
+    base = sdev.randn((B, D + 1, V), 3.0, seed + 701, device=dev, dtype=torch.float32)
+    dep = torch.tensor(depth, device=dev)
+    z = (base[:, dep, :] + sdev.randn((B, N, V), 0.7, seed + 702, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+    top = torch.topk(base, K, dim=-1).indices  # [B, D + 1, K]: the candidates of each depth
+    child_rank = torch.tensor([0] + [(i - 1) % K for i in range(1, N)], device=dev)
+    parent_depth = torch.tensor([0] + [depth[i] - 1 for i in range(1, N)], device=dev)
+    tokens = top[:, parent_depth, child_rank].to(torch.int32).contiguous()
+    tokens[:, 0] = 0
+    par = torch.tensor(parents, dtype=torch.int32, device=dev).expand(B, N).contiguous()
+    u = uno.philox_uniforms(0, 9, 0, B * N, device=dev).view(B, N)
+    ws = uno.Workspace(dev)
+    out = uno.tree_verify(z.contiguous(), par, tokens, u, T, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        uno.tree_verify(z, par, tokens, u, T, outputs=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 2.0 * B * N * V * 2
+    return {"trees": B, "nodes_per_tree": N, "branching": K, "depth": D, "vocab": V, "us_per_call": round(us, 2),
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "mean_accepted": round(float(out[0].float().mean()), 3)}
 
 
 def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):
