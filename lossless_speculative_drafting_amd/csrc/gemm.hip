@@ -324,6 +324,11 @@ struct TileCfg {
     static constexpr int BM_ = BM;
     static constexpr int WM = BM / WGM;
     static constexpr int WN = BN / WGN;
+    // The epilogue stages each wavefront's results as [WM][WN] bf16 with
+    // columns XORed by 32 on alternate groups of four rows (bank spread);
+    // the XOR applies to the first SWZ columns, a power of two (all of them
+    // unless WN is not one, as 96).
+    static constexpr int SWZ = (WN & (WN - 1)) == 0 ? WN : 64;
     static constexpr int MI = WM / 32;         // 32x32 MFMA blocks per wavefront
     static constexpr int NJ = WN / 32;
     static constexpr int AQ = BM / (RB * NWAVES);  // copy instructions per wavefront per stage (A)
@@ -867,13 +872,16 @@ void gated_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    const int c = (j * 32 + (lane & 31)) ^ (((r >> 2) & 1) << 5);
+                    const int col = j * 32 + (lane & 31);
+                    const int c = col < C::SWZ ? col ^ (((r >> 2) & 1) << 5) : col;
                     st[r * C::WN + c] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v] * a.alpha));
                 }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's staging writes are done
         constexpr int CPR = C::WN / 8;  // 16-byte chunks per wavefront row
         constexpr int RPI = kWave / CPR;  // rows per store instruction
         const int c = lane % CPR;
+        // (lanes past RPI whole rows -- WN = 96: lanes 60..63 -- take none)
+        const int lane_row0 = lane < RPI * CPR ? lane / CPR : C::WM;
         const int64_t n = n0 + wn * C::WN + c * 8;
         if constexpr (!TMODE && BN == 2 * kSwigluBlock && WGN % 2 == 0) {
             if (a.epi == kEpiSwiglu) {
@@ -887,10 +895,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 const int64_t ng = n0 + pw * C::WN + c * 8;          // gate column
                 const int64_t na = (n0 >> 1) + pw * C::WN + c * 8;   // act column
 #pragma unroll 4
-                for (int r = half * (C::WM / 2) + lane / CPR; r < (half + 1) * (C::WM / 2); r += RPI) {
+                for (int r = half * (C::WM / 2) + lane_row0; r < (half + 1) * (C::WM / 2); r += RPI) {
                     const int32_t orow = s_orow[wm * C::WM + r];
                     if (orow < 0 || ng >= gend) continue;
-                    const int pc = c ^ (((r >> 2) & 1) << 2);
+                    const int pc = c * 8 < C::SWZ ? c ^ (((r >> 2) & 1) << 2) : c;
                     *reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + na) =
                         swiglu8_bf16(*reinterpret_cast<const uint4*>(&sg[r * C::WN + pc * 8]),
                                      *reinterpret_cast<const uint4*>(&su[r * C::WN + pc * 8]));
@@ -906,7 +914,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 stats_epilogue<C, WGN>(a, smem, s_orow, nt, n0, wave, lane);
                 if (gy == nullptr) return;
                 if ((gend % 8) != 0 || (gldy % 8) != 0 || (reinterpret_cast<uintptr_t>(gy) % 16) != 0) {
-                    for (int r = lane / CPR; r < C::WM; r += RPI) {  // rows not 16-byte aligned
+                    for (int r = lane_row0; r < C::WM; r += RPI) {  // rows not 16-byte aligned
                         const int32_t orow = s_orow[wm * C::WM + r];
                         if (orow < 0 || n >= gend) continue;
                         const int pc = c ^ (((r >> 2) & 1) << 2);
@@ -923,10 +931,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
         }
         const bool accumulate = a.epi == kEpiAccumulate;
 #pragma unroll 8
-        for (int r = lane / CPR; r < C::WM; r += RPI) {
+        for (int r = lane_row0; r < C::WM; r += RPI) {
             const int32_t orow = s_orow[wm * C::WM + r];
             if (orow < 0 || n >= gend) continue;
-            const int pc = c ^ (((r >> 2) & 1) << 2);
+            const int pc = c * 8 < C::SWZ ? c ^ (((r >> 2) & 1) << 2) : c;
             uint4* dst = reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + (n - gstart));
             const uint4 v = *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
             *dst = accumulate ? add8_bf16(*dst, v) : v;
@@ -1114,9 +1122,9 @@ bool tile_supported(Tile t) {
     if (t.kg == 2)  // two K groups: the 128 x 128 tile with four stage buffers
         return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.nb == 4;
     if (t.kg != 1) return false;
-    if (t.nbb > 0)  // split ring (two A and three B buffers): the 256 x 256 tile
-        return t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 && t.bm == 256 && t.bn == 256 &&
-               (t.waves == 8 || t.waves == 4);
+    if (t.nbb > 0)  // split ring (two A and three B buffers): the 256 x 256 and 256 x 192 tiles
+        return t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 && t.bm == 256 &&
+               ((t.bn == 256 && (t.waves == 8 || t.waves == 4)) || (t.bn == 192 && t.waves == 8));
     if (t.nb > 0 && t.nb != 128 / t.kb)  // extra stage buffers: the one-workgroup-per-CU 128 x 128 tile
         return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nb >= 3 && t.nb <= 5;
     if (t.pp) return t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 32;
@@ -1279,6 +1287,7 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
+        else if (t.nbb == 3 && t.bn == 192) launch_tile<256, 192, 4, 2, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.nbb == 3 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.nbb == 3) launch_tile<256, 256, 2, 2, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8 && t.kb == 64)
