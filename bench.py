@@ -1,6 +1,6 @@
 """Benchmark one Uno draft+verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-extras]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 the gated-LoRA forward of the mixed batch through every projection of the
@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack32_b32", choices=["stack32_b32", "layer_b1", "layer_b64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    # (profiling runs: skip the measurements that follow the timed region --
+    # early-exit verifier, LM head, tree verification -- so that a kernel
+    # trace holds the timed steps' kernels only)
+    ap.add_argument("--no-extras", action="store_true")
     return ap.parse_args()
 
 
@@ -170,29 +174,31 @@ def main():
     digest = source_digest("gemm.hip")
     traffic = committed_traffic("gated_gemm", digest)
 
-    # The early-exit verifier on the last step's inputs (outside the timed
-    # region): its time per call, the share of logit rows it streams, and a
-    # check that its outputs are the one-pass verifier's.
-    last = total_steps - 1
-    uno.philox_uniforms(0, 0, last * B * (L + 1), B * (L + 1), out=u)
-    e_out = (torch.empty_like(n_acc[0]), torch.empty_like(out_tok[0]), torch.empty_like(n_emit[0]))
-    ews = uno.Workspace(dev)
-    for _ in range(3):
-        uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
-    ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ee0.record()
-    for _ in range(20):
-        uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
-    ee1.record()
-    torch.cuda.synchronize()
-    same = all(torch.equal(a, b) for a, b in zip(e_out, (n_acc[last], out_tok[last], n_emit[last])))
-    chunks_read = torch.clamp((n_acc[last].long() + EARLY_CHUNK) // EARLY_CHUNK, max=(L + EARLY_CHUNK - 1) // EARLY_CHUNK)
-    rows_read = torch.clamp(chunks_read * EARLY_CHUNK, max=L).sum().item() / (B * L)
-    verify_early = {"chunk": EARLY_CHUNK, "us_per_call": round(ee0.elapsed_time(ee1) / 20 * 1e3, 3),
-                    "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
+    verify_early, lm_head, tree = None, None, None
+    if not args.no_extras:
+        # The early-exit verifier on the last step's inputs (outside the timed
+        # region): its time per call, the share of logit rows it streams, and a
+        # check that its outputs are the one-pass verifier's.
+        last = total_steps - 1
+        uno.philox_uniforms(0, 0, last * B * (L + 1), B * (L + 1), out=u)
+        e_out = (torch.empty_like(n_acc[0]), torch.empty_like(out_tok[0]), torch.empty_like(n_emit[0]))
+        ews = uno.Workspace(dev)
+        for _ in range(3):
+            uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
+        ee0, ee1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ee0.record()
+        for _ in range(20):
+            uno.block_verify(z, d, drafts, u, T, False, outputs=e_out, workspace=ews, early_chunk=EARLY_CHUNK)
+        ee1.record()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(e_out, (n_acc[last], out_tok[last], n_emit[last])))
+        chunks_read = torch.clamp((n_acc[last].long() + EARLY_CHUNK) // EARLY_CHUNK, max=(L + EARLY_CHUNK - 1) // EARLY_CHUNK)
+        rows_read = torch.clamp(chunks_read * EARLY_CHUNK, max=L).sum().item() / (B * L)
+        verify_early = {"chunk": EARLY_CHUNK, "us_per_call": round(ee0.elapsed_time(ee1) / 20 * 1e3, 3),
+                        "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
 
-    lm_head = lm_head_measure(uno, sdev, torch, B, L, V, wl.projections[0][1], T, wl.seed, dev)
-    tree = tree_measure(uno, sdev, torch, B, V, T, wl.seed, dev)
+        lm_head = lm_head_measure(uno, sdev, torch, B, L, V, wl.projections[0][1], T, wl.seed, dev)
+        tree = tree_measure(uno, sdev, torch, B, V, T, wl.seed, dev)
 
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)

@@ -37,8 +37,6 @@
 
 #include <math.h>
 
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "uno_device.h"
@@ -788,7 +786,7 @@ __global__ __launch_bounds__(kTailThreads) void verify_tail_kernel(DecideArgs a,
 // ---------------------------------------------------------------- planning
 
 struct Plan {
-    int32_t c1;       // chunks per row in row_stats (past kMergeChunks: merged by stat_merge_kernel)
+    int32_t c1;       // chunks per row in row_stats
     int64_t chunk1;   // tokens per chunk
     int32_t c3;       // chunks per job in redraw_mass
     int64_t spc3;     // segments per chunk
@@ -796,23 +794,12 @@ struct Plan {
     int32_t n_arr;    // segment-sum arrays per job
     int64_t rows;     // rows streamed by row_stats
     int64_t n_jobs;
-    size_t off_stats, off_merged, off_jobs, off_seg, total;
+    size_t off_stats, off_jobs, off_seg, total;
 };
 
 constexpr int64_t kTargetBlocks = 2048;
-constexpr int32_t kMergeChunks = 64;
 
-// UNO_VERIFY_STAT_CHUNK (tests): tokens per row-statistics chunk of the
-// one-pass verifier, a multiple of 8 (256 gives the chunking of the LM head's
-// statistics epilogue).
-int64_t env_stat_chunk() {
-    const char* e = getenv("UNO_VERIFY_STAT_CHUNK");
-    const long v = e ? strtol(e, nullptr, 10) : 0;
-    return (v >= 8 && v % 8 == 0) ? v : 0;
-}
-
-Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr,
-               int64_t stat_chunk = 0) {
+Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
     Plan p{};
     p.rows = B * rows_per_seq;
     const int64_t max_c1 = (V + kStatTile - 1) / kStatTile;
@@ -820,7 +807,6 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     c1 = std::max<int64_t>(1, std::min(c1, max_c1));
     int64_t chunk = (V + c1 - 1) / c1;
     chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
-    if (stat_chunk > 0) chunk = stat_chunk;
     p.chunk1 = chunk;
     p.c1 = static_cast<int32_t>((V + chunk - 1) / chunk);
     p.nseg = (V + kSeg - 1) / kSeg;
@@ -836,8 +822,6 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     size_t off = 0;
     p.off_stats = off;
     off = align_up(off + static_cast<size_t>(p.rows) * p.c1 * sizeof(ChunkStat), kWorkspaceAlign);
-    p.off_merged = off;
-    off = align_up(off + static_cast<size_t>(p.rows) * sizeof(ChunkStat), kWorkspaceAlign);
     p.off_jobs = off;
     off = align_up(off + static_cast<size_t>(n_jobs) * sizeof(RedrawJob), kWorkspaceAlign);
     p.off_seg = off;
@@ -857,7 +841,7 @@ bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
 template <bool BF16, bool VEC>
 hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const int32_t nb = pr.has_bonus ? 1 : 0;
-    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2, chunk <= 0 ? env_stat_chunk() : 0);
+    const Plan p = make_plan(pr.B, pr.L, pr.V, pr.L + nb, pr.B, 2);
     char* base = static_cast<char*>(ws);
     ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + p.off_stats);
     RedrawJob* jobs = reinterpret_cast<RedrawJob*>(base + p.off_jobs);
@@ -887,13 +871,6 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
         hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
                            0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
                            p.chunk1, p.c1, c2, stats, 0, pr.L + nb, nullptr);
-        if (p.c1 > kMergeChunks) {
-            ChunkStat* merged = reinterpret_cast<ChunkStat*>(base + p.off_merged);
-            hipLaunchKernelGGL(stat_merge_kernel, dim3(static_cast<uint32_t>((p.rows + 3) / 4)), dim3(kThreads), 0,
-                               stream, stats, p.c1, p.rows, pr.L + nb, pr.L, invT, merged);
-            da.stats = merged;
-            da.n_chunks = 1;
-        }
     } else {
         // The statistics of a row are the same bits as in the one-pass plan
         // (same chunking of V), so every decision is the one-pass decision.
@@ -953,7 +930,7 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
 
 size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
     const int32_t nb = has_bonus ? 1 : 0;
-    return std::max(make_plan(B, L, V, L + nb, B, 2).total, make_plan(B, L, V, L + nb, B, 2, env_stat_chunk()).total);
+    return make_plan(B, L, V, L + nb, B, 2).total;
 }
 
 size_t verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
