@@ -343,8 +343,9 @@ struct TileCfg {
     // The output-row table (BM int32) goes behind the epilogue's staging area
     // in the stage buffers when they have room for it, else into LDS of its own.
     static constexpr bool OROW_IN_STAGE = LDS_ELEMS * 2 >= BM * BN * 2 + BM * 4;
-    // K groups hand accumulators over behind the staging area and the row table
-    static constexpr int XCH_BYTE = (BM * BN * 2 + BM * 4 + 1023) / 1024 * 1024;
+    // K groups hand accumulators over through the stage buffers, which are
+    // free after the main loop (the row table and the staging come after)
+    static constexpr int XCH_BYTE = 0;
     static_assert(KG == 1 || (OROW_IN_STAGE && XCH_BYTE + NWAVES_T * BM / WGM * BN / WGN * 4 <= LDS_ELEMS * 2),
                   "K-group exchange must fit in the stage buffers");
     static_assert(LDS_ELEMS * 2 + (OROW_IN_STAGE ? 0 : BM * 4) <= 160 * 1024, "LDS");
@@ -1079,6 +1080,7 @@ TileModel tile_model(Tile t) {
     if (t.bm == 256 && t.bn == 256 && t.pp) return {4.2e12, 10.0};
     if (t.bm == 256 && t.bn == 256 && t.nbb > 0) return t.waves == 8 ? TileModel{5.05e12, 9.0} : TileModel{4.2e12, 15.0};
     if (t.bm == 256 && t.bn == 256) return t.waves == 8 ? TileModel{4.8e12, 9.0} : TileModel{4.3e12, 15.0};
+    if (t.bm == 256 && t.bn == 128 && t.kg == 2) return {4.6e12, 8.0};  // one per CU, eight wavefronts
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
     if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {t.kg == 2 ? 4.3e12 : 4.1e12, 8.0};  // one per CU
     if (t.bm == 128) return {2.2e12, 8.0};
@@ -1119,8 +1121,9 @@ Tile env_tile() {
 }
 
 bool tile_supported(Tile t) {
-    if (t.kg == 2)  // two K groups: the 128 x 128 tile with four stage buffers
-        return t.bm == 128 && t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.nb == 4;
+    if (t.kg == 2)  // two K groups: the 128 x 128 tile with four stage buffers, 256 x 128 with three
+        return t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp &&
+               ((t.bm == 128 && t.nb == 4) || (t.bm == 256 && t.nb == 3));
     if (t.kg != 1) return false;
     if (t.nbb > 0)  // split ring (two A and three B buffers): the 256 x 256 and 256 x 192 tiles
         return t.kb == 64 && t.nbb == 3 && !t.pp && t.nb == 0 && t.bm == 256 &&
@@ -1193,8 +1196,9 @@ Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bo
                              getenv("UNO_GEMM_TILE"));
         warned = true;
     }
-    const Tile cands[] = {{256, 256, 8, false, 64, 0, 3}, {256, 128, 4, false, 32}, {128, 256, 4, false, 32},
-                          {128, 128, 4, false, 64, 4, 0, 2}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
+    const Tile cands[] = {{256, 256, 8, false, 64, 0, 3}, {256, 128, 4, false, 64, 3, 0, 2}, {256, 128, 4, false, 32},
+                          {128, 256, 4, false, 32},       {128, 128, 4, false, 64, 4, 0, 2}, {128, 128, 4, false, 64},
+                          {64, 128, 4, false, 64}};
     Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
@@ -1295,6 +1299,8 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else if (t.bm == 256 && t.bn == 256 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 32>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256 && t.kb == 64) launch_tile<256, 256, 2, 2, false, 64>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 256) launch_tile<256, 256, 2, 2, false, 32>(ka, blocks, stream);
+        else if (t.bm == 256 && t.bn == 128 && t.kg == 2)
+            launch_tile<256, 128, 2, 2, false, 64, false, 3, 0, 2>(ka, blocks, stream);
         else if (t.bm == 256 && t.bn == 128) launch_tile<256, 128, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 256) launch_tile<128, 256, 2, 2, false, 32>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 128 && t.kg == 2 && stage_buffers(t) == 4)

@@ -123,7 +123,7 @@ def test_deterministic_repeat():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x128b5", "128x128b4kg2", "128x256",
-                                  "256x128", "256x256", "256x192w8k64r3",
+                                  "256x128", "256x128k64b3kg2", "256x256", "256x192w8k64r3",
                                   "256x256k64", "256x256k64r3", "256x256w8", "256x256w8k64", "256x256w8k64r3",
                                   "256x256pp"])
 def test_every_tile_shape_ragged(tile, monkeypatch):
