@@ -329,10 +329,10 @@ def tree_measure(uno, sdev, torch, B, V, T, seed, dev, K=2, D=5, reps=10):
     """Tree verification (the tree sampler) outside the timed region: B
     trees, each the K-ary prefix tree of depth D over per-depth top-K
     candidates (2^(D+1) - 1 = 63 nodes for K = 2, D = 5), node logits the
-    depth's base logits plus noise, bf16 over V.  Per-call HIP-event time
-    and the algorithmic bytes it streams (every node row twice: statistics,
-    then segment masses)."""
-    N = (K ** (D + 1) - 1) // (K - 1)
+    depth's base logits plus noise, bf16 over V.  Per-call HIP-event time,
+    and the rows the walks read (n_accepted + 1 per tree, each twice:
+    statistics, then segment masses) per second."""
+    N = (K ** (D + 1) - 1) // (K - 1) if K > 1 else D + 1
     parents, depth, frontier = [-1], [0], [0]
     for d in range(D):
         nxt = []
@@ -361,9 +361,11 @@ def tree_measure(uno, sdev, torch, B, V, T, seed, dev, K=2, D=5, reps=10):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
-    nbytes = 2.0 * B * N * V * 2
+    rows = float((out[0].float() + 1).sum())
+    nbytes = 2.0 * rows * V * 2
     return {"trees": B, "nodes_per_tree": N, "branching": K, "depth": D, "vocab": V, "us_per_call": round(us, 2),
-            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "mean_accepted": round(float(out[0].float().mean()), 3)}
+            "rows_read_per_tree": round(rows / B, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "mean_accepted": round(float(out[0].float().mean()), 3)}
 
 
 def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):

@@ -333,8 +333,11 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
  * out_tokens  : device int32 [B, N]; n_accepted, n_emitted, last_node [B]
  * A tree breaking the parent or token rule gives n_accepted = -1,
  * n_emitted = 0, last_node = -1 and out_tokens all -1.  Arithmetic: that of
- * uno_draft_sample (every node draws its token with its depth's uniform;
- * only the walked path's draws are used).
+ * uno_draft_sample (fp32 exponentials, fp64 sums, the same inverse CDF).
+ * Large problems run one workgroup per tree that reads only the walked
+ * rows; small ones draw every node's token with its depth's uniform across
+ * the GPU and then walk (the two differ only where a uniform falls within
+ * rounding of a CDF boundary).
  *
  * Domain: B >= 0 (B = 0 is a no-op), 1 <= N <= 4096, V >= 1, T > 0 and
  * finite, logits UNO_BF16 or UNO_F32 with a finite value in every row.

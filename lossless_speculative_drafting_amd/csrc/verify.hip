@@ -37,6 +37,9 @@
 
 #include <math.h>
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <algorithm>
 
 #include "uno_device.h"
@@ -1039,6 +1042,136 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(const int32_t* __re
     }
 }
 
+// The whole walk of one tree in one workgroup (rows whose segment masses fit
+// in LDS): at each node, the row's max and sum of exponentials (the online
+// form of row_stats, merged over the block in wavefront order), the segment
+// masses of p into LDS and the inverse-CDF draw of the verifier's tail, then
+// the child look-up.  Only the walked path's rows are read.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTailThreads) void tree_walk_draw_kernel(
+    const void* __restrict__ logits, int64_t seq_stride, const int32_t* __restrict__ parents,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int32_t N, int64_t V, int64_t nseg,
+    float c2, float* __restrict__ seg, int32_t* __restrict__ n_accepted, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ n_emitted, int32_t* __restrict__ last_node) {
+    constexpr int NT = kTailThreads;
+    extern __shared__ float s_seg[];  // segment g at g + g / 32
+    __shared__ RedrawJob s_job;
+    __shared__ Online s_on[NT / kWave];
+    __shared__ int32_t s_tok, s_next;
+    const int64_t s = blockIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int32_t* par = parents + s * N;
+    const int32_t* tok = tokens + s * N;
+    int32_t* out = out_tokens + s * N;
+    if (wave == 0) {
+        bool bad = false;
+        for (int32_t c = lane; c < N; c += kWave) {
+            const int32_t pc = par[c];
+            const int32_t t = tok[c];
+            bad |= c == 0 ? pc != -1 : (pc < 0 || pc >= c || t < 0 || static_cast<int64_t>(t) >= V);
+        }
+        const uint64_t any_bad = __ballot(bad);
+        if (lane == 0) s_next = any_bad != 0 ? -2 : 0;
+    }
+    __syncthreads();
+    if (s_next == -2) {  // uniform for the workgroup
+        for (int32_t c = threadIdx.x; c < N; c += NT) out[c] = -1;
+        if (threadIdx.x == 0) {
+            n_accepted[s] = -1;
+            n_emitted[s] = 0;
+            last_node[s] = -1;
+        }
+        return;
+    }
+    const size_t esz = BF16 ? 2 : 4;
+    int32_t v = 0, depth = 0;
+    while (true) {  // v rises at every step (children are numbered above their parent)
+        const char* row = static_cast<const char*>(logits) + (s * seq_stride + static_cast<int64_t>(v) * V) * esz;
+        Online o{-INFINITY, 0.0};
+        constexpr int kU = 4;  // vectors in flight per thread
+        constexpr int64_t kStride = static_cast<int64_t>(NT) * kVec;
+        for (int64_t k0 = static_cast<int64_t>(threadIdx.x) * kVec; k0 < V; k0 += kU * kStride) {
+            float f[kU][kVec];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (k0 + u * kStride < V) load8<BF16, VEC>(row, k0 + u * kStride, V, f[u]);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (k0 + u * kStride < V) online_add8(o, f[u], c2);
+        }
+        o = wave_merge(o, c2);
+        if (lane == 0) s_on[wave] = o;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            Online r = s_on[0];
+            for (int w = 1; w < NT / kWave; ++w) r = online_merge(r, s_on[w], c2);
+            RedrawJob job;
+            job.a = row;
+            job.b = nullptr;
+            job.out = &s_tok;
+            job.Ma = r.m;
+            job.invSa = static_cast<float>(1.0 / r.s);
+            job.Mb = 0.f;
+            job.invSb = 0.f;
+            job.u = uniforms[s * N + depth];
+            job.mode = kJobSingle;
+            s_job = job;
+        }
+        __syncthreads();
+        const RedrawJob job = s_job;
+        constexpr int kBatch = 4;
+        for (int64_t base = threadIdx.x; base < nseg; base += kBatch * NT) {
+            float w[kBatch][kSeg];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t g = base + static_cast<int64_t>(u) * NT;
+                if (g < nseg) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t g = base + static_cast<int64_t>(u) * NT;
+                if (g < nseg) {
+                    float sr = 0.f;
+#pragma unroll
+                    for (int j = 0; j < kSeg; ++j) sr += w[u][j];
+                    s_seg[g + (g >> 5)] = sr;
+                }
+            }
+        }
+        __syncthreads();
+        select_job<BF16, VEC, NT>(job, nseg, 1, V, c2, seg + s * nseg, s_seg, true);
+        __syncthreads();
+        const int32_t y = s_tok;
+        if (wave == 0) {
+            int32_t child = -1;
+            for (int32_t b = v + 1; b < N; b += kWave) {
+                const int32_t c = b + lane;
+                const uint64_t hit = __ballot(c < N && par[c] == v && tok[c] == y);
+                if (hit != 0) {
+                    child = b + static_cast<int32_t>(__builtin_ctzll(hit));
+                    break;
+                }
+            }
+            if (lane == 0) {
+                out[depth] = y;
+                s_next = child;
+            }
+        }
+        __syncthreads();
+        const int32_t child = s_next;
+        if (child < 0) break;  // uniform for the workgroup
+        v = child;
+        ++depth;
+    }
+    for (int32_t c = depth + 1 + threadIdx.x; c < N; c += NT) out[c] = -1;
+    if (threadIdx.x == 0) {
+        n_accepted[s] = depth;
+        n_emitted[s] = depth + 1;
+        last_node[s] = v;
+    }
+}
+
 }  // namespace
 
 size_t tree_verify_workspace_size(int64_t B, int32_t N, int64_t V) {
@@ -1048,6 +1181,37 @@ size_t tree_verify_workspace_size(int64_t B, int32_t N, int64_t V) {
 
 hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t stream) {
     char* base = static_cast<char*>(ws);
+    const int64_t nseg = (tp.V + kSeg - 1) / kSeg;
+    const size_t lds = select_lds_bytes(nseg);
+    // Two forms: one workgroup walks each tree, reading only the walked rows
+    // (about 75 us per level on MI355X, V = 128256: latency of one CU per
+    // tree), or every node row is drawn by the whole GPU and then walked
+    // (streams 4 N V bytes per tree).  The walk wins once the node rows
+    // would take longer to stream than a level takes, from about 350 MB.
+    // UNO_TREE_PATH=walk|nodes forces one (tests).
+    bool walk = static_cast<double>(tp.B) * tp.N * tp.V * 4.0 > 3.5e8;
+    if (const char* e = getenv("UNO_TREE_PATH")) {
+        if (strcmp(e, "walk") == 0) walk = true;
+        if (strcmp(e, "nodes") == 0) walk = false;
+    }
+    if (walk && lds > 0) {
+        const bool vec = vec_ok(tp.logits, nullptr, tp.V, tp.seq_stride, 0);
+        const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(tp.temperature));
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(tp.B)), dim3(kTailThreads), lds, stream, tp.logits,
+                               tp.seq_stride, tp.parents, tp.tokens, tp.uniforms, tp.N, tp.V, nseg, c2,
+                               reinterpret_cast<float*>(base), tp.n_accepted, tp.out_tokens, tp.n_emitted,
+                               tp.last_node);
+        };
+        if (tp.bf16) {
+            if (vec) go(tree_walk_draw_kernel<true, true>);
+            else go(tree_walk_draw_kernel<true, false>);
+        } else {
+            if (vec) go(tree_walk_draw_kernel<false, true>);
+            else go(tree_walk_draw_kernel<false, false>);
+        }
+        return hipGetLastError();
+    }
     const size_t dws = draft_sample_workspace_size(tp.B, tp.N, tp.V);
     float* u_node = reinterpret_cast<float*>(base + dws);
     int32_t* drawn = reinterpret_cast<int32_t*>(base + dws + align_up(static_cast<size_t>(tp.B) * tp.N * 4,

@@ -93,14 +93,16 @@ CASES = [  # B, K, D, V, dtype, T
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("path", ["walk", "nodes"])
 @pytest.mark.parametrize("B,K,D,V,dtype,T", CASES)
-def test_topk_trees_match_the_oracle(B, K, D, V, dtype, T):
+def test_topk_trees_match_the_oracle(B, K, D, V, dtype, T, path, monkeypatch):
+    monkeypatch.setenv("UNO_TREE_PATH", path)
     z, parents, tokens = tree_inputs(B, K, D, V, seed=B * 13 + K * 7 + D + V, noise=0.7)
     if dtype == "bf16":
         z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
     N = parents.shape[1]
     u = oracle.philox_uniforms(3, 0, 0, B * N).reshape(B, N)
-    say("tree verify", B, K, D, V, dtype, T, "nodes", N)
+    say("tree verify", path, B, K, D, V, dtype, T, "nodes", N)
     gpu = _run(z, parents, tokens, u, T, dtype)
     ref = oracle.tree.tree_verify(z, parents, tokens, u.astype(np.float64), T)
     exact, excused, fails = _compare(gpu, ref, z, parents, tokens, u, T)
@@ -110,7 +112,9 @@ def test_topk_trees_match_the_oracle(B, K, D, V, dtype, T):
 
 
 @pytest.mark.gpu
-def test_degenerate_trees():
+@pytest.mark.parametrize("path", ["walk", "nodes"])
+def test_degenerate_trees(path, monkeypatch):
+    monkeypatch.setenv("UNO_TREE_PATH", path)
     V = 16
     # root only; a certain chain; a malformed tree; duplicate siblings
     N = 4
@@ -136,7 +140,9 @@ def test_degenerate_trees():
 
 
 @pytest.mark.gpu
-def test_full_vocabulary_trees_sampled_against_the_oracle():
+@pytest.mark.parametrize("path", ["walk", "nodes"])
+def test_full_vocabulary_trees_sampled_against_the_oracle(path, monkeypatch):
+    monkeypatch.setenv("UNO_TREE_PATH", path)
     B, K, D, V, T = 32, 2, 5, 128256, 1.0
     N = 2 ** (D + 1) - 1
     say("tree verify full size", B, N, V)
