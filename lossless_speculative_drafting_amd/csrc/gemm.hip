@@ -989,9 +989,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int64_t ncols = swiglu ? N / 2 : N;
     const int64_t total = rows_valid * ncols;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    // (the first 16 partials are loaded together, so that one memory latency
+    // covers them, then added in split order: the same sums as a plain loop)
     auto sum = [&](int64_t p, int64_t n) {
+        constexpr int kBatch = 16;
+        float v[kBatch];
+#pragma unroll
+        for (int zz = 0; zz < kBatch; ++zz)
+            v[zz] = zz < splits ? partial[(static_cast<int64_t>(zz) * rows_cap + p) * N + n] : 0.f;
         float s = 0.f;
-        for (int32_t zz = 0; zz < splits; ++zz) s += partial[(static_cast<int64_t>(zz) * rows_cap + p) * N + n];
+#pragma unroll
+        for (int zz = 0; zz < kBatch; ++zz)
+            if (zz < splits) s += v[zz];
+        for (int32_t zz = kBatch; zz < splits; ++zz) s += partial[(static_cast<int64_t>(zz) * rows_cap + p) * N + n];
         return f32_to_bf16_bits(s * alpha);
     };
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total; e += stride) {
