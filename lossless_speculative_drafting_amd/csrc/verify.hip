@@ -1184,10 +1184,11 @@ hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t strea
     const int64_t nseg = (tp.V + kSeg - 1) / kSeg;
     const size_t lds = select_lds_bytes(nseg);
     // Two forms: one workgroup walks each tree, reading only the walked rows
-    // (about 75 us per level on MI355X, V = 128256: latency of one CU per
-    // tree), or every node row is drawn by the whole GPU and then walked
-    // (streams 4 N V bytes per tree).  The walk wins once the node rows
-    // would take longer to stream than a level takes, from about 350 MB.
+    // (about 30 us per level on MI355X, V = 128256: latency of one CU per
+    // tree; a call lasts as long as the deepest walk), or every node row is
+    // drawn by the whole GPU and then walked (streams 4 N V bytes per tree).
+    // The walk wins once the node rows would take longer to stream than a
+    // few levels take, from about 350 MB.
     // UNO_TREE_PATH=walk|nodes forces one (tests).
     bool walk = static_cast<double>(tp.B) * tp.N * tp.V * 4.0 > 3.5e8;
     if (const char* e = getenv("UNO_TREE_PATH")) {
