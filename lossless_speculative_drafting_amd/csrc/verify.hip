@@ -51,6 +51,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVec = 8;    // tokens per 16-byte (bf16) vector
 constexpr int kSeg = 16;   // tokens per redraw segment
+constexpr int kMaxSplit = 64;  // most workgroups a redraw row is split over (one wavefront's lanes)
 constexpr int kStatTile = kThreads * kVec;
 
 enum : int32_t { kJobNone = 0, kJobResidual = 1, kJobSingle = 2 };
@@ -409,7 +410,7 @@ __device__ __forceinline__ void decide_sequence(const DecideArgs& a, int64_t s, 
                 if (write_outputs) a.n_emitted[s] = L;
             }
         }
-        if (a.rc_perm != nullptr) {
+        if (a.rc_perm != nullptr && write_outputs) {
             const int64_t jrow = job.mode == kJobResidual ? n_acc : L;
             a.rc_perm[2 * s] = job.mode != kJobNone ? static_cast<int32_t>(s * (L + a.nb) + jrow) : -1;
             a.rc_perm[2 * s + 1] =
@@ -516,6 +517,37 @@ __device__ __forceinline__ void segment_weights(const RedrawJob& job, int64_t g,
 // ---------------------------------------------------------------- redraw_mass
 // seg layout: [job][n_arr][nseg]; array 0 = drawn weights, array 1 = p for
 // residual jobs, filled by redraw_select only when the residual has no mass.
+// Segment masses g in [g0, g1) of one job into out0[g], by the threads of a
+// workgroup of NT, four segments per thread per round with their loads issued
+// together.
+// Returns the thread's fp64 sum of the masses it wrote, in the order written.
+template <bool BF16, bool VEC, int NT>
+__device__ __forceinline__ double chunk_masses(const RedrawJob& job, int64_t g0, int64_t g1, int64_t V, float c2,
+                                               float* __restrict__ out0) {
+    constexpr int kBatch = 4;
+    double acc = 0.0;
+    for (int64_t base = g0 + threadIdx.x; base < g1; base += kBatch * NT) {
+        float w[kBatch][kSeg];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * NT;
+            if (g < g1) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g = base + static_cast<int64_t>(u) * NT;
+            if (g < g1) {
+                float sr = 0.f;
+#pragma unroll
+                for (int j = 0; j < kSeg; ++j) sr += w[u][j];
+                out0[g] = sr;
+                acc += static_cast<double>(sr);
+            }
+        }
+    }
+    return acc;
+}
+
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void redraw_mass_kernel(const RedrawJob* __restrict__ jobs,
                                                               int32_t n_chunks, int64_t seg_per_chunk,
@@ -525,29 +557,8 @@ __global__ __launch_bounds__(kThreads) void redraw_mass_kernel(const RedrawJob* 
     const int32_t c = static_cast<int32_t>(blockIdx.x % n_chunks);
     const RedrawJob job = jobs[jid];
     if (job.mode == kJobNone) return;
-    float* out0 = seg + jid * n_arr * nseg;
     const int64_t g0 = static_cast<int64_t>(c) * seg_per_chunk;
-    const int64_t g1 = min(nseg, g0 + seg_per_chunk);
-    // four segments per thread per round, their loads issued together
-    constexpr int kBatch = 4;
-    for (int64_t base = g0 + threadIdx.x; base < g1; base += kBatch * kThreads) {
-        float w[kBatch][kSeg];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t g = base + static_cast<int64_t>(u) * kThreads;
-            if (g < g1) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t g = base + static_cast<int64_t>(u) * kThreads;
-            if (g < g1) {
-                float sr = 0.f;
-#pragma unroll
-                for (int j = 0; j < kSeg; ++j) sr += w[u][j];
-                out0[g] = sr;
-            }
-        }
-    }
+    chunk_masses<BF16, VEC, kThreads>(job, g0, min(nseg, g0 + seg_per_chunk), V, c2, seg + jid * n_arr * nseg);
 }
 
 // Exclusive block scan of one double per thread (fixed order); returns the
@@ -786,6 +797,214 @@ __global__ __launch_bounds__(kTailThreads) void verify_tail_kernel(DecideArgs a,
     select_job<BF16, VEC, NT>(job, nseg, 2, V, c2, seg + s * 2 * nseg, s_seg, true);
 }
 
+// ---------------------------------------------------------------- split tail
+// The same tail spread over n_chunks workgroups per sequence, for batches too
+// small to fill the chip with one workgroup per sequence: every workgroup
+// takes the sequence's decision (wavefront 0; chunk 0 alone writes the
+// outputs and the job) and the segment masses of its share of the redraw
+// row, then redraw_select_kernel draws from them.  DECIDE = false: the job
+// was decided before and is read from a.jobs.
+template <bool BF16, bool VEC, bool DECIDE = true>
+__global__ __launch_bounds__(kThreads) void verify_split_kernel(DecideArgs a, int32_t n_chunks,
+                                                               int64_t seg_per_chunk, int64_t nseg, float c2,
+                                                               float* __restrict__ seg, double* __restrict__ tot) {
+    __shared__ RedrawJob s_job;
+    __shared__ double sh[kThreads / kWave];
+    const int64_t s = blockIdx.x / n_chunks;
+    const int32_t c = static_cast<int32_t>(blockIdx.x % n_chunks);
+    if constexpr (DECIDE) {
+        if (threadIdx.x < kWave) decide_sequence<BF16>(a, s, static_cast<int>(threadIdx.x), &s_job, c == 0);
+    } else {
+        if (threadIdx.x == 0) s_job = a.jobs[s];
+    }
+    __syncthreads();
+    const RedrawJob job = s_job;
+    if constexpr (DECIDE) {
+        if (c == 0 && threadIdx.x == 0) a.jobs[s] = job;
+    }
+    if (job.mode == kJobNone) return;  // uniform for the workgroup
+    const int64_t g0 = static_cast<int64_t>(c) * seg_per_chunk;
+    const double part =
+        chunk_masses<BF16, VEC, kThreads>(job, g0, min(nseg, g0 + seg_per_chunk), a.V, c2, seg + s * 2 * nseg);
+    double total;
+    block_excl_scan<kThreads>(part, sh, &total);
+    if (threadIdx.x == 0) tot[s * kMaxSplit + c] = total;
+}
+
+// The draw after verify_split_kernel, one workgroup per sequence: wavefront 0
+// scans the chunk totals (fp64, fixed order) and finds the chunk where the
+// running mass first exceeds u times the total; the workgroup then scans that
+// chunk's segment masses (contiguous runs per thread) from the chunk's start
+// and the thread whose run crosses the target draws within its segment.  If
+// rounding leaves no crossing inside the chunk, the chunk's last token with
+// weight is taken; if the whole residual has no mass, the one-workgroup
+// select (which then draws from p) runs instead.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void redraw_pick_kernel(const RedrawJob* __restrict__ jobs, int32_t n_chunks,
+                                                              int64_t seg_per_chunk, int64_t nseg, int64_t V,
+                                                              float c2, float* __restrict__ seg,
+                                                              const double* __restrict__ tot) {
+    __shared__ double sh[kThreads / kWave];
+    __shared__ double s_base, s_target;
+    __shared__ int32_t s_chunk;
+    __shared__ int32_t first_wave_lane[kThreads / kWave];
+    __shared__ int32_t chosen;
+    const int64_t s = blockIdx.x;
+    const RedrawJob job = jobs[s];
+    if (job.mode == kJobNone) return;  // uniform for the workgroup
+    float* sg = seg + s * 2 * nseg;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    if (wave == 0) {
+        const double t = lane < n_chunks ? tot[s * kMaxSplit + lane] : 0.0;
+        double incl = t;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double up = __shfl_up(incl, off);
+            if (lane >= off) incl += up;
+        }
+        const double R = __shfl(incl, kWave - 1);
+        const double target = static_cast<double>(job.u) * R;
+        const uint64_t hit = __ballot(lane < n_chunks && t > 0.0 && incl > target);
+        const uint64_t any = __ballot(lane < n_chunks && t > 0.0);
+        // (no crossing: rounding; the last chunk with mass)
+        const int c = hit ? static_cast<int>(__builtin_ctzll(hit)) : (any ? 63 - __builtin_clzll(any) : -1);
+        const double below = __shfl_up(incl, 1);  // the chunks before this lane's
+        if (lane == 0) {
+            s_chunk = R > 0.0 ? c : -1;
+            s_target = target;
+        }
+        if (lane == (c < 0 ? 0 : c)) s_base = lane == 0 ? 0.0 : below;
+    }
+    __syncthreads();
+    const int32_t c = s_chunk;
+    if (c < 0) {
+        // the residual has no mass: the one-workgroup select draws from p
+        select_job<BF16, VEC, kThreads>(job, nseg, 2, V, c2, sg, nullptr);
+        return;
+    }
+    const double target = s_target;
+    const int64_t cs = static_cast<int64_t>(c) * seg_per_chunk;
+    const int64_t ce = min(nseg, cs + seg_per_chunk);
+    const int64_t per = (ce - cs + kThreads - 1) / kThreads;
+    const int64_t g0 = min(ce, cs + static_cast<int64_t>(threadIdx.x) * per);
+    const int64_t g1 = min(ce, g0 + per);
+    constexpr int kRun = 4;  // run lengths up to this are loaded together
+    float v[kRun];
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) v[k] = g0 + k < g1 ? sg[g0 + k] : 0.f;
+    double own = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) own += static_cast<double>(v[k]);
+    for (int64_t g = g0 + kRun; g < g1; ++g) own += static_cast<double>(sg[g]);
+    double ctot;
+    const double excl = s_base + block_excl_scan<kThreads>(own, sh, &ctot);
+    // The running value at the end of this thread's run, summed as the walk
+    // below sums it.
+    double run = excl;
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) run += static_cast<double>(v[k]);
+    for (int64_t g = g0 + kRun; g < g1; ++g) run += static_cast<double>(sg[g]);
+    const bool cand = (g1 > g0) && (run > target);
+    const uint64_t m = __ballot(cand);
+    if (lane == 0) first_wave_lane[wave] = m ? static_cast<int32_t>(__builtin_ctzll(m)) : -1;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t ch = -1;
+        for (int w = 0; w < kThreads / kWave; ++w) {
+            if (first_wave_lane[w] >= 0) {
+                ch = w * kWave + first_wave_lane[w];
+                break;
+            }
+        }
+        chosen = ch;
+    }
+    __syncthreads();
+    const int32_t who = chosen;
+    if (static_cast<int32_t>(threadIdx.x) == (who >= 0 ? who : 0)) {
+        int64_t token = -1;
+        if (who >= 0) {
+            double r = excl;
+            for (int64_t g = g0; g < g1 && token < 0; ++g) {
+                const float sgg = sg[g];
+                const double next = r + static_cast<double>(sgg);
+                if (next > target && sgg > 0.f) {
+                    float w[kSeg];
+                    segment_weights<BF16, VEC>(job, g, V, c2, false, w);
+                    float run32 = 0.f;
+                    for (int j = 0; j < kSeg; ++j) {
+                        run32 += w[j];
+                        if (w[j] > 0.f && r + static_cast<double>(run32) > target) {
+                            token = g * kSeg + j;
+                            break;
+                        }
+                    }
+                }
+                r = next;
+            }
+        }
+        // Rounding left no crossing: the chunk's last token with weight.
+        for (int64_t g = ce - 1; g >= cs && token < 0; --g) {
+            if (sg[g] > 0.f) {
+                float w[kSeg];
+                segment_weights<BF16, VEC>(job, g, V, c2, false, w);
+                for (int j = kSeg - 1; j >= 0; --j) {
+                    if (w[j] > 0.f) {
+                        token = g * kSeg + j;
+                        break;
+                    }
+                }
+            }
+        }
+        *job.out = static_cast<int32_t>(token < 0 ? 0 : token);
+    }
+}
+
+// The tail, in one of two forms.  One workgroup per sequence
+// (verify_tail_kernel) once the batch fills the chip that way; below that,
+// each redraw row is spread over several workgroups (verify_split_kernel,
+// about kSplitBlocks of them in all) and redraw_pick_kernel draws.  Rows
+// past the LDS staging of the one-workgroup form (V above 245,760) always
+// take the split form.  The two forms differ only in the fp64 summation order
+// of the row's masses (a token differs only where u times the total lies
+// within rounding of a boundary).  UNO_VERIFY_TAIL=fused|split forces one (tests).
+constexpr int64_t kSplitBlocks = 1024;
+constexpr int64_t kFusedMinSeqs = 256;
+
+template <bool BF16, bool VEC>
+void launch_tail(const DecideArgs& da, int64_t nseg, bool decided, float c2, float* seg, double* tot,
+                 hipStream_t stream) {
+    const size_t tail_lds = select_lds_bytes(nseg);
+    bool fused = da.B >= kFusedMinSeqs;
+    if (const char* e = getenv("UNO_VERIFY_TAIL")) {
+        if (strcmp(e, "fused") == 0) fused = true;
+        if (strcmp(e, "split") == 0) fused = false;
+    }
+    const uint32_t B = static_cast<uint32_t>(da.B);
+    if (fused && tail_lds > 0) {
+        if (decided)
+            hipLaunchKernelGGL((verify_tail_kernel<BF16, VEC, false>), dim3(B), dim3(kTailThreads), tail_lds, stream,
+                               da, nseg, c2, seg);
+        else
+            hipLaunchKernelGGL((verify_tail_kernel<BF16, VEC, true>), dim3(B), dim3(kTailThreads), tail_lds, stream,
+                               da, nseg, c2, seg);
+        return;
+    }
+    const int64_t max_c = std::min<int64_t>(kMaxSplit, (nseg + kThreads - 1) / kThreads);
+    int64_t c = std::max<int64_t>(1, std::min(max_c, (kSplitBlocks + da.B - 1) / da.B));
+    const int64_t spc = (nseg + c - 1) / c;
+    c = (nseg + spc - 1) / spc;
+    const dim3 grid(static_cast<uint32_t>(da.B * c));
+    if (decided)
+        hipLaunchKernelGGL((verify_split_kernel<BF16, VEC, false>), grid, dim3(kThreads), 0, stream, da,
+                           static_cast<int32_t>(c), spc, nseg, c2, seg, tot);
+    else
+        hipLaunchKernelGGL((verify_split_kernel<BF16, VEC, true>), grid, dim3(kThreads), 0, stream, da,
+                           static_cast<int32_t>(c), spc, nseg, c2, seg, tot);
+    hipLaunchKernelGGL((redraw_pick_kernel<BF16, VEC>), dim3(B), dim3(kThreads), 0, stream, da.jobs,
+                       static_cast<int32_t>(c), spc, nseg, da.V, c2, seg, tot);
+}
+
 // ---------------------------------------------------------------- planning
 
 struct Plan {
@@ -797,7 +1016,7 @@ struct Plan {
     int32_t n_arr;    // segment-sum arrays per job
     int64_t rows;     // rows streamed by row_stats
     int64_t n_jobs;
-    size_t off_stats, off_jobs, off_seg, total;
+    size_t off_stats, off_jobs, off_seg, off_tot, total;
 };
 
 constexpr int64_t kTargetBlocks = 2048;
@@ -829,6 +1048,8 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     off = align_up(off + static_cast<size_t>(n_jobs) * sizeof(RedrawJob), kWorkspaceAlign);
     p.off_seg = off;
     off = align_up(off + static_cast<size_t>(n_jobs) * n_arr * p.nseg * sizeof(float), kWorkspaceAlign);
+    p.off_tot = off;  // chunk totals of the split tail
+    off = align_up(off + static_cast<size_t>(n_jobs) * kMaxSplit * sizeof(double), kWorkspaceAlign);
     p.total = off;
     (void)L;
     return p;
@@ -891,18 +1112,7 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
                                live);
         }
     }
-    const size_t tail_lds = select_lds_bytes(p.nseg);
-    if (tail_lds > 0) {
-        hipLaunchKernelGGL((verify_tail_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kTailThreads),
-                           tail_lds, stream, da, p.nseg, c2, seg);
-        return hipGetLastError();
-    }
-    const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
-    hipLaunchKernelGGL((verify_decide_kernel<BF16>), dim3(dblocks), dim3(kThreads), 0, stream, da);
-    hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * p.c3)), dim3(kThreads), 0,
-                       stream, jobs, p.c3, p.spc3, p.nseg, p.n_arr, pr.V, c2, seg);
-    hipLaunchKernelGGL((redraw_select_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B)), dim3(kThreads),
-                       select_lds_bytes(p.nseg), stream, jobs, p.nseg, p.n_arr, pr.V, c2, seg);
+    launch_tail<BF16, VEC>(da, p.nseg, false, c2, seg, reinterpret_cast<double*>(base + p.off_tot), stream);
     return hipGetLastError();
 }
 
@@ -1241,7 +1451,7 @@ hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t strea
 // ---------------------------------------------------------------- LM head + verification
 namespace {
 struct LmLayout {
-    size_t plan, rc_plan, stat_map, row_token, gathered, stats, merged, jobs, seg, rc_logits, total;
+    size_t plan, rc_plan, stat_map, row_token, gathered, stats, merged, jobs, seg, tot, rc_logits, total;
     int64_t rows, chunks;
     Plan vp;  // redraw geometry
 };
@@ -1266,32 +1476,16 @@ LmLayout lm_layout(int64_t B, int32_t L, int64_t V, int32_t nb) {
     l.merged = take(static_cast<size_t>(B) * (L + nb) * sizeof(ChunkStat));
     l.jobs = take(static_cast<size_t>(B) * sizeof(RedrawJob));
     l.seg = take(static_cast<size_t>(B) * 2 * l.vp.nseg * sizeof(float));
+    l.tot = take(static_cast<size_t>(B) * kMaxSplit * sizeof(double));
     l.rc_logits = take(static_cast<size_t>(2 * B) * V * sizeof(uint16_t));
     l.total = off;
     return l;
 }
 
 template <bool VEC>
-void lm_tail(const DecideArgs& da, const Plan& p, bool decided, float c2, float* seg, hipStream_t stream) {
-    const size_t tail_lds = select_lds_bytes(p.nseg);
-    const uint32_t B = static_cast<uint32_t>(da.B);
-    if (tail_lds > 0) {
-        if (decided)
-            hipLaunchKernelGGL((verify_tail_kernel<true, VEC, false>), dim3(B), dim3(kTailThreads), tail_lds, stream,
-                               da, p.nseg, c2, seg);
-        else
-            hipLaunchKernelGGL((verify_tail_kernel<true, VEC, true>), dim3(B), dim3(kTailThreads), tail_lds, stream,
-                               da, p.nseg, c2, seg);
-        return;
-    }
-    if (!decided) {
-        const uint32_t dblocks = static_cast<uint32_t>((da.B + kThreads / kWave - 1) / (kThreads / kWave));
-        hipLaunchKernelGGL((verify_decide_kernel<true>), dim3(dblocks), dim3(kThreads), 0, stream, da);
-    }
-    hipLaunchKernelGGL((redraw_mass_kernel<true, VEC>), dim3(static_cast<uint32_t>(da.B * p.c3)), dim3(kThreads), 0,
-                       stream, da.jobs, p.c3, p.spc3, p.nseg, p.n_arr, da.V, c2, seg);
-    hipLaunchKernelGGL((redraw_select_kernel<true, VEC>), dim3(B), dim3(kThreads), select_lds_bytes(p.nseg), stream,
-                       da.jobs, p.nseg, p.n_arr, da.V, c2, seg);
+void lm_tail(const DecideArgs& da, const Plan& p, bool decided, float c2, float* seg, double* tot,
+             hipStream_t stream) {
+    launch_tail<true, VEC>(da, p.nseg, decided, c2, seg, tot, stream);
 }
 }  // namespace
 
@@ -1346,6 +1540,7 @@ hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t 
     da.gd = gathered + nt;
     da.gd_stride = pr.L;
     float* seg = reinterpret_cast<float*>(base + l.seg);
+    double* tot = reinterpret_cast<double*>(base + l.tot);
     if (pr.logits != nullptr) {
         const uint16_t* lg = static_cast<const uint16_t*>(pr.logits);
         da.target = lg;
@@ -1353,9 +1548,9 @@ hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t 
         da.draft = lg + nt * pr.V;
         da.d_stride = static_cast<int64_t>(pr.L) * pr.V;
         if (vec_ok(da.target, da.draft, pr.V, da.t_stride, da.d_stride))
-            lm_tail<true>(da, l.vp, false, c2, seg, stream);
+            lm_tail<true>(da, l.vp, false, c2, seg, tot, stream);
         else
-            lm_tail<false>(da, l.vp, false, c2, seg, stream);
+            lm_tail<false>(da, l.vp, false, c2, seg, tot, stream);
         return hipGetLastError();
     }
     da.target = rc;
@@ -1371,9 +1566,9 @@ hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t 
                             nullptr, nullptr, c2, stream);
     if (e != hipSuccess) return e;
     if (vec_ok(da.target, da.draft, pr.V, da.t_stride, da.d_stride))
-        lm_tail<true>(da, l.vp, true, c2, seg, stream);
+        lm_tail<true>(da, l.vp, true, c2, seg, tot, stream);
     else
-        lm_tail<false>(da, l.vp, true, c2, seg, stream);
+        lm_tail<false>(da, l.vp, true, c2, seg, tot, stream);
     return hipGetLastError();
 }
 

@@ -74,8 +74,11 @@ def test_exact_inputs_match_the_oracle(B, L, V, K, has_bonus, T, store):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("tail", ["default", "fused"])
 @pytest.mark.parametrize("B,L,V,K,has_bonus,T", [(8, 16, 8192 + 96, 512, True, 1.0), (5, 9, 3000, 256, False, 0.8)])
-def test_modes_agree_bitwise_and_match_the_unfused_verifier(B, L, V, K, has_bonus, T):
+def test_modes_agree_bitwise_and_match_the_unfused_verifier(B, L, V, K, has_bonus, T, tail, monkeypatch):
+    if tail != "default":
+        monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
     inp = lm_head_inputs(B, L, V, K, seed=V + K, has_bonus=has_bonus, kind="normal")
     hidden, w = to_dev(inp["hidden"], "bf16"), to_dev(inp["w"], "bf16")
     nb = 1 if has_bonus else 0

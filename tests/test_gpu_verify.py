@@ -60,8 +60,12 @@ CASES = [  # B, L, V, dtype, kind, sigma, T, bonus
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("tail", ["fused", "split"])
 @pytest.mark.parametrize("B,L,V,dtype,kind,sigma,T,bonus", CASES)
-def test_random_cases(B, L, V, dtype, kind, sigma, T, bonus):
+def test_random_cases(B, L, V, dtype, kind, sigma, T, bonus, tail, monkeypatch):
+    """Both forms of the tail (one workgroup per sequence, or each redraw row
+    spread over several workgroups) against the oracle."""
+    monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
     z, d = verify_inputs(B, L, V, seed=B * 31 + L + V, kind=kind, target_sigma=3.0, draft_sigma=sigma,
                          has_bonus=bonus, dtype=dtype)
     x = _drafts(d, T)
@@ -166,14 +170,20 @@ def test_layer_b64_full_size(sigma):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("tail", ["default", "split"])
 @pytest.mark.parametrize("T", [0.6, 1.0])
-def test_serve_b256_full_size(T):
+def test_serve_b256_full_size(T, tail, monkeypatch):
+    if tail != "default":
+        monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
     wl = WORKLOADS["serve_b256"]
     _full_vocab_case(256, wl.block, wl.vocab, "zipf", 0.5, T, wl.seed, np.arange(0, 256, 16))
 
 
 @pytest.mark.gpu
-def test_stack32_b32_full_size():
+@pytest.mark.parametrize("tail", ["default", "fused"])
+def test_stack32_b32_full_size(tail, monkeypatch):
+    if tail != "default":
+        monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
     wl = WORKLOADS["stack32_b32"]
     _full_vocab_case(32, wl.block, wl.vocab, "normal", 1.0, 1.0, wl.seed, np.arange(32))
 
