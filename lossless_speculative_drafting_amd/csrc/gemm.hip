@@ -1093,6 +1093,7 @@ TileModel tile_model(Tile t) {
     if (t.bm == 256 && t.bn == 128 && t.kg == 2) return {4.6e12, 8.0};  // one per CU, eight wavefronts
     if (t.bm * t.bn == 256 * 128) return {3.7e12, 12.0};
     if (t.bm == 128 && t.bn == 128 && stage_buffers(t) >= 4) return {t.kg == 2 ? 4.3e12 : 4.1e12, 8.0};  // one per CU
+    if (t.bm == 128 && t.bn == 192) return {t.kg == 2 ? 3.9e12 : 3.55e12, 8.0};  // one per CU
     if (t.bm == 128) return {2.2e12, 8.0};
     return {0.9e12, 8.0};
 }
@@ -1131,6 +1132,8 @@ Tile env_tile() {
 }
 
 bool tile_supported(Tile t) {
+    if (t.bm == 128 && t.bn == 192)  // 256 tiles (one per CU) at M = 1024, N = 6144
+        return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && (t.nb == 3 || t.nb == 4) && t.kg <= 2;
     if (t.kg == 2)  // two K groups: the 128 x 128 tile with four stage buffers, 256 x 128 with three
         return t.bn == 128 && t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp &&
                ((t.bm == 128 && t.nb == 4) || (t.bm == 256 && t.nb == 3));
@@ -1207,8 +1210,8 @@ Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bo
         warned = true;
     }
     const Tile cands[] = {{256, 256, 8, false, 64, 0, 3}, {256, 128, 4, false, 64, 3, 0, 2}, {256, 128, 4, false, 32},
-                          {128, 256, 4, false, 32},       {128, 128, 4, false, 64, 4, 0, 2}, {128, 128, 4, false, 64},
-                          {64, 128, 4, false, 64}};
+                          {128, 256, 4, false, 32},       {128, 192, 4, false, 64, 4, 0, 2},
+                          {128, 128, 4, false, 64, 4, 0, 2}, {128, 128, 4, false, 64}, {64, 128, 4, false, 64}};
     Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
@@ -1301,6 +1304,14 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 192 && t.kg == 2 && t.nb == 4)
+            launch_tile<128, 192, 2, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 192 && t.kg == 2)
+            launch_tile<128, 192, 2, 2, false, 64, false, 3, 0, 2>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 192 && t.nb == 4)
+            launch_tile<128, 192, 2, 2, false, 64, false, 4>(ka, blocks, stream);
+        else if (t.bm == 128 && t.bn == 192)
+            launch_tile<128, 192, 2, 2, false, 64, false, 3>(ka, blocks, stream);
         else if (t.nbb == 3 && t.bn == 192) launch_tile<256, 192, 4, 2, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.nbb == 3 && t.waves == 8) launch_tile<256, 256, 2, 4, false, 64, false, 0, 3>(ka, blocks, stream);
         else if (t.nbb == 3) launch_tile<256, 256, 2, 2, false, 64, false, 0, 3>(ka, blocks, stream);

@@ -125,7 +125,7 @@ def test_deterministic_repeat():
 @pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x128b5", "128x128b4kg2", "128x256",
                                   "256x128", "256x128k64b3kg2", "256x256", "256x192w8k64r3",
                                   "256x256k64", "256x256k64r3", "256x256w8", "256x256w8k64", "256x256w8k64r3",
-                                  "256x256pp"])
+                                  "256x256pp", "128x192b3", "128x192b4", "128x192b3kg2", "128x192b4kg2"])
 def test_every_tile_shape_ragged(tile, monkeypatch):
     """Each workgroup tile on a problem ragged in M, N and K, through the split steps."""
     monkeypatch.setenv("UNO_GEMM_TILE", tile)
@@ -144,6 +144,27 @@ def test_every_tile_shape_ragged(tile, monkeypatch):
     assert err <= BF16_TOL, err
     y_full = _run(inp, "bf16")
     assert np.array_equal(y, y_full), "split steps and the one-call projection must agree bitwise"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tile,split", [("128x192b4kg2", 3), ("128x192b3", 2), ("128x128b4kg2", 4)])
+def test_tiles_with_split_k_ragged(tile, split, monkeypatch):
+    """A tile with K split over workgroups (fp32 partials, ordered reduction) on a ragged problem."""
+    monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    monkeypatch.setenv("UNO_GEMM_SPLIT", str(split))
+    M, K, N, r = 300, 1000, 700, 128
+    rng = np.random.default_rng(12)
+    gate = (rng.random(M) < 0.4).astype(np.uint8)
+    inp = gemm_inputs(M, K, N, r, seed=22, dtype="bf16", gate=gate)
+    say("gemm tile split", tile, split)
+    x, w = to_dev(inp["x"], "bf16"), to_dev(inp["w"], "bf16")
+    a, b = to_dev(inp["a"], "bf16"), to_dev(inp["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, a, plan, 2.0)
+    y = to_host(uno.gated_gemm(x, w, t, b, plan))
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], gate, 2.0)
+    err = floored_rel_err(y, ref)
+    assert err <= BF16_TOL, err
 
 
 @pytest.mark.gpu
