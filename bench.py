@@ -51,6 +51,16 @@ def parse():
     return ap.parse_args()
 
 
+def pct(sorted_vals, q):
+    """The q-th percentile of an ascending list (linear interpolation)."""
+    if len(sorted_vals) == 1:
+        return sorted_vals[0]
+    pos = (len(sorted_vals) - 1) * q / 100.0
+    i = int(pos)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (pos - i)
+
+
 def verify_bytes(B, L, V, esz=2, redraws=None):
     """Algorithmic bytes of block verification: both logit arrays once, the redraw row pair
     of each sequence that redraws, tokens, uniforms and outputs."""
@@ -173,6 +183,19 @@ def main():
         gemm_achieved, gemm_peak, gemm_unit = gemm_bytes / gemm_s / 1e9, PEAK_HBM_GBS, "GB/s"
     digest = source_digest("gemm.hip")
     traffic = committed_traffic("gated_gemm", digest)
+    # Per projection launch of a layer (the stack's order: q|k|v, o, gate|up
+    # with SwiGLU, down), over the 32 layers of the bracketed step: median and
+    # p10 / p90 time, and the algorithmic rate at the median.
+    per_launch = {}
+    kinds = ("q|k|v", "o", "gate|up", "down")
+    if n_gemm % len(kinds) == 0:
+        for j, kind in enumerate(kinds):
+            evs = gemm_events[j::len(kinds)]
+            ts = sorted(ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs)
+            med = pct(ts, 50)
+            per_launch[kind] = {"median_us": round(med, 2), "p10_us": round(pct(ts, 10), 2),
+                                "p90_us": round(pct(ts, 90), 2),
+                                "tflops_at_median": round(evs[0][2] / med / 1e6, 1)}
 
     verify_early, lm_head, tree = None, None, None
     if not args.no_extras:
@@ -201,6 +224,7 @@ def main():
         tree = tree_measure(uno, sdev, torch, B, V, T, wl.seed, dev)
 
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
+    v_us = sorted(a.elapsed_time(b) * 1e3 for a, b, _ in verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
     v_gbs = verify_bytes(B, L, V, 2, redraws) / vt / 1e9
 
@@ -241,6 +265,7 @@ def main():
             "avg_launch_us": round(gemm_s / n_gemm * 1e6, 3),
             "algorithmic_gflop_per_launch": round(gemm_flop / n_gemm / 1e9, 4),
             "algorithmic_mb_per_launch": round(gemm_bytes / n_gemm / 1e6, 3),
+            "per_launch": per_launch,
         },
         "verify_roofline": {
             "bound": "hbm",
@@ -249,6 +274,9 @@ def main():
             "unit": "GB/s",
             "frac": round(v_gbs / PEAK_HBM_GBS, 4),
             "us_per_call": round(vt * 1e6, 3),
+            "median_us": round(pct(v_us, 50), 2),
+            "p10_us": round(pct(v_us, 10), 2),
+            "p90_us": round(pct(v_us, 90), 2),
             "redraws_per_call": redraws,
             "early_exit": verify_early,
         },

@@ -522,11 +522,19 @@ void gated_gemm_kernel(const GemmKArgs a) {
         trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - info.Pv) * ldt2;
         brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2;
     }
-    // output group of this tile (tiles never straddle groups); its draft rows
-    // read T from column grp.g * r on
+    // output groups of this tile: its columns may fall in groups g_s .. g_s +
+    // nsl - 1 (group ends are multiples of 8); its draft rows read T from
+    // column g_s * r on, one slice of r columns per group
     const GroupRef grp = find_group(a.out, n0);
     const int32_t g_s = __builtin_amdgcn_readfirstlane(grp.g);
+    const int32_t nsl = __builtin_amdgcn_readfirstlane(
+        find_group(a.out, std::min<int64_t>(a.N, n0 + BN) - 1).g - grp.g + 1);
     const uint32_t t_skip = static_cast<uint32_t>(g_s) * static_cast<uint32_t>(a.r) * 2u;  // bytes
+    // slice (group - g_s) of the B rows this lane copies
+    int32_t bsl[BQ];
+#pragma unroll
+    for (int qb = 0; qb < BQ; ++qb)
+        bsl[qb] = nsl > 1 ? find_group(a.out, n0 + wave * (BN / C::NWAVES) + qb * RB + lrow).g - g_s : 0;
     // source bases and byte ranges (scalars; the descriptors are built per copy)
     // (every scalar the copy lambdas use is a plain value, never a field read
     // through a captured reference, so the compiler keeps them in registers)
@@ -548,7 +556,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
     const bool tile_has_draft =
         !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
     const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
-    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? (a.r + kBK - 1) / kBK : 0);
+    const int32_t spr_s = __builtin_amdgcn_readfirstlane((a.r + kBK - 1) / kBK);  // extension stages per slice
+    const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? nsl * spr_s : 0);
     const int nk_main_s = __builtin_amdgcn_readfirstlane(nk_main);
     const int nk_s = __builtin_amdgcn_readfirstlane(nk_main + nk_ext);
     const int32_t kb_s = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(kb));
@@ -566,7 +575,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
     struct StageSrc {
         uint64_t abase, bbase;    // A and B source addresses
         uint32_t arange, brange;  // their byte ranges (0 past the last stage)
-        uint32_t kbytes;          // byte offset of the stage's first K within a row
+        uint32_t kbytes;          // byte offset of the stage's first K within an A row
+        uint32_t kbytes_b;        // ... within a B row (extension: within the slice)
+        int32_t slice;            // extension: group slice of the stage (B rows of other groups read zeros)
         uint32_t krem;            // K columns left in the stage's source (>= kBK: none masked)
         uint32_t lds;             // LDS byte address of the stage's A buffer
         uint32_t ldsb;            // ... and of its B buffer
@@ -576,14 +587,18 @@ void gated_gemm_kernel(const GemmKArgs a) {
         StageSrc ss;
         const bool e = it >= nk_main_s;
         const bool live = it < nk_s;
-        const int32_t kfirst = e ? (it - nk_main_s) * kBK : kb_s + it * kBK;
+        const int32_t ei = it - nk_main_s;
+        const int32_t sl = e ? ei / spr_s : 0;
+        const int32_t kfirst = e ? (ei - sl * spr_s) * kBK : kb_s + it * kBK;
         const int32_t klim = e ? r_s : ke_s;
         ss.ext = __builtin_amdgcn_readfirstlane(e ? 1u : 0u);
         ss.abase = e ? t_base : x_base;
         ss.bbase = e ? b_base : w_base;
         ss.arange = __builtin_amdgcn_readfirstlane(live ? (e ? t_range : x_range) : 0u);
         ss.brange = __builtin_amdgcn_readfirstlane(live ? (e ? b_range : w_range) : 0u);
-        ss.kbytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kfirst * 2));
+        ss.kbytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((sl * r_s + kfirst) * 2));
+        ss.kbytes_b = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kfirst * 2));
+        ss.slice = __builtin_amdgcn_readfirstlane(sl);
         ss.krem = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(klim > kfirst ? klim - kfirst : 0));
         if constexpr (C::SPLIT) {
             ss.lds = __builtin_amdgcn_readfirstlane(lds_base + static_cast<uint32_t>((it % kNBUF) * BM * kBK * 2));
@@ -607,8 +622,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
             const uint32_t lb = ss.ldsb + static_cast<uint32_t>(((wave * (BN / C::NWAVES) + qb * RB) * kBK) * 2);
             const uint32_t off_w = wrow0 + static_cast<uint32_t>(qb * RB) * ldw2;
             const uint32_t off_b = brow0 + static_cast<uint32_t>(qb * RB) * ldb2;
-            uint32_t off = (ss.ext ? off_b : off_w) + kcB[qb & 1] + ss.kbytes;
+            uint32_t off = (ss.ext ? off_b : off_w) + kcB[qb & 1] + ss.kbytes_b;
             if (kcolB[qb & 1] >= ss.krem) off = kOOB;
+            if (ss.ext && bsl[qb] != ss.slice) off = kOOB;  // a row of another group's slice
             dma16(lb, off, make_rsrc(reinterpret_cast<const void*>(ss.bbase), ss.brange));
         }
     };
@@ -931,12 +947,13 @@ void gated_gemm_kernel(const GemmKArgs a) {
             }
         }
         const bool accumulate = a.epi == kEpiAccumulate;
+        const GroupRef lg = find_group(a.out, n);  // this lane's 8 columns lie in one group
 #pragma unroll 8
         for (int r = lane_row0; r < C::WM; r += RPI) {
             const int32_t orow = s_orow[wm * C::WM + r];
-            if (orow < 0 || n >= gend) continue;
+            if (orow < 0 || n >= lg.end) continue;
             const int pc = c * 8 < C::SWZ ? c ^ (((r >> 2) & 1) << 2) : c;
-            uint4* dst = reinterpret_cast<uint4*>(gy + static_cast<int64_t>(orow) * gldy + (n - gstart));
+            uint4* dst = reinterpret_cast<uint4*>(lg.y + static_cast<int64_t>(orow) * lg.ldy + (n - lg.start));
             const uint4 v = *reinterpret_cast<const uint4*>(&st[r * C::WN + pc * 8]);
             *dst = accumulate ? add8_bf16(*dst, v) : v;
         }
@@ -955,8 +972,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
-                    if (n < gend) {
-                        uint16_t* dst = gy + orow * gldy + (n - gstart);
+                    const GroupRef eg = find_group(a.out, n);
+                    if (n < eg.end) {
+                        uint16_t* dst = eg.y + orow * eg.ldy + (n - eg.start);
                         const uint32_t yb = f32_to_bf16_bits(acc[i][j][v] * a.alpha);
                         *dst = static_cast<uint16_t>(
                             a.epi == kEpiAccumulate ? f32_to_bf16_bits(bf16_bits_to_f32(*dst) + bf16_bits_to_f32(yb))
@@ -1151,7 +1169,7 @@ bool tile_supported(Tile t) {
            (t.bm == 256 && t.bn == 128) || (t.bm == 256 && t.bn == 256);
 }
 
-// Output groups: every group end but the last must fall on a tile edge.
+// Output groups: a group end inside a tile must be a multiple of 8.
 struct GroupSpec {
     int32_t n;
     int64_t end[kMaxGroups];
@@ -1165,8 +1183,10 @@ GroupSpec one_group(int64_t N) {
 }
 
 bool tile_fits(Tile t, const GroupSpec& gs) {
+    // a group end inside a tile must be a multiple of 8 (the tile's 16-byte
+    // stores then lie in one group each)
     for (int i = 0; i + 1 < gs.n; ++i)
-        if (gs.end[i] % t.bn != 0) return false;
+        if (gs.end[i] % t.bn != 0 && gs.end[i] % 8 != 0) return false;
     return true;
 }
 

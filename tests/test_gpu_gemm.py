@@ -293,6 +293,24 @@ def _group_inputs(M, K, group_n, r, seed, gate):
 @pytest.mark.gpu
 @pytest.mark.parametrize("M,K,group_n,r", GROUPED)
 def test_grouped_gemm_vs_oracle(M, K, group_n, r):
+    _grouped_case(M, K, group_n, r)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tile,M,K,group_n,r", [
+    ("128x192b4kg2", 64, 4096, (4096, 1024, 1024), 128),  # q | k | v: tiles across 4096 and 5120
+    ("128x192b3", 96, 512, (128, 128, 128, 128), 16),     # tiles over two groups; r not a stage multiple
+    ("256x256w8k64r3", 96, 512, (128, 128, 128, 128), 64),  # split ring, two groups per tile
+    ("128x128b4kg2", 75, 1000, (256, 128, 72), 64),       # group ends on tile edges (no straddle)
+])
+def test_grouped_gemm_tiles_across_groups(tile, M, K, group_n, r, monkeypatch):
+    """Tiles whose columns fall in several output groups: each group's columns
+    take their own slice of T (the other slices read zero B rows)."""
+    monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    _grouped_case(M, K, group_n, r, check_single=False)
+
+
+def _grouped_case(M, K, group_n, r, check_single=True):
     rng = np.random.default_rng(M + K)
     gate = (rng.random(M) < 0.5).astype(np.uint8)
     x, groups = _group_inputs(M, K, group_n, r, 40 + M, gate)
@@ -314,7 +332,7 @@ def test_grouped_gemm_vs_oracle(M, K, group_n, r):
     outs0 = [to_host(o) for o in uno.gated_gemm_grouped(xd, w, t0, b, plan0, group_n)]
     for g in range(len(group_n)):
         assert np.array_equal(outs[g][gate == 0], outs0[g][gate == 0])
-    if K == 256:
+    if K == 256 and check_single:
         # no split anywhere: each group equals its own ungrouped call bitwise
         for g, (wg, ag, bg) in enumerate(groups):
             tg = uno.lora_down(xd, to_dev(ag, "bf16"), plan, 2.0)
