@@ -125,7 +125,8 @@ def test_deterministic_repeat():
 @pytest.mark.parametrize("tile", ["64x128", "128x128", "128x128b3", "128x128b4", "128x128b5", "128x128b4kg2", "128x256",
                                   "256x128", "256x128k64b3kg2", "256x256", "256x192w8k64r3",
                                   "256x256k64", "256x256k64r3", "256x256w8", "256x256w8k64", "256x256w8k64r3",
-                                  "256x256pp", "128x192b3", "128x192b4", "128x192b3kg2", "128x192b4kg2"])
+                                  "256x256pp", "128x192b3", "128x192b4", "128x192b3kg2", "128x192b4kg2",
+                                  "64x256", "64x256b3"])
 def test_every_tile_shape_ragged(tile, monkeypatch):
     """Each workgroup tile on a problem ragged in M, N and K, through the split steps."""
     monkeypatch.setenv("UNO_GEMM_TILE", tile)
@@ -197,6 +198,8 @@ EPILOGUE = [  # M, K, N (per projection), forced tile or None, forced split or N
     (32, 256, 256, None, None),          # few rows: the 128 x 256 tile (SwiGLU) / 64 x 128 (residual)
     (96, 512, 768, "128x256", None),
     (300, 1000, 512, "256x256w8k64r3", None),  # split ring, ragged
+    (32, 1000, 768, "64x256b3", "3"),     # few rows, the weight-streaming tile, ragged K, split-K
+    (60, 512, 512, "64x256", None),       # two stage buffers, ragged M
 ]
 
 
