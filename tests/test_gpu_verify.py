@@ -56,6 +56,7 @@ CASES = [  # B, L, V, dtype, kind, sigma, T, bonus
     (64, 16, 2048, "bf16", "zipf", 0.5, 0.6, False),
     (5, 3, 1, "bf16", "normal", 1.0, 1.0, True),          # single-token vocabulary
     (300, 2, 17, "f32", "normal", 1.0, 2.0, False),       # many sequences, odd V
+    (3, 4, 300000, "bf16", "normal", 1.0, 1.0, True),     # rows past the one-workgroup tail's LDS staging
 ]
 
 
