@@ -49,6 +49,7 @@ CASES = [  # B, L, V, K, has_bonus, T
     (2, 16, 4096, 512, True, 1.0),
     (1, 1, 256, 64, False, 1.3),     # one position, one tile
     (37, 4, 600, 64, True, 1.0),     # many sequences
+    (2, 3, 262400, 64, True, 1.0),   # redraw rows past the one-workgroup tail's LDS staging
 ]
 
 
