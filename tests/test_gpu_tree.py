@@ -89,6 +89,7 @@ CASES = [  # B, K, D, V, dtype, T
     (3, 3, 4, 520, "bf16", 1.3),     # 121 nodes
     (40, 1, 6, 64, "bf16", 1.0),     # chains
     (6, 8, 1, 2048, "f32", 1.0),     # one level, eight siblings
+    (2, 2, 2, 300000, "bf16", 1.0),  # rows past the walk's LDS staging: every node drawn either way
 ]
 
 
