@@ -13,7 +13,8 @@ from synthetic import device as sdev, verify_inputs
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("B,L,V,dtype,T", [(3, 5, 999, "f32", 1.0), (8, 4, 4096, "bf16", 0.6),
-                                           (2, 3, 1, "bf16", 1.0), (50, 70, 64, "f32", 1.0)])
+                                           (2, 3, 1, "bf16", 1.0), (50, 70, 64, "f32", 1.0),
+                                           (2, 2, 300000, "bf16", 1.0)])  # segment sums past the LDS staging
 def test_draft_sample_small(B, L, V, dtype, T):
     _, d = verify_inputs(B, L, V, seed=B + L + V, dtype=dtype)
     u = oracle.philox_uniforms(0, 1, 0, B * L).reshape(B, L)
