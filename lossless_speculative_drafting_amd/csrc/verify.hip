@@ -1020,11 +1020,15 @@ struct Plan {
 };
 
 constexpr int64_t kTargetBlocks = 2048;
+constexpr int64_t kMaxStatChunks = 16;
 
 Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
     Plan p{};
     p.rows = B * rows_per_seq;
-    const int64_t max_c1 = (V + kStatTile - 1) / kStatTile;
+    // (at most kMaxStatChunks chunks per row: the decision merges a row's
+    // chunks one after another in fp64, about 0.25 us per chunk, which at one
+    // sequence cost more than the wider grid saved)
+    const int64_t max_c1 = std::min<int64_t>(kMaxStatChunks, (V + kStatTile - 1) / kStatTile);
     int64_t c1 = p.rows > 0 ? (kTargetBlocks + p.rows - 1) / p.rows : 1;
     c1 = std::max<int64_t>(1, std::min(c1, max_c1));
     int64_t chunk = (V + c1 - 1) / c1;
