@@ -89,13 +89,20 @@ def inverse_cdf(weights, u):
     return k.astype(np.int64)
 
 
-def residual_weights(logp_row, logq_row):
-    """max(0, p - q) over the vocabulary, or p itself if that has zero mass."""
+def residual_weights(logp_row, logq_row, with_fallback=False):
+    """max(0, p - q) over the vocabulary, or p itself if that has zero mass.
+
+    The redraw law after a rejection (step 4 above).  logp_row, logq_row:
+    [..., V] log-probabilities.  With with_fallback, also returns a bool
+    array [...] that is True where the residual had zero mass and p was
+    taken instead.
+    """
     p = np.exp(np.asarray(logp_row, dtype=np.float64))
     q = np.exp(np.asarray(logq_row, dtype=np.float64))
     r = np.maximum(0.0, p - q)
     zero = np.sum(r, axis=-1, keepdims=True) == 0.0
-    return np.where(zero, p, r)
+    w = np.where(zero, p, r)
+    return (w, zero[..., 0]) if with_fallback else w
 
 
 def _broadcast_lead(arr, B):
@@ -158,13 +165,7 @@ def block_verify(target_logits, draft_logits, draft_tokens, uniforms,
     rej = np.nonzero((n_acc < L) & valid)[0]
     if rej.size:
         j = n_acc[rej]
-        lp_j = lp[bz[rej], j, :]
-        lq_j = lq[bd[rej], j, :]
-        p = np.exp(lp_j)
-        q = np.exp(lq_j)
-        r = np.maximum(0.0, p - q)
-        zero = np.sum(r, axis=-1) == 0.0
-        r[zero] = p[zero]
+        r, zero = residual_weights(lp[bz[rej], j, :], lq[bd[rej], j, :], with_fallback=True)
         out[rej, j] = inverse_cdf(r, u[rej, L])
         mode[rej] = np.where(zero, 2, 1)
         row[rej] = j

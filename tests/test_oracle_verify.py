@@ -69,6 +69,45 @@ def test_hand_derived_cases(repo_root):
         assert res["n_emitted"][0] == case["n_emitted"], case["name"]
 
 
+def _residual_golden_failures(fn, repo_root):
+    """Hand-derived residual laws (tests/golden/verify_hand.json) that fn gets wrong."""
+    with open(os.path.join(repo_root, "tests", "golden", "verify_hand.json")) as f:
+        g = json.load(f)
+    fails = []
+    for case in g["residual_cases"]:
+        with np.errstate(divide="ignore"):
+            lp = np.log(np.array(case["p"], float))
+            lq = np.log(np.array(case["q"], float))
+        w, fb = fn(lp, lq, with_fallback=True)
+        if not (np.allclose(w, case["residual"], rtol=0, atol=1e-15) and bool(fb) == case["fallback"]):
+            fails.append(case["name"])
+        if not np.allclose(fn(lp, lq), case["residual"], rtol=0, atol=1e-15):
+            fails.append(case["name"] + " (weights only)")
+    return fails
+
+
+def test_residual_weights_hand_derived(repo_root):
+    assert _residual_golden_failures(ov.residual_weights, repo_root) == []
+
+
+def test_residual_pins_catch_planted_mistakes(repo_root):
+    """Plausible mistakes in the residual (sign, |p - q|, no clamp, no fallback) each fail a pin."""
+    def plant(kind):
+        def fn(lp, lq, with_fallback=False):
+            p, q = np.exp(lp), np.exp(lq)
+            r = {"q-p": np.maximum(0.0, q - p), "abs": np.abs(p - q),
+                 "nofallback": np.maximum(0.0, p - q), "nomax": p - q}[kind]
+            zero = np.sum(r, axis=-1, keepdims=True) == 0.0
+            if kind == "nofallback":
+                w = r
+            else:
+                w = np.where(zero, p, r)
+            return (w, zero[..., 0]) if with_fallback else w
+        return fn
+    for kind in ("q-p", "abs", "nofallback", "nomax"):
+        assert _residual_golden_failures(plant(kind), repo_root), kind
+
+
 # ---------------------------------------------------------------- exact integration
 
 
