@@ -107,9 +107,13 @@ uno_status uno_philox_uniforms(uint64_t seed, uint64_t stream_id, uint64_t offse
  * Domain: M >= 0 (M = 0 is a no-op), N >= 1, K >= 1, 1 <= r <= 256 and scale
  * finite.  UNO_BF16 additionally needs K and r multiples of 8, 16-byte
  * aligned tensors, and every operand under 2 GiB (M*K, N*K < 2^30 elements).
- * A gate byte other than 0/1 is treated as 1.
+ * Gate bytes other than 0 and 1 are a caller error that never passes
+ * silently: such a row runs neither pathway, its output row is written as
+ * NaN (every column), and the row plan at the start of the workspace counts
+ * it -- uno_row_plan_gate_errors(workspace, ...) reports the count and the
+ * first such row.
  * workspace: device memory of at least uno_gated_lora_workspace_size() bytes
- * (256-byte aligned).
+ * (256-byte aligned); it begins with the call's row plan (both dtypes).
  *
  * For UNO_BF16 the call runs three steps, also exported below so that many
  * projections over the same rows (a layer stack) can plan the rows once:
@@ -127,10 +131,22 @@ uno_status uno_gated_lora_fwd(const void* x, const void* w, const void* lora_a,
 
 /* Row plan: opaque device buffer of uno_row_plan_size(M) bytes (256-byte
  * aligned) written by uno_segment_rows from gate [M] (device uint8).  It stays
- * valid while the gate values are unchanged. */
+ * valid while the gate values are unchanged.  Rows whose gate byte is neither
+ * 0 nor 1 are kept out of both pathways and counted in the plan; every gated
+ * GEMM launched with the plan writes NaN into their output rows. */
 size_t uno_row_plan_size(int64_t M);
 uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size_t row_plan_bytes,
                             hipStream_t stream);
+
+/* Gate check of a row plan ("Two Decoupled Weight Sets" on the
+ * aifromscratch.in page: a token runs the draft pathway or the verification
+ * pathway, nothing else).  Enqueues on `stream` a copy into out (device
+ * int32[2]) of {number of rows whose gate byte was neither 0 nor 1, the first
+ * such row or -1}, as seen by the uno_segment_rows (or uno_gated_lora_fwd,
+ * whose workspace starts with its plan) that last wrote row_plan with M >= 1.
+ * row_plan 256-byte aligned, out 4-byte aligned; null pointers are
+ * UNO_ERR_INVALID_ARG. */
+uno_status uno_row_plan_gate_errors(const void* row_plan, int32_t* out, hipStream_t stream);
 
 /* LoRA down-projection on draft rows (bf16): t receives scale * (x A) for the
  * draft rows in plan order, zero rows for padding; t is a device buffer of

@@ -33,6 +33,7 @@ SIGNATURES = {
                                       _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_size, _c_ptr]),
     "uno_row_plan_size": (_c_size, [_c_int64]),
     "uno_segment_rows": (_c_int32, [_c_ptr, _c_int64, _c_ptr, _c_size, _c_ptr]),
+    "uno_row_plan_gate_errors": (_c_int32, [_c_ptr, _c_ptr, _c_ptr]),
     "uno_lora_t_size": (_c_size, [_c_int64, _c_int32]),
     "uno_lora_down_workspace_size": (_c_size, [_c_int64, _c_int64, _c_int32]),
     "uno_lora_down": (_c_int32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int64, _c_int64, _c_int32, _c_float, _c_ptr,
@@ -137,28 +138,38 @@ def _need_cuda(*ts):
 
 
 class Workspace:
-    """A grow-only device byte buffer reused across calls on one stream."""
+    """A grow-only device byte buffer reused across calls.
+
+    Calls that share a Workspace must not overlap in time (the library's
+    rule for any workspace).  The buffer is marked as used on the stream of
+    each call, so that when it grows the caching allocator does not hand the
+    old buffer out again while work on that stream may still read it.
+    """
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes):
+    def get(self, nbytes, stream=None):
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device or "cuda")
+        if stream is not None:
+            self.buf.record_stream(stream)
         return self.buf
 
 
 _default_ws = {}
 
 
-def _workspace(ws, nbytes, device):
+def _workspace(ws, nbytes, device, stream=None):
+    """The caller's workspace, or a default one per (device, stream)."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
     if ws is None:
-        key = (device.index if device.index is not None else torch.cuda.current_device())
+        key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
         ws = _default_ws.setdefault(key, Workspace(device))
-    return ws.get(nbytes)
+    return ws.get(nbytes, s)
 
 
 # ------------------------------------------------------------------ Philox
@@ -180,8 +191,14 @@ def gated_lora_workspace_size(M, N, K, r, dtype):
     return int(_lib.uno_gated_lora_workspace_size(M, N, K, r, _dtype_code(dtype)))
 
 
-def gated_lora_fwd(x, w, lora_a, lora_b, gate, scale=2.0, out=None, workspace=None, stream=None):
-    """y = x W_AR + gate * scale * (x A) B with storage w [N,K], lora_a [r,K], lora_b [N,r]."""
+def gated_lora_fwd(x, w, lora_a, lora_b, gate, scale=2.0, out=None, workspace=None, stream=None,
+                   gate_errors=None):
+    """y = x W_AR + gate * scale * (x A) B with storage w [N,K], lora_a [r,K], lora_b [N,r].
+
+    Rows whose gate byte is neither 0 nor 1 come out as NaN; with
+    gate_errors (a device int32 tensor of 2 elements) the call also writes
+    {number of such rows, first such row or -1} there.
+    """
     _need_cuda(x, w, lora_a, lora_b, gate)
     M, K = x.shape
     N = w.shape[0]
@@ -197,9 +214,19 @@ def gated_lora_fwd(x, w, lora_a, lora_b, gate, scale=2.0, out=None, workspace=No
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     _need_cuda(out)
     need = int(_lib.uno_gated_lora_workspace_size(M, N, K, r, dt))
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_gated_lora_fwd(_ptr(x), _ptr(w), _ptr(lora_a), _ptr(lora_b), _ptr(gate), _ptr(out),
                                    M, N, K, r, float(scale), dt, _ptr(ws), need, _stream(stream)))
+    if gate_errors is not None:
+        _gate_errors_into(ws, gate_errors, stream)
+    return out
+
+
+def _gate_errors_into(plan_buf, out, stream):
+    _need_cuda(out)
+    if out.dtype != torch.int32 or out.numel() < 2:
+        raise ValueError("gate_errors must be a device int32 tensor of 2 elements")
+    _check(_lib.uno_row_plan_gate_errors(_ptr(plan_buf), _ptr(out), _stream(stream)))
     return out
 
 
@@ -216,6 +243,12 @@ class RowPlan:
         self.buf = torch.empty(max(self.nbytes, 256), dtype=torch.uint8, device=gate.device)
         _check(_lib.uno_segment_rows(_ptr(gate), self.M, _ptr(self.buf), self.nbytes, _stream(stream)))
 
+    def gate_errors(self, out=None, stream=None):
+        """Device int32 [2]: rows whose gate byte is neither 0 nor 1, and the first such row (-1 if none)."""
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.buf.device)
+        return _gate_errors_into(self.buf, out, stream)
+
 
 def lora_t_size(M, r):
     return int(_lib.uno_lora_t_size(M, r))
@@ -231,7 +264,7 @@ def lora_down(x, lora_a, plan, scale=2.0, t=None, workspace=None, stream=None):
     if t is None:
         t = torch.empty(lora_t_size(M, r) // 2, dtype=torch.bfloat16, device=x.device)
     need = int(_lib.uno_lora_down_workspace_size(M, K, r))
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_lora_down(_ptr(x), _ptr(lora_a), _ptr(plan.buf), _ptr(t), M, K, r, float(scale), _ptr(ws), need,
                               _stream(stream)))
     return t
@@ -250,7 +283,7 @@ def gated_gemm(x, w, t, lora_b, plan, out=None, workspace=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
     need = int(_lib.uno_gated_gemm_workspace_size(M, N, K, r))
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_gated_gemm(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), _ptr(out), M, N, K, r,
                                _ptr(ws), need, _stream(stream)))
     return out
@@ -280,7 +313,7 @@ def gated_gemm_grouped(x, w, t, lora_b, plan, group_n, outs=None, workspace=None
     ns = (ctypes.c_int64 * G)(*group_n)
     ys = (ctypes.c_void_p * G)(*[_ptr(o) for o in outs])
     need = int(_lib.uno_gated_gemm_grouped_workspace_size(M, K, r, ns, G))  # 0 also on bad shapes: the call reports those
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_gated_gemm_grouped(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), ys, ns, G, M, K, r,
                                        _ptr(ws), need, _stream(stream)))
     return outs
@@ -297,7 +330,7 @@ def gated_gemm_residual(x, w, t, lora_b, plan, y, workspace=None, stream=None):
     if t.numel() * t.element_size() < lora_t_size(M, r):
         raise ValueError("t buffer too small")
     need = int(_lib.uno_gated_gemm_residual_workspace_size(M, N, K, r))
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_gated_gemm_residual(_ptr(x), _ptr(w), _ptr(t), _ptr(lora_b), _ptr(plan.buf), _ptr(y), M, N, K,
                                         r, _ptr(ws), need, _stream(stream)))
     return y
@@ -333,7 +366,7 @@ def gated_gemm_swiglu(x, w_packed, t, b_packed, plan, out=None, workspace=None, 
     if out.shape != (M, Nh) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [M, N] tensor")
     need = int(_lib.uno_gated_gemm_swiglu_workspace_size(M, Nh, K, rt))
-    ws = _workspace(workspace, need, x.device)
+    ws = _workspace(workspace, need, x.device, stream)
     _check(_lib.uno_gated_gemm_swiglu(_ptr(x), _ptr(w_packed), _ptr(t), _ptr(b_packed), _ptr(plan.buf), _ptr(out), M,
                                       Nh, K, rt, _ptr(ws), need, _stream(stream)))
     return out
@@ -375,7 +408,7 @@ def tree_verify(node_logits, parents, tokens, uniforms, temperature=1.0, outputs
                    torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
     n_acc, out_tok, n_emit, last = outputs
     need = int(_lib.uno_tree_verify_workspace_size(B, N, V))
-    ws = _workspace(workspace, need, dev)
+    ws = _workspace(workspace, need, dev, stream)
     _check(_lib.uno_tree_verify(_ptr(node_logits), N * V, _ptr(parents), _ptr(tokens), _ptr(uniforms), int(B), int(N),
                                 int(V), float(temperature), _dtype_code(node_logits.dtype), _ptr(n_acc), _ptr(out_tok),
                                 _ptr(n_emit), _ptr(last), _ptr(ws), need, _stream(stream)))
@@ -419,7 +452,7 @@ def lm_head_verify(hidden, w_lm, draft_tokens, uniforms, temperature=1.0, has_bo
                    torch.empty(B, dtype=torch.int32, device=dev))
     n_acc, out_tok, n_emit = outputs
     need = int(_lib.uno_lm_head_verify_workspace_size(B, L, V, K, nb))
-    ws = _workspace(workspace, need, dev)
+    ws = _workspace(workspace, need, dev, stream)
     _check(_lib.uno_lm_head_verify(_ptr(hidden), _ptr(w_lm), int(B), int(L), int(V), int(K), nb, float(temperature),
                                    _ptr(draft_tokens), _ptr(uniforms), _ptr(n_acc), _ptr(out_tok), _ptr(n_emit),
                                    _ptr(logits), _ptr(ws), need, _stream(stream)))
@@ -465,14 +498,14 @@ def block_verify(target_logits, draft_logits, draft_tokens, uniforms, temperatur
     n_acc, out_tok, n_emit = outputs
     if early_chunk is None:
         need = int(_lib.uno_block_verify_workspace_size(B, L, V, nb))
-        ws = _workspace(workspace, need, dev)
+        ws = _workspace(workspace, need, dev, stream)
         _check(_lib.uno_block_verify(_ptr(target_logits), _ptr(draft_logits), int(target_seq_stride),
                                      int(draft_seq_stride), _ptr(draft_tokens), _ptr(uniforms), int(B), int(L),
                                      int(V), nb, float(temperature), _dtype_code(target_logits.dtype),
                                      _ptr(n_acc), _ptr(out_tok), _ptr(n_emit), _ptr(ws), need, _stream(stream)))
     else:
         need = int(_lib.uno_block_verify_early_workspace_size(B, L, V, nb))
-        ws = _workspace(workspace, need, dev)
+        ws = _workspace(workspace, need, dev, stream)
         _check(_lib.uno_block_verify_early(_ptr(target_logits), _ptr(draft_logits), int(target_seq_stride),
                                            int(draft_seq_stride), _ptr(draft_tokens), _ptr(uniforms), int(B),
                                            int(L), int(V), nb, float(temperature),
@@ -500,7 +533,7 @@ def draft_sample(draft_logits, uniforms, temperature=1.0, B=None, L=None, V=None
     if out is None:
         out = torch.empty((B, L), dtype=torch.int32, device=draft_logits.device)
     need = int(_lib.uno_draft_sample_workspace_size(B, L, V))
-    ws = _workspace(workspace, need, draft_logits.device)
+    ws = _workspace(workspace, need, draft_logits.device, stream)
     _check(_lib.uno_draft_sample(_ptr(draft_logits), int(seq_stride), _ptr(uniforms), int(B), int(L), int(V),
                                  float(temperature), _dtype_code(draft_logits.dtype), _ptr(out), _ptr(ws), need,
                                  _stream(stream)))

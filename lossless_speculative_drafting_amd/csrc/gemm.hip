@@ -54,16 +54,23 @@ constexpr uint32_t kOOB = 0x80000000u;       // buffer offset past every range: 
 constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 struct SegInfo {
-    int32_t Mv;      // verify rows
-    int32_t Md;      // draft rows
-    int32_t Pv;      // first permuted draft row (Mv rounded up to 32)
-    int32_t Md_pad;  // Md rounded up to 32
+    int32_t Mv;         // verify rows
+    int32_t Md;         // draft rows
+    int32_t Pv;         // first permuted draft row (Mv rounded up to 32)
+    int32_t Md_pad;     // Md rounded up to 32
+    int32_t Mb;         // rows whose gate byte is neither 0 nor 1 (in neither segment)
+    int32_t first_bad;  // the first such row, -1 if none
+    int32_t pad_[2];
 };
+static_assert(sizeof(SegInfo) == 32, "row plan header");
 
-// Row plan layout: SegInfo at byte 0, perm[rows_cap] at byte 256.
+// Row plan layout: SegInfo at byte 0, perm[rows_cap] at byte 256, then the
+// rows with an invalid gate byte, bad[M] (the first Mb entries used).
 constexpr size_t kPlanPermOffset = 256;
 
 int64_t rows_cap_for(int64_t M) { return (M + kRowAlign - 1) / kRowAlign * kRowAlign + kRowAlign; }
+
+__device__ __forceinline__ const int32_t* plan_bad_rows(const int32_t* perm, int64_t rows_cap) { return perm + rows_cap; }
 
 // ------------------------------------------------------------ segmentation
 constexpr int kSegThreads = 1024;
@@ -89,33 +96,50 @@ __device__ __forceinline__ int32_t block_excl_scan_i32(int32_t v, int32_t* sh, i
     return base + incl - v;
 }
 
+// Gate byte 1: draft row, 0: verify row.  Any other byte is a caller error:
+// the row joins neither segment (nothing is computed for it), it is listed
+// in the plan's bad-row list, whose length and first entry the header keeps,
+// and the GEMM writes NaN into its output row.
 __global__ __launch_bounds__(kSegThreads) void segment_rows_kernel(const uint8_t* __restrict__ gate,
                                                                    int64_t M, int64_t rows_cap,
                                                                    int32_t* __restrict__ perm,
                                                                    SegInfo* __restrict__ info) {
     __shared__ int32_t sh[kSegThreads / kWave];
+    __shared__ int32_t s_first_bad;
+    if (threadIdx.x == 0) s_first_bad = -1;  // (published by the scans' barriers)
     const int64_t per = (M + kSegThreads - 1) / kSegThreads;
     const int64_t r0 = std::min<int64_t>(M, static_cast<int64_t>(threadIdx.x) * per);
     const int64_t r1 = std::min<int64_t>(M, r0 + per);
-    int32_t nd = 0;
-    for (int64_t r = r0; r < r1; ++r) nd += gate[r] != 0;
-    const int32_t nv = static_cast<int32_t>(r1 - r0) - nd;
-    int32_t Md, Mv;
+    int32_t nd = 0, nb = 0;
+    for (int64_t r = r0; r < r1; ++r) {
+        const uint8_t g = gate[r];
+        nd += g == 1;
+        nb += g > 1;
+    }
+    const int32_t nv = static_cast<int32_t>(r1 - r0) - nd - nb;
+    int32_t Md, Mv, Mb;
     const int32_t dpos0 = block_excl_scan_i32(nd, sh, &Md);
     const int32_t vpos0 = block_excl_scan_i32(nv, sh, &Mv);
+    const int32_t bpos0 = block_excl_scan_i32(nb, sh, &Mb);
     const int32_t Pv = (Mv + kRowAlign - 1) / kRowAlign * kRowAlign;
     const int32_t Md_pad = (Md + kRowAlign - 1) / kRowAlign * kRowAlign;
-    int32_t vp = vpos0, dp = Pv + dpos0;
+    int32_t* const bad = perm + rows_cap;
+    int32_t vp = vpos0, dp = Pv + dpos0, bp = bpos0;
     for (int64_t r = r0; r < r1; ++r) {
-        if (gate[r] != 0) {
+        const uint8_t g = gate[r];
+        if (g == 1) {
             perm[dp++] = static_cast<int32_t>(r);
-        } else {
+        } else if (g == 0) {
             perm[vp++] = static_cast<int32_t>(r);
+        } else {
+            if (bp == 0) s_first_bad = static_cast<int32_t>(r);  // rows are listed in order
+            bad[bp++] = static_cast<int32_t>(r);
         }
     }
     for (int64_t p = Mv + threadIdx.x; p < Pv; p += kSegThreads) perm[p] = -1;
     for (int64_t p = static_cast<int64_t>(Pv) + Md + threadIdx.x; p < rows_cap; p += kSegThreads) perm[p] = -1;
-    if (threadIdx.x == 0) *info = SegInfo{Mv, Md, Pv, Md_pad};
+    __syncthreads();
+    if (threadIdx.x == 0) *info = SegInfo{Mv, Md, Pv, Md_pad, Mb, s_first_bad, {0, 0}};
 }
 
 // ------------------------------------------------------------ MFMA GEMM
@@ -414,6 +438,32 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
     }
 }
 
+// Rows with an invalid gate byte get NaN in every output column: the tile
+// (m tile mt, n tile at n0) writes entries [mt BM, mt BM + BM) of the plan's
+// bad-row list over its own columns (SwiGLU: the act columns of its gate and
+// up blocks).  A cold path: scalar stores.
+template <int BM, int BN, int THREADS>
+__device__ void poison_bad_rows(const GemmKArgs& a, int64_t m0, int64_t n0, int32_t Mb) {
+    constexpr uint16_t kNaN = 0x7FC0;  // bf16 quiet NaN
+    const int32_t* bad = a.perm + a.rows_cap;
+    const bool swiglu = a.epi == kEpiSwiglu;
+    const int64_t c0 = swiglu ? n0 / 2 : n0;
+    const int64_t cend = std::min<int64_t>(swiglu ? a.N / 2 : a.N, c0 + (swiglu ? BN / 2 : BN));
+    const int64_t rows = std::min<int64_t>(BM, Mb - m0);
+    const int64_t cols = cend - c0;
+    for (int64_t e = threadIdx.x; e < rows * cols; e += THREADS) {
+        const int64_t i = e / cols;
+        const int64_t col = c0 + (e - i * cols);
+        const int64_t orow = bad[m0 + i];
+        if (swiglu) {
+            a.out.y[0][orow * a.out.ldy[0] + col] = kNaN;
+        } else {
+            const GroupRef g = find_group(a.out, col);
+            g.y[orow * g.ldy + (col - g.start)] = kNaN;
+        }
+    }
+}
+
 template <int BM, int BN, int WGM, int WGN, int KB, bool TMODE, bool PP, int NB, int NBB = 0, int KG = 1>
 __global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::THREADS),
                              (TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::OCC))
@@ -450,6 +500,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
     info.Md_pad = __builtin_amdgcn_readfirstlane(info.Md_pad);
     const int64_t m0 = static_cast<int64_t>(mt) * BM;
     const int64_t n0 = static_cast<int64_t>(nt) * BN;
+    if constexpr (!TMODE) {
+        const int32_t Mb = __builtin_amdgcn_readfirstlane(info.Mb);
+        if (z == 0 && m0 < Mb) poison_bad_rows<BM, BN, C::THREADS>(a, m0, n0, Mb);
+    }
     const int64_t rows_valid = TMODE ? info.Md_pad : static_cast<int64_t>(info.Pv) + info.Md_pad;
     if (m0 >= rows_valid) return;  // uniform for the workgroup, before any barrier
 
@@ -1050,7 +1104,7 @@ __global__ __launch_bounds__(256) void lora_t_f32_kernel(const float* __restrict
     if (e >= M * r) return;
     const int64_t m = e / r;
     const int64_t j = e - m * r;
-    if (gate[m] == 0) return;
+    if (gate[m] != 1) return;
     float s = 0.f;
     for (int64_t k = 0; k < K; ++k) s = fmaf(x[m * K + k], la[j * K + k], s);
     t[m * r + j] = scale * s;
@@ -1064,9 +1118,13 @@ __global__ __launch_bounds__(256) void gated_gemm_f32_kernel(const float* __rest
     if (e >= M * N) return;
     const int64_t m = e / N;
     const int64_t n = e - m * N;
+    if (gate[m] > 1) {  // invalid gate byte: NaN row (the row plan counts it)
+        y[m * N + n] = __builtin_nanf("");
+        return;
+    }
     float s = 0.f;
     for (int64_t k = 0; k < K; ++k) s = fmaf(x[m * K + k], w[n * K + k], s);
-    if (gate[m] != 0) {
+    if (gate[m] == 1) {
         for (int32_t j = 0; j < r; ++j) s = fmaf(t[m * r + j], lb[n * r + j], s);
     }
     y[m * N + n] = s;
@@ -1221,10 +1279,14 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 }
 
 // bn256: only tiles 256 columns wide (the SwiGLU epilogue pairs columns c and
-// c + 128 of a tile).
-Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256) {
+// c + 128 of a tile).  single_kg: only tiles with one K group, whose sums all
+// run over K in the same order (tiles with two K groups add their even and
+// odd sub-steps apart, so their bits differ).
+Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256, bool single_kg = false) {
     const Tile forced = env_tile();
-    if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256)) return forced;
+    if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256) &&
+        (!single_kg || forced.kg == 1))
+        return forced;
     if (forced.bm > 0 && !tile_supported(forced)) {
         static bool warned = false;  // (tuning aid: say once that the forced tile is not one of ours)
         if (!warned) fprintf(stderr, "libuno: UNO_GEMM_TILE=%s is not a supported tile; planning instead\n",
@@ -1237,7 +1299,7 @@ Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bo
     Tile best = bn256 ? Tile{128, 256, 4, false, 32} : Tile{64, 128, 4, false, 64};
     double best_us = 1e300;
     for (const Tile& t : cands) {
-        if (!tile_fits(t, gs) || (bn256 && t.bn != 256)) continue;
+        if (!tile_fits(t, gs) || (bn256 && t.bn != 256) || (single_kg && t.kg != 1)) continue;
         double us = 0;
         choose_split_for(t, rows_cap, N, K, &us);
         if (us < best_us * 0.999) {
@@ -1256,7 +1318,10 @@ struct GemmPlan {
     size_t partial_bytes;
 };
 
-// one_pass: no split of K (the statistics epilogue needs whole sums).
+// one_pass: no split of K and one K group (the statistics epilogue needs
+// whole sums, and the LM head's recompute of the redraw rows must give the
+// bits of its first pass: every one-group tile family adds the same K slices
+// in the same order).
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec& gs, bool bn256 = false,
                    bool one_pass = false) {
     GemmPlan p{};
@@ -1269,7 +1334,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     // 64 x 128 tiles, measured faster there than 128 x 128 by 10-30%.
     // (four stage buffers: the prologue puts three stages in flight at once,
     // measured 3-10% faster than two)
-    p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs, bn256);
+    p.tile = tmode ? Tile{64, 128, 4, false, 64, 4} : choose_tile(rows_model, N, K, gs, bn256, one_pass);
     if (const char* e = tmode ? getenv("UNO_T_TILE") : nullptr) {  // tuning: "128" (two buffers), "64b2", "64kg2"
         if (atoi(e) == 128) p.tile = Tile{128, 128, 4, false, 64};
         if (strstr(e, "b2")) p.tile.nb = 2;
@@ -1382,8 +1447,10 @@ const int32_t* plan_perm(const void* plan) {
 
 // ---------------------------------------------------------------- a1: row plan
 size_t row_plan_bytes(int64_t M) {
-    return align_up(kPlanPermOffset + static_cast<size_t>(rows_cap_for(M)) * sizeof(int32_t), kWorkspaceAlign);
+    return align_up(kPlanPermOffset + static_cast<size_t>(rows_cap_for(M) + M) * sizeof(int32_t), kWorkspaceAlign);
 }
+
+size_t row_plan_gate_error_offset() { return offsetof(SegInfo, Mb); }
 
 hipError_t segment_rows_launch(const uint8_t* gate, int64_t M, void* plan, hipStream_t stream) {
     hipLaunchKernelGGL(segment_rows_kernel, dim3(1), dim3(kSegThreads), 0, stream, gate, M, rows_cap_for(M),
@@ -1505,7 +1572,10 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     l.total = off;
     return l;
 }
-size_t f32_workspace(int64_t M, int32_t r) { return align_up(static_cast<size_t>(M) * r * sizeof(float), kWorkspaceAlign); }
+// fp32 path: the row plan (its gate-error count), then T [M, r] fp32
+size_t f32_workspace(int64_t M, int32_t r) {
+    return row_plan_bytes(M) + align_up(static_cast<size_t>(M) * r * sizeof(float), kWorkspaceAlign);
+}
 }  // namespace
 
 size_t gated_lora_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r, bool bf16) {
@@ -1517,7 +1587,9 @@ hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, h
     (void)ws_bytes;
     if (pr.M == 0) return hipSuccess;
     if (!pr.bf16) {
-        float* t = static_cast<float*>(ws);
+        hipError_t e = segment_rows_launch(pr.gate, pr.M, ws, stream);
+        if (e != hipSuccess) return e;
+        float* t = reinterpret_cast<float*>(static_cast<char*>(ws) + row_plan_bytes(pr.M));
         const int64_t nt = pr.M * pr.r;
         hipLaunchKernelGGL(lora_t_f32_kernel, dim3(static_cast<uint32_t>((nt + 255) / 256)), dim3(256), 0, stream,
                            static_cast<const float*>(pr.x), static_cast<const float*>(pr.a), pr.gate, pr.M, pr.K,
@@ -1578,9 +1650,9 @@ __global__ __launch_bounds__(256) void lm_rows_kernel(int64_t B, int32_t L, int3
     if (r < rc_cap) rc_perm[r] = -1;
     if (r == 0) {
         const int32_t pv = static_cast<int32_t>((rows + kRowAlign - 1) / kRowAlign * kRowAlign);
-        *info = SegInfo{static_cast<int32_t>(rows), 0, pv, 0};
+        *info = SegInfo{static_cast<int32_t>(rows), 0, pv, 0, 0, -1, {0, 0}};
         const int32_t rpv = static_cast<int32_t>((rc_rows + kRowAlign - 1) / kRowAlign * kRowAlign);
-        *rc_info = SegInfo{static_cast<int32_t>(rc_rows), 0, rpv, 0};
+        *rc_info = SegInfo{static_cast<int32_t>(rc_rows), 0, rpv, 0, 0, -1, {0, 0}};
     }
 }
 }  // namespace
@@ -1607,8 +1679,9 @@ hipError_t lm_head_gemm_launch(const void* x, int64_t x_rows, const void* w, con
                                int64_t K, void* y, int32_t out_compact, void* stats, const int32_t* stat_map,
                                const int32_t* row_token, float* gathered, float c2, hipStream_t stream) {
     const GroupSpec gs = one_group(V);
-    // (the statistics take 256-column tiles; every tile family without a
-    // split of K gives the same bits, so a store-only pass may take any)
+    // (the statistics take 256-column tiles; every one-group tile family
+    // without a split of K gives the same bits, so a store-only pass may take
+    // any of those)
     const GemmPlan p = plan_gemm(M, V, K, false, gs, stats != nullptr, true);
     GemmKArgs ka{};
     ka.x = static_cast<const uint16_t*>(x);

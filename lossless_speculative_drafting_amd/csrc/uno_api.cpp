@@ -153,6 +153,15 @@ uno_status uno_segment_rows(const uint8_t* gate, int64_t M, void* row_plan, size
     return from_hip(uno::segment_rows_launch(gate, M, row_plan, stream), "segment rows launch");
 }
 
+uno_status uno_row_plan_gate_errors(const void* row_plan, int32_t* out, hipStream_t stream) {
+    if (row_plan == nullptr || out == nullptr) return fail(UNO_ERR_INVALID_ARG, "row_plan and out must not be null");
+    if (!aligned256(row_plan)) return fail(UNO_ERR_INVALID_ARG, "row_plan must be 256-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0) return fail(UNO_ERR_INVALID_ARG, "out must be 4-byte aligned");
+    const char* src = static_cast<const char*>(row_plan) + uno::row_plan_gate_error_offset();
+    return from_hip(hipMemcpyAsync(out, src, 2 * sizeof(int32_t), hipMemcpyDeviceToDevice, stream),
+                    "gate error copy");
+}
+
 // T may hold several adapters side by side (their A rows stacked): its width
 // is the sum of their ranks.
 static uno_status check_lora_t(int64_t M, int64_t K, int32_t rt) {

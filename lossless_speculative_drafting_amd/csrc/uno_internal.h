@@ -63,6 +63,8 @@ hipError_t gated_lora_launch(const GemmProblem& p, void* ws, size_t ws_bytes, hi
 
 // The three steps of the bf16 projection, exported separately.
 size_t row_plan_bytes(int64_t M);
+// byte offset in a row plan of int32 {rows with an invalid gate byte, first such row or -1}
+size_t row_plan_gate_error_offset();
 hipError_t segment_rows_launch(const uint8_t* gate, int64_t M, void* plan, hipStream_t stream);
 size_t lora_t_bytes(int64_t M, int32_t r);
 size_t lora_down_workspace_size(int64_t M, int64_t K, int32_t r);

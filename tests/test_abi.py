@@ -73,7 +73,23 @@ def test_gated_lora_validation(lib):
     assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE   # not 256-byte aligned
     assert call(M=0, x=NULL) == OK                            # empty batch is a no-op
     assert lib.uno_gated_lora_workspace_size(2048, 4096, 4096, 128, 0) > 0
-    assert lib.uno_gated_lora_workspace_size(24, 512, 512, 128, 1) == 24 * 128 * 4 + (256 - (24 * 128 * 4) % 256) % 256
+    # fp32 path: the row plan (gate-error count), then T [M, r] fp32
+    assert lib.uno_gated_lora_workspace_size(24, 512, 512, 128, 1) == lib.uno_row_plan_size(24) + 24 * 128 * 4
+
+
+def test_row_plan_gate_error_query(lib):
+    # the plan holds a 256-byte header (gate-error count and first bad row
+    # among it), the permutation over 32-row-padded segments, and the list of
+    # rows with an invalid gate byte
+    for M in (1, 24, 1024, 1000003):
+        rows_cap = (M + 31) // 32 * 32 + 32
+        need = 256 + 4 * (rows_cap + M)
+        assert lib.uno_row_plan_size(M) >= need and lib.uno_row_plan_size(M) % 256 == 0
+    assert lib.uno_row_plan_size(-1) == 0
+    assert lib.uno_row_plan_gate_errors(NULL, FAKE, STREAM) == INVALID
+    assert lib.uno_row_plan_gate_errors(FAKE, NULL, STREAM) == INVALID
+    assert lib.uno_row_plan_gate_errors(ctypes.c_void_p(0x100010), FAKE, STREAM) == INVALID  # plan not 256-aligned
+    assert lib.uno_row_plan_gate_errors(FAKE, ctypes.c_void_p(0x100002), STREAM) == INVALID  # out not 4-aligned
 
 
 def test_grouped_gemm_and_lora_t_validation(lib):

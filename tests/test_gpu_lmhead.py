@@ -8,11 +8,15 @@
   Drafts are drawn with the oracle's inverse CDF from the oracle's draft
   distribution.
 * Normal inputs: both modes (logits stored, or redraw rows recomputed) must
-  agree bit for bit, and uno_block_verify run on the stored logits must give
-  the same outputs (its sums of exponentials run in another order, which
-  could move a decision only where a uniform lies within about 1e-7 of an
-  acceptance probability or CDF boundary); the stored logits are checked
-  against the oracle's to the bf16 GEMM tolerance.
+  agree bit for bit; the fused outputs and those of uno_block_verify on the
+  stored logits must each match the oracle run on those stored logits under
+  the tie rule (the two sum their exponentials in different orders, so a
+  decision may differ between them only where a uniform lies within about
+  1e-7 of an acceptance probability or CDF boundary); the stored logits are
+  checked against the oracle's to the bf16 GEMM tolerance.
+* The redraw rows recomputed when no logits are stored are bitwise the
+  stored logit rows, at shapes where the planner's cheapest tile for the
+  recompute would be a two-K-group one, and with such a tile forced.
 * The bench's size (32 sequences x 16 drafted positions, V = 128256,
   K = 4096): both modes agree, and four sampled sequences match the oracle.
 """
@@ -97,8 +101,16 @@ def test_modes_agree_bitwise_and_match_the_unfused_verifier(B, L, V, K, has_bonu
         np.testing.assert_array_equal(a, b)
     out = uno.block_verify(logits[:nt].view(B, L + nb, V), logits[nt:].view(B, L, V), x, u, T, has_bonus)
     torch.cuda.synchronize()
-    for a, b in zip(store, (to_host(t) for t in out)):
-        np.testing.assert_array_equal(a, b)
+    unfused = tuple(to_host(t) for t in out)
+    lg = to_host(logits).astype(np.float64)
+    z, d = lg[:nt].reshape(B, L + nb, V), lg[nt:].reshape(B, L, V)
+    uh = to_host(u).astype(np.float64).reshape(B, L + 1)
+    ref = oracle.block_verify(z, d, to_host(x), uh, T, has_bonus)
+    for name, res in (("fused", store), ("unfused", unfused)):
+        exact, excused, fails = compare_verify(res, ref, z, d, uh, T, has_bonus)
+        print(f"  {name}: exact {exact} excused ties {excused}", flush=True)
+        assert not fails, (name, fails[:5])
+        assert excused <= 1
     acc = store[0]
     print(f"  mean accepted {acc.mean():.2f} of {L}", flush=True)
     rows = np.array([0, nt - 1, nt, hidden.shape[0] - 1, nt // 2])
@@ -132,3 +144,44 @@ def test_bench_size_modes_agree_and_sampled_sequences_match_the_oracle():
     exact, excused, fails = compare_verify(gpu, ref, z, d, uh, T, has_bonus)
     print(f"  sampled: exact {exact} excused {excused}; mean accepted (all) {store[0].mean():.2f}", flush=True)
     assert not fails, fails[:5]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,L,V,K,has_bonus,tile", [
+    (32, 4, 32000, 4096, False, None),            # 64 recomputed rows: the planner's two-K-group pick
+    (64, 2, 32000, 4096, True, None),
+    (24, 3, 32000, 4096, False, "128x128b4kg2"),  # a forced two-K-group tile is not taken either
+])
+def test_recomputed_redraw_rows_are_the_stored_logits(B, L, V, K, has_bonus, tile, monkeypatch):
+    """Without stored logits, the 2 B redraw rows are recomputed by the LM-head GEMM into the
+    last 2 B V bf16 values of the workspace (row 2s: the target row of sequence s's redraw,
+    2s + 1: its draft row, for a residual redraw); they must be the bits of the stored logits."""
+    if tile:
+        monkeypatch.setenv("UNO_GEMM_TILE", tile)
+    say("lm_head recompute rows", B, L, V, K, has_bonus, tile)
+    hidden, w, x, u = sdev.lm_head_tensors(B, L, V, K, seed=B + V, has_bonus=has_bonus, kind="normal")
+    nb = 1 if has_bonus else 0
+    nt = B * (L + nb)
+    store, logits = _run(hidden, w, x, u, T=1.0, has_bonus=has_bonus, store=True)
+    ws = uno.Workspace(hidden.device)
+    out = uno.lm_head_verify(hidden, w, x, u, 1.0, has_bonus, logits=None, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(store, (to_host(t) for t in out)):
+        np.testing.assert_array_equal(a, b)
+    need = uno.lm_head_verify_workspace_size(B, L, V, K, has_bonus)
+    rc_bytes = (2 * B * V * 2 + 255) // 256 * 256
+    rc = ws.buf[need - rc_bytes:need - rc_bytes + 2 * B * V * 2].view(torch.int16).view(2 * B, V)
+    lg = logits.view(torch.int16)
+    n_acc, _, n_emit = store
+    checked = 0
+    for s in range(B):
+        if n_acc[s] < L:   # residual redraw at position n_acc: target and draft rows
+            j = int(n_acc[s])
+            assert torch.equal(rc[2 * s], lg[s * (L + nb) + j]), s
+            assert torch.equal(rc[2 * s + 1], lg[nt + s * L + j]), s
+            checked += 1
+        elif has_bonus:   # bonus draw from the target row L
+            assert torch.equal(rc[2 * s], lg[s * (L + nb) + L]), s
+            checked += 1
+    print(f"  redraw rows checked: {checked} of {B} sequences", flush=True)
+    assert checked >= 4
