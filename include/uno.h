@@ -275,6 +275,30 @@ uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Block verification without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, arithmetic, domain and outputs are those
+ * of uno_block_verify (the same kernels: the outputs are bitwise equal); the
+ * scratch space is the library's own device array of
+ * uno_block_verify_noalloc_max_bytes() bytes (32 MiB), one per GPU, held
+ * until the process ends.  A problem whose uno_block_verify_workspace_size()
+ * exceeds it returns UNO_ERR_UNSUPPORTED before anything is enqueued
+ * (B = 256, L = 32, V = 128256 needs 16 MiB).  Every call on one GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU (two streams,
+ * two host threads) race and must be ordered by the caller.  The first call
+ * on a device looks the array's device address up (no allocation); nothing
+ * in the array needs to start at zero.
+ * ------------------------------------------------------------------------ */
+size_t uno_block_verify_noalloc_max_bytes(void);
+uno_status uno_block_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                    int64_t target_seq_stride, int64_t draft_seq_stride,
+                                    const int32_t* draft_tokens, const float* uniforms,
+                                    int64_t B, int32_t L, int64_t V, int32_t has_bonus,
+                                    float temperature, int32_t logits_dtype,
+                                    int32_t* n_accepted, int32_t* out_tokens, int32_t* n_emitted,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Block verification with early exit.  Only the prefix up to the first
  * rejection decides the output ("The Psi-Spec Sampler" on the
  * aifromscratch.in page: the longest valid prefix is kept), so positions are

@@ -56,6 +56,9 @@ SIGNATURES = {
     "uno_block_verify": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
                                     _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                     _c_size, _c_ptr]),
+    "uno_block_verify_noalloc_max_bytes": (_c_size, []),
+    "uno_block_verify_noalloc": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
+                                            _c_int64, _c_int32, _c_float, _c_int32, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "uno_block_verify_early_workspace_size": (_c_size, [_c_int64, _c_int32, _c_int64, _c_int32]),
     "uno_block_verify_early": (_c_int32, [_c_ptr, _c_ptr, _c_int64, _c_int64, _c_ptr, _c_ptr, _c_int64, _c_int32,
                                           _c_int64, _c_int32, _c_float, _c_int32, _c_int32, _c_ptr, _c_ptr, _c_ptr,
@@ -461,14 +464,16 @@ def lm_head_verify(hidden, w_lm, draft_tokens, uniforms, temperature=1.0, has_bo
 
 def block_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature=1.0, has_bonus=False,
                  B=None, L=None, V=None, target_seq_stride=None, draft_seq_stride=None,
-                 outputs=None, workspace=None, stream=None, early_chunk=None):
+                 outputs=None, workspace=None, stream=None, early_chunk=None, noalloc=False):
     """Verify one drafted block per sequence.
 
     By default target_logits is [B, L + has_bonus, V] and draft_logits [B, L, V]
     (a leading dimension of 1 broadcasts with stride 0).  Explicit B, L, V and
     strides (in elements) address logits inside a larger buffer.  early_chunk
     selects the early-exit verifier (uno_block_verify_early) with that many
-    positions per chunk; its outputs are the same.
+    positions per chunk; its outputs are the same.  noalloc selects
+    uno_block_verify_noalloc (the library's own scratch, no workspace; pass
+    outputs to allocate nothing here either).
     Returns (n_accepted [B], out_tokens [B, L+1], n_emitted [B]) int32 tensors.
     """
     _need_cuda(target_logits, draft_logits, draft_tokens, uniforms)
@@ -496,7 +501,15 @@ def block_verify(target_logits, draft_logits, draft_tokens, uniforms, temperatur
                    torch.empty((B, L + 1), dtype=torch.int32, device=dev),
                    torch.empty(B, dtype=torch.int32, device=dev))
     n_acc, out_tok, n_emit = outputs
-    if early_chunk is None:
+    if noalloc:
+        if early_chunk is not None or workspace is not None:
+            raise ValueError("the no-allocation verifier takes neither early_chunk nor a workspace")
+        _check(_lib.uno_block_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), int(target_seq_stride),
+                                             int(draft_seq_stride), _ptr(draft_tokens), _ptr(uniforms), int(B),
+                                             int(L), int(V), nb, float(temperature),
+                                             _dtype_code(target_logits.dtype), _ptr(n_acc), _ptr(out_tok),
+                                             _ptr(n_emit), _stream(stream)))
+    elif early_chunk is None:
         need = int(_lib.uno_block_verify_workspace_size(B, L, V, nb))
         ws = _workspace(workspace, need, dev, stream)
         _check(_lib.uno_block_verify(_ptr(target_logits), _ptr(draft_logits), int(target_seq_stride),

@@ -357,12 +357,14 @@ size_t uno_block_verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t 
     return uno::verify_workspace_size(B, L, V, has_bonus ? 1 : 0);
 }
 
+// noalloc: the workspace is the library's own per-device scratch array (the
+// caller passes none); sizes past it are rejected before anything runs.
 static uno_status block_verify_common(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
                                       int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms,
                                       int64_t B, int32_t L, int64_t V, int32_t has_bonus, float temperature,
                                       int32_t logits_dtype, int32_t* n_accepted, int32_t* out_tokens,
                                       int32_t* n_emitted, void* workspace, size_t workspace_bytes,
-                                      hipStream_t stream, int32_t chunk) {
+                                      hipStream_t stream, int32_t chunk, bool noalloc = false) {
     uno_status st = check_logits(B, L, V, temperature, logits_dtype);
     if (st != UNO_OK) return st;
     if (has_bonus != 0 && has_bonus != 1) return fail(UNO_ERR_INVALID_ARG, "has_bonus must be 0 or 1");
@@ -380,6 +382,16 @@ static uno_status block_verify_common(const void* target_logits, const void* dra
     if (rows * max_chunks > kMaxGridX || B > kMaxGridX) return fail(UNO_ERR_UNSUPPORTED, "problem too large for one launch");
     const size_t need = chunk > 0 ? uno::verify_early_workspace_size(B, L, V, has_bonus)
                                   : uno::verify_workspace_size(B, L, V, has_bonus);
+    if (noalloc) {
+        if (need > uno::noalloc_scratch_bytes())
+            return fail(UNO_ERR_UNSUPPORTED,
+                        "B = %lld, L = %d, V = %lld needs %zu bytes of scratch; the no-allocation entry point "
+                        "holds %zu (use uno_block_verify with a workspace)",
+                        static_cast<long long>(B), L, static_cast<long long>(V), need, uno::noalloc_scratch_bytes());
+        const hipError_t e = uno::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return from_hip(e, "scratch symbol address");
+        workspace_bytes = uno::noalloc_scratch_bytes();
+    }
     st = check_workspace(workspace, workspace_bytes, need);
     if (st != UNO_OK) return st;
     uno::VerifyProblem p{};
@@ -410,6 +422,18 @@ uno_status uno_block_verify(const void* target_logits, const void* draft_logits,
                                uniforms, B, L, V, has_bonus, temperature, logits_dtype, n_accepted, out_tokens,
                                n_emitted, workspace, workspace_bytes, stream, 0);
 }
+
+uno_status uno_block_verify_noalloc(const void* target_logits, const void* draft_logits, int64_t target_seq_stride,
+                                    int64_t draft_seq_stride, const int32_t* draft_tokens, const float* uniforms,
+                                    int64_t B, int32_t L, int64_t V, int32_t has_bonus, float temperature,
+                                    int32_t logits_dtype, int32_t* n_accepted, int32_t* out_tokens,
+                                    int32_t* n_emitted, hipStream_t stream) {
+    return block_verify_common(target_logits, draft_logits, target_seq_stride, draft_seq_stride, draft_tokens,
+                               uniforms, B, L, V, has_bonus, temperature, logits_dtype, n_accepted, out_tokens,
+                               n_emitted, nullptr, 0, stream, 0, true);
+}
+
+size_t uno_block_verify_noalloc_max_bytes(void) { return uno::noalloc_scratch_bytes(); }
 
 size_t uno_block_verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
     if (B < 0 || L < 1 || L > 64 || V < 1) return 0;

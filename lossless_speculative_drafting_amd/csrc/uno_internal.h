@@ -43,6 +43,10 @@ size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V);
 // chunk = 0: one pass over every row; chunk > 0: early exit in chunks of positions
 hipError_t block_verify_launch(const VerifyProblem& p, void* ws, hipStream_t stream, int32_t chunk = 0);
 hipError_t draft_sample_launch(const VerifyProblem& p, void* ws, hipStream_t stream);
+// Scratch of the verifier's no-allocation entry point: its size, and its
+// device address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 
 // ---- gated-LoRA projection ----------------------------------------------------
 struct GemmProblem {

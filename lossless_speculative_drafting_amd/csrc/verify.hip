@@ -41,6 +41,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "uno_device.h"
 #include "uno_internal.h"
@@ -1163,6 +1164,41 @@ hipError_t block_verify_launch(const VerifyProblem& pr, void* ws, hipStream_t st
     if (pr.bf16)
         return vec ? verify_impl<true, true>(pr, ws, stream, chunk) : verify_impl<true, false>(pr, ws, stream, chunk);
     return vec ? verify_impl<false, true>(pr, ws, stream, chunk) : verify_impl<false, false>(pr, ws, stream, chunk);
+}
+
+// ---------------------------------------------------------------- verification without a workspace
+// Scratch of uno_block_verify_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and is kept per device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static_assert(kNoAllocScratchBytes % kWorkspaceAlign == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & (kWorkspaceAlign - 1)) != 0) return hipErrorInvalidValue;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t draft_sample_launch(const VerifyProblem& pr, void* ws, hipStream_t stream) {
