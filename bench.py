@@ -48,6 +48,10 @@ def parse():
     # early-exit verifier, LM head, tree verification -- so that a kernel
     # trace holds the timed steps' kernels only)
     ap.add_argument("--no-extras", action="store_true")
+    # (the per-workload measurements of the other configurations: skipped,
+    # or only one of them -- profiling runs)
+    ap.add_argument("--no-configs", action="store_true")
+    ap.add_argument("--only-config", default=None, choices=["layer_b1", "layer_b64", "serve_b256"])
     return ap.parse_args()
 
 
@@ -105,6 +109,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_config:
+        print(json.dumps({args.only_config: CONFIG_MEASURES[args.only_config](uno, sdev, torch, dev)}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     B, L, V = wl.n_seq, wl.block, wl.vocab
     M = wl.rows
@@ -122,6 +129,7 @@ def main():
     z, d = sdev.verify_logits(B, L, V, wl.seed, kind=wl.logits, target_sigma=wl.target_sigma,
                               draft_sigma=sigma)
     drafts = uno.draft_sample(d, uno.philox_uniforms(0, 1, 0, B * L, device=dev), T)
+    z_sample, d_sample = z[:4].clone(), d[:4].clone()  # the oracle baseline's sequences
     u = torch.empty(B * (L + 1), dtype=torch.float32, device=dev)
     total_steps = args.warmup + args.steps
     n_acc = torch.empty((total_steps, B), dtype=torch.int32, device=dev)
@@ -224,6 +232,13 @@ def main():
         lm_head = lm_head_measure(uno, sdev, torch, B, L, V, wl.projections[0][1], T, wl.seed, dev)
         tree = tree_measure(uno, sdev, torch, B, V, T, wl.seed, dev)
 
+    platform = platform_info(torch)  # (right after the timed steps: clocks under recent load)
+    configs = None
+    if not args.no_configs:
+        del z, d
+        torch.cuda.empty_cache()
+        configs = {name: fn(uno, sdev, torch, dev) for name, fn in CONFIG_MEASURES.items()}
+
     vt = sum(a.elapsed_time(b) for a, b, _ in verify_events) / 1e3 / len(verify_events)
     v_us = sorted(a.elapsed_time(b) * 1e3 for a, b, _ in verify_events)
     redraws = sum(int((n_acc[i] < L).sum().item()) for _, _, i in verify_events) / len(verify_events)
@@ -283,10 +298,12 @@ def main():
         },
         "lm_head": lm_head,
         "tree_verify": tree,
+        "configs": configs,
+        "platform": platform,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, stack.layers, x0, z, d, drafts, u, gate_np, T, L)
+        result["cpu_baseline"] = cpu_baseline(wl, stack.layers, x0, z_sample, d_sample, drafts, u, gate_np, T, L)
     print(json.dumps(result), flush=True)
 
 
@@ -395,6 +412,214 @@ def tree_measure(uno, sdev, torch, B, V, T, seed, dev, K=2, D=5, reps=10):
     return {"trees": B, "nodes_per_tree": N, "branching": K, "depth": D, "vocab": V, "us_per_call": round(us, 2),
             "rows_read_per_tree": round(rows / B, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "mean_accepted": round(float(out[0].float().mean()), 3)}
+
+
+def platform_info(torch):
+    """What the numbers were measured on: device, ROCm and torch versions, and the
+    clocks, power and performance level rocm-smi reports (None where unavailable)."""
+    import subprocess
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "torch": torch.__version__, "torch_hip": torch.version.hip, "rocm": None, "smi": None}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--showperflevel",
+                              "--json"], capture_output=True, text=True, timeout=30)
+        cards = json.loads(out.stdout)
+        card = next(iter(v for k, v in cards.items() if k.startswith("card")), None)
+        if card:
+            keep = ("sclk", "mclk", "fclk", "socclk", "power", "perf")
+            info["smi"] = {k.strip(" :"): v for k, v in card.items() if any(w in k.lower() for w in keep)}
+    except Exception as e:  # noqa: BLE001  (metadata only: never fail the bench on it)
+        info["smi"] = f"unavailable: {type(e).__name__}"
+    return info
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _median(xs):
+    return pct(sorted(xs), 50)
+
+
+def _layer_gemm_measure(uno, sdev, torch, wl, dev, copies=3, reps=6):
+    """One 8B-shaped layer (seven gated-LoRA projections as four launches:
+    grouped q|k|v, o, gate|up with SwiGLU, down) over the workload's mixed
+    batch, rotating through `copies` independent copies of the weights so that
+    a repetition never finds its weights in the 256 MB MALL (each forward
+    touches about 320 MB of weights; a copy is reused only after the others'
+    640 MB).  Per launch kind: median time of the gated GEMM (HIP events) and
+    its algorithmic rate; the whole layer (LoRA down-projections and glue
+    included) per repetition."""
+    from synthetic import gate_vector
+
+    gate = torch.from_numpy(gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)).to(dev)
+    stacks = [uno.GatedLoraStack([sdev.layer_weights(wl.projections, wl.seed * 1000 + 7919 * c)], gate, SCALE)
+              for c in range(copies)]
+    x0 = sdev.randn((wl.rows, wl.projections[0][1]), 1.0, wl.seed + 3)
+    for st in stacks:
+        st.forward(x0)
+    torch.cuda.synchronize()
+    kinds = ("q|k|v", "o", "gate|up", "down")
+    per = {k: [] for k in kinds}
+    layer_us = []
+    for i in range(reps * copies):
+        st = stacks[i % copies]
+        st.timer = []
+        a, b = _events(torch)
+        a.record()
+        st.forward(x0)
+        b.record()
+        torch.cuda.synchronize()
+        layer_us.append(a.elapsed_time(b) * 1e3)
+        for k, ev in zip(kinds, st.timer):
+            per[k].append((ev[0].elapsed_time(ev[1]) * 1e3, ev[2], ev[3]))
+        st.timer = None
+    out, tot_f, tot_b, tot_t = {}, 0.0, 0.0, 0.0
+    for k in kinds:
+        t = _median([p[0] for p in per[k]])
+        f, nb = per[k][0][1], per[k][0][2]
+        tot_f, tot_b, tot_t = tot_f + f, tot_b + nb, tot_t + t
+        out[k] = {"median_us": round(t, 2), "tflops": round(f / t / 1e6, 1), "gbs": round(nb / t / 1e3, 1)}
+    del stacks
+    torch.cuda.empty_cache()
+    return out, {"gemm_us": round(tot_t, 2), "gflop": round(tot_f / 1e9, 2), "mb": round(tot_b / 1e6, 1),
+                 "tflops": round(tot_f / tot_t / 1e6, 1), "gbs": round(tot_b / tot_t / 1e3, 1),
+                 "layer_us_median": round(_median(layer_us), 2)}
+
+
+def _verify_measure(uno, sdev, torch, B, L, V, seed, kind, sigma, temps, dev, copies=1, reps=10, zipf_slope=1.1):
+    """Block verification per call (HIP events over `reps` calls with fresh
+    uniforms), rotating through `copies` independent logit sets when one set
+    would fit in the MALL.  Drafts are drawn on the GPU from each set's draft
+    logits at the call's temperature.  Per temperature: time, algorithmic GB/s
+    (with the redraws that happened) and the tokens emitted per call."""
+    sets = [sdev.verify_logits(B, L, V, seed + 13 * c, kind=kind, target_sigma=3.0, draft_sigma=sigma,
+                               zipf_slope=zipf_slope) for c in range(copies)]
+    res = {}
+    outs = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, L + 1), dtype=torch.int32, device=dev),
+            torch.empty(B, dtype=torch.int32, device=dev))
+    ws = uno.Workspace(dev)
+    u = torch.empty(B * (L + 1), dtype=torch.float32, device=dev)
+    for T in temps:
+        drafts = [uno.draft_sample(d, uno.philox_uniforms(0, 1, 0, B * L, device=dev), T) for _, d in sets]
+        ts, emitted, redraws = [], 0, 0
+        for i in range(reps + 2):
+            z, d = sets[i % copies]
+            uno.philox_uniforms(0, 0, i * B * (L + 1), B * (L + 1), out=u)
+            a, b = _events(torch)
+            a.record()
+            uno.block_verify(z, d, drafts[i % copies], u, T, False, outputs=outs, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:  # (two warm-up calls)
+                ts.append(a.elapsed_time(b) * 1e3)
+                emitted += int(outs[2].sum().item())
+                redraws += int((outs[0] < L).sum().item())
+        t = _median(ts)
+        nbytes = verify_bytes(B, L, V, 2, redraws / reps)
+        res[f"T={T}"] = {"median_us": round(t, 2), "gbs": round(nbytes / t / 1e3, 1),
+                         "frac": round(nbytes / t / 1e3 / PEAK_HBM_GBS, 4),
+                         "tokens_per_call": round(emitted / reps, 2),
+                         "verify_only_tokens_per_s": round(emitted / reps / (t * 1e-6), 1)}
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_layer_b1(uno, sdev, torch, dev):
+    """Batch 1 (one sequence of [16 verify | 16 draft] rows): the layer's
+    gated GEMMs stream their weights (HBM-bound, ~31 flop/B), verification
+    of 16 positions over V = 128256 is latency (8.2 MB; 64 logit sets are
+    rotated so each call reads from HBM, not the MALL)."""
+    from synthetic import WORKLOADS
+
+    wl = WORKLOADS["layer_b1"]
+    kinds, layer = _layer_gemm_measure(uno, sdev, torch, wl, dev)
+    layer["bound"], layer["frac"] = "hbm", round(layer["gbs"] / PEAK_HBM_GBS, 4)
+    ver = _verify_measure(uno, sdev, torch, wl.n_seq, wl.block, wl.vocab, wl.seed, "normal", 1.0, (1.0,), dev,
+                          copies=64, reps=20)
+    return {"workload": "1 layer x 7 projections, 1 seq x [16 verify | 16 draft] rows; verify 1 x 16 over "
+                        "V=128256, sigma=1, T=1; weights rotated over 3 copies, logits over 64 (MALL defeated)",
+            "gemm_per_launch": kinds, "gemm_layer": layer, "verify": ver}
+
+
+def measure_layer_b64(uno, sdev, torch, dev):
+    """Batch 64 (64 sequences x [16 | 16] rows, M = 2048): the layer's gated
+    GEMMs are MFMA-bound; verification of 1024 positions (525 MB of logits)
+    at draft noise sigma 0.25, 1 and 4."""
+    from synthetic import WORKLOADS
+
+    wl = WORKLOADS["layer_b64"]
+    kinds, layer = _layer_gemm_measure(uno, sdev, torch, wl, dev)
+    layer["bound"], layer["frac"] = "mfma", round(layer["tflops"] / PEAK_BF16_TFLOPS, 4)
+    ver = {}
+    for sigma in wl.draft_sigmas:
+        ver[f"sigma={sigma}"] = _verify_measure(uno, sdev, torch, wl.n_seq, wl.block, wl.vocab, wl.seed, "normal",
+                                                sigma, (1.0,), dev)["T=1.0"]
+    return {"workload": "1 layer x 7 projections, 64 seqs x [16 verify | 16 draft] rows (M=2048); verify "
+                        "64 x 16 over V=128256, sigma in {0.25, 1, 4}, T=1; weights rotated over 3 copies",
+            "gemm_per_launch": kinds, "gemm_layer": layer, "verify": ver}
+
+
+def measure_serve_b256(uno, sdev, torch, dev, reps=4):
+    """Large-batch serving (256 sequences x [32 | 32] rows, M = 16384): the
+    up (4096 -> 14336) and down (14336 -> 4096) gated-LoRA projections,
+    MFMA-bound, each as its LoRA down-projection plus its gated GEMM; then
+    verification of 8192 positions over V = 128256 with Zipf-skewed logits
+    (4.2 GB) at T = 0.6 and 1.0."""
+    from synthetic import WORKLOADS, gate_vector
+
+    wl = WORKLOADS["serve_b256"]
+    M = wl.rows
+    Md = wl.n_seq * wl.draft_rows
+    gate = torch.from_numpy(gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)).to(dev)
+    plan = uno.RowPlan(gate)
+    gemm = {}
+    ws = uno.Workspace(dev)
+    for i, (name, K, N) in enumerate(wl.projections):
+        w, a, b = sdev.projection_weights(K, N, wl.seed * 1000 + 10 * i)
+        x = sdev.randn((M, K), 1.0, wl.seed + i)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t = uno.lora_down(x, a, plan, SCALE, workspace=ws)
+        uno.gated_gemm(x, w, t, b, plan, out=y, workspace=ws)
+        tg, tl = [], []
+        for _ in range(reps):
+            e0, e1 = _events(torch)
+            e2, e3 = _events(torch)
+            e0.record()
+            uno.lora_down(x, a, plan, SCALE, t=t, workspace=ws)
+            e1.record()
+            e2.record()
+            uno.gated_gemm(x, w, t, b, plan, out=y, workspace=ws)
+            e3.record()
+            torch.cuda.synchronize()
+            tl.append(e0.elapsed_time(e1) * 1e3)
+            tg.append(e2.elapsed_time(e3) * 1e3)
+        t_g, t_l = _median(tg), _median(tl)
+        flop = 2.0 * M * K * N + 2.0 * Md * 128 * N
+        flop_l = 2.0 * Md * K * 128
+        gemm[name] = {"gemm_us": round(t_g, 2), "gemm_tflops": round(flop / t_g / 1e6, 1),
+                      "gemm_frac": round(flop / t_g / 1e6 / PEAK_BF16_TFLOPS, 4),
+                      "lora_down_us": round(t_l, 2),
+                      "projection_tflops": round((flop + flop_l) / (t_g + t_l) / 1e6, 1)}
+        del w, a, b, x, y, t
+        torch.cuda.empty_cache()
+    ver = _verify_measure(uno, sdev, torch, wl.n_seq, wl.block, wl.vocab, wl.seed, "zipf", wl.draft_sigmas[0],
+                          wl.temperatures, dev, reps=5, zipf_slope=wl.extra["zipf_slope"])
+    return {"workload": "up 4096->14336 and down 14336->4096 gated-LoRA projections (r=128), 256 seqs x "
+                        "[32 verify | 32 draft] rows (M=16384); verify 256 x 32 over V=128256, Zipf logits "
+                        "(slope 1.1, noise 0.5), T in {0.6, 1.0}",
+            "gemm": gemm, "verify": ver}
+
+
+CONFIG_MEASURES = {"layer_b1": measure_layer_b1, "layer_b64": measure_layer_b64, "serve_b256": measure_serve_b256}
 
 
 def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):
