@@ -473,6 +473,9 @@ def _layer_gemm_measure(uno, sdev, torch, wl, dev, copies=3, reps=6):
         st = stacks[i % copies]
         st.timer = []
         a, b = _events(torch)
+        # (the GPU spins while the host enqueues the layer, so that the events
+        # time the kernels and not the host's launch rate)
+        torch.cuda._sleep(1_000_000)
         a.record()
         st.forward(x0)
         b.record()
@@ -514,6 +517,7 @@ def _verify_measure(uno, sdev, torch, B, L, V, seed, kind, sigma, temps, dev, co
             z, d = sets[i % copies]
             uno.philox_uniforms(0, 0, i * B * (L + 1), B * (L + 1), out=u)
             a, b = _events(torch)
+            torch.cuda._sleep(200_000)  # (the host enqueues the call while the GPU spins)
             a.record()
             uno.block_verify(z, d, drafts[i % copies], u, T, False, outputs=outs, workspace=ws)
             b.record()
@@ -593,6 +597,7 @@ def measure_serve_b256(uno, sdev, torch, dev, reps=4):
         for _ in range(reps):
             e0, e1 = _events(torch)
             e2, e3 = _events(torch)
+            torch.cuda._sleep(200_000)  # (the host enqueues both launches while the GPU spins)
             e0.record()
             uno.lora_down(x, a, plan, SCALE, t=t, workspace=ws)
             e1.record()

@@ -438,17 +438,16 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
     }
 }
 
-// Rows with an invalid gate byte get NaN in every output column: the tile
-// (m tile mt, n tile at n0) writes entries [mt BM, mt BM + BM) of the plan's
-// bad-row list over its own columns (SwiGLU: the act columns of its gate and
-// up blocks).  A cold path: scalar stores.
-template <int BM, int BN, int THREADS>
-__device__ void poison_bad_rows(const GemmKArgs& a, int64_t m0, int64_t n0, int32_t Mb) {
+// Rows with an invalid gate byte get NaN in every output column: a
+// workgroup writes entries [m0, m0 + BM) of the plan's bad-row list over
+// output columns [c0, c0 + ncols) (SwiGLU: act columns).  A cold path:
+// scalar stores.
+template <int BM, int THREADS>
+__device__ void poison_bad_rows(const GemmKArgs& a, int64_t m0, int64_t c0, int64_t ncols, int32_t Mb) {
     constexpr uint16_t kNaN = 0x7FC0;  // bf16 quiet NaN
     const int32_t* bad = a.perm + a.rows_cap;
     const bool swiglu = a.epi == kEpiSwiglu;
-    const int64_t c0 = swiglu ? n0 / 2 : n0;
-    const int64_t cend = std::min<int64_t>(swiglu ? a.N / 2 : a.N, c0 + (swiglu ? BN / 2 : BN));
+    const int64_t cend = std::min<int64_t>(swiglu ? a.N / 2 : a.N, c0 + ncols);
     const int64_t rows = std::min<int64_t>(BM, Mb - m0);
     const int64_t cols = cend - c0;
     for (int64_t e = threadIdx.x; e < rows * cols; e += THREADS) {
@@ -502,7 +501,10 @@ void gated_gemm_kernel(const GemmKArgs a) {
     const int64_t n0 = static_cast<int64_t>(nt) * BN;
     if constexpr (!TMODE) {
         const int32_t Mb = __builtin_amdgcn_readfirstlane(info.Mb);
-        if (z == 0 && m0 < Mb) poison_bad_rows<BM, BN, C::THREADS>(a, m0, n0, Mb);
+        // (a SwiGLU tile's 256 interleaved columns are 128 act columns)
+        if (z == 0 && m0 < Mb)
+            poison_bad_rows<BM, C::THREADS>(a, m0, a.epi == kEpiSwiglu ? n0 / 2 : n0,
+                                            a.epi == kEpiSwiglu ? BN / 2 : BN, Mb);
     }
     const int64_t rows_valid = TMODE ? info.Md_pad : static_cast<int64_t>(info.Pv) + info.Md_pad;
     if (m0 >= rows_valid) return;  // uniform for the workgroup, before any barrier
@@ -1047,6 +1049,289 @@ void gated_gemm_kernel(const GemmKArgs a) {
     }
 }
 
+// ------------------------------------------------------------ weight streaming
+// At 32 rows or fewer (a batch of one sequence: 16 verify + 16 draft rows) a
+// projection does about 31 flop per byte of W_AR: it is bound by streaming
+// the weights from HBM.  Here a workgroup of eight wavefronts owns NB blocks
+// of 32 output columns over every row and the whole of its K range: all rows
+// fit one 32-row MFMA block (verify rows first, then draft rows: lane row r
+// is plan row r below Mv, plan row Pv + r - Mv after).  Wavefront w takes the
+// 64-deep chunks w, w + 8, w + 16, ... of K, so that at any moment the eight
+// wavefronts read eight adjacent 128-byte pieces of each weight row.
+// Operands go from global memory straight into registers (nothing is reused
+// across wavefronts but x, which the L2 holds), two chunks ahead of the
+// MFMAs; a load past a row's range or past K returns zeros.  Within a chunk,
+// lane half h of the MFMA 32x32x16 operands takes K slots 32h .. 32h + 31 as
+// four 16-byte loads, MFMA i using the lane's slots 8i .. 8i + 7: both
+// operands use the same assignment, so each chunk adds every k exactly once
+// (in another order than the tiles above).  The eight wavefronts' sums are
+// added in wavefront order through LDS.  The adapter extension (T, B) runs
+// as further chunks, taken by wavefronts 0 .. r/64 - 1 after their K chunks;
+// verify rows read zero T rows and so add exact zeros to accumulators that
+// started at +0 (never -0): they keep the bits of an all-verify call.  T mode
+// (the LoRA down-projection) reads the draft rows and writes T in plan
+// order.  With SWIGLU the two column blocks are matching gate and up columns
+// of the interleaved weights and the epilogue forms bf16(silu(g) u).
+constexpr int kStreamWaves = 8;
+constexpr int kStreamChunk = 64;
+constexpr int kStreamSets = 3;  // register sets: loads run two chunks ahead
+
+__device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const int32_t __attribute__((ext_vector_type(4))) v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int NB, bool TMODE, bool SWIGLU>
+__global__ __launch_bounds__(kStreamWaves * kWave, 1) void stream_gemm_kernel(const GemmKArgs a) {
+    static_assert(!SWIGLU || (NB == 2 && !TMODE), "SwiGLU: a gate block and an up block");
+    constexpr int kThreads = kStreamWaves * kWave;
+    __shared__ float red[kStreamWaves][NB][16][kWave];
+    __shared__ int32_t s_src[32];   // block row -> source (and output) row, -1: none
+    __shared__ int32_t s_prow[32];  // block row -> plan row, -1: none
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int h = lane >> 5;  // K half of a chunk
+    const int32_t nt = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(blockIdx.x % a.n_tiles));
+    const int32_t z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(blockIdx.x / a.n_tiles));
+    SegInfo info = *a.info;
+    info.Mv = __builtin_amdgcn_readfirstlane(info.Mv);
+    info.Md = __builtin_amdgcn_readfirstlane(info.Md);
+    info.Pv = __builtin_amdgcn_readfirstlane(info.Pv);
+    info.Md_pad = __builtin_amdgcn_readfirstlane(info.Md_pad);
+    info.Mb = __builtin_amdgcn_readfirstlane(info.Mb);
+    const int32_t rows = TMODE ? info.Md : info.Mv + info.Md;  // rows of the block (<= 32)
+
+    // output columns: act columns [c0, c0 + 32) of gate / up blocks, or
+    // columns [c0, c0 + 32 NB); col0[j]: first weight row of column block j
+    int64_t c0, col0[NB];
+    if constexpr (SWIGLU) {
+        c0 = static_cast<int64_t>(nt) * 32;
+        col0[0] = 2 * kSwigluBlock * (c0 / kSwigluBlock) + c0 % kSwigluBlock;
+        col0[1] = col0[0] + kSwigluBlock;
+    } else {
+        c0 = static_cast<int64_t>(nt) * 32 * NB;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) col0[j] = c0 + 32 * j;
+    }
+    if constexpr (!TMODE) {
+        if (z == 0 && info.Mb > 0) poison_bad_rows<32, kThreads>(a, 0, c0, SWIGLU ? 32 : 32 * NB, info.Mb);
+    }
+    if (threadIdx.x < 32) {
+        const int32_t r = threadIdx.x;
+        int32_t prow = -1;
+        if constexpr (TMODE) prow = r < info.Md ? info.Pv + r : -1;
+        else prow = r < info.Mv ? r : (r < rows ? info.Pv + (r - info.Mv) : -1);
+        s_prow[r] = prow;
+        s_src[r] = prow >= 0 ? a.perm[prow] : -1;
+    }
+    __syncthreads();
+    if (!TMODE && rows == 0) return;  // (uniform; T mode still writes its zero padding rows)
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, a.x_bytes, kRsrcWord3);
+    const int32_t w_range = static_cast<int32_t>(std::min<int64_t>(a.w_bytes, a.N * a.ldw * 2));
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w), 0, w_range, kRsrcWord3);
+    const int32_t my_src = s_src[lane & 31];
+    const uint32_t xoff = my_src >= 0 ? static_cast<uint32_t>(my_src * a.ldx * 2) : kOOB;
+    uint32_t woff[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int64_t col = col0[j] + (lane & 31);
+        woff[j] = col < a.N ? static_cast<uint32_t>(col * a.ldw * 2) : kOOB;
+    }
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+    const int64_t kb = static_cast<int64_t>(z) * a.k_per_split;
+    const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
+
+    bf16x8 xf[kStreamSets][4], wf[kStreamSets][NB][4];
+    // Per-lane offsets are loop-invariant (the lane's row plus its K slots
+    // 32h + 8i within a chunk); a chunk moves the descriptors' base (scalar
+    // arithmetic only), so that no vector register is rewritten while loads
+    // into the other register sets are in flight.  A look-ahead past the last
+    // full chunk gets an empty range: zeros, no memory traffic.
+    uint32_t xv[4], wv[NB][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t slot = static_cast<uint32_t>((32 * h + 8 * i) * 2);
+        xv[i] = xoff == kOOB ? kOOB : xoff + slot;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) wv[j][i] = woff[j] == kOOB ? kOOB : woff[j] + slot;
+    }
+    const int32_t nfull = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((ke - kb) / kStreamChunk));
+    const int32_t x_range = static_cast<int32_t>(a.x_bytes);
+    auto load_chunk = [&](int c, int set) __attribute__((always_inline)) {
+        const int32_t cb = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((kb + static_cast<int64_t>(c) * kStreamChunk) * 2));
+        const bool in = c < nfull;
+        const __amdgpu_buffer_rsrc_t xc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(const_cast<uint16_t*>(a.x)) + (in ? cb : 0), 0, in ? x_range - cb : 0, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t wc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(const_cast<uint16_t*>(a.w)) + (in ? cb : 0), 0, in ? w_range - cb : 0, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xf[set][i] = load16(xc, xv[i]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) wf[set][j][i] = load16(wc, wv[j][i]);
+        }
+    };
+    auto mfma_chunk = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[set][i], wf[set][j][i], acc[j], 0, 0, 0);
+    };
+    // full chunks wave, wave + 8, ...: loads two chunks ahead of the MFMAs
+    // (sched_barrier fences keep each group of loads ahead of the MFMAs that
+    // follow it: hoisted above them, the MFMAs would wait for every load)
+    constexpr int S = kStreamWaves;
+    int c = wave;
+    load_chunk(c, 0);
+    load_chunk(c + S, 1);
+    for (; c < nfull; c += 3 * S) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk(c + 2 * S, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + S >= nfull) break;
+        load_chunk(c + 3 * S, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 * S >= nfull) break;
+        load_chunk(c + 4 * S, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_chunk(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // a last, partial chunk (K or the split not a multiple of 64): slots past
+    // the end load zeros; taken by the wavefront whose turn it is
+    if (nfull * kStreamChunk < ke - kb && (nfull % kStreamWaves) == wave) {
+        const int64_t k0 = kb + static_cast<int64_t>(nfull) * kStreamChunk + 32 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = k0 + 8 * i + 8 <= ke;
+            const uint32_t kbytes = static_cast<uint32_t>((k0 + 8 * i) * 2);
+            xf[0][i] = load16(xr, ok ? xoff + kbytes : kOOB);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) wf[0][j][i] = load16(wr, ok ? woff[j] + kbytes : kOOB);
+        }
+        mfma_chunk(0);
+    }
+
+    // adapter extension (main mode, last split): T rows of the draft rows,
+    // columns g r .. g r + r - 1 of the group g the workgroup's columns fall
+    // in, against lora_b rows
+    if constexpr (!TMODE) {
+        const int32_t nE = __builtin_amdgcn_readfirstlane((a.r + kStreamChunk - 1) / kStreamChunk);
+        if (z == a.splits - 1 && a.r > 0 && info.Md > 0 && wave < nE) {
+            const GroupRef grp = find_group(a.out, col0[0]);
+            const uint32_t t_skip = static_cast<uint32_t>(grp.g) * static_cast<uint32_t>(a.r) * 2u;
+            const int32_t t_range = static_cast<int32_t>(std::max<int64_t>(
+                std::min<int64_t>(a.t_bytes, static_cast<int64_t>(info.Md_pad) * a.ldt * 2) - t_skip, 0));
+            const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+                reinterpret_cast<char*>(const_cast<uint16_t*>(a.t)) + t_skip, 0, t_range, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.lb), 0, static_cast<int32_t>(std::min<int64_t>(a.b_bytes, a.N * a.ldb * 2)),
+                kRsrcWord3);
+            const int32_t r = lane & 31;
+            const uint32_t toff = (r >= info.Mv && r < rows) ? static_cast<uint32_t>((r - info.Mv) * a.ldt * 2) : kOOB;
+            uint32_t boff[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int64_t col = col0[j] + (lane & 31);
+                boff[j] = col < a.N ? static_cast<uint32_t>(col * a.ldb * 2) : kOOB;
+            }
+            for (int e = wave; e < nE; e += kStreamWaves) {
+                const int64_t k0 = static_cast<int64_t>(e) * kStreamChunk + 32 * h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = k0 + 8 * i + 8 <= a.r;
+                    const uint32_t kbytes = static_cast<uint32_t>((k0 + 8 * i) * 2);
+                    xf[0][i] = load16(tr, ok && toff != kOOB ? toff + kbytes : kOOB);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) wf[0][j][i] = load16(br, ok && boff[j] != kOOB ? boff[j] + kbytes : kOOB);
+                }
+                mfma_chunk(0);
+            }
+        }
+    }
+
+    // ---- the eight wavefronts' sums, added in wavefront order
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[wave][j][v][lane] = acc[j][v];
+    __syncthreads();
+    // lane holds D[row][col] with col = lane % 32, row = 8 (v / 4) + 4 (lane / 32) + v % 4
+    auto row_of = [&](int v) { return 8 * (v >> 2) + 4 * h + (v & 3); };
+    auto sum_of = [&](int j, int v) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStreamWaves; ++w) s += red[w][j][v][lane];
+        return s;
+    };
+    if (a.splits > 1) {
+        // fp32 partials (unscaled) for the split-K reduction: main mode at
+        // the rows' plan positions (the reduction skips padding positions);
+        // T mode at T rows 0 .. Md_pad - 1 (the draft rows, then the zero
+        // padding rows the reduction writes too)
+        if (wave < NB) {
+            const int j = wave;
+            const int64_t col = col0[j] + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int32_t br = row_of(v);
+                const float sv = sum_of(j, v);
+                const int64_t p = TMODE ? (br < info.Md_pad ? br : -1) : s_prow[br];
+                if (p >= 0 && col < a.N) a.partial[(static_cast<int64_t>(z) * a.rows_cap + p) * a.N + col] = sv;
+            }
+        }
+        return;
+    }
+    if constexpr (SWIGLU) {
+        if (wave == 0) {
+            const int64_t ac = c0 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float g = bf16_bits_to_f32(f32_to_bf16_bits(sum_of(0, v) * a.alpha));
+                const float u = bf16_bits_to_f32(f32_to_bf16_bits(sum_of(1, v) * a.alpha));
+                const int32_t orow = s_src[row_of(v)];
+                if (orow >= 0 && ac < a.N / 2)
+                    a.out.y[0][static_cast<int64_t>(orow) * a.out.ldy[0] + ac] =
+                        static_cast<uint16_t>(f32_to_bf16_bits(silu_mul_f32(g, u)));
+            }
+        }
+        return;
+    }
+    if (wave < NB) {
+        const int j = wave;
+        const int64_t col = col0[j] + (lane & 31);
+        const GroupRef g = find_group(a.out, col);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int32_t br = row_of(v);
+            const uint32_t yb = f32_to_bf16_bits(sum_of(j, v) * a.alpha);
+            if (col >= a.N) continue;
+            if constexpr (TMODE) {
+                // T rows in plan order: the draft rows, then zero rows up to Md_pad
+                if (br < info.Md_pad) a.out.y[0][static_cast<int64_t>(br) * a.out.ldy[0] + col] = static_cast<uint16_t>(yb);
+            } else {
+                const int32_t orow = s_src[br];
+                if (orow < 0 || col >= g.end) continue;
+                uint16_t* dst = g.y + static_cast<int64_t>(orow) * g.ldy + (col - g.start);
+                *dst = static_cast<uint16_t>(
+                    a.epi == kEpiAccumulate ? f32_to_bf16_bits(bf16_bits_to_f32(*dst) + bf16_bits_to_f32(yb)) : yb);
+            }
+        }
+    }
+}
+
 // Sum split-K partials in split order, scale, round to bf16 and scatter
 // through the epilogue (SwiGLU: one output per gate / up column pair).
 template <bool TMODE>
@@ -1139,6 +1424,7 @@ struct Tile {
     int nb = 0; // LDS stage buffers when not the default 128 / kb
     int nbb = 0; // > 0: a split ring, two A buffers and nbb B buffers
     int kg = 1;  // K groups of wavefronts (2: twice the wavefronts, alternate sub-steps)
+    int stream = 0;  // > 0: the weight-streaming kernel with this many 32-column blocks (bm, bn unused)
 };
 
 int stage_buffers(Tile t) { return t.nb > 0 ? t.nb : 128 / t.kb; }
@@ -1187,6 +1473,10 @@ int default_kb(int bm, int bn) { return bm * bn >= 256 * 128 ? 32 : 64; }
 Tile env_tile() {
     const char* s = getenv("UNO_GEMM_TILE");
     Tile t{0, 0, 4, false, 64};
+    if (s && strncmp(s, "stream", 6) == 0) {  // the weight-streaming kernel (64 plan rows or fewer)
+        t.stream = 1;
+        return t;
+    }
     if (!s || sscanf(s, "%dx%d", &t.bm, &t.bn) != 2) return Tile{0, 0, 4, false, 64};
     t.kb = default_kb(t.bm, t.bn);
     if (strstr(s, "w8")) t.waves = 8;
@@ -1287,7 +1577,7 @@ Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bo
     if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256) &&
         (!single_kg || forced.kg == 1))
         return forced;
-    if (forced.bm > 0 && !tile_supported(forced)) {
+    if (forced.bm > 0 && forced.stream == 0 && !tile_supported(forced)) {
         static bool warned = false;  // (tuning aid: say once that the forced tile is not one of ours)
         if (!warned) fprintf(stderr, "libuno: UNO_GEMM_TILE=%s is not a supported tile; planning instead\n",
                              getenv("UNO_GEMM_TILE"));
@@ -1340,12 +1630,41 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
         if (strstr(e, "b2")) p.tile.nb = 2;
         if (strstr(e, "kg2")) p.tile.kg = 2;
     }
-    // 64 rows or fewer stream the weights: 64-row tiles, 128-byte row
-    // segments (the SwiGLU launch's 64 x 256 tile with two stage buffers runs
-    // two workgroups per CU: 77 against 89 us for 128 x 256 at M = 32,
-    // N = 28672, K = 4096)
-    if (!tmode && p.rows_cap <= 64 && env_tile().bm == 0)
-        p.tile = bn256 ? Tile{64, 256, 4, false, 64} : Tile{64, 128, 4, false, 64};
+    // 32 rows or fewer (a plan of at most 64 rows): the weight-streaming
+    // kernel for the LoRA down-projection and the SwiGLU launch, where it was
+    // measured faster than the 64-row tiles (one sequence of [16 | 16] rows,
+    // weights cold: gate|up 81 against 90 us, the four down-projections of a
+    // layer 8 us less); the plain projections keep the tiles (q|k|v 25 against
+    // 26, o 23 against 25, down 38 against 65 us: its per-CU streaming rate,
+    // with x read again by every column block, falls short of the tiles'
+    // split of K).  UNO_GEMM_TILE=stream forces it for any epilogue,
+    // UNO_STREAM=0 turns it off (tests and tuning); never for a plan that
+    // must give the bits of a tiled pass (one_pass: the LM head).
+    const Tile forced = env_tile();
+    const char* st_env = getenv("UNO_STREAM");
+    const bool stream = p.rows_cap <= 64 && !one_pass && (forced.stream > 0 || (forced.bm == 0 && (tmode || bn256))) &&
+                        !(tmode && getenv("UNO_T_TILE") != nullptr) && !(st_env && st_env[0] == '0');
+    if (stream) {
+        p.tile = Tile{64, 64, 8, false, 64};
+        p.tile.stream = (bn256 || N > 16384) ? 2 : 1;  // SwiGLU: a gate and an up block
+        p.m_tiles = 1;
+        p.n_tiles = bn256 ? (N / 2 + 31) / 32 : (N + 32 * p.tile.stream - 1) / (32 * p.tile.stream);
+        // no split of K for the projections (one workgroup per column block
+        // streams its rows of W whole); the down-projection's few column
+        // blocks split K to use the GPU: about 192 workgroups, 256 K or more each
+        int64_t sk = 1;
+        if (tmode) sk = std::max<int64_t>(1, std::min<int64_t>(K / 256, 192 / p.n_tiles));
+        if (const char* e = getenv(tmode ? "UNO_T_SPLIT" : "UNO_GEMM_SPLIT")) {
+            const long v = strtol(e, nullptr, 10);
+            if (v >= 1 && v <= 64) sk = v;
+        }
+        p.kps = split_k(K, sk);
+        p.splits = static_cast<int32_t>((K + p.kps - 1) / p.kps);
+        p.partial_bytes = p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * p.rows_cap * N * sizeof(float),
+                                                  kWorkspaceAlign)
+                                       : 0;
+        return p;
+    }
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
     int64_t s;
@@ -1389,7 +1708,16 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
     ka.rows_cap = p.rows_cap;
     const int64_t blocks = p.m_tiles * p.n_tiles * p.splits;
     const Tile t = p.tile;
-    if constexpr (TMODE) {
+    if (t.stream > 0) {
+        const dim3 grid(static_cast<uint32_t>(blocks)), block(kStreamWaves * kWave);
+        if constexpr (TMODE) {
+            hipLaunchKernelGGL((stream_gemm_kernel<1, true, false>), grid, block, 0, stream, ka);
+        } else {
+            if (ka.epi == kEpiSwiglu) hipLaunchKernelGGL((stream_gemm_kernel<2, false, true>), grid, block, 0, stream, ka);
+            else if (t.stream == 2) hipLaunchKernelGGL((stream_gemm_kernel<2, false, false>), grid, block, 0, stream, ka);
+            else hipLaunchKernelGGL((stream_gemm_kernel<1, false, false>), grid, block, 0, stream, ka);
+        }
+    } else if constexpr (TMODE) {
         if (t.bm == 128) launch_tile<128, 128, 2, 2, true>(ka, blocks, stream);
         else if (stage_buffers(t) == 4 && t.kg == 2) launch_tile<64, 128, 2, 2, true, 64, false, 4, 0, 2>(ka, blocks, stream);
         else if (stage_buffers(t) == 4) launch_tile<64, 128, 2, 2, true, 64, false, 4>(ka, blocks, stream);

@@ -341,3 +341,97 @@ def _grouped_case(M, K, group_n, r, check_single=True):
             tg = uno.lora_down(xd, to_dev(ag, "bf16"), plan, 2.0)
             yg = to_host(uno.gated_gemm(xd, to_dev(wg, "bf16"), tg, to_dev(bg, "bf16"), plan))
             assert np.array_equal(yg, outs[g]), g
+
+
+STREAM = [  # M, K, N, r, gate pattern: 32 rows or fewer run the weight-streaming kernel
+    (1, 64, 16, 8, "draft"),
+    (7, 1000, 300, 16, "random"),      # ragged K (a partial last chunk) and N
+    (20, 520, 1024, 128, "random"),
+    (32, 4096, 1024, 128, "seq"),      # one sequence of [16 verify | 16 draft]
+    (32, 4096, 700, 128, "verify"),
+    (32, 2048, 96, 256, "draft"),
+    (29, 14336, 256, 128, "random"),   # the down-projection's depth
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,r,pattern", STREAM)
+def test_weight_streaming_kernel(M, K, N, r, pattern, monkeypatch):
+    """The weight-streaming kernel (forced for the plain epilogue; its LoRA down-projection is
+    split over K) against the oracle; verify rows bitwise those of an all-verify call; the
+    split steps equal the one call."""
+    monkeypatch.setenv("UNO_GEMM_TILE", "stream")
+    rng = np.random.default_rng(M * 3 + K + N)
+    gate = {"random": (rng.random(M) < 0.5).astype(np.uint8), "draft": np.ones(M, np.uint8),
+            "verify": np.zeros(M, np.uint8), "seq": gate_vector(1, M // 2, M - M // 2)}[pattern]
+    inp = gemm_inputs(M, K, N, r, seed=M + 2 * K + N, dtype="bf16", gate=gate)
+    say("gemm streaming", M, K, N, r, pattern)
+    y = _run(inp, "bf16")
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], gate, 2.0)
+    err = floored_rel_err(y, ref)
+    assert err <= BF16_TOL, err
+    y0 = _run(inp, "bf16", gate=np.zeros_like(gate))
+    assert np.array_equal(y[gate == 0], y0[gate == 0]), "verify rows must match the all-verify call bitwise"
+    x, w = to_dev(inp["x"], "bf16"), to_dev(inp["w"], "bf16")
+    a, b = to_dev(inp["a"], "bf16"), to_dev(inp["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, a, plan, 2.0)
+    assert np.array_equal(to_host(uno.gated_gemm(x, w, t, b, plan)), y)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("t_split", ["1", "3", "16"])
+def test_weight_streaming_lora_down_splits_agree(t_split, monkeypatch):
+    """T from the streaming down-projection: the oracle's scale (x A) within bf16 rounding
+    for every split of K (fp32 partials summed in split order)."""
+    M, K, r = 30, 4096, 384
+    rng = np.random.default_rng(40)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    inp = gemm_inputs(M, K, 64, r, seed=41, dtype="bf16", gate=gate)
+    monkeypatch.setenv("UNO_T_SPLIT", t_split)
+    say("streaming lora_down split", t_split)
+    x, a = to_dev(inp["x"], "bf16"), to_dev(inp["a"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = to_host(uno.lora_down(x, a, plan, 2.0)).reshape(-1, r)
+    Md = int(gate.sum())
+    ref = 2.0 * inp["x"][gate == 1].astype(np.float64) @ inp["a"].astype(np.float64).T
+    assert floored_rel_err(t[:Md], ref) <= BF16_TOL
+    assert np.all(t[Md:(Md + 31) // 32 * 32] == 0), "padding rows of T are zero"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 17, 32])
+def test_weight_streaming_grouped_swiglu_residual(M, monkeypatch):
+    """The streaming kernel's epilogues on a layer's shapes (forced for every launch):
+    grouped q|k|v against the oracle per group, SwiGLU bitwise silu_mul of the grouped
+    gate|up, residual add bitwise the separate add."""
+    monkeypatch.setenv("UNO_GEMM_TILE", "stream")
+    K, r = 512, 128
+    rng = np.random.default_rng(M + 5)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    group_n = (512, 128, 128)
+    x, groups = _group_inputs(M, K, group_n, r, 90 + M, gate)
+    say("streaming epilogues", M)
+    xd = to_dev(x, "bf16")
+    w = torch.cat([to_dev(g[0], "bf16") for g in groups])
+    a = torch.cat([to_dev(g[1], "bf16") for g in groups])
+    b = torch.cat([to_dev(g[2], "bf16") for g in groups])
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(xd, a, plan, 2.0)
+    outs = [to_host(o) for o in uno.gated_gemm_grouped(xd, w, t, b, plan, list(group_n))]
+    for g, (wg, ag, bg) in enumerate(groups):
+        err = floored_rel_err(outs[g], oracle.gated_lora(x, wg, ag, bg, gate, 2.0))
+        assert err <= BF16_TOL, (g, err)
+    # SwiGLU over the first two groups as gate (512) and up (2 x 128 -> 256 rows repeated)
+    wg, wu = w[:256].contiguous(), w[256:512].contiguous()
+    bg, bu = b[:256].contiguous(), b[256:512].contiguous()
+    t2 = uno.lora_down(xd, torch.cat([a[:r], a[r:2 * r]]), plan, 2.0)
+    w_p, b_p = uno.swiglu_pack(wg, wu, bg, bu)
+    act = uno.gated_gemm_swiglu(xd, w_p, t2, b_p, plan)
+    gg, uu = uno.gated_gemm_grouped(xd, torch.cat([wg, wu]), t2, torch.cat([bg, bu]), plan, [256, 256])
+    assert torch.equal(act, uno.silu_mul(gg, uu))
+    y0 = sdev.randn((M, 256), 2.0, M + 9)
+    ref = uno.residual_add(y0, uno.gated_gemm(xd, wg, uno.lora_down(xd, a[:r].contiguous(), plan, 2.0), bg, plan))
+    y = y0.clone()
+    uno.gated_gemm_residual(xd, wg, uno.lora_down(xd, a[:r].contiguous(), plan, 2.0), bg, plan, y)
+    assert torch.equal(y, ref)
