@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 SCALE = 2.0                   # alpha / r = 256 / 128
-EARLY_CHUNK = 4  # positions per chunk of the early-exit verifier
+EARLY_CHUNK = 8  # positions in the early-exit verifier's first chunk (then 16, 32, ...)
 
 
 def parse():
@@ -224,8 +224,15 @@ def main():
         ee1.record()
         torch.cuda.synchronize()
         same = all(torch.equal(a, b) for a, b in zip(e_out, (n_acc[last], out_tok[last], n_emit[last])))
-        chunks_read = torch.clamp((n_acc[last].long() + EARLY_CHUNK) // EARLY_CHUNK, max=(L + EARLY_CHUNK - 1) // EARLY_CHUNK)
-        rows_read = torch.clamp(chunks_read * EARLY_CHUNK, max=L).sum().item() / (B * L)
+        # rows streamed: up to the end of the chunk (lengths EARLY_CHUNK, 2 EARLY_CHUNK, ...)
+        # holding the first rejection
+        ends, e, ln = [], 0, EARLY_CHUNK
+        while e < L:
+            e = min(L, e + ln)
+            ends.append(e)
+            ln *= 2
+        na = n_acc[last].cpu().tolist()
+        rows_read = sum(next(x for x in ends if x > min(a, L - 1)) for a in na) / (B * L)
         verify_early = {"chunk": EARLY_CHUNK, "us_per_call": round(ee0.elapsed_time(ee1) / 20 * 1e3, 3),
                         "rows_read_frac": round(rows_read, 4), "same_outputs_as_one_pass": bool(same)}
 

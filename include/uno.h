@@ -305,18 +305,19 @@ uno_status uno_block_verify_noalloc(const void* target_logits, const void* draft
  * Block verification with early exit.  Only the prefix up to the first
  * rejection decides the output ("The Psi-Spec Sampler" on the
  * aifromscratch.in page: the longest valid prefix is kept), so positions are
- * taken in chunks of `chunk`: the logit rows of a chunk are streamed only for
- * sequences with no rejection in earlier chunks, and a sequence stops at the
- * chunk holding its first rejection (the bonus row, if any, streams with the
- * last chunk).  Rows read per sequence fall from L (+1) to about
- * chunk * ceil((n_acc + 1) / chunk).
+ * taken in chunks of chunk, 2 chunk, 4 chunk, ... positions: the logit rows of
+ * a chunk are streamed only for sequences with no rejection in earlier
+ * chunks, and a sequence stops at the chunk holding its first rejection (the
+ * bonus row, if any, streams with the last chunk).  Rows read per sequence
+ * fall from L (+1) to the end of that chunk.
  *
  * Arguments, arithmetic, domain and outputs are those of uno_block_verify,
  * plus chunk in [1, 64]; every output equals uno_block_verify's bit for bit
  * (a row's statistics are formed with the same chunking of V, and every
- * position is decided by the same code).  Launches 2 * ceil(L / chunk) + 2
- * kernels instead of 2, so it pays where rejections come early and rows
- * are long.
+ * position is decided by the same code).  Launches one statistics kernel per
+ * chunk -- each opens with the decision on the positions before its chunk,
+ * and a sequence already rejected streams nothing -- then the one-pass
+ * verifier's tail, so it pays where rejections come early and rows are long.
  * workspace: at least uno_block_verify_early_workspace_size() bytes.
  * ------------------------------------------------------------------------ */
 size_t uno_block_verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus);

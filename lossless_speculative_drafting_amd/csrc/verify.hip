@@ -114,20 +114,18 @@ __device__ __forceinline__ Online wave_merge(Online o, float c2) {
 
 // ---------------------------------------------------------------- row_stats
 // Rows are (s, i) with i in [i0, i0 + rows_per_seq) of rows_full rows per
-// sequence; array B exists for i < rows_with_b.  With live flags, sequences
-// whose flag is 0 are skipped (their statistics are not written).
+// sequence; array B exists for i < rows_with_b.  Workgroup blk takes chunk
+// blk % n_chunks of row blk / n_chunks.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(
-    const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
+__device__ __forceinline__ void row_stats_body(
+    int64_t blk, const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
     int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
-    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full, const int32_t* __restrict__ live) {
-    const int64_t blk = blockIdx.x;
+    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full) {
     const int64_t lrow = blk / n_chunks;
     const int32_t c = static_cast<int32_t>(blk % n_chunks);
     const int64_t s = lrow / rows_per_seq;
     const int32_t i = i0 + static_cast<int32_t>(lrow % rows_per_seq);
     const int64_t row = s * rows_full + i;
-    if (live != nullptr && live[s] == 0) return;  // uniform for the workgroup
     const size_t esz = BF16 ? 2 : 4;
     const char* arow = static_cast<const char*>(A) + (s * a_stride + static_cast<int64_t>(i) * V) * esz;
     const bool has_b = (B != nullptr) && (i < rows_with_b);
@@ -187,6 +185,15 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
         st.mB = rb.m;
         stats[row * n_chunks + c] = st;
     }
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void row_stats_kernel(
+    const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
+    int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
+    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full) {
+    row_stats_body<BF16, VEC>(blockIdx.x, A, a_stride, B, b_stride, rows_per_seq, rows_with_b, V, chunk, n_chunks,
+                              c2, stats, i0, rows_full);
 }
 
 // Merge the chunk statistics of one row in fp64: M = max, S = sum s_c e^{(m_c - M)/T}.
@@ -430,26 +437,32 @@ __global__ __launch_bounds__(kThreads) void verify_decide_kernel(DecideArgs a) {
 }
 
 // ---------------------------------------------------------------- early exit
-// Verification in chunks of positions: the statistics of positions [i0, i1)
-// are streamed only for sequences with no rejection before i0, and this
-// kernel (one wavefront per sequence) clears a sequence's live flag at its
-// first rejection (or out-of-range token) in [i0, i1).
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void chunk_decide_kernel(DecideArgs a, int32_t i0, int32_t i1,
-                                                                int32_t* __restrict__ live) {
-    const int lane = threadIdx.x % kWave;
-    const int64_t s = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
-    if (s >= a.B) return;  // whole wavefronts leave together; no block barrier follows
-    if (live[s] == 0) return;
-    const bool in = lane >= i0 && lane < i1;
-    const LaneDecision d = lane_decision<BF16>(a, s, lane, in, in);
-    const uint64_t stop = __ballot(in && (!d.valid || !d.acc));
-    if (lane == 0 && stop != 0) live[s] = 0;
-}
-
-__global__ __launch_bounds__(kThreads) void live_init_kernel(int32_t* __restrict__ live, int64_t B) {
-    const int64_t s = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (s < B) live[s] = 1;
+// Statistics of positions [i0, i0 + rows_per_seq) streamed only for
+// sequences with no rejection (and no out-of-range token) before i0: each
+// workgroup's first wavefront decides positions 0 .. i0 - 1 from the
+// statistics earlier launches wrote (lane_decision, the decision every
+// verifier takes), and the workgroup leaves if one of them is rejected.  A
+// sequence's statistics are then missing only past its first rejection,
+// where no output depends on them.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void row_stats_gated_kernel(
+    DecideArgs da, int32_t rows_per_seq, int32_t rows_with_b, int64_t chunk, int32_t n_chunks, float c2,
+    ChunkStat* __restrict__ stats, int32_t i0) {
+    __shared__ int32_t s_stop;
+    const int64_t s = (static_cast<int64_t>(blockIdx.x) / n_chunks) / rows_per_seq;
+    if (i0 > 0) {
+        if (threadIdx.x < kWave) {
+            const int lane = static_cast<int>(threadIdx.x);
+            const bool in = lane < i0;
+            const LaneDecision d = lane_decision<BF16>(da, s, lane, in, in);
+            const uint64_t stop = __ballot(in && (!d.valid || !d.acc));
+            if (lane == 0) s_stop = stop != 0;
+        }
+        __syncthreads();
+        if (s_stop) return;  // uniform for the workgroup
+    }
+    row_stats_body<BF16, VEC>(blockIdx.x, da.target, da.t_stride, da.draft, da.d_stride, rows_per_seq, rows_with_b,
+                              da.V, chunk, n_chunks, c2, stats, i0, da.L + da.nb);
 }
 
 // ---------------------------------------------------------------- draft_decide
@@ -1066,7 +1079,7 @@ bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
 }
 
 // chunk = 0: one pass over every row; chunk > 0: early exit, positions in
-// chunks of `chunk` (the live flags follow the plan's workspace).
+// chunks of `chunk`.
 template <bool BF16, bool VEC>
 hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const int32_t nb = pr.has_bonus ? 1 : 0;
@@ -1099,22 +1112,19 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
     if (chunk <= 0) {
         hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
                            0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
-                           p.chunk1, p.c1, c2, stats, 0, pr.L + nb, nullptr);
+                           p.chunk1, p.c1, c2, stats, 0, pr.L + nb);
     } else {
-        // The statistics of a row are the same bits as in the one-pass plan
-        // (same chunking of V), so every decision is the one-pass decision.
-        int32_t* live = reinterpret_cast<int32_t*>(base + p.total);
-        const uint32_t sblocks = static_cast<uint32_t>((pr.B + kThreads - 1) / kThreads);
-        hipLaunchKernelGGL(live_init_kernel, dim3(sblocks), dim3(kThreads), 0, stream, live, pr.B);
-        const uint32_t dblocks = static_cast<uint32_t>((pr.B + kThreads / kWave - 1) / (kThreads / kWave));
-        for (int32_t i0 = 0; i0 < pr.L; i0 += chunk) {
-            const int32_t i1 = std::min(pr.L, i0 + chunk);
+        // One statistics launch per chunk of positions, each gated by the
+        // decision on the positions before it; chunks double in length
+        // (chunk, 2 chunk, 4 chunk, ...): most sequences stop in the first,
+        // and the few that go on are served in few launches.  The statistics
+        // of a row are the same bits as in the one-pass plan (same chunking
+        // of V), so every decision is the one-pass decision.
+        for (int32_t i0 = 0, len = chunk; i0 < pr.L; i0 += len, len *= 2) {
+            const int32_t i1 = std::min(pr.L, i0 + len);
             const int32_t nrows = (i1 - i0) + (i1 == pr.L ? nb : 0);  // the bonus row rides with the last chunk
-            hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * nrows * p.c1)),
-                               dim3(kThreads), 0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, nrows,
-                               pr.L, pr.V, p.chunk1, p.c1, c2, stats, i0, pr.L + nb, live);
-            hipLaunchKernelGGL((chunk_decide_kernel<BF16>), dim3(dblocks), dim3(kThreads), 0, stream, da, i0, i1,
-                               live);
+            hipLaunchKernelGGL((row_stats_gated_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(pr.B * nrows * p.c1)),
+                               dim3(kThreads), 0, stream, da, nrows, pr.L, p.chunk1, p.c1, c2, stats, i0);
         }
     }
     launch_tail<BF16, VEC>(da, p.nseg, false, c2, seg, reinterpret_cast<double*>(base + p.off_tot), stream);
@@ -1133,7 +1143,7 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
     hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
                        stream, pr.draft, pr.d_stride, nullptr, int64_t(0), pr.L, 0, pr.V, p.chunk1, p.c1, c2,
-                       stats, 0, pr.L, nullptr);
+                       stats, 0, pr.L);
     hipLaunchKernelGGL((draft_decide_kernel<BF16>), dim3(static_cast<uint32_t>((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, invT, stats, p.c1,
                        pr.uniforms, pr.sampled, jobs);
@@ -1152,7 +1162,7 @@ size_t verify_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus)
 }
 
 size_t verify_early_workspace_size(int64_t B, int32_t L, int64_t V, int32_t has_bonus) {
-    return verify_workspace_size(B, L, V, has_bonus) + align_up(static_cast<size_t>(B) * sizeof(int32_t), kWorkspaceAlign);
+    return verify_workspace_size(B, L, V, has_bonus);
 }
 
 size_t draft_sample_workspace_size(int64_t B, int32_t L, int64_t V) {
