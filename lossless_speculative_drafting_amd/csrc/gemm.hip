@@ -366,13 +366,16 @@ struct TileCfg {
     static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
     // The output-row table (BM int32) goes behind the epilogue's staging area
     // in the stage buffers when they have room for it, else into LDS of its own.
-    static constexpr bool OROW_IN_STAGE = LDS_ELEMS * 2 >= BM * BN * 2 + BM * 4;
+    // (tiles that may run the statistics epilogue also keep each row's drafted
+    // token and statistics slot there: three int32 per tile row)
+    static constexpr int ROWTAB = BN == kStatCols ? 3 : 1;
+    static constexpr bool OROW_IN_STAGE = LDS_ELEMS * 2 >= BM * BN * 2 + ROWTAB * BM * 4;
     // K groups hand accumulators over through the stage buffers, which are
     // free after the main loop (the row table and the staging come after)
     static constexpr int XCH_BYTE = 0;
     static_assert(KG == 1 || (OROW_IN_STAGE && XCH_BYTE + NWAVES_T * BM / WGM * BN / WGN * 4 <= LDS_ELEMS * 2),
                   "K-group exchange must fit in the stage buffers");
-    static_assert(LDS_ELEMS * 2 + (OROW_IN_STAGE ? 0 : BM * 4) <= 160 * 1024, "LDS");
+    static_assert(LDS_ELEMS * 2 + (OROW_IN_STAGE ? 0 : ROWTAB * BM * 4) <= 160 * 1024, "LDS");
     static_assert(THREADS >= BM, "one output row per thread");
     static_assert(BM * BN <= LDS_ELEMS, "epilogue staging must fit in the stage buffers");
 };
@@ -392,27 +395,31 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
     const int p = lane & 7;  // this lane's part of its row
     constexpr int kRowsPerPass = 8 * C::NWAVES;
     static_assert(C::BM_ % kRowsPerPass == 0, "whole passes over the tile rows");
+    // only the last column tile can reach past N (a uniform branch; the
+    // per-value tests are 32-bit)
+    const bool ragged = n0 + kStatCols > a.N;
+    const int32_t ncol = ragged ? static_cast<int32_t>(a.N - n0) : kStatCols;
 #pragma unroll
     for (int it = 0; it < C::BM_ / kRowsPerPass; ++it) {
         const int R = it * kRowsPerPass + wave * 8 + (lane >> 3);
         const int32_t orow = s_orow[R];
+        const int32_t tok = s_orow[C::BM_ + R];     // drafted token of the row (-1: none)
+        const int32_t sm = s_orow[2 * C::BM_ + R];  // its statistics slot (-1: none)
         const int wm_r = R / C::WM, rl = R % C::WM;
         const uint16_t* rowp = smem + wm_r * WGN * C::WM * C::WN + rl * C::WN;
         const int sw = ((rl >> 2) & 1) << 5;
-        const int32_t tok = orow >= 0 ? a.row_token[orow] : -1;
         const int64_t dt = static_cast<int64_t>(tok) - n0;  // token's column in the tile
         Online o{-INFINITY, 0.0};
-        float g = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = 64 * q + 8 * p;  // tile column of the vector
             const int wn_c = c / C::WN, cc = c % C::WN;
             float v[8];
             unpack8(*reinterpret_cast<const uint4*>(rowp + wn_c * C::WM * C::WN + (cc ^ sw)), v);
+            if (ragged) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (n0 + c + j >= a.N) v[j] = -INFINITY;
-                if (dt == c + j) g = v[j];
+                for (int j = 0; j < 8; ++j)
+                    if (c + j >= ncol) v[j] = -INFINITY;
             }
             online_add8(o, v, a.c2);
         }
@@ -422,7 +429,6 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
             o = online_merge(o, q, a.c2);
         }
         if (orow < 0) continue;
-        const int32_t sm = a.stat_map[orow];
         if (p == 0 && sm >= 0) {
             ChunkStat* st = a.stats + static_cast<int64_t>(sm >> 1) * a.stat_ld + nt;
             if (sm & 1) {
@@ -433,8 +439,12 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
                 st->mA = o.m;
             }
         }
-        if (tok >= 0 && tok < a.N && dt >= 0 && dt < kStatCols && ((dt >> 3) & 7) == p)
-            a.gathered[orow] = g;
+        // the drafted token's logit, when its column is in this tile: one
+        // lane of the row reads it from the staged tile
+        if (p == 0 && tok >= 0 && tok < a.N && dt >= 0 && dt < kStatCols) {
+            const int d = static_cast<int>(dt);
+            a.gathered[orow] = bf16_bits_to_f32(rowp[(d / C::WN) * C::WM * C::WN + ((d % C::WN) ^ sw)]);
+        }
     }
 }
 
@@ -475,7 +485,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
     constexpr int RB = C::RB;
     constexpr int MI = C::MI, NJ = C::NJ, AQ = C::AQ, BQ = C::BQ;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[C::LDS_ELEMS];
-    __shared__ int32_t s_orow_own[C::OROW_IN_STAGE ? 1 : BM];
+    __shared__ int32_t s_orow_own[C::OROW_IN_STAGE ? 1 : C::ROWTAB * BM];
     // output row of each tile row (-1: none)
     int32_t* const s_orow = C::OROW_IN_STAGE ? reinterpret_cast<int32_t*>(smem + BM * BN) : s_orow_own;
 
@@ -524,7 +534,23 @@ void gated_gemm_kernel(const GemmKArgs a) {
             if (a.out_compact && my_orow >= 0) my_orow = static_cast<int32_t>(m0 + tid);
         }
     }
-    if (!C::OROW_IN_STAGE && tid < BM) s_orow[tid] = my_orow;
+    // statistics epilogue: the row's drafted token and statistics slot, also
+    // loaded now (they land during the main loop instead of holding up the
+    // epilogue, when nothing else runs on the CU)
+    int32_t my_tok = -1, my_sm = -1;
+    if constexpr (C::ROWTAB == 3) {
+        if (a.epi == kEpiStats && my_orow >= 0) {
+            my_tok = a.row_token[my_orow];
+            my_sm = a.stat_map[my_orow];
+        }
+    }
+    if (!C::OROW_IN_STAGE && tid < BM) {
+        s_orow[tid] = my_orow;
+        if constexpr (C::ROWTAB == 3) {
+            s_orow[BM + tid] = my_tok;
+            s_orow[2 * BM + tid] = my_sm;
+        }
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar: per-block decisions stay uniform
     const int lane = tid % kWave;
     const int kg = wave / C::NWAVES_T;  // K group (scalar)
@@ -920,7 +946,13 @@ void gated_gemm_kernel(const GemmKArgs a) {
     }
     if constexpr (C::OROW_IN_STAGE) {
         __syncthreads();  // every wavefront is done with the stage buffers
-        if (tid < BM) s_orow[tid] = my_orow;
+        if (tid < BM) {
+            s_orow[tid] = my_orow;
+            if constexpr (C::ROWTAB == 3) {
+                s_orow[BM + tid] = my_tok;
+                s_orow[2 * BM + tid] = my_sm;
+            }
+        }
         __syncthreads();
     }
     // lane holds D[row][col] of each 32x32 block with col = lane % 32 and
