@@ -382,8 +382,8 @@ struct TileCfg {
 
 // Statistics epilogue over a staged BM x kStatCols tile (bf16, staged per
 // wavefront as [WM][WN] with the column XOR of the store path).  Eight lanes
-// take one row: lane p of the eight accumulates, in order, the 8-column
-// vectors p, p + 8, p + 16, p + 24 of the row (an online max / sum of exp),
+// take one row: lane p of the eight accumulates the 8-column vectors p,
+// p + 8 together, then p + 16, p + 24 (an online max / sum of exp),
 // then the eight states merge in an xor tree (offsets 4, 2, 1).  At each step
 // the eight lanes of a row read eight different 16-byte chunks of one staged
 // 64-column block, and two rows fill the 16 bank groups, so the reads are
@@ -411,17 +411,20 @@ __device__ __forceinline__ void stats_epilogue(const GemmKArgs& a, const uint16_
         const int64_t dt = static_cast<int64_t>(tok) - n0;  // token's column in the tile
         Online o{-INFINITY, 0.0};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 64 * q + 8 * p;  // tile column of the vector
-            const int wn_c = c / C::WN, cc = c % C::WN;
-            float v[8];
-            unpack8(*reinterpret_cast<const uint4*>(rowp + wn_c * C::WM * C::WN + (cc ^ sw)), v);
-            if (ragged) {
+        for (int q2 = 0; q2 < 2; ++q2) {  // vectors 2 q2 and 2 q2 + 1, sixteen values at a time
+            float v[16];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (c + j >= ncol) v[j] = -INFINITY;
+            for (int h = 0; h < 2; ++h) {
+                const int c = 64 * (2 * q2 + h) + 8 * p;  // tile column of the vector
+                const int wn_c = c / C::WN, cc = c % C::WN;
+                unpack8(*reinterpret_cast<const uint4*>(rowp + wn_c * C::WM * C::WN + (cc ^ sw)), v + 8 * h);
+                if (ragged) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (c + j >= ncol) v[8 * h + j] = -INFINITY;
+                }
             }
-            online_add8(o, v, a.c2);
+            online_add16(o, v, a.c2);
         }
 #pragma unroll
         for (int off = 4; off >= 1; off >>= 1) {

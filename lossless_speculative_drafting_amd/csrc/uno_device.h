@@ -66,25 +66,57 @@ struct Online {
     double s;
 };
 
+// max of three (one v_max3_f32); maxima are exact, so the grouping of a
+// max tree changes no bits
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Rescale a running state to the maximum m of the values being added:
+// s e^{(m_old - m)/T} when the maximum grows and s is not empty, else s
+// unchanged.  Selects, not branches: both sides are formed and one is kept.
+__device__ __forceinline__ double online_rescale(const Online& o, bool grow, float m, float c2) {
+#pragma clang fp contract(off)
+    const float f = fast_exp2((o.m - m) * c2);
+    const double scaled = o.s * static_cast<double>(f);
+    return (grow && o.s != 0.0) ? scaled : o.s;
+}
+
 // Add eight logits: fp32 exponentials of the max-subtracted values, summed in
-// a fixed pairwise order in fp32, accumulated in fp64.  Written without
-// branches (selects keep the untaken side's value), so that a wavefront runs
-// it in lockstep: rescaling an empty state (s = 0) and adding a set that is
-// all -inf both leave the state as it was, bit for bit.
+// a fixed pairwise order in fp32, accumulated in fp64.  Rescaling an empty
+// state (s = 0) and adding a set that is all -inf both leave the state as it
+// was, bit for bit.
 __device__ __forceinline__ void online_add8(Online& o, const float* v, float c2) {
 #pragma clang fp contract(off)
-    const float vm = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                           fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    const float vm = fmaxf(max3f(v[0], v[1], v[2]), max3f(max3f(v[3], v[4], v[5]), v[6], v[7]));
     const bool grow = vm > o.m;
-    const float f = fast_exp2((o.m - vm) * c2);
-    if (grow && o.s != 0.0) o.s *= static_cast<double>(f);
     const float m = grow ? vm : o.m;
-    o.m = m;
+    const double s = online_rescale(o, grow, m, c2);
     float e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] = fast_exp2((v[j] - m) * c2);
     const float t = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    if (m != -INFINITY) o.s += static_cast<double>(t);
+    o.m = m;
+    o.s = m != -INFINITY ? s + static_cast<double>(t) : s;
+}
+
+// Add sixteen logits (two vectors of eight) the same way, with one maximum,
+// one rescale and one fp64 addition for the sixteen: the pairwise fp32 sum
+// runs over all sixteen exponentials.  The form the statistics passes use
+// (the row statistics of verification and the LM head's epilogue), so that
+// their per-value work is mostly the exponentials.
+__device__ __forceinline__ void online_add16(Online& o, const float* v, float c2) {
+#pragma clang fp contract(off)
+    const float vm = fmaxf(max3f(max3f(v[0], v[1], v[2]), max3f(v[3], v[4], v[5]), max3f(v[6], v[7], v[8])),
+                           max3f(max3f(v[9], v[10], v[11]), max3f(v[12], v[13], v[14]), v[15]));
+    const bool grow = vm > o.m;
+    const float m = grow ? vm : o.m;
+    const double s = online_rescale(o, grow, m, c2);
+    float e[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) e[j] = fast_exp2((v[j] - m) * c2);
+    const float t = (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+                    (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
+    o.m = m;
+    o.s = m != -INFINITY ? s + static_cast<double>(t) : s;
 }
 
 // Merge two running states: s = s_a e^{(m_a - m)/T} + s_b e^{(m_b - m)/T}

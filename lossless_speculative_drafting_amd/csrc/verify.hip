@@ -136,20 +136,18 @@ __device__ __forceinline__ void row_stats_body(
 
     Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
     int64_t k = k0 + static_cast<int64_t>(threadIdx.x) * kVec;
-    // two vectors per array in flight per iteration
+    // two vectors per array in flight per iteration, added sixteen values at a time
     for (; k + kStatTile < k1; k += 2 * kStatTile) {
-        float va0[kVec], va1[kVec];
-        load8<BF16, VEC>(arow, k, V, va0);
-        load8<BF16, VEC>(arow, k + kStatTile, V, va1);
+        float va[2 * kVec];
+        load8<BF16, VEC>(arow, k, V, va);
+        load8<BF16, VEC>(arow, k + kStatTile, V, va + kVec);
         if (has_b) {
-            float vb0[kVec], vb1[kVec];
-            load8<BF16, VEC>(brow, k, V, vb0);
-            load8<BF16, VEC>(brow, k + kStatTile, V, vb1);
-            online_add8(ob, vb0, c2);
-            online_add8(ob, vb1, c2);
+            float vb[2 * kVec];
+            load8<BF16, VEC>(brow, k, V, vb);
+            load8<BF16, VEC>(brow, k + kStatTile, V, vb + kVec);
+            online_add16(ob, vb, c2);
         }
-        online_add8(oa, va0, c2);
-        online_add8(oa, va1, c2);
+        online_add16(oa, va, c2);
     }
     if (k < k1) {
         float va[kVec];
