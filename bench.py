@@ -434,6 +434,11 @@ def platform_info(torch):
             info["rocm"] = f.read().strip()
     except OSError:
         pass
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # (under the profiler the tool's library is preloaded into every child;
+        # rocm-smi's launcher would replace itself in a process that has it)
+        info["smi"] = "not queried under the profiler"
+        return info
     try:
         out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--showperflevel",
                               "--json"], capture_output=True, text=True, timeout=30)

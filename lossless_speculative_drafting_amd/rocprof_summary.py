@@ -9,6 +9,19 @@
         Run one plain device copy of N MiB (torch copy_ of a bf16 tensor): the
         known-size reference whose FETCH_SIZE / WRITE_SIZE calibrate the counters.
 
+    python -m lossless_speculative_drafting_amd.rocprof_summary trace KERNEL_TRACE_CSV --match SUBSTRING ...
+        Launches of a `--kernel-trace` run by kernel and grid (calls, average,
+        median, min, max duration), in order of first launch.
+
+    python -m lossless_speculative_drafting_amd.rocprof_summary counters CSV [CSV ...] \\
+        --group NAME=SUBSTRING ... [--copy-fetch CSV --copy-write CSV --copy-mib N] [--cus N]
+        Per-dispatch averages of every counter of `--pmc` runs by kernel group,
+        with derived figures: scaled FETCH_SIZE / WRITE_SIZE bytes and their
+        rate over the counter run's duration, the clock (GRBM_GUI_ACTIVE, which
+        adds up the --xcds XCDs' busy cycles, per XCD over the duration), MFMA
+        busy as a share of the SIMD cycles (over cycles x CUs x 4), bf16 MFMA
+        flop (512 per MOP), L2 hit rate, LDS bank-conflict cycles.
+
     python -m lossless_speculative_drafting_amd.rocprof_summary traffic \\
         --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --copy-mib N \\
         --key NAME --launch SUBSTRING [--also SUBSTRING] --source FILE ...
@@ -147,6 +160,99 @@ def traffic(args):
     print(text)
 
 
+def _dispatches(path):
+    """{dispatch id: (kernel name, duration ns, {counter: value summed over its rows})}."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        if d not in out:
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            out[d] = (r["Kernel_Name"], dur, defaultdict(float))
+        out[d][2][r["Counter_Name"]] += float(r["Counter_Value"])
+    return out
+
+
+def counters(args):
+    """Per-dispatch averages of every counter in one or more --pmc runs, by kernel group,
+    with the derived figures the counters allow (see the table notes)."""
+    scale = {}
+    known = args.copy_mib * float(1 << 20)
+    if args.copy_fetch:
+        scale["FETCH_SIZE"] = known / (_copy_kib(args.copy_fetch, "FETCH_SIZE") * 1024.0)
+    if args.copy_write:
+        scale["WRITE_SIZE"] = known / (_copy_kib(args.copy_write, "WRITE_SIZE") * 1024.0)
+    groups = [g.split("=", 1) for g in args.group]
+    rows = []
+    for path in args.csv:
+        disp = _dispatches(path)
+        for gname, sub in groups:
+            sel = [v for v in disp.values() if sub in v[0]]
+            if not sel:
+                continue
+            n = len(sel)
+            dur_us = sum(v[1] for v in sel) / n / 1e3
+            avg = defaultdict(float)
+            for v in sel:
+                for k, x in v[2].items():
+                    avg[k] += x / n
+            rows.append((gname, os.path.basename(os.path.dirname(path)) or path, n, dur_us, dict(avg)))
+    cus = args.cus
+    lines = [f"| group | run | dispatches | us per dispatch (counter run) | figures per dispatch |",
+             "|---|---|---:|---:|---|"]
+    for gname, run, n, dur_us, c in rows:
+        figs = []
+        for k in ("FETCH_SIZE", "WRITE_SIZE"):
+            if k in c:
+                b = c[k] * 1024.0 * scale.get(k, 1.0)
+                figs.append(f"{k} {b / 1e6:.2f} MB{' (scaled)' if k in scale else ' (raw KiB x 1024)'}"
+                            f" = {b / dur_us / 1e3:.0f} GB/s")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if gui:
+            cyc = gui / args.xcds  # (the counter adds up the busy cycles of every XCD)
+            figs.append(f"{cyc / (dur_us * 1e3) * 1e3:.0f} MHz (GPU-busy cycles per XCD over the duration)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                figs.append(f"MFMA busy {100.0 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * cus * 4):.1f}% of SIMD cycles")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            fl = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+            figs.append(f"bf16 MFMA {fl / 1e9:.1f} GFLOP = {fl / dur_us / 1e6:.0f} TFLOP/s")
+        if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+            tot = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+            figs.append(f"L2 hit {100.0 * c['TCC_HIT_sum'] / max(tot, 1.0):.1f}%")
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
+            figs.append(f"LDS bank-conflict cycles {100.0 * c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1.0):.1f}% of LDS-active")
+        raw = ", ".join(f"{k} {v:.4g}" for k, v in sorted(c.items()))
+        lines.append(f"| {gname} | {run} | {n} | {dur_us:.2f} | {'; '.join(figs)}<br>raw: {raw} |")
+    text = "\n".join(lines)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text + "\n")
+    print(text)
+
+
+def trace(args):
+    """Launches of a `--kernel-trace` run by kernel and grid: calls and duration
+    statistics, for the kernels whose names contain one of the --match substrings."""
+    groups = defaultdict(list)
+    first = {}
+    for r in csv.DictReader(open(args.csv)):
+        name = r["Kernel_Name"]
+        hit = next((m for m in args.match if m in name), None)
+        if hit is None:
+            continue
+        key = (_short(name), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]),
+               int(r["Workgroup_Size_X"]))
+        d = int(r["Dispatch_Id"])
+        first[key] = min(first.get(key, d), d)
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid (threads) | workgroup | calls | avg us | median us | min us | max us |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for key in sorted(groups, key=lambda k: first[k]):
+        v = sorted(groups[key])
+        lines.append(f"| `{key[0]}` | {key[1]} | {key[2]} | {len(v)} | {sum(v) / len(v):.2f} | "
+                     f"{v[len(v) // 2]:.2f} | {v[0]:.2f} | {v[-1]:.2f} |")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -167,8 +273,20 @@ def main(argv=None):
     t.add_argument("--also", action="append", default=[])
     t.add_argument("--source", action="append", required=True)
     t.add_argument("--out", default=None)
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--match", action="append", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("csv", nargs="+")
+    k.add_argument("--group", action="append", required=True, help="NAME=SUBSTRING of the kernel name")
+    k.add_argument("--copy-fetch", default=None)
+    k.add_argument("--copy-write", default=None)
+    k.add_argument("--copy-mib", type=int, default=1024)
+    k.add_argument("--cus", type=int, default=256)
+    k.add_argument("--xcds", type=int, default=8)
+    k.add_argument("--out", default=None)
     args = ap.parse_args(argv)
-    {"stats": stats, "copy-probe": copy_probe, "traffic": traffic}[args.cmd](args)
+    {"stats": stats, "copy-probe": copy_probe, "traffic": traffic, "counters": counters, "trace": trace}[args.cmd](args)
 
 
 if __name__ == "__main__":
