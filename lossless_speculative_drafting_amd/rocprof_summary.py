@@ -243,13 +243,15 @@ def trace(args):
                int(r["Workgroup_Size_X"]))
         d = int(r["Dispatch_Id"])
         first[key] = min(first.get(key, d), d)
-        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        groups[key].append((d, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     lines = ["| kernel | grid (threads) | workgroup | calls | avg us | median us | min us | max us |",
              "|---|---:|---:|---:|---:|---:|---:|---:|"]
     for key in sorted(groups, key=lambda k: first[k]):
-        v = sorted(groups[key])
+        v = sorted(t for _, t in groups[key])
         lines.append(f"| `{key[0]}` | {key[1]} | {key[2]} | {len(v)} | {sum(v) / len(v):.2f} | "
                      f"{v[len(v) // 2]:.2f} | {v[0]:.2f} | {v[-1]:.2f} |")
+        if args.calls:  # every call's duration, in launch order
+            lines.append("|  | calls in order: " + " ".join(f"{t:.1f}" for _, t in sorted(groups[key])) + " |||||||")
     print("\n".join(lines))
 
 
@@ -276,6 +278,7 @@ def main(argv=None):
     tr = sub.add_parser("trace")
     tr.add_argument("csv")
     tr.add_argument("--match", action="append", required=True)
+    tr.add_argument("--calls", action="store_true", help="also list every call's duration in launch order")
     k = sub.add_parser("counters")
     k.add_argument("csv", nargs="+")
     k.add_argument("--group", action="append", required=True, help="NAME=SUBSTRING of the kernel name")
