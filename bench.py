@@ -96,8 +96,8 @@ def committed_traffic(kernel_key, digest):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
