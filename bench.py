@@ -51,7 +51,7 @@ def parse():
     # (the per-workload measurements of the other configurations: skipped,
     # or only one of them -- profiling runs)
     ap.add_argument("--no-configs", action="store_true")
-    ap.add_argument("--only-config", default=None, choices=["layer_b1", "layer_b64", "serve_b256"])
+    ap.add_argument("--only-config", default=None, choices=["tiny", "layer_b1", "layer_b64", "serve_b256"])
     return ap.parse_args()
 
 
@@ -549,6 +549,75 @@ def _verify_measure(uno, sdev, torch, B, L, V, seed, kind, sigma, temps, dev, co
     return res
 
 
+def measure_tiny(uno, sdev, torch, dev, reps=10):
+    """The small fp32 configuration: one 512 -> 512 gated-LoRA projection over
+    2 sequences x [8 verify | 4 draft] rows, and block verification of 10**6
+    trials of one block (L = 4, V = 64, fp32 logits broadcast with sequence
+    stride 0: the same block for every trial, as in the lossless chi-square
+    test).  Both are latency-bound; reported as time per call, trials and
+    verified tokens per second, and the mean emitted length beside its
+    closed form (sum over m < L of the product of the first m acceptance
+    rates, sum min(p, q) per position)."""
+    import numpy as np
+
+    from synthetic import WORKLOADS, gate_vector, gemm_inputs, verify_inputs
+
+    wl = WORKLOADS["tiny"]
+    L, V, T = wl.block, wl.vocab, 1.0
+    trials = int(wl.extra["trials"])
+    gate = gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)
+    (_, K, N), = wl.projections
+    inp = gemm_inputs(gate.size, K, N, 128, seed=wl.seed, dtype="f32", gate=gate)
+    x, w, a, b = (torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev) for k in ("x", "w", "a", "b"))
+    g = torch.from_numpy(gate).to(dev)
+    ws = uno.Workspace(dev)
+    y = uno.gated_lora_fwd(x, w, a, b, g, SCALE, workspace=ws)
+    tg = []
+    for _ in range(reps):
+        e0, e1 = _events(torch)
+        torch.cuda._sleep(200_000)
+        e0.record()
+        uno.gated_lora_fwd(x, w, a, b, g, SCALE, out=y, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        tg.append(e0.elapsed_time(e1) * 1e3)
+    z, d = verify_inputs(1, L, V, wl.seed, "normal", wl.target_sigma, wl.draft_sigmas[0], dtype="f32")
+    zt, dt = (torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev) for v in (z, d))
+    xd = uno.draft_sample(dt, uno.philox_uniforms(0, 1, 0, trials * L, device=dev), T, B=trials, L=L, V=V,
+                          seq_stride=0)
+    u = uno.philox_uniforms(0, 0, 0, trials * (L + 1), device=dev)
+    vws = uno.Workspace(dev)
+    outs = (torch.empty(trials, dtype=torch.int32, device=dev), torch.empty((trials, L + 1), dtype=torch.int32, device=dev),
+            torch.empty(trials, dtype=torch.int32, device=dev))
+    call = lambda: uno.block_verify(zt, dt, xd, u, T, False, B=trials, L=L, V=V, target_seq_stride=0,  # noqa: E731
+                                    draft_seq_stride=0, outputs=outs, workspace=vws)
+    call()
+    tv = []
+    for _ in range(reps):
+        e0, e1 = _events(torch)
+        torch.cuda._sleep(200_000)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        tv.append(e0.elapsed_time(e1) * 1e3)
+    t_v = _median(tv)
+    emitted = int(outs[2].sum().item())
+    zz, dd = z[0].astype(np.float64), d[0].astype(np.float64)
+    p = np.exp(zz - zz.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    q = np.exp(dd - dd.max(axis=1, keepdims=True))
+    q /= q.sum(axis=1, keepdims=True)
+    alpha = np.minimum(p, q).sum(axis=1)
+    expect = float(sum(np.prod(alpha[:m]) for m in range(L)))
+    return {"workload": "one 512->512 fp32 gated-LoRA projection over 2 seqs x [8 verify | 4 draft] rows; verify "
+                        "10^6 trials of one block (L=4, V=64, fp32, sequence stride 0), T=1",
+            "gemm": {"us_per_call": round(_median(tg), 2)},
+            "verify": {"us_per_call": round(t_v, 2), "trials_per_s": round(trials / (t_v * 1e-6), 1),
+                       "verified_tokens_per_s": round(emitted / (t_v * 1e-6), 1),
+                       "mean_emitted": round(emitted / trials, 5), "mean_emitted_closed_form": round(expect, 5)}}
+
+
 def measure_layer_b1(uno, sdev, torch, dev):
     """Batch 1 (one sequence of [16 verify | 16 draft] rows): the layer's
     gated GEMMs stream their weights (HBM-bound, ~31 flop/B), verification
@@ -636,7 +705,7 @@ def measure_serve_b256(uno, sdev, torch, dev, reps=4):
             "gemm": gemm, "verify": ver}
 
 
-CONFIG_MEASURES = {"layer_b1": measure_layer_b1, "layer_b64": measure_layer_b64, "serve_b256": measure_serve_b256}
+CONFIG_MEASURES = {"tiny": measure_tiny, "layer_b1": measure_layer_b1, "layer_b64": measure_layer_b64, "serve_b256": measure_serve_b256}
 
 
 def cpu_baseline(wl, layers, x0, z, d, drafts, u, gate_np, T, L):
