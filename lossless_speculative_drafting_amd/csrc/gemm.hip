@@ -1416,38 +1416,51 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------------ fp32 path
+// One wavefront per output: lane l sums the products of K indices l, l + 64,
+// ... in order (coalesced loads of both operand rows), then the 64 lane sums
+// add in an xor tree; a fixed order, so the results are deterministic.
+__device__ __forceinline__ float wave_sum_f32(float s) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    return s;
+}
+
 // T[m, j] = scale * sum_k x[m, k] a[j, k] for draft rows (read only for draft rows).
 __global__ __launch_bounds__(256) void lora_t_f32_kernel(const float* __restrict__ x, const float* __restrict__ la,
                                                         const uint8_t* __restrict__ gate, int64_t M, int64_t K,
                                                         int32_t r, float scale, float* __restrict__ t) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (e >= M * r) return;
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;  // output (wavefront)
+    const int lane = threadIdx.x % kWave;
+    if (e >= M * r) return;  // (whole wavefronts)
     const int64_t m = e / r;
     const int64_t j = e - m * r;
     if (gate[m] != 1) return;
     float s = 0.f;
-    for (int64_t k = 0; k < K; ++k) s = fmaf(x[m * K + k], la[j * K + k], s);
-    t[m * r + j] = scale * s;
+    for (int64_t k = lane; k < K; k += kWave) s = fmaf(x[m * K + k], la[j * K + k], s);
+    s = wave_sum_f32(s);
+    if (lane == 0) t[m * r + j] = scale * s;
 }
 
 __global__ __launch_bounds__(256) void gated_gemm_f32_kernel(const float* __restrict__ x, const float* __restrict__ w,
                                                             const float* __restrict__ t, const float* __restrict__ lb,
                                                             const uint8_t* __restrict__ gate, int64_t M, int64_t N,
                                                             int64_t K, int32_t r, float* __restrict__ y) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (e >= M * N) return;
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;  // output (wavefront)
+    const int lane = threadIdx.x % kWave;
+    if (e >= M * N) return;  // (whole wavefronts)
     const int64_t m = e / N;
     const int64_t n = e - m * N;
     if (gate[m] > 1) {  // invalid gate byte: NaN row (the row plan counts it)
-        y[m * N + n] = __builtin_nanf("");
+        if (lane == 0) y[m * N + n] = __builtin_nanf("");
         return;
     }
     float s = 0.f;
-    for (int64_t k = 0; k < K; ++k) s = fmaf(x[m * K + k], w[n * K + k], s);
+    for (int64_t k = lane; k < K; k += kWave) s = fmaf(x[m * K + k], w[n * K + k], s);
     if (gate[m] == 1) {
-        for (int32_t j = 0; j < r; ++j) s = fmaf(t[m * r + j], lb[n * r + j], s);
+        for (int32_t j = lane; j < r; j += kWave) s = fmaf(t[m * r + j], lb[n * r + j], s);
     }
-    y[m * N + n] = s;
+    s = wave_sum_f32(s);
+    if (lane == 0) y[m * N + n] = s;
 }
 
 // ------------------------------------------------------------ planning
@@ -1953,12 +1966,13 @@ hipError_t gated_lora_launch(const GemmProblem& pr, void* ws, size_t ws_bytes, h
         hipError_t e = segment_rows_launch(pr.gate, pr.M, ws, stream);
         if (e != hipSuccess) return e;
         float* t = reinterpret_cast<float*>(static_cast<char*>(ws) + row_plan_bytes(pr.M));
+        // (one wavefront per output: four outputs per 256-thread workgroup)
         const int64_t nt = pr.M * pr.r;
-        hipLaunchKernelGGL(lora_t_f32_kernel, dim3(static_cast<uint32_t>((nt + 255) / 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(lora_t_f32_kernel, dim3(static_cast<uint32_t>((nt + 3) / 4)), dim3(256), 0, stream,
                            static_cast<const float*>(pr.x), static_cast<const float*>(pr.a), pr.gate, pr.M, pr.K,
                            pr.r, pr.scale, t);
         const int64_t ny = pr.M * pr.N;
-        hipLaunchKernelGGL(gated_gemm_f32_kernel, dim3(static_cast<uint32_t>((ny + 255) / 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(gated_gemm_f32_kernel, dim3(static_cast<uint32_t>((ny + 3) / 4)), dim3(256), 0, stream,
                            static_cast<const float*>(pr.x), static_cast<const float*>(pr.w), t,
                            static_cast<const float*>(pr.b), pr.gate, pr.M, pr.N, pr.K, pr.r,
                            static_cast<float*>(pr.y));
