@@ -260,7 +260,9 @@ uno_status uno_swiglu_pack(const void* w_gate, const void* w_up, const void* b_g
  * Arithmetic: row maxima and sums of exp stream in fp32 per element with
  * fp64 accumulation; the acceptance ratio is formed in fp64 in log space;
  * the redraw CDF sums fp32 weights of 16-token segments and carries across
- * segments in fp64.
+ * segments in fp64.  Vocabularies of at most 1024 tokens are verified by one
+ * wavefront per sequence (the workspace is then not touched), larger ones by
+ * a statistics pass over every row followed by the decision and the draw.
  *
  * Domain: B >= 0 (B = 0 is a no-op), 1 <= L <= 64 (L <= 63 with has_bonus),
  * V >= 1, T > 0 and finite, logits UNO_BF16 or UNO_F32, each row holding at

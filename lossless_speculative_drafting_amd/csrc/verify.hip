@@ -280,6 +280,10 @@ struct DecideArgs {
     double invT;
     const ChunkStat* stats;
     int32_t n_chunks;
+    // ChunkStats between sequences (-1: rows x n_chunks, the stats array's
+    // own layout; 0: every sequence reads the same rows, e.g. a per-wavefront
+    // copy in LDS)
+    int64_t stats_seq = -1;
     RedrawJob* jobs;
     int32_t* n_accepted;
     int32_t* out_tokens;
@@ -336,7 +340,8 @@ __device__ __forceinline__ LaneDecision lane_decision(const DecideArgs& a, int64
         }
     }
     if (stat_row) {
-        const ChunkStat* st = a.stats + (s * rows + lane) * a.n_chunks;
+        const ChunkStat* st = a.stats + (a.stats_seq >= 0 ? s * a.stats_seq : s * rows * a.n_chunks) +
+                              static_cast<int64_t>(lane) * a.n_chunks;
         merge_chunks(st, a.n_chunks, false, a.invT, d.Mz, d.Sz);
         if (drafted) merge_chunks(st, a.n_chunks, true, a.invT, d.Md, d.Sd);
     }
@@ -1078,6 +1083,153 @@ bool vec_ok(const void* p0, const void* p1, int64_t V, int64_t s0, int64_t s1) {
 
 // chunk = 0: one pass over every row; chunk > 0: early exit, positions in
 // chunks of `chunk`.
+// Verification when the vocabulary fits one wavefront's segments (V <= 1024:
+// at most 64 segments of 16 tokens): one wavefront per sequence does it
+// all, four sequences per workgroup, nothing in global scratch.  Lane g
+// takes segment g of a row.  (1) For every row of the sequence, the online
+// (max, sum of exp) of its segment in sixteen-value form, merged over the
+// wavefront; the row's statistics go to LDS.  (2) The decision the other
+// verifiers take (decide_sequence, reading those statistics).  (3) The
+// redraw or bonus draw by inverse CDF: each lane's segment mass (the weights
+// of segment_weights summed in order, fp32), an exclusive fp64 scan over the
+// lanes, the target u R, and the walk inside the first segment whose
+// running total passes it (a residual with no mass draws from p; rounding
+// that leaves no crossing takes the last weighted token), as the
+// workgroup-wide select takes them with one segment per thread.  Many short
+// sequences (the lossless check's 10^6 trials of one block) run as many
+// wavefronts at once instead of one workgroup per sequence.
+constexpr int64_t kSmallV = static_cast<int64_t>(kWave) * kSeg;
+constexpr int kSmallSeqs = kThreads / kWave;  // sequences per workgroup
+
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load_segment(const char* row, int64_t g, int64_t V, float* v) {
+    const int64_t k = g * kSeg;
+    load8<BF16, VEC>(row, k, V, v);
+    if (k + kVec < V) {
+        load8<BF16, VEC>(row, k + kVec, V, v + kVec);
+    } else {
+#pragma unroll
+        for (int j = kVec; j < kSeg; ++j) v[j] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ double wave_excl_scan(double v, double* total) {
+    const int lane = threadIdx.x % kWave;
+    double inc = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    *total = __shfl(inc, kWave - 1);
+    return inc - v;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void verify_small_kernel(DecideArgs a, float c2) {
+    __shared__ ChunkStat s_st[kSmallSeqs][kWave];
+    __shared__ RedrawJob s_job[kSmallSeqs];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * kSmallSeqs + wave;
+    if (s >= a.B) return;  // whole wavefronts; only wavefront-level steps follow
+    const int32_t L = a.L;
+    const int32_t rows = L + a.nb;
+    const int64_t nseg = (a.V + kSeg - 1) / kSeg;
+    const size_t esz = BF16 ? 2 : 4;
+    const char* tbase = static_cast<const char*>(a.target) + s * a.t_stride * esz;
+    const char* dbase = static_cast<const char*>(a.draft) + s * a.d_stride * esz;
+    for (int32_t i = 0; i < rows; ++i) {
+        Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
+        if (lane < nseg) {
+            float v[kSeg];
+            load_segment<BF16, VEC>(tbase + static_cast<int64_t>(i) * a.V * esz, lane, a.V, v);
+            online_add16(oa, v, c2);
+            if (i < L) {
+                load_segment<BF16, VEC>(dbase + static_cast<int64_t>(i) * a.V * esz, lane, a.V, v);
+                online_add16(ob, v, c2);
+            }
+        }
+        oa = wave_merge(oa, c2);
+        ob = wave_merge(ob, c2);
+        if (lane == 0) {
+            ChunkStat st;
+            st.sA = oa.s;
+            st.mA = oa.m;
+            st.sB = ob.s;
+            st.mB = ob.m;
+            s_st[wave][i] = st;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lane 0's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    DecideArgs d = a;
+    d.stats = &s_st[wave][0];
+    d.stats_seq = 0;
+    d.n_chunks = 1;
+    decide_sequence<BF16>(d, s, lane, &s_job[wave]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // lane 0's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const RedrawJob job = s_job[wave];
+    if (job.mode == kJobNone) return;  // (uniform for the wavefront)
+    float w[kSeg];
+    auto segment_mass = [&](bool use_p) __attribute__((always_inline)) {
+        float m = 0.f;
+        if (lane < nseg) {
+            segment_weights<BF16, VEC>(job, lane, a.V, c2, use_p, w);
+#pragma unroll
+            for (int j = 0; j < kSeg; ++j) m += w[j];
+        }
+        return m;
+    };
+    float m = segment_mass(false);
+    double R;
+    double excl = wave_excl_scan(static_cast<double>(m), &R);
+    bool use_p = false;
+    if (job.mode == kJobResidual && R == 0.0) {  // the residual lost all mass to rounding: draw from p
+        use_p = true;
+        m = segment_mass(true);
+        excl = wave_excl_scan(static_cast<double>(m), &R);
+    }
+    const double target = static_cast<double>(job.u) * R;
+    const bool cand = lane < nseg && m > 0.f && excl + static_cast<double>(m) > target;
+    const uint64_t hit = __ballot(cand);
+    int64_t token = -1;
+    if (hit != 0) {
+        const int c = static_cast<int>(__builtin_ctzll(hit));
+        if (lane == c) {
+            float run32 = 0.f;
+            for (int j = 0; j < kSeg; ++j) {
+                run32 += w[j];
+                if (w[j] > 0.f && excl + static_cast<double>(run32) > target) {
+                    token = static_cast<int64_t>(lane) * kSeg + j;
+                    break;
+                }
+            }
+        }
+        token = __shfl(token, c);
+    }
+    if (token < 0) {
+        // rounding left no crossing: the last token with weight
+        const uint64_t pos = __ballot(lane < nseg && m > 0.f);
+        if (pos != 0) {
+            const int c = 63 - static_cast<int>(__builtin_clzll(pos));
+            if (lane == c) {
+                for (int j = kSeg - 1; j >= 0; --j) {
+                    if (w[j] > 0.f) {
+                        token = static_cast<int64_t>(lane) * kSeg + j;
+                        break;
+                    }
+                }
+            }
+            token = __shfl(token, c);
+        }
+        if (token < 0) token = 0;
+    }
+    (void)use_p;
+    if (lane == 0) *job.out = static_cast<int32_t>(token);
+}
+
 template <bool BF16, bool VEC>
 hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, int32_t chunk) {
     const int32_t nb = pr.has_bonus ? 1 : 0;
@@ -1107,6 +1259,12 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
     da.n_accepted = pr.n_accepted;
     da.out_tokens = pr.out_tokens;
     da.n_emitted = pr.n_emitted;
+    if (pr.V <= kSmallV) {
+        // (the early-exit form takes this path too: its outputs are the one-pass form's)
+        hipLaunchKernelGGL((verify_small_kernel<BF16, VEC>), dim3(static_cast<uint32_t>((pr.B + kSmallSeqs - 1) / kSmallSeqs)),
+                           dim3(kThreads), 0, stream, da, c2);
+        return hipGetLastError();
+    }
     if (chunk <= 0) {
         hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
                            0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
