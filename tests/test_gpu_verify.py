@@ -38,8 +38,11 @@ def _check(z, d, x, u, T, has_bonus, dtype, label, max_excused_frac=0.01):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("path", ["default", "general"])
 @pytest.mark.parametrize("has_bonus", [False, True])
-def test_tiny_workload(has_bonus):
+def test_tiny_workload(has_bonus, path, monkeypatch):
+    if path == "general":  # (V <= 1024 otherwise takes the one-wavefront-per-sequence kernel)
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
     wl = WORKLOADS["tiny"]
     B, L, V, T = 2, wl.block, wl.vocab, 1.0
     z, d = verify_inputs(B, L, V, wl.seed, "normal", wl.target_sigma, wl.draft_sigmas[0], has_bonus, "f32")
@@ -61,12 +64,15 @@ CASES = [  # B, L, V, dtype, kind, sigma, T, bonus
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("tail", ["fused", "split"])
+@pytest.mark.parametrize("tail", ["default", "fused", "split"])
 @pytest.mark.parametrize("B,L,V,dtype,kind,sigma,T,bonus", CASES)
 def test_random_cases(B, L, V, dtype, kind, sigma, T, bonus, tail, monkeypatch):
-    """Both forms of the tail (one workgroup per sequence, or each redraw row
-    spread over several workgroups) against the oracle."""
-    monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
+    """The default path (at V <= 1024 one wavefront per sequence) and both
+    forms of the general path's tail (one workgroup per sequence, or each
+    redraw row spread over several workgroups) against the oracle."""
+    if tail != "default":
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
+        monkeypatch.setenv("UNO_VERIFY_TAIL", tail)
     z, d = verify_inputs(B, L, V, seed=B * 31 + L + V, kind=kind, target_sigma=3.0, draft_sigma=sigma,
                          has_bonus=bonus, dtype=dtype)
     x = _drafts(d, T)
@@ -75,7 +81,10 @@ def test_random_cases(B, L, V, dtype, kind, sigma, T, bonus, tail, monkeypatch):
 
 
 @pytest.mark.gpu
-def test_edge_cases_masks_invalid_tokens_broadcast():
+@pytest.mark.parametrize("path", ["default", "general"])
+def test_edge_cases_masks_invalid_tokens_broadcast(path, monkeypatch):
+    if path == "general":
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
     rng = np.random.default_rng(4)
     B, L, V = 6, 5, 300
     z, d = verify_inputs(B, L, V, seed=11, kind="normal", target_sigma=2.0, draft_sigma=1.0, dtype="bf16")
@@ -97,7 +106,10 @@ def test_edge_cases_masks_invalid_tokens_broadcast():
 
 
 @pytest.mark.gpu
-def test_q_equal_p_accepts_all_and_disjoint_rejects_first():
+@pytest.mark.parametrize("path", ["default", "general"])
+def test_q_equal_p_accepts_all_and_disjoint_rejects_first(path, monkeypatch):
+    if path == "general":
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
     B, L, V = 40, 8, 777
     z, _ = verify_inputs(B, L, V, seed=2, kind="normal", dtype="bf16")
     x = _drafts(z, 0.8)
@@ -202,9 +214,13 @@ EARLY = [  # B, L, V, dtype, kind, sigma, T, bonus, chunk
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("path", ["default", "general"])
 @pytest.mark.parametrize("B,L,V,dtype,kind,sigma,T,bonus,chunk", EARLY)
-def test_early_exit_matches_one_pass_and_oracle(B, L, V, dtype, kind, sigma, T, bonus, chunk):
-    """Early-exit verification: the same bits as the one-pass verifier, and the oracle's tokens."""
+def test_early_exit_matches_one_pass_and_oracle(B, L, V, dtype, kind, sigma, T, bonus, chunk, path, monkeypatch):
+    """Early-exit verification: the same bits as the one-pass verifier, and the oracle's tokens
+    (the general path forced at every V, so that its chunk schedule runs on the small vocabularies)."""
+    if path == "general":
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
     z, d = verify_inputs(B, L, V, seed=B * 37 + L + V, kind=kind, target_sigma=3.0, draft_sigma=sigma,
                          has_bonus=bonus, dtype=dtype)
     x = _drafts(d, T)
@@ -222,8 +238,11 @@ def test_early_exit_matches_one_pass_and_oracle(B, L, V, dtype, kind, sigma, T, 
 
 
 @pytest.mark.gpu
-def test_early_exit_invalid_tokens_and_accept_all():
+@pytest.mark.parametrize("path", ["default", "general"])
+def test_early_exit_invalid_tokens_and_accept_all(path, monkeypatch):
     """Out-of-range tokens past a rejection still give -1; q == p accepts every chunk."""
+    if path == "general":
+        monkeypatch.setenv("UNO_VERIFY_SMALL", "0")
     B, L, V = 12, 9, 300
     z, d = verify_inputs(B, L, V, seed=5, kind="normal", target_sigma=2.0, draft_sigma=1.0, dtype="bf16")
     x = _drafts(d, 1.0)
