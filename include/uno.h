@@ -381,9 +381,10 @@ uno_status uno_draft_sample(const void* draft_logits, int64_t seq_stride,
  * n_emitted = 0, last_node = -1 and out_tokens all -1.  Arithmetic: that of
  * uno_draft_sample (fp32 exponentials, fp64 sums, the same inverse CDF).
  * Large problems run one workgroup per tree that reads only the walked
- * rows; small ones draw every node's token with its depth's uniform across
- * the GPU and then walk (the two differ only where a uniform falls within
- * rounding of a CDF boundary).
+ * rows, each once (a 16-token segment's mass is formed from the segment's
+ * own maximum, then scaled to the row's); small ones draw every node's
+ * token with its depth's uniform across the GPU and then walk (the two
+ * differ only where a uniform falls within rounding of a CDF boundary).
  *
  * Domain: B >= 0 (B = 0 is a no-op), 1 <= N <= 4096, V >= 1, T > 0 and
  * finite, logits UNO_BF16 or UNO_F32 with a finite value in every row.

@@ -1460,39 +1460,52 @@ __global__ __launch_bounds__(kThreads) void tree_walk_kernel(const int32_t* __re
 }
 
 // The whole walk of one tree in one workgroup (rows whose segment masses fit
-// in LDS): at each node, the row's max and sum of exponentials (the online
-// form of row_stats, merged over the block in wavefront order), the segment
-// masses of p into LDS and the inverse-CDF draw of the verifier's tail, then
-// the child look-up.  Only the walked path's rows are read.
+// in LDS): at each node, one pass over the row gives every 16-token
+// segment's maximum and sum of exponentials and the row maximum, the segment
+// masses relative to that maximum go to LDS, the verifier's inverse-CDF draw
+// runs on them, then the child look-up.  Only the walked path's rows are
+// read, once each.
+// (512 threads: the walk's loads and the draw's select keep their registers,
+// where 1024 threads would cap each lane at 128 and spill)
+constexpr int kWalkThreads = 512;
+constexpr int kWalkLdsNodes = 1024;
+constexpr int kWalkRawSegs = 8;
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kTailThreads) void tree_walk_draw_kernel(
+__global__ __launch_bounds__(kWalkThreads) void tree_walk_draw_kernel(
     const void* __restrict__ logits, int64_t seq_stride, const int32_t* __restrict__ parents,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int32_t N, int64_t V, int64_t nseg,
     float c2, float* __restrict__ seg, int32_t* __restrict__ n_accepted, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ n_emitted, int32_t* __restrict__ last_node) {
-    constexpr int NT = kTailThreads;
-    extern __shared__ float s_seg[];  // segment g at g + g / 32
-    __shared__ RedrawJob s_job;
-    __shared__ Online s_on[NT / kWave];
+    constexpr int NT = kWalkThreads;
+    extern __shared__ float s_seg[];  // segment g's mass at g + g / 32, then its maximum at nseg + nseg / 32 + 1 + g
+    float* s_m = s_seg + nseg + nseg / 32 + 1;
+    __shared__ float s_max[NT / kWave];
     __shared__ int32_t s_tok, s_next;
+    // the tree (parents, tokens) and the uniforms of its depths, in LDS for
+    // trees of up to kWalkLdsNodes nodes (larger ones are read from memory)
+    __shared__ int32_t s_par[kWalkLdsNodes], s_tk[kWalkLdsNodes];
+    __shared__ float s_u[kWalkLdsNodes];
     const int64_t s = blockIdx.x;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     const int32_t* par = parents + s * N;
     const int32_t* tok = tokens + s * N;
+    const float* us = uniforms + s * N;
     int32_t* out = out_tokens + s * N;
-    if (wave == 0) {
-        bool bad = false;
-        for (int32_t c = lane; c < N; c += kWave) {
-            const int32_t pc = par[c];
-            const int32_t t = tok[c];
-            bad |= c == 0 ? pc != -1 : (pc < 0 || pc >= c || t < 0 || static_cast<int64_t>(t) >= V);
+    const bool in_lds = N <= kWalkLdsNodes;
+    bool bad = false;
+    for (int32_t c = threadIdx.x; c < N; c += NT) {
+        const int32_t pc = par[c];
+        const int32_t t = tok[c];
+        bad |= c == 0 ? pc != -1 : (pc < 0 || pc >= c || t < 0 || static_cast<int64_t>(t) >= V);
+        if (in_lds) {
+            s_par[c] = pc;
+            s_tk[c] = t;
+            s_u[c] = us[c];
         }
-        const uint64_t any_bad = __ballot(bad);
-        if (lane == 0) s_next = any_bad != 0 ? -2 : 0;
     }
-    __syncthreads();
-    if (s_next == -2) {  // uniform for the workgroup
+    if (__syncthreads_or(bad)) {  // uniform for the workgroup
         for (int32_t c = threadIdx.x; c < N; c += NT) out[c] = -1;
         if (threadIdx.x == 0) {
             n_accepted[s] = -1;
@@ -1505,57 +1518,89 @@ __global__ __launch_bounds__(kTailThreads) void tree_walk_draw_kernel(
     int32_t v = 0, depth = 0;
     while (true) {  // v rises at every step (children are numbered above their parent)
         const char* row = static_cast<const char*>(logits) + (s * seq_stride + static_cast<int64_t>(v) * V) * esz;
-        Online o{-INFINITY, 0.0};
-        constexpr int kU = 4;  // vectors in flight per thread
-        constexpr int64_t kStride = static_cast<int64_t>(NT) * kVec;
-        for (int64_t k0 = static_cast<int64_t>(threadIdx.x) * kVec; k0 < V; k0 += kU * kStride) {
-            float f[kU][kVec];
+        // One pass over the row: each 16-token segment's maximum and sum of
+        // exponentials relative to it (fp32, pairwise), kept in LDS, and the
+        // row maximum M over the block; then, in place, each segment's mass
+        // relative to M, s_g 2^{(m_g - M) c2}, and the inverse-CDF draw of the
+        // verifier's tail on those masses (weights 2^{(z - M) c2} inside the
+        // drawn segment; the draw scales u by the masses' own total).
+        float tmax = -INFINITY;
+        auto add_segment = [&](int64_t g, const float* f) __attribute__((always_inline)) {
+            Online o{-INFINITY, 0.0};
+            online_add16(o, f, c2);
+            s_seg[g + (g >> 5)] = static_cast<float>(o.s);
+            s_m[g] = o.m;
+            tmax = fmaxf(tmax, o.m);
+        };
+        if constexpr (BF16 && VEC) {
+            // bf16 rows: the raw 16-byte vectors of kR segments per thread in
+            // flight at once (128 KB per workgroup), unpacked after they land
+            constexpr int kR = kWalkRawSegs;
+            typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+            for (int64_t base = threadIdx.x; base < nseg; base += kR * NT) {
+                u32x4_t raw[kR][2];
 #pragma unroll
-            for (int u = 0; u < kU; ++u)
-                if (k0 + u * kStride < V) load8<BF16, VEC>(row, k0 + u * kStride, V, f[u]);
+                for (int u = 0; u < kR; ++u) {
+                    const int64_t g = base + static_cast<int64_t>(u) * NT;
+                    const int64_t k = g * kSeg;
+                    const u32x4_t ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+                    raw[u][0] = g < nseg ? gptr<u32x4_t>(reinterpret_cast<const uint16_t*>(row) + k)[0] : ninf;
+                    raw[u][1] = (g < nseg && k + kVec < V)
+                                    ? gptr<u32x4_t>(reinterpret_cast<const uint16_t*>(row) + k + kVec)[0]
+                                    : ninf;
+                }
 #pragma unroll
-            for (int u = 0; u < kU; ++u)
-                if (k0 + u * kStride < V) online_add8(o, f[u], c2);
-        }
-        o = wave_merge(o, c2);
-        if (lane == 0) s_on[wave] = o;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            Online r = s_on[0];
-            for (int w = 1; w < NT / kWave; ++w) r = online_merge(r, s_on[w], c2);
-            RedrawJob job;
-            job.a = row;
-            job.b = nullptr;
-            job.out = &s_tok;
-            job.Ma = r.m;
-            job.invSa = static_cast<float>(1.0 / r.s);
-            job.Mb = 0.f;
-            job.invSb = 0.f;
-            job.u = uniforms[s * N + depth];
-            job.mode = kJobSingle;
-            s_job = job;
-        }
-        __syncthreads();
-        const RedrawJob job = s_job;
-        constexpr int kBatch = 4;
-        for (int64_t base = threadIdx.x; base < nseg; base += kBatch * NT) {
-            float w[kBatch][kSeg];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t g = base + static_cast<int64_t>(u) * NT;
-                if (g < nseg) segment_weights<BF16, VEC>(job, g, V, c2, false, w[u]);
+                for (int u = 0; u < kR; ++u) {
+                    const int64_t g = base + static_cast<int64_t>(u) * NT;
+                    if (g < nseg) {
+                        float f[kSeg];
+                        uint4 v0, v1;
+                        v0.x = raw[u][0].x; v0.y = raw[u][0].y; v0.z = raw[u][0].z; v0.w = raw[u][0].w;
+                        v1.x = raw[u][1].x; v1.y = raw[u][1].y; v1.z = raw[u][1].z; v1.w = raw[u][1].w;
+                        unpack8(v0, f);
+                        unpack8(v1, f + kVec);
+                        add_segment(g, f);
+                    }
+                }
             }
+        } else {
+            constexpr int kB = 8;  // segments in flight per thread (16 loads)
+            for (int64_t base = threadIdx.x; base < nseg; base += kB * NT) {
+                float f[kB][kSeg];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t g = base + static_cast<int64_t>(u) * NT;
-                if (g < nseg) {
-                    float sr = 0.f;
+                for (int u = 0; u < kB; ++u) {
+                    const int64_t g = base + static_cast<int64_t>(u) * NT;
+                    if (g < nseg) load_segment<BF16, VEC>(row, g, V, f[u]);
+                }
 #pragma unroll
-                    for (int j = 0; j < kSeg; ++j) sr += w[u][j];
-                    s_seg[g + (g >> 5)] = sr;
+                for (int u = 0; u < kB; ++u) {
+                    const int64_t g = base + static_cast<int64_t>(u) * NT;
+                    if (g < nseg) add_segment(g, f[u]);
                 }
             }
         }
+#pragma unroll
+        for (int off = kWave / 2; off >= 1; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+        if (lane == 0) s_max[wave] = tmax;
+        __syncthreads();
+        float M = s_max[0];
+#pragma unroll
+        for (int w = 1; w < NT / kWave; ++w) M = fmaxf(M, s_max[w]);
+        for (int64_t g = threadIdx.x; g < nseg; g += NT) {  // the segments this thread wrote
+            const float mg = s_m[g];
+            const float sg = s_seg[g + (g >> 5)];
+            s_seg[g + (g >> 5)] = mg == -INFINITY ? 0.f : sg * fast_exp2((mg - M) * c2);
+        }
+        RedrawJob job;
+        job.a = row;
+        job.b = nullptr;
+        job.out = &s_tok;
+        job.Ma = M;
+        job.invSa = 1.f;
+        job.Mb = 0.f;
+        job.invSb = 0.f;
+        job.u = in_lds ? s_u[depth] : us[depth];
+        job.mode = kJobSingle;
         __syncthreads();
         select_job<BF16, VEC, NT>(job, nseg, 1, V, c2, seg + s * nseg, s_seg, true);
         __syncthreads();
@@ -1564,7 +1609,9 @@ __global__ __launch_bounds__(kTailThreads) void tree_walk_draw_kernel(
             int32_t child = -1;
             for (int32_t b = v + 1; b < N; b += kWave) {
                 const int32_t c = b + lane;
-                const uint64_t hit = __ballot(c < N && par[c] == v && tok[c] == y);
+                bool is_child = false;
+                if (c < N) is_child = in_lds ? (s_par[c] == v && s_tk[c] == y) : (par[c] == v && tok[c] == y);
+                const uint64_t hit = __ballot(is_child);
                 if (hit != 0) {
                     child = b + static_cast<int32_t>(__builtin_ctzll(hit));
                     break;
@@ -1599,15 +1646,17 @@ size_t tree_verify_workspace_size(int64_t B, int32_t N, int64_t V) {
 hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t stream) {
     char* base = static_cast<char*>(ws);
     const int64_t nseg = (tp.V + kSeg - 1) / kSeg;
-    const size_t lds = select_lds_bytes(nseg);
+    // (the walk's LDS: the staged masses, then a maximum per segment)
+    const size_t lds = select_lds_bytes(nseg) > 0 ? select_lds_bytes(nseg) + static_cast<size_t>(nseg) * sizeof(float) : 0;
     // Two forms: one workgroup walks each tree, reading only the walked rows
-    // (about 30 us per level on MI355X, V = 128256: latency of one CU per
-    // tree; a call lasts as long as the deepest walk), or every node row is
-    // drawn by the whole GPU and then walked (streams 4 N V bytes per tree).
-    // The walk wins once the node rows would take longer to stream than a
-    // few levels take, from about 350 MB.
+    // (on MI355X at V = 128256 about 21 us for the root and 16 us per further
+    // level -- one CU per tree streams a row at about 30 GB/s; a call lasts
+    // as long as the deepest walk), or every node row is drawn by the whole
+    // GPU and then walked (streams 4 N V bytes per tree: about 32 us plus
+    // 3.4 TB/s).  The walk wins once the node rows take longer to stream than
+    // four or five levels take, from about 150 MB.
     // UNO_TREE_PATH=walk|nodes forces one (tests).
-    bool walk = static_cast<double>(tp.B) * tp.N * tp.V * 4.0 > 3.5e8;
+    bool walk = static_cast<double>(tp.B) * tp.N * tp.V * 4.0 > 1.5e8;
     if (const char* e = getenv("UNO_TREE_PATH")) {
         if (strcmp(e, "walk") == 0) walk = true;
         if (strcmp(e, "nodes") == 0) walk = false;
@@ -1616,7 +1665,7 @@ hipError_t tree_verify_launch(const TreeProblem& tp, void* ws, hipStream_t strea
         const bool vec = vec_ok(tp.logits, nullptr, tp.V, tp.seq_stride, 0);
         const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(tp.temperature));
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(tp.B)), dim3(kTailThreads), lds, stream, tp.logits,
+            hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(tp.B)), dim3(kWalkThreads), lds, stream, tp.logits,
                                tp.seq_stride, tp.parents, tp.tokens, tp.uniforms, tp.N, tp.V, nseg, c2,
                                reinterpret_cast<float*>(base), tp.n_accepted, tp.out_tokens, tp.n_emitted,
                                tp.last_node);

@@ -90,6 +90,8 @@ CASES = [  # B, K, D, V, dtype, T
     (40, 1, 6, 64, "bf16", 1.0),     # chains
     (6, 8, 1, 2048, "f32", 1.0),     # one level, eight siblings
     (2, 2, 2, 300000, "bf16", 1.0),  # rows past the walk's LDS staging: every node drawn either way
+    (2, 2, 2, 240000, "bf16", 1.0),  # the walk's largest staging (15000 segments: masses and maxima)
+    (2, 2, 10, 256, "bf16", 1.0),    # 2047 nodes: the walk reads the tree from memory, not LDS
 ]
 
 
