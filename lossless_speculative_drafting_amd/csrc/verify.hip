@@ -215,54 +215,52 @@ __device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, boo
     S = s;
 }
 
-// The chunk statistics of each row merged into one chunk: M = max_c m_c and
-// S = sum_c s_c e^{(m_c - M)/T} in fp64, as merge_chunks forms them but in a
-// fixed parallel order: lane l of the row's wavefront sums chunks l, l + 64,
-// ... in order, then the 64 lane sums add in an xor tree.  Rows with many
-// chunks (the LM head's 256-column tiles) are merged here once; the decision
-// then merges one chunk per row, which leaves the values unchanged
-// (e^0 = 1).  Array B is merged for rows i < rows_with_b of each sequence.
+// The chunk statistics of each row merged into one chunk by the online merge
+// of the statistics passes: M = max_c m_c and S = sum_c s_c 2^{(m_c - M) c2}
+// (the smaller side's factor in fp32, the sums in fp64), in a fixed parallel
+// order: lane l of the row's wavefront merges chunks l, l + 64, ... in order
+// (eight of them loaded together), then the 64 lane states merge in an xor
+// tree.  Rows with many chunks (the LM head's 256-column tiles) are merged
+// here once; the decision then merges one chunk per row, which leaves the
+// values unchanged (e^0 = 1).  Array B is merged for rows i < rows_with_b of
+// each sequence.
 __global__ __launch_bounds__(kThreads) void stat_merge_kernel(const ChunkStat* __restrict__ in, int32_t n_chunks,
                                                              int64_t rows, int32_t rows_per_seq,
-                                                             int32_t rows_with_b, double invT,
+                                                             int32_t rows_with_b, float c2,
                                                              ChunkStat* __restrict__ out) {
     const int lane = threadIdx.x % kWave;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (row >= rows) return;  // whole wavefronts leave together
     const bool has_b = (row % rows_per_seq) < rows_with_b;
     const ChunkStat* st = in + row * n_chunks;
-    float ma = -INFINITY, mb = -INFINITY;
-    for (int32_t c = lane; c < n_chunks; c += kWave) {
-        ma = fmaxf(ma, st[c].mA);
-        if (has_b) mb = fmaxf(mb, st[c].mB);
-    }
+    constexpr int kBatch = 8;
+    Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
+    for (int32_t c0 = lane; c0 < n_chunks; c0 += kBatch * kWave) {
+        ChunkStat cs[kBatch];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        ma = fmaxf(ma, __shfl_xor(ma, off));
-        mb = fmaxf(mb, __shfl_xor(mb, off));
-    }
-    double sa = 0.0, sb = 0.0;
-    for (int32_t c = lane; c < n_chunks; c += kWave) {
-        const float mca = st[c].mA;
-        if (ma != -INFINITY && mca != -INFINITY)
-            sa += st[c].sA * exp((static_cast<double>(mca) - static_cast<double>(ma)) * invT);
-        if (has_b) {
-            const float mcb = st[c].mB;
-            if (mb != -INFINITY && mcb != -INFINITY)
-                sb += st[c].sB * exp((static_cast<double>(mcb) - static_cast<double>(mb)) * invT);
+        for (int u = 0; u < kBatch; ++u) {
+            const int32_t c = c0 + u * kWave;
+            if (c < n_chunks) cs[u] = st[c];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (c0 + u * kWave < n_chunks) {
+                oa = online_merge(oa, Online{cs[u].mA, cs[u].sA}, c2);
+                if (has_b) ob = online_merge(ob, Online{cs[u].mB, cs[u].sB}, c2);
+            }
         }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        sa += __shfl_xor(sa, off);
-        sb += __shfl_xor(sb, off);
+        oa = online_merge(oa, Online{__shfl_xor(oa.m, off), __shfl_xor(oa.s, off)}, c2);
+        ob = online_merge(ob, Online{__shfl_xor(ob.m, off), __shfl_xor(ob.s, off)}, c2);
     }
     if (lane == 0) {
         ChunkStat r;
-        r.sA = sa;
-        r.mA = ma;
-        r.sB = has_b ? sb : 0.0;
-        r.mB = has_b ? mb : -INFINITY;
+        r.sA = oa.s;
+        r.mA = oa.m;
+        r.sB = has_b ? ob.s : 0.0;
+        r.mB = has_b ? ob.m : -INFINITY;
         out[row] = r;
     }
 }
@@ -1775,7 +1773,7 @@ hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t 
                             row_token, gathered, c2, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(stat_merge_kernel, dim3(static_cast<uint32_t>((nt + 3) / 4)), dim3(kThreads), 0, stream, stats,
-                       static_cast<int32_t>(l.chunks), nt, pr.L + nb, pr.L, invT, merged);
+                       static_cast<int32_t>(l.chunks), nt, pr.L + nb, pr.L, c2, merged);
 
     DecideArgs da{};
     da.tokens = pr.tokens;
