@@ -314,13 +314,14 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def lm_head_measure(uno, sdev, torch, B, L, V, K, T, seed, dev, reps=5):
+def lm_head_measure(uno, sdev, torch, B, L, V, K, T, seed, dev, reps=7):
     """The LM head fused with the verification statistics, on this workload's
     rows (B sequences x L drafted positions, target and draft rows: 2 B L rows
-    of K = hidden over V tokens), outside the timed region.  Per-call times
-    (HIP events, `reps` calls) of uno_lm_head_verify with the redraw rows
-    recomputed (no logit row written) and with the logits stored, and of the
-    unfused chain: the plain GEMM writing the logits, then uno_block_verify.
+    of K = hidden over V tokens), outside the timed region.  Median per-call
+    times (HIP events, `reps` calls each, the forms interleaved) of
+    uno_lm_head_verify with the redraw rows recomputed (no logit row written)
+    and with the logits stored, and of the unfused chain: the plain GEMM
+    writing the logits, then uno_block_verify.
     Drafts come from the draft rows' own distribution.  All three must give
     the same outputs (up to the unfused verifier's different chunking of the
     statistics, which can move a decision only on an exact tie)."""
@@ -350,19 +351,25 @@ def lm_head_measure(uno, sdev, torch, B, L, V, K, T, seed, dev, reps=5):
         "fused_store": lambda o: uno.lm_head_verify(hidden, w, x, u, T, logits=logits, outputs=o, workspace=ws),
         "unfused": unfused,
     }
-    res, got = {}, {}
-    for name, fn in calls.items():
-        o = outs()
-        for _ in range(2):
-            fn(o)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn(o)
-        e1.record()
-        torch.cuda.synchronize()
-        res[name + "_us"] = round(e0.elapsed_time(e1) / reps * 1e3, 2)
-        got[name] = o
+    # The three forms interleaved call by call (the order rotating each
+    # round), each call between its own events: the clock drifts over a
+    # second of back-to-back 1 ms GEMMs, and timing the forms one after
+    # another would hand that drift to whichever form ran last.
+    res, got, times = {}, {name: outs() for name in calls}, {name: [] for name in calls}
+    names = list(calls)
+    for r in range(2 + reps):
+        for j in range(len(names)):
+            name = names[(r + j) % len(names)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            calls[name](got[name])
+            e1.record()
+            if r >= 2:
+                times[name].append((e0, e1))
+    torch.cuda.synchronize()
+    for name in names:
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in times[name])
+        res[name + "_us"] = round(ts[len(ts) // 2], 2)
     same = all(torch.equal(a, b) for a, b in zip(got["fused_recompute"], got["fused_store"]))
     agree = sum(int(torch.equal(got["fused_store"][1][s], got["unfused"][1][s])) for s in range(B)) / B
     flop = 2.0 * rows * V * K
