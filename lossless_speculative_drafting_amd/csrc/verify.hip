@@ -115,12 +115,17 @@ __device__ __forceinline__ Online wave_merge(Online o, float c2) {
 // ---------------------------------------------------------------- row_stats
 // Rows are (s, i) with i in [i0, i0 + rows_per_seq) of rows_full rows per
 // sequence; array B exists for i < rows_with_b.  Workgroup blk takes chunk
-// blk % n_chunks of row blk / n_chunks.
+// blk % n_chunks of row blk / n_chunks.  With `tokens` given (one per
+// drafted position i < rows_with_b, sequence stride rows_with_b), the
+// workgroup whose chunk holds the drafted token also copies its two logits
+// to gz and gd (same layout as the tokens), so that the decision reads them
+// with the statistics instead of after the token.
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void row_stats_body(
     int64_t blk, const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
     int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
-    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full) {
+    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full, const int32_t* __restrict__ tokens = nullptr,
+    float* __restrict__ gz = nullptr, float* __restrict__ gd = nullptr) {
     const int64_t lrow = blk / n_chunks;
     const int32_t c = static_cast<int32_t>(blk % n_chunks);
     const int64_t s = lrow / rows_per_seq;
@@ -133,6 +138,9 @@ __device__ __forceinline__ void row_stats_body(
                              : nullptr;
     const int64_t k0 = static_cast<int64_t>(c) * chunk;
     const int64_t k1 = min(V, k0 + chunk);
+    const int64_t tok_at = s * rows_with_b + i;
+    const bool gather = tokens != nullptr && has_b;
+    const int32_t x = gather && threadIdx.x == 0 ? tokens[tok_at] : -1;  // (lands while the row streams)
 
     Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
     int64_t k = k0 + static_cast<int64_t>(threadIdx.x) * kVec;
@@ -182,6 +190,10 @@ __device__ __forceinline__ void row_stats_body(
         st.sB = rb.s;
         st.mB = rb.m;
         stats[row * n_chunks + c] = st;
+        if (gather && x >= k0 && x < k1) {
+            gz[tok_at] = load_one<BF16>(arow, x);
+            gd[tok_at] = load_one<BF16>(brow, x);
+        }
     }
 }
 
@@ -189,9 +201,10 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(
     const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
     int32_t rows_with_b, int64_t V, int64_t chunk, int32_t n_chunks, float c2,
-    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full) {
+    ChunkStat* __restrict__ stats, int32_t i0, int32_t rows_full, const int32_t* __restrict__ tokens,
+    float* __restrict__ gz, float* __restrict__ gd) {
     row_stats_body<BF16, VEC>(blockIdx.x, A, a_stride, B, b_stride, rows_per_seq, rows_with_b, V, chunk, n_chunks,
-                              c2, stats, i0, rows_full);
+                              c2, stats, i0, rows_full, tokens, gz, gd);
 }
 
 // Merge the chunk statistics of one row in fp64: M = max, S = sum s_c e^{(m_c - M)/T}.
@@ -463,7 +476,8 @@ __global__ __launch_bounds__(kThreads) void row_stats_gated_kernel(
         if (s_stop) return;  // uniform for the workgroup
     }
     row_stats_body<BF16, VEC>(blockIdx.x, da.target, da.t_stride, da.draft, da.d_stride, rows_per_seq, rows_with_b,
-                              da.V, chunk, n_chunks, c2, stats, i0, da.L + da.nb);
+                              da.V, chunk, n_chunks, c2, stats, i0, da.L + da.nb, da.tokens, const_cast<float*>(da.gz),
+                              const_cast<float*>(da.gd));
 }
 
 // ---------------------------------------------------------------- draft_decide
@@ -865,13 +879,14 @@ __global__ __launch_bounds__(kThreads) void redraw_pick_kernel(const RedrawJob* 
     __shared__ int32_t first_wave_lane[kThreads / kWave];
     __shared__ int32_t chosen;
     const int64_t s = blockIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    // (the chunk totals are loaded with the job, not after it)
+    const double t = wave == 0 && lane < n_chunks ? tot[s * kMaxSplit + lane] : 0.0;
     const RedrawJob job = jobs[s];
     if (job.mode == kJobNone) return;  // uniform for the workgroup
     float* sg = seg + s * 2 * nseg;
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
     if (wave == 0) {
-        const double t = lane < n_chunks ? tot[s * kMaxSplit + lane] : 0.0;
         double incl = t;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
@@ -1031,7 +1046,7 @@ struct Plan {
     int32_t n_arr;    // segment-sum arrays per job
     int64_t rows;     // rows streamed by row_stats
     int64_t n_jobs;
-    size_t off_stats, off_jobs, off_seg, off_tot, total;
+    size_t off_stats, off_jobs, off_seg, off_tot, off_gather, total;
 };
 
 constexpr int64_t kTargetBlocks = 2048;
@@ -1069,6 +1084,8 @@ Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_
     off = align_up(off + static_cast<size_t>(n_jobs) * n_arr * p.nseg * sizeof(float), kWorkspaceAlign);
     p.off_tot = off;  // chunk totals of the split tail
     off = align_up(off + static_cast<size_t>(n_jobs) * kMaxSplit * sizeof(double), kWorkspaceAlign);
+    p.off_gather = off;  // the drafted tokens' target and draft logits, [B, L] each
+    off = align_up(off + static_cast<size_t>(2) * B * L * sizeof(float), kWorkspaceAlign);
     p.total = off;
     (void)L;
     return p;
@@ -1264,10 +1281,16 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
                            dim3(kThreads), 0, stream, da, c2);
         return hipGetLastError();
     }
+    // the statistics passes gather the drafted tokens' logits for the decision
+    float* gather = reinterpret_cast<float*>(base + p.off_gather);
+    da.gz = gather;
+    da.gd = gather + pr.B * pr.L;
+    da.gz_stride = pr.L;
+    da.gd_stride = pr.L;
     if (chunk <= 0) {
         hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads),
                            0, stream, pr.target, pr.t_stride, pr.draft, pr.d_stride, pr.L + nb, pr.L, pr.V,
-                           p.chunk1, p.c1, c2, stats, 0, pr.L + nb);
+                           p.chunk1, p.c1, c2, stats, 0, pr.L + nb, pr.tokens, gather, gather + pr.B * pr.L);
     } else {
         // One statistics launch per chunk of positions, each gated by the
         // decision on the positions before it; chunks double in length
@@ -1298,7 +1321,7 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
     hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
                        stream, pr.draft, pr.d_stride, nullptr, int64_t(0), pr.L, 0, pr.V, p.chunk1, p.c1, c2,
-                       stats, 0, pr.L);
+                       stats, 0, pr.L, nullptr, nullptr, nullptr);
     hipLaunchKernelGGL((draft_decide_kernel<BF16>), dim3(static_cast<uint32_t>((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, invT, stats, p.c1,
                        pr.uniforms, pr.sampled, jobs);
