@@ -1222,27 +1222,37 @@ __global__ __launch_bounds__(kStreamWaves * kWave, 1) void stream_gemm_kernel(co
     };
     // full chunks wave, wave + 8, ...: loads two chunks ahead of the MFMAs
     // (sched_barrier fences keep each group of loads ahead of the MFMAs that
-    // follow it: hoisted above them, the MFMAs would wait for every load)
+    // follow it: hoisted above them, the MFMAs would wait for every load).
+    // The loop runs whole rounds of three chunks and has one back edge, on
+    // which the loads in flight are those on entry (sets 0 then 1), so that
+    // the compiler's count-based waits let each MFMA group wait for its own
+    // set only; the one or two chunks left after the rounds follow it.
     constexpr int S = kStreamWaves;
-    int c = wave;
+    const int c = wave;
+    const int32_t mine = __builtin_amdgcn_readfirstlane(nfull > wave ? (nfull - wave + S - 1) / S : 0);
+    const int32_t rounds = mine / 3;
     load_chunk(c, 0);
     load_chunk(c + S, 1);
-    for (; c < nfull; c += 3 * S) {
+    for (int32_t t = 0; t < rounds; ++t) {
+        const int ct = c + 3 * S * t;
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk(c + 2 * S, 2);
+        load_chunk(ct + 2 * S, 2);
         __builtin_amdgcn_sched_barrier(0);
         mfma_chunk(0);
         __builtin_amdgcn_sched_barrier(0);
-        if (c + S >= nfull) break;
-        load_chunk(c + 3 * S, 0);
+        load_chunk(ct + 3 * S, 0);
         __builtin_amdgcn_sched_barrier(0);
         mfma_chunk(1);
         __builtin_amdgcn_sched_barrier(0);
-        if (c + 2 * S >= nfull) break;
-        load_chunk(c + 4 * S, 1);
+        load_chunk(ct + 4 * S, 1);
         __builtin_amdgcn_sched_barrier(0);
         mfma_chunk(2);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int32_t left = mine - 3 * rounds;  // chunks in sets 0 and 1 still to add
+    if (left > 0) mfma_chunk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (left > 1) mfma_chunk(1);
     __builtin_amdgcn_sched_barrier(0);
     // a last, partial chunk (K or the split not a multiple of 64): slots past
     // the end load zeros; taken by the wavefront whose turn it is
