@@ -3,7 +3,7 @@
 The pages add the diffusion (LoRA) pathway to every projection of every
 transformer layer ("How It Works: The 'Uno' Architecture" and "Two Decoupled
 Weight Sets" on the aifromscratch.in page) and say nothing about the rest of
-the layer.  This driver runs the plainest Llama-like chain with the
+the layer.  This module runs the plainest Llama-like chain with the
 attention mixing left out, every projection a gated-LoRA call on the same
 mixed batch of verify and draft rows:
 

@@ -1,4 +1,4 @@
-"""Layer-stack glue and the stack driver on the GPU vs the oracle.
+"""Layer-stack glue and the layer stack on the GPU vs the oracle.
 
 Glue kernels are compared elementwise with the fp64 oracle (bf16 output
 rounding bounds the error by 2^-8 relative; the test uses 1e-2 floored).
