@@ -1689,19 +1689,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
         if (strstr(e, "kg2")) p.tile.kg = 2;
     }
     // 32 rows or fewer (a plan of at most 64 rows): the weight-streaming
-    // kernel for the LoRA down-projection and the SwiGLU launch, where it was
-    // measured faster than the 64-row tiles (one sequence of [16 | 16] rows,
-    // weights cold: gate|up 81 against 90 us, the four down-projections of a
-    // layer 8 us less); the plain projections keep the tiles (q|k|v 25 against
-    // 26, o 23 against 25, down 38 against 65 us: its per-CU streaming rate,
-    // with x read again by every column block, falls short of the tiles'
-    // split of K).  UNO_GEMM_TILE=stream forces it for any epilogue,
-    // UNO_STREAM=0 turns it off (tests and tuning); never for a plan that
-    // must give the bits of a tiled pass (one_pass: the LM head).
+    // kernel for the LoRA down-projection, where it was measured faster than
+    // the 64-row tiles (one sequence of [16 | 16] rows, weights cold: the four
+    // down-projections of a layer 8 us less); the SwiGLU launch takes the
+    // 64 x 256 tile with two stage buffers (gate|up 73 against 79-80 us for
+    // the streaming kernel and the three-buffer tile); the plain projections
+    // keep the planner's tiles (q|k|v 25 against 26, o 23 against 25, down 38
+    // against 65 us for the streaming kernel: its per-CU streaming rate, with
+    // x read again by every column block, falls short of the tiles' split of
+    // K).  UNO_GEMM_TILE=stream forces it for any epilogue, UNO_STREAM=0
+    // turns it off (tests and tuning); never for a plan that must give the
+    // bits of a tiled pass (one_pass: the LM head).
     const Tile forced = env_tile();
     const char* st_env = getenv("UNO_STREAM");
-    const bool stream = p.rows_cap <= 64 && !one_pass && (forced.stream > 0 || (forced.bm == 0 && (tmode || bn256))) &&
+    const bool stream = p.rows_cap <= 64 && !one_pass && (forced.stream > 0 || (forced.bm == 0 && tmode)) &&
                         !(tmode && getenv("UNO_T_TILE") != nullptr) && !(st_env && st_env[0] == '0');
+    if (!stream && !tmode && bn256 && !one_pass && p.rows_cap <= 64 && forced.bm == 0 && forced.stream == 0)
+        p.tile = Tile{64, 256, 4, false, 64, 2};
     if (stream) {
         p.tile = Tile{64, 64, 8, false, 64};
         p.tile.stream = (bn256 || N > 16384) ? 2 : 1;  // SwiGLU: a gate and an up block

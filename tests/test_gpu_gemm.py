@@ -266,6 +266,32 @@ def test_swiglu_epilogue_is_separate_silu_mul(M, K, N, tile, split, monkeypatch)
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 17, 32])
+def test_swiglu_default_plan_few_rows(M, monkeypatch):
+    """The SwiGLU launch as planned for a single sequence (32 rows or fewer: the 64 x 256 tile
+    with two stage buffers) against the oracle's silu(g) u of the exact projections."""
+    for var in ("UNO_GEMM_TILE", "UNO_GEMM_SPLIT", "UNO_STREAM"):
+        monkeypatch.delenv(var, raising=False)
+    K, N = 1024, 512
+    rng = np.random.default_rng(M + 77)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    g_in = gemm_inputs(M, K, N, 128, seed=M + 11, dtype="bf16", gate=gate)
+    u_in = gemm_inputs(M, K, N, 128, seed=M + 12, dtype="bf16", gate=gate)
+    say("swiglu default plan", M, K, N)
+    x = to_dev(g_in["x"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, torch.cat([to_dev(g_in["a"], "bf16"), to_dev(u_in["a"], "bf16")], 0), plan, 2.0)
+    w_p, b_p = uno.swiglu_pack(to_dev(g_in["w"], "bf16"), to_dev(u_in["w"], "bf16"), to_dev(g_in["b"], "bf16"),
+                               to_dev(u_in["b"], "bf16"))
+    act = to_host(uno.gated_gemm_swiglu(x, w_p, t, b_p, plan))
+    g_ref = oracle.gated_lora(g_in["x"], g_in["w"], g_in["a"], g_in["b"], gate, 2.0)
+    u_ref = oracle.gated_lora(g_in["x"], u_in["w"], u_in["a"], u_in["b"], gate, 2.0)
+    err = floored_rel_err(act, oracle.stack.silu_mul(g_ref, u_ref))
+    print(f"  floored rel err vs exact {err:.3e}", flush=True)
+    assert err <= 2 * BF16_TOL, err
+
+
+@pytest.mark.gpu
 def test_swiglu_pack_layout():
     """Packed rows and the block-diagonal B, checked element by element on the host."""
     N, K, r = 256, 64, 16
