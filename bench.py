@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 SCALE = 2.0                   # alpha / r = 256 / 128
-EARLY_CHUNK = 8  # positions in the early-exit verifier's first chunk (then 16, 32, ...)
+EARLY_CHUNK = 6  # positions in the early-exit verifier's first chunk (then 12, 24, ...)
 
 
 def parse():
