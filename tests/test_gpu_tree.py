@@ -143,6 +143,34 @@ def test_degenerate_trees(path, monkeypatch):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deep_chain_walk_past_the_lds_tree(dtype, monkeypatch):
+    """A chain of 1200 nodes whose every drafted child is certain: the walk goes to the leaf,
+    reading parents, tokens and the depths' uniforms from memory past depth 1024."""
+    monkeypatch.setenv("UNO_TREE_PATH", "walk")
+    B, N, V = 2, 1200, 64
+    rng = np.random.default_rng(21)
+    par = np.tile(np.arange(-1, N - 1), (B, 1))
+    tok = rng.integers(0, V, (B, N))
+    tok[:, 0] = 0
+    z = rng.standard_normal((B, N, V)).astype(np.float32)
+    for s in range(B):
+        for c in range(1, N):
+            z[s, c - 1, :] = -np.inf
+            z[s, c - 1, tok[s, c]] = 0.0   # the child's token is the only one with mass
+    if dtype == "bf16":
+        z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
+    u = oracle.philox_uniforms(6, 0, 0, B * N).reshape(B, N)
+    say("tree verify deep chain", B, N, V, dtype)
+    gpu = _run(z, par, tok, u, 1.0, dtype)
+    ref = oracle.tree.tree_verify(z, par, tok, u.astype(np.float64), 1.0)
+    exact, excused, fails = _compare(gpu, ref, z, par, tok, u, 1.0)
+    assert not fails and excused == 0
+    assert np.all(gpu[0] == N - 1) and np.all(gpu[2] == N) and np.all(gpu[3] == N - 1)
+    np.testing.assert_array_equal(gpu[1][:, :N - 1], tok[:, 1:])
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("path", ["walk", "nodes"])
 def test_full_vocabulary_trees_sampled_against_the_oracle(path, monkeypatch):
     monkeypatch.setenv("UNO_TREE_PATH", path)
