@@ -70,6 +70,15 @@ constexpr size_t kPlanPermOffset = 256;
 
 int64_t rows_cap_for(int64_t M) { return (M + kRowAlign - 1) / kRowAlign * kRowAlign + kRowAlign; }
 
+// 32-row tiles serve plans of at most 32 rows (one sequence of verify and
+// draft rows): tile row p is the p-th row of [verify rows | draft rows] with
+// the segments' padding squeezed out, so every tile row is a real row and a
+// 32-row stage leaves LDS for twice the weight stages of a 64-row one.
+// Returns the plan row of tile row p, -1 past the last row.
+__device__ __forceinline__ int32_t compact_plan_row(int32_t p, const SegInfo& info) {
+    return p < info.Mv ? p : (p < info.Mv + info.Md ? info.Pv + (p - info.Mv) : -1);
+}
+
 __device__ __forceinline__ const int32_t* plan_bad_rows(const int32_t* perm, int64_t rows_cap) { return perm + rows_cap; }
 
 // ------------------------------------------------------------ segmentation
@@ -481,6 +490,10 @@ __global__ __launch_bounds__((TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::THREAD
                              (TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>::OCC))
 void gated_gemm_kernel(const GemmKArgs a) {
     using C = TileCfg<BM, BN, WGM, WGN, KB, NB, NBB, KG>;
+    // a 32-row tile takes the plan's rows compacted (compact_plan_row): one
+    // tile row band, planned only for 32 rows or fewer, never in T mode
+    constexpr bool CPT = BM == 32;
+    static_assert(!CPT || !TMODE, "compact tiles: main mode only");
     static_assert(!PP || (WGM == 4 && WGN == 2 && KB == 32 && C::NBUF == 4 && !C::SPLIT && KG == 1),
                   "ping-pong: 8 wavefronts, two teams of 2 x 2, KB 32, four buffers");
     constexpr int kBK = KB;
@@ -529,7 +542,13 @@ void gated_gemm_kernel(const GemmKArgs a) {
     // main loop's barriers publishing it; else after the main loop, when the
     // stage buffers are free).
     int32_t my_orow = -1;
-    if (tid < BM && m0 + tid < rows_valid) {
+    if constexpr (CPT) {
+        const int32_t pr = tid < BM ? compact_plan_row(tid, info) : -1;
+        if (pr >= 0) {
+            my_orow = a.perm[pr];
+            if (a.out_compact && my_orow >= 0) my_orow = pr;
+        }
+    } else if (tid < BM && m0 + tid < rows_valid) {
         if constexpr (TMODE) {
             my_orow = static_cast<int32_t>(m0 + tid);
         } else {
@@ -591,6 +610,9 @@ void gated_gemm_kernel(const GemmKArgs a) {
         int64_t src;
         if constexpr (TMODE) {
             src = (p < info.Md) ? a.perm[info.Pv + p] : -1;
+        } else if constexpr (CPT) {
+            const int32_t pr = compact_plan_row(static_cast<int32_t>(p), info);
+            src = pr >= 0 ? a.perm[pr] : -1;
         } else {
             src = (p < rows_valid) ? a.perm[p] : -1;
         }
@@ -604,7 +626,8 @@ void gated_gemm_kernel(const GemmKArgs a) {
         ldb2 = static_cast<uint32_t>(a.ldb * 2);
         // T row of this lane's first A block; verify rows give a negative
         // row whose wrapped byte offset is far past the range
-        trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - info.Pv) * ldt2;
+        // (a compact tile's draft rows start at tile row Mv)
+        trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - (CPT ? info.Mv : info.Pv)) * ldt2;
         brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2;
     }
     // output groups of this tile: its columns may fall in groups g_s .. g_s +
@@ -639,7 +662,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
     const int64_t ke = std::min<int64_t>(a.K, kb + a.k_per_split);
     const int nk_main = static_cast<int>((ke - kb + kBK - 1) / kBK);
     const bool tile_has_draft =
-        !TMODE && (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0);
+        !TMODE && (CPT ? info.Md > 0 : (m0 + BM > info.Pv) && (static_cast<int64_t>(info.Pv) + info.Md_pad > m0));
     const bool ext = tile_has_draft && (z == a.splits - 1) && a.r > 0;
     const int32_t spr_s = __builtin_amdgcn_readfirstlane((a.r + kBK - 1) / kBK);  // extension stages per slice
     const int nk_ext = __builtin_amdgcn_readfirstlane(ext ? nsl * spr_s : 0);
@@ -1055,10 +1078,11 @@ void gated_gemm_kernel(const GemmKArgs a) {
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int64_t p = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (p >= rows_valid) continue;
+            const int32_t tr = wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);  // tile row
+            const int64_t p = CPT ? compact_plan_row(tr, info) : m0 + tr;  // its plan row
+            if (p < 0 || p >= rows_valid) continue;
             if (a.splits == 1) {
-                const int64_t orow = s_orow[wm * C::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)];
+                const int64_t orow = s_orow[tr];
                 if (orow < 0) continue;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -1556,6 +1580,9 @@ Tile env_tile() {
 }
 
 bool tile_supported(Tile t) {
+    if (t.bm == 32)  // compact 32-row tiles (plans of 32 rows or fewer): 32 x 128 with two K groups, 32 x 256 with one
+        return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp &&
+               ((t.bn == 128 && t.kg == 2 && (t.nb == 4 || t.nb == 7)) || (t.bn == 256 && t.kg == 1 && t.nb == 4));
     if (t.bm == 64 && t.bn == 256)  // weight streaming at 64 rows or fewer (two or three stage buffers)
         return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.kg == 1 && (t.nb == 0 || t.nb == 2 || t.nb == 3);
     if (t.bm == 128 && t.bn == 192)  // 256 tiles (one per CU) at M = 1024, N = 6144
@@ -1633,7 +1660,7 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256, bool single_kg = false) {
     const Tile forced = env_tile();
     if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256) &&
-        (!single_kg || forced.kg == 1))
+        (!single_kg || forced.kg == 1) && (forced.bm != 32 || rows_cap <= kRowAlign))  // (rows_cap: modelled rows)
         return forced;
     if (forced.bm > 0 && forced.stream == 0 && !tile_supported(forced)) {
         static bool warned = false;  // (tuning aid: say once that the forced tile is not one of ours)
@@ -1704,8 +1731,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     const char* st_env = getenv("UNO_STREAM");
     const bool stream = p.rows_cap <= 64 && !one_pass && (forced.stream > 0 || (forced.bm == 0 && tmode)) &&
                         !(tmode && getenv("UNO_T_TILE") != nullptr) && !(st_env && st_env[0] == '0');
-    if (!stream && !tmode && bn256 && !one_pass && p.rows_cap <= 64 && forced.bm == 0 && forced.stream == 0)
-        p.tile = Tile{64, 256, 4, false, 64, 2};
+    // The plain and SwiGLU launches at 32 rows or fewer take the compact
+    // 32-row tiles: every LDS row holds a real row, so 32 x 128 keeps six
+    // 16 KB weight stages in flight per CU (seven buffers, two K groups) and
+    // 32 x 256 three 32 KB ones, where the 64-row tiles halve that with
+    // padding rows.  UNO_COMPACT=0 keeps the 64-row tiles (the 64 x 256 tile
+    // with two stage buffers for SwiGLU), for tuning.
+    const char* cp_env = getenv("UNO_COMPACT");
+    if (!stream && !tmode && !one_pass && p.rows_cap <= 2 * kRowAlign && forced.bm == 0 && forced.stream == 0) {
+        const Tile ct = bn256 ? Tile{32, 256, 4, false, 64, 4} : Tile{32, 128, 4, false, 64, 7, 0, 2};
+        if (!(cp_env && cp_env[0] == '0') && tile_fits(ct, gs)) p.tile = ct;
+        else if (bn256) p.tile = Tile{64, 256, 4, false, 64, 2};
+    }
     if (stream) {
         p.tile = Tile{64, 64, 8, false, 64};
         p.tile.stream = (bn256 || N > 16384) ? 2 : 1;  // SwiGLU: a gate and an up block
@@ -1730,7 +1767,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     p.m_tiles = (p.rows_cap + p.tile.bm - 1) / p.tile.bm;
     p.n_tiles = (N + p.tile.bn - 1) / p.tile.bn;
     int64_t s;
-    if (tmode) {
+    if (p.tile.bm == 32) {
+        // one band of compact rows; K split so that the column blocks times
+        // the splits come near one workgroup per CU (at least 256 K each)
+        p.m_tiles = 1;
+        s = std::max<int64_t>(1, std::min<int64_t>(K / 256, kNumCUs / p.n_tiles));
+    } else if (tmode) {
         // T mode works on the draft rows only; its work is tiny and its time
         // is latency: about 512 K per split measured best (K = 4096: 8 ways,
         // K = 14336: 16), capped so that the grid stays near 4 waves
@@ -1785,7 +1827,10 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else if (stage_buffers(t) == 4) launch_tile<64, 128, 2, 2, true, 64, false, 4>(ka, blocks, stream);
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
-        if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
+        if (t.bm == 32 && t.bn == 256) launch_tile<32, 256, 1, 4, false, 64, false, 4>(ka, blocks, stream);
+        else if (t.bm == 32 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
+        else if (t.bm == 32) launch_tile<32, 128, 1, 2, false, 64, false, 7, 0, 2>(ka, blocks, stream);
+        else if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 192 && t.kg == 2 && t.nb == 4)
             launch_tile<128, 192, 2, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
         else if (t.bm == 128 && t.bn == 192 && t.kg == 2)

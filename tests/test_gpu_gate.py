@@ -40,6 +40,8 @@ def _check_errors(ge, gate):
     ("bf16", 1024, 512, 512, 128, 40),  # many rows, several m tiles of bad rows
     ("bf16", 40, 256, 128, 16, 40),     # every row bad: both segments empty
     ("bf16", 33, 4096, 1024, 128, 1),   # split of K
+    ("bf16", 32, 1024, 512, 128, 4),    # 32 rows or fewer: the compact 32-row tile
+    ("bf16", 24, 256, 128, 16, 24),     # ... every row bad
     ("f32", 24, 512, 512, 128, 3),      # fp32 correctness path
 ])
 def test_bad_gate_rows_are_nan_and_counted(dtype, M, K, N, r, n_bad):
@@ -66,15 +68,17 @@ def test_bad_gate_rows_are_nan_and_counted(dtype, M, K, N, r, n_bad):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("tile,split", [(None, None), ("256x256w8k64r3", "3"), ("64x256b3", None)])
-def test_bad_gate_rows_in_grouped_and_swiglu_launches(tile, split, monkeypatch):
+@pytest.mark.parametrize("tile,split,M", [(None, None, 300), ("256x256w8k64r3", "3", 300), ("64x256b3", None, 300),
+                                          (None, None, 30), (None, "1", 30)])
+def test_bad_gate_rows_in_grouped_and_swiglu_launches(tile, split, M, monkeypatch):
     """The plan-based launches of a layer: grouped q|k|v-like and SwiGLU gate|up, with the
-    planner's tiles, a split of K (reduction launch), and the weight-streaming tile."""
+    planner's tiles, a split of K (reduction launch), the 64 x 256 tile, and at 30 rows the
+    compact 32-row tiles (split as planned, or not at all)."""
     if tile:
         monkeypatch.setenv("UNO_GEMM_TILE", tile)
     if split:
         monkeypatch.setenv("UNO_GEMM_SPLIT", split)
-    M, K, r = 300, 1000, 64
+    K, r = 1000, 64
     group_n = [256, 128, 128]
     gate, bad = _bad_gate(M, 11, 17)
     clean = np.where(gate > 1, 0, gate).astype(np.uint8)

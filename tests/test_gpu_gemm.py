@@ -268,8 +268,8 @@ def test_swiglu_epilogue_is_separate_silu_mul(M, K, N, tile, split, monkeypatch)
 @pytest.mark.gpu
 @pytest.mark.parametrize("M", [1, 17, 32])
 def test_swiglu_default_plan_few_rows(M, monkeypatch):
-    """The SwiGLU launch as planned for a single sequence (32 rows or fewer: the 64 x 256 tile
-    with two stage buffers) against the oracle's silu(g) u of the exact projections."""
+    """The SwiGLU launch as planned for a single sequence (32 rows or fewer: the compact
+    32 x 256 tile) against the oracle's silu(g) u of the exact projections."""
     for var in ("UNO_GEMM_TILE", "UNO_GEMM_SPLIT", "UNO_STREAM"):
         monkeypatch.delenv(var, raising=False)
     K, N = 1024, 512
@@ -316,6 +316,8 @@ GROUPED = [  # (M, K, group sizes, r)
     (300, 1000, (384, 256), 128),           # ragged K
     (64, 4096, (4096, 1024, 1024), 128),    # q | k | v of the 8B layer, 2 x [16 | 16] rows
     (96, 512, (128, 128, 128, 128), 16),    # four groups
+    (32, 4096, (4096, 1024, 1024), 128),    # q | k | v of one sequence: the compact 32-row tile
+    (29, 1000, (256, 128, 72), 64),         # compact tile, ragged K and last group
 ]
 
 
@@ -409,6 +411,73 @@ def test_weight_streaming_kernel(M, K, N, r, pattern, monkeypatch):
     plan = uno.RowPlan(to_dev(gate, "u8"))
     t = uno.lora_down(x, a, plan, 2.0)
     assert np.array_equal(to_host(uno.gated_gemm(x, w, t, b, plan)), y)
+
+
+COMPACT = [  # M, K, N, r, gate pattern, forced tile (None: the planner's), forced split (None: planned)
+    (1, 64, 16, 8, "draft", None, None),
+    (1, 64, 16, 8, "verify", None, None),
+    (7, 1000, 300, 16, "random", "32x128b4kg2", None),    # ragged K (a partial last stage) and N
+    (20, 520, 1024, 128, "random", "32x128b7kg2", "3"),
+    (32, 4096, 1024, 128, "seq", None, None),             # one sequence of [16 verify | 16 draft]
+    (32, 4096, 700, 128, "verify", None, None),
+    (32, 2048, 96, 256, "draft", "32x128b7kg2", "1"),     # r = 256: four extension stages, no split
+    (29, 14336, 256, 128, "random", None, None),          # the down-projection's depth
+    (31, 1000, 512, 64, "random", "32x256b4", "2"),       # the SwiGLU tile on a plain epilogue
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,r,pattern,tile,split", COMPACT)
+def test_compact_tiles(M, K, N, r, pattern, tile, split, monkeypatch):
+    """The 32-row tiles (rows of both segments compacted into one band) against the oracle;
+    verify rows bitwise those of an all-verify call; the split steps equal the one call."""
+    for var, val in (("UNO_GEMM_TILE", tile), ("UNO_GEMM_SPLIT", split)):
+        if val is None:
+            monkeypatch.delenv(var, raising=False)
+        else:
+            monkeypatch.setenv(var, val)
+    monkeypatch.delenv("UNO_COMPACT", raising=False)
+    rng = np.random.default_rng(M * 5 + K + N)
+    gate = {"random": (rng.random(M) < 0.5).astype(np.uint8), "draft": np.ones(M, np.uint8),
+            "verify": np.zeros(M, np.uint8), "seq": gate_vector(1, M // 2, M - M // 2)}[pattern]
+    inp = gemm_inputs(M, K, N, r, seed=M + 3 * K + N, dtype="bf16", gate=gate)
+    say("gemm compact", M, K, N, r, pattern, tile, split)
+    y = _run(inp, "bf16")
+    ref = oracle.gated_lora(inp["x"], inp["w"], inp["a"], inp["b"], gate, 2.0)
+    err = floored_rel_err(y, ref)
+    assert err <= BF16_TOL, err
+    y0 = _run(inp, "bf16", gate=np.zeros_like(gate))
+    assert np.array_equal(y[gate == 0], y0[gate == 0]), "verify rows must match the all-verify call bitwise"
+    x, w = to_dev(inp["x"], "bf16"), to_dev(inp["w"], "bf16")
+    a, b = to_dev(inp["a"], "bf16"), to_dev(inp["b"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, a, plan, 2.0)
+    assert np.array_equal(to_host(uno.gated_gemm(x, w, t, b, plan)), y)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_compact_tiles_match_64_row_tiles(M, monkeypatch):
+    """The compact tile against the 64-row tile it replaces at few rows (UNO_COMPACT=0), on a
+    batch-1 q projection: the same sums up to the fp32 order of the split (bf16 bound), and
+    with one K split and one K group each, the same bits."""
+    K, N, r = 4096, 1024, 128
+    rng = np.random.default_rng(M + 3)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    inp = gemm_inputs(M, K, N, r, seed=M + 9, dtype="bf16", gate=gate)
+    say("gemm compact vs 64-row", M)
+    for var in ("UNO_GEMM_TILE", "UNO_GEMM_SPLIT", "UNO_STREAM"):
+        monkeypatch.delenv(var, raising=False)
+    y_c = _run(inp, "bf16")
+    monkeypatch.setenv("UNO_COMPACT", "0")
+    y_p = _run(inp, "bf16")
+    assert floored_rel_err(y_c.astype(np.float64), y_p.astype(np.float64)) <= BF16_TOL
+    monkeypatch.setenv("UNO_GEMM_SPLIT", "1")
+    monkeypatch.setenv("UNO_GEMM_TILE", "64x128")
+    y_p1 = _run(inp, "bf16")
+    monkeypatch.setenv("UNO_GEMM_TILE", "32x256b4")
+    y_c1 = _run(inp, "bf16")
+    assert np.array_equal(y_c1, y_p1), "one K pass, one K group: same K slices in the same order"
 
 
 @pytest.mark.gpu
