@@ -5,8 +5,9 @@
 (run as a script: importing the package first would load the library it rebuilds)
 
 Every source under csrc/ is compiled to an object in _build/ and linked into
-lossless_speculative_drafting_amd/libuno.so.  Packed-fp32 instructions are
-disabled for all device code.
+lossless_speculative_drafting_amd/libuno.so.  The measurement probes under
+probes/ (stand-alone HIP programs, not part of the library) are built next to
+their sources.  Packed-fp32 instructions are disabled for all device code.
 """
 
 import argparse
@@ -21,6 +22,7 @@ REPO = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(REPO, "_build", "libuno")
 LIB_PATH = os.path.join(PKG_DIR, "libuno.so")
+PROBES = os.path.join(PKG_DIR, "probes")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -61,13 +63,30 @@ def _compile(src, verbose):
     return obj
 
 
+def _build_probe(src, verbose):
+    exe = os.path.splitext(src)[0]
+    cmd = [_hipcc(), *[f for f in COMMON_FLAGS if f != "-fPIC"], src, "-o", exe]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        noise = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
+        raise RuntimeError(f"probe build failed: {src}\n" + "\n".join(noise))
+    return exe
+
+
 def build(jobs=None, verbose=False):
-    """Compile every source and link libuno.so; returns the library path."""
+    """Compile every source and link libuno.so (and build the probes); returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(8, len(srcs))
+    probes = sorted(os.path.join(PROBES, f) for f in os.listdir(PROBES) if f.endswith(".hip")) \
+        if os.path.isdir(PROBES) else []
+    jobs = jobs or min(8, len(srcs) + len(probes))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        probe_jobs = [ex.submit(_build_probe, p, verbose) for p in probes]
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        for j in probe_jobs:
+            j.result()
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
