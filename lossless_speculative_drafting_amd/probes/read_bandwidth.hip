@@ -13,7 +13,12 @@
 //                a statistics workgroup's share of a logit row pair);
 //   row block    a workgroup reads a block of 128 rows of 8 KB (a weight tile
 //                of a K = 4096 bf16 projection), P bytes of every row per step,
-//                steps in K order -- the order a GEMM tile streams its weights.
+//                steps in K order -- the order a GEMM tile streams its weights;
+//   L2-resident  every workgroup reads the same 2 MB region (each XCD's 4 MB
+//                L2 holds it after the first touch), with plain 16-byte loads
+//                into registers or with buffer loads that write LDS directly
+//                (16 copies of 1 KB in flight per wavefront, into a ring of
+//                LDS slots that nothing reads) -- the GEMM tiles' copy path.
 // Every workgroup folds what it read into one word, written only in the
 // impossible case that it equals a sentinel, so the loads cannot be removed.
 #include <hip/hip_runtime.h>
@@ -89,6 +94,68 @@ __global__ __launch_bounds__(kThreads) void row_block(const char* __restrict__ b
     if (acc == kSentinel) out[blockIdx.x] = acc;
 }
 
+constexpr int kRegion = 2 << 20;  // bytes: the L2-resident region
+constexpr int kRegionVecs = kRegion / 16;
+
+template <int UNR>
+__global__ __launch_bounds__(kThreads) void l2_plain(const u32x4* __restrict__ p, int passes, unsigned* out) {
+    unsigned acc = 0;
+    const int start = static_cast<int>((blockIdx.x * 4096u) % kRegionVecs);  // workgroups start apart
+    for (int ps = 0; ps < passes; ++ps)
+        for (int i = threadIdx.x; i < kRegionVecs; i += kThreads * UNR) {
+            u32x4 v[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                int k = i + u * kThreads + start;  // < 2 kRegionVecs
+                k = k < kRegionVecs ? k : k - kRegionVecs;
+                k = k < kRegionVecs ? k : k - kRegionVecs;
+                v[u] = p[k];
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) acc ^= fold(v[u]);
+        }
+    if (acc == kSentinel) out[blockIdx.x] = acc;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte chunk per lane from the buffer at byte offset voff into LDS at
+// lds_addr + 16 * lane (the buffer load's LDS-write form).
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(m0v), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+constexpr int kDmaSlots = 16;  // per wavefront, 1 KB each; also the copies in flight
+
+__global__ __launch_bounds__(kThreads) void l2_dma(const char* __restrict__ p, int passes, unsigned* out) {
+    __shared__ __attribute__((aligned(1024))) uint32_t ring[kThreads / 64 * kDmaSlots * 256];
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint64_t addr = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr)));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(addr >> 32)));
+    r.z = kRegion;
+    r.w = 0x00020000;  // raw buffer, 32-bit data format
+    const uint32_t lds0 =
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(ring))) +
+        static_cast<uint32_t>(wave * kDmaSlots * 1024);
+    constexpr int kPieces = kRegion / 1024;
+    const int start = static_cast<int>((blockIdx.x * 64u) % kPieces);
+    int n = 0;
+    for (int ps = 0; ps < passes; ++ps)
+        for (int c = wave; c < kPieces; c += kThreads / 64, ++n) {
+            int k = c + start;
+            k = k < kPieces ? k : k - kPieces;
+            dma16(lds0 + static_cast<uint32_t>(n % kDmaSlots) * 1024u, static_cast<uint32_t>(k) * 1024u + lane * 16u, r);
+            asm volatile("s_waitcnt vmcnt(15)" ::: "memory");  // kDmaSlots - 1: the slot reused next has landed
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ring[threadIdx.x] == kSentinel) out[blockIdx.x] = ring[threadIdx.x];
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -140,6 +207,30 @@ int main(int argc, char** argv) {
     run("row block 128 x 8 KB, 128 B per row per step", [&](char* b) { row_block<128><<<row_blocks, kThreads>>>(b, out); });
     run("row block 128 x 8 KB, 512 B per row per step", [&](char* b) { row_block<512><<<row_blocks, kThreads>>>(b, out); });
     run("row block 128 x 8 KB, 1 KB per row per step", [&](char* b) { row_block<1024><<<row_blocks, kThreads>>>(b, out); });
+    // L2-resident region: the first 2 MB of buffer 0, read twice per workgroup
+    std::printf("L2-resident reads (every workgroup reads the same 2 MB twice):\n");
+    auto run_l2 = [&](const char* name, unsigned wgs, auto launch) {
+        launch();
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipEventRecord(e0));
+        for (int r = 0; r < 5; ++r) launch();
+        CHECK(hipEventRecord(e1));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0.f;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        const double total = 5.0 * wgs * 2 * static_cast<double>(kRegion);
+        std::printf("%-40s %6.2f TB/s aggregate, %5.1f GB/s per CU\n", name, total / (ms * 1e-3) / 1e12,
+                    total / (ms * 1e-3) / 1e9 / 256);
+        std::fflush(stdout);
+    };
+    for (unsigned g : {256u, 512u, 2048u}) {
+        char name[64];
+        std::snprintf(name, sizeof name, "plain loads, 8 per step, %u WGs", g);
+        run_l2(name, g, [&] { l2_plain<8><<<g, kThreads>>>(v(buf[0]), 2, out); });
+        std::snprintf(name, sizeof name, "LDS-DMA copies, %u WGs", g);
+        run_l2(name, g, [&] { l2_dma<<<g, kThreads>>>(buf[0], 2, out); });
+    }
     for (auto& b : buf) CHECK(hipFree(b));
     CHECK(hipFree(out));
     return 0;
