@@ -618,8 +618,20 @@ void gated_gemm_kernel(const GemmKArgs a) {
         }
         xoff[q] = (src >= 0 ? static_cast<uint32_t>(src * a.ldx * 2) : kOOB) + kcA[q & 1];
     }
+    // Weight row of tile column i.  A SwiGLU launch on a 128-column tile (the
+    // compact 32-row tile) pairs half of a gate block with the same half of
+    // its up block: tile t covers act columns [64 t, 64 t + 64); its columns
+    // [0, 64) are gate rows 256 (t / 2) + 64 (t % 2) + i of the interleaved
+    // weights and [64, 128) the up rows 128 further.  (Each wavefront's copy
+    // rows lie in one of the two halves, so a row block maps linearly.)
+    const bool swz128 = BN == kSwigluBlock && a.epi == kEpiSwiglu;
+    auto wcol = [&](int64_t i) -> int64_t {
+        if (!swz128) return n0 + i;
+        const int64_t t = n0 / kSwigluBlock;
+        return 2 * kSwigluBlock * (t >> 1) + (kSwigluBlock / 2) * (t & 1) + (i < kSwigluBlock / 2 ? i : i + kSwigluBlock / 2);
+    };
     const uint32_t ldw2 = static_cast<uint32_t>(a.ldw * 2);
-    const uint32_t wrow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldw2;
+    const uint32_t wrow0 = static_cast<uint32_t>(wcol(wave * (BN / C::NWAVES) + lrow)) * ldw2;
     uint32_t ldt2 = 0, ldb2 = 0, trow0 = 0, brow0 = 0;
     if constexpr (!TMODE) {
         ldt2 = static_cast<uint32_t>(a.ldt * 2);
@@ -628,7 +640,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
         // row whose wrapped byte offset is far past the range
         // (a compact tile's draft rows start at tile row Mv)
         trow0 = static_cast<uint32_t>(m0 + wave * (BM / C::NWAVES) + lrow - (CPT ? info.Mv : info.Pv)) * ldt2;
-        brow0 = static_cast<uint32_t>(n0 + wave * (BN / C::NWAVES) + lrow) * ldb2;
+        brow0 = static_cast<uint32_t>(wcol(wave * (BN / C::NWAVES) + lrow)) * ldb2;
     }
     // output groups of this tile: its columns may fall in groups g_s .. g_s +
     // nsl - 1 (group ends are multiples of 8); its draft rows read T from
@@ -1014,7 +1026,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
         // (lanes past RPI whole rows -- WN = 96: lanes 60..63 -- take none)
         const int lane_row0 = lane < RPI * CPR ? lane / CPR : C::WM;
         const int64_t n = n0 + wn * C::WN + c * 8;
-        if constexpr (!TMODE && BN == 2 * kSwigluBlock && WGN % 2 == 0) {
+        if constexpr (!TMODE && ((BN == 2 * kSwigluBlock && WGN % 2 == 0) || (BN == kSwigluBlock && WGN == 2))) {
             if (a.epi == kEpiSwiglu) {
                 // Wavefront (wm, pw) holds gate columns [pw WN, pw WN + WN) of the
                 // tile and (wm, pw + WGN / 2) the matching up columns; the two
@@ -1100,7 +1112,7 @@ void gated_gemm_kernel(const GemmKArgs a) {
                 float* prow = a.partial + (static_cast<int64_t>(z) * a.rows_cap + p) * a.N;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const int64_t n = n0 + wn * C::WN + j * 32 + (lane & 31);
+                    const int64_t n = wcol(wn * C::WN + j * 32 + (lane & 31));  // (a weight row: partial column)
                     if (n < a.N) prow[n] = acc[i][j][v];
                 }
             }
@@ -1562,6 +1574,7 @@ Tile env_tile() {
     if (!s || sscanf(s, "%dx%d", &t.bm, &t.bn) != 2) return Tile{0, 0, 4, false, 64};
     t.kb = default_kb(t.bm, t.bn);
     if (strstr(s, "w8")) t.waves = 8;
+    if (strstr(s, "w2")) t.waves = 2;
     if (strstr(s, "k64")) t.kb = 64;
     if (strstr(s, "pp")) {
         t.waves = 8;
@@ -1580,9 +1593,12 @@ Tile env_tile() {
 }
 
 bool tile_supported(Tile t) {
-    if (t.bm == 32)  // compact 32-row tiles (plans of 32 rows or fewer): 32 x 128 with two K groups, 32 x 256 with one
-        return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp &&
-               ((t.bn == 128 && t.kg == 2 && (t.nb == 4 || t.nb == 7)) || (t.bn == 256 && t.kg == 1 && t.nb == 4));
+    if (t.bm == 32)  // compact 32-row tiles (plans of 32 rows or fewer): 32 x 128 with two K groups (or one, two
+                     // wavefronts: the SwiGLU form), 32 x 256 with one
+        return t.kb == 64 && t.nbb == 0 && !t.pp &&
+               ((t.waves == 4 && t.bn == 128 && t.kg == 2 && (t.nb == 4 || t.nb == 7)) ||
+                (t.waves == 2 && t.bn == 128 && t.kg == 1 && t.nb == 7) ||
+                (t.waves == 4 && t.bn == 256 && t.kg == 1 && t.nb == 4));
     if (t.bm == 64 && t.bn == 256)  // weight streaming at 64 rows or fewer (two or three stage buffers)
         return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.kg == 1 && (t.nb == 0 || t.nb == 2 || t.nb == 3);
     if (t.bm == 128 && t.bn == 192)  // 256 tiles (one per CU) at M = 1024, N = 6144
@@ -1659,7 +1675,9 @@ int64_t choose_split_for(Tile t, int64_t rows_cap, int64_t N, int64_t K, double*
 // odd sub-steps apart, so their bits differ).
 Tile choose_tile(int64_t rows_cap, int64_t N, int64_t K, const GroupSpec& gs, bool bn256, bool single_kg = false) {
     const Tile forced = env_tile();
-    if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || forced.bn == 256) &&
+    // (SwiGLU needs 256 columns, or the compact 128-column tile that pairs half blocks)
+    const bool swiglu_ok = forced.bn == 256 || (forced.bm == 32 && forced.bn == 128 && forced.kg == 1);
+    if (tile_supported(forced) && tile_fits(forced, gs) && (!bn256 || swiglu_ok) &&
         (!single_kg || forced.kg == 1) && (forced.bm != 32 || rows_cap <= kRowAlign))  // (rows_cap: modelled rows)
         return forced;
     if (forced.bm > 0 && forced.stream == 0 && !tile_supported(forced)) {
@@ -1733,13 +1751,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
                         !(tmode && getenv("UNO_T_TILE") != nullptr) && !(st_env && st_env[0] == '0');
     // The plain and SwiGLU launches at 32 rows or fewer take the compact
     // 32-row tiles: every LDS row holds a real row, so 32 x 128 keeps six
-    // 16 KB weight stages in flight per CU (seven buffers, two K groups) and
-    // 32 x 256 three 32 KB ones, where the 64-row tiles halve that with
-    // padding rows.  UNO_COMPACT=0 keeps the 64-row tiles (the 64 x 256 tile
-    // with two stage buffers for SwiGLU), for tuning.
+    // 16 KB weight stages in flight per CU (seven buffers), where the 64-row
+    // tiles carry padding rows.  The plain launches run it with two K groups;
+    // SwiGLU runs it with one K group of two wavefronts, each tile pairing
+    // half of a gate block with half of its up block, so that a layer's
+    // 28672 interleaved columns make 224 tiles and need no split of K (and no
+    // reduction launch).  UNO_COMPACT=0 keeps the 64-row tiles (the 64 x 256
+    // tile with two stage buffers for SwiGLU), for tuning.
     const char* cp_env = getenv("UNO_COMPACT");
     if (!stream && !tmode && !one_pass && p.rows_cap <= 2 * kRowAlign && forced.bm == 0 && forced.stream == 0) {
-        const Tile ct = bn256 ? Tile{32, 256, 4, false, 64, 4} : Tile{32, 128, 4, false, 64, 7, 0, 2};
+        const Tile ct = bn256 ? Tile{32, 128, 2, false, 64, 7} : Tile{32, 128, 4, false, 64, 7, 0, 2};
         if (!(cp_env && cp_env[0] == '0') && tile_fits(ct, gs)) p.tile = ct;
         else if (bn256) p.tile = Tile{64, 256, 4, false, 64, 2};
     }
@@ -1828,6 +1849,7 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.bm == 32 && t.bn == 256) launch_tile<32, 256, 1, 4, false, 64, false, 4>(ka, blocks, stream);
+        else if (t.bm == 32 && t.kg == 1) launch_tile<32, 128, 1, 2, false, 64, false, 7>(ka, blocks, stream);
         else if (t.bm == 32 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
         else if (t.bm == 32) launch_tile<32, 128, 1, 2, false, 64, false, 7, 0, 2>(ka, blocks, stream);
         else if (t.pp) launch_tile<256, 256, 4, 2, false, 32, true>(ka, blocks, stream);

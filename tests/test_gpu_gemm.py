@@ -292,6 +292,41 @@ def test_swiglu_default_plan_few_rows(M, monkeypatch):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("M", [1, 20, 32])
+def test_swiglu_compact_tile_pairs_half_blocks(M, monkeypatch):
+    """The compact SwiGLU tile (32 rows x 128 columns: half a gate block and the same half
+    of its up block) against the 64 x 256 tile it replaces, both with one K pass and one
+    K group: the same K slices in the same order, so the same bits; with K split three
+    ways (partials in weight-row order, summed by the reduction) within the bf16 bound."""
+    K, N_half, r = 1024, 768, 128
+    rng = np.random.default_rng(M + 91)
+    gate = (rng.random(M) < 0.5).astype(np.uint8)
+    g_in = gemm_inputs(M, K, N_half, r, seed=M + 21, dtype="bf16", gate=gate)
+    u_in = gemm_inputs(M, K, N_half, r, seed=M + 22, dtype="bf16", gate=gate)
+    say("swiglu compact tile", M)
+    for var in ("UNO_GEMM_TILE", "UNO_GEMM_SPLIT", "UNO_STREAM", "UNO_COMPACT"):
+        monkeypatch.delenv(var, raising=False)
+    x = to_dev(g_in["x"], "bf16")
+    plan = uno.RowPlan(to_dev(gate, "u8"))
+    t = uno.lora_down(x, torch.cat([to_dev(g_in["a"], "bf16"), to_dev(u_in["a"], "bf16")], 0), plan, 2.0)
+    w_p, b_p = uno.swiglu_pack(to_dev(g_in["w"], "bf16"), to_dev(u_in["w"], "bf16"), to_dev(g_in["b"], "bf16"),
+                               to_dev(u_in["b"], "bf16"))
+    monkeypatch.setenv("UNO_GEMM_SPLIT", "1")
+    act_c = to_host(uno.gated_gemm_swiglu(x, w_p, t, b_p, plan))
+    monkeypatch.setenv("UNO_COMPACT", "0")
+    act_64 = to_host(uno.gated_gemm_swiglu(x, w_p, t, b_p, plan))
+    assert np.array_equal(act_c, act_64)
+    monkeypatch.delenv("UNO_COMPACT")
+    monkeypatch.setenv("UNO_GEMM_SPLIT", "3")
+    act_s = to_host(uno.gated_gemm_swiglu(x, w_p, t, b_p, plan))
+    assert floored_rel_err(act_s.astype(np.float64), act_c.astype(np.float64)) <= BF16_TOL
+    g_ref = oracle.gated_lora(g_in["x"], g_in["w"], g_in["a"], g_in["b"], gate, 2.0)
+    u_ref = oracle.gated_lora(g_in["x"], u_in["w"], u_in["a"], u_in["b"], gate, 2.0)
+    err = floored_rel_err(act_c, oracle.stack.silu_mul(g_ref, u_ref))
+    assert err <= 2 * BF16_TOL, err
+
+
+@pytest.mark.gpu
 def test_swiglu_pack_layout():
     """Packed rows and the block-diagonal B, checked element by element on the host."""
     N, K, r = 256, 64, 16
@@ -422,7 +457,8 @@ COMPACT = [  # M, K, N, r, gate pattern, forced tile (None: the planner's), forc
     (32, 4096, 700, 128, "verify", None, None),
     (32, 2048, 96, 256, "draft", "32x128b7kg2", "1"),     # r = 256: four extension stages, no split
     (29, 14336, 256, 128, "random", None, None),          # the down-projection's depth
-    (31, 1000, 512, 64, "random", "32x256b4", "2"),       # the SwiGLU tile on a plain epilogue
+    (31, 1000, 512, 64, "random", "32x256b4", "2"),       # a 256-column compact tile on a plain epilogue
+    (30, 1000, 640, 64, "random", "32x128w2b7", None),    # the SwiGLU form (one K group) on a plain epilogue
 ]
 
 
