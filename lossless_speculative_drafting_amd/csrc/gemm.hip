@@ -1597,7 +1597,7 @@ bool tile_supported(Tile t) {
                      // wavefronts: the SwiGLU form), 32 x 256 with one
         return t.kb == 64 && t.nbb == 0 && !t.pp &&
                ((t.waves == 4 && t.bn == 128 && t.kg == 2 && (t.nb == 4 || t.nb == 7)) ||
-                (t.waves == 2 && t.bn == 128 && t.kg == 1 && t.nb == 7) ||
+                (t.waves == 2 && t.bn == 128 && t.kg == 1 && (t.nb == 2 || t.nb == 3 || t.nb == 4 || t.nb == 7)) ||
                 (t.waves == 4 && t.bn == 256 && t.kg == 1 && t.nb == 4));
     if (t.bm == 64 && t.bn == 256)  // weight streaming at 64 rows or fewer (two or three stage buffers)
         return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.kg == 1 && (t.nb == 0 || t.nb == 2 || t.nb == 3);
@@ -1750,17 +1750,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool tmode, const GroupSpec&
     const bool stream = p.rows_cap <= 64 && !one_pass && (forced.stream > 0 || (forced.bm == 0 && tmode)) &&
                         !(tmode && getenv("UNO_T_TILE") != nullptr) && !(st_env && st_env[0] == '0');
     // The plain and SwiGLU launches at 32 rows or fewer take the compact
-    // 32-row tiles: every LDS row holds a real row, so 32 x 128 keeps six
-    // 16 KB weight stages in flight per CU (seven buffers), where the 64-row
-    // tiles carry padding rows.  The plain launches run it with two K groups;
-    // SwiGLU runs it with one K group of two wavefronts, each tile pairing
-    // half of a gate block with half of its up block, so that a layer's
-    // 28672 interleaved columns make 224 tiles and need no split of K (and no
-    // reduction launch).  UNO_COMPACT=0 keeps the 64-row tiles (the 64 x 256
-    // tile with two stage buffers for SwiGLU), for tuning.
+    // 32-row tiles: every LDS row holds a real row (the 64-row tiles carry 32
+    // padding rows).  32 x 128 with four stage buffers (80 KB; seven, or
+    // three, measured no faster, two slower); the plain launches run it with
+    // two K groups, SwiGLU with one K group of two wavefronts, each tile
+    // pairing half of a gate block with half of its up block, so that a
+    // layer's 28672 interleaved columns make 224 tiles and need no split of
+    // K (and no reduction launch).  UNO_COMPACT=0 keeps the 64-row tiles (the
+    // 64 x 256 tile with two stage buffers for SwiGLU), for tuning.
     const char* cp_env = getenv("UNO_COMPACT");
     if (!stream && !tmode && !one_pass && p.rows_cap <= 2 * kRowAlign && forced.bm == 0 && forced.stream == 0) {
-        const Tile ct = bn256 ? Tile{32, 128, 2, false, 64, 7} : Tile{32, 128, 4, false, 64, 7, 0, 2};
+        const Tile ct = bn256 ? Tile{32, 128, 2, false, 64, 4} : Tile{32, 128, 4, false, 64, 4, 0, 2};
         if (!(cp_env && cp_env[0] == '0') && tile_fits(ct, gs)) p.tile = ct;
         else if (bn256) p.tile = Tile{64, 256, 4, false, 64, 2};
     }
@@ -1849,6 +1849,9 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.bm == 32 && t.bn == 256) launch_tile<32, 256, 1, 4, false, 64, false, 4>(ka, blocks, stream);
+        else if (t.bm == 32 && t.kg == 1 && t.nb == 2) launch_tile<32, 128, 1, 2, false, 64, false, 2>(ka, blocks, stream);
+        else if (t.bm == 32 && t.kg == 1 && t.nb == 3) launch_tile<32, 128, 1, 2, false, 64, false, 3>(ka, blocks, stream);
+        else if (t.bm == 32 && t.kg == 1 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4>(ka, blocks, stream);
         else if (t.bm == 32 && t.kg == 1) launch_tile<32, 128, 1, 2, false, 64, false, 7>(ka, blocks, stream);
         else if (t.bm == 32 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);
         else if (t.bm == 32) launch_tile<32, 128, 1, 2, false, 64, false, 7, 0, 2>(ka, blocks, stream);
