@@ -212,9 +212,9 @@ uno_status uno_gated_gemm_residual(const void* x, const void* w, const void* t, 
  * act [M, N_half] = bf16(silu(g) * u) with g, u the bf16 gate and up
  * projections, bitwise the result of uno_gated_gemm_grouped for gate and up
  * under the same plan followed by uno_silu_mul.  (At 32 rows or fewer this
- * launch streams the weights with a kernel of its own, whose fp32 sums run
- * in another order than the grouped launch's tiles: there the two agree to
- * rounding.)
+ * launch takes a tile of its own -- 32 rows by half a gate block and half
+ * its up block, one K group -- whose fp32 sums run in another order than
+ * the grouped launch's two-K-group tiles: there the two agree to rounding.)
  * Domain: N_half a positive multiple of 128, rt a multiple of 8 in [8, 256],
  * otherwise as uno_gated_gemm; act must not alias the inputs. */
 size_t uno_gated_gemm_swiglu_workspace_size(int64_t M, int64_t N_half, int64_t K, int32_t rt);
