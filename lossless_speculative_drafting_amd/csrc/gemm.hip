@@ -372,7 +372,10 @@ struct TileCfg {
     static_assert(MI >= 1 && NJ >= 1 && WN >= 64, "wavefront tile");
     static constexpr int STAGE_ELEMS = (BM + BN) * KB;
     static constexpr int LDS_ELEMS = SPLIT ? NBUF * BM * KB + NBUF_B * BN * KB : NBUF * STAGE_ELEMS;
-    static constexpr int OCC = LDS_ELEMS * 2 > 80 * 1024 ? 1 : 2;
+    // workgroups per CU the registers are budgeted for: two where LDS allows
+    // (80 KB or less), one for the two-wavefront compact tile, whose grid is
+    // one workgroup per CU and whose register sets need the room
+    static constexpr int OCC = (LDS_ELEMS * 2 > 80 * 1024 || NWAVES == 2) ? 1 : 2;
     // The output-row table (BM int32) goes behind the epilogue's staging area
     // in the stage buffers when they have room for it, else into LDS of its own.
     // (tiles that may run the statistics epilogue also keep each row's drafted
@@ -1597,7 +1600,7 @@ bool tile_supported(Tile t) {
                      // wavefronts: the SwiGLU form), 32 x 256 with one
         return t.kb == 64 && t.nbb == 0 && !t.pp &&
                ((t.waves == 4 && t.bn == 128 && t.kg == 2 && (t.nb == 4 || t.nb == 7)) ||
-                (t.waves == 2 && t.bn == 128 && t.kg == 1 && (t.nb == 2 || t.nb == 3 || t.nb == 4 || t.nb == 7)) ||
+                (t.waves == 2 && t.bn == 128 && t.kg == 1 && (t.nb == 4 || t.nb == 7)) ||
                 (t.waves == 4 && t.bn == 256 && t.kg == 1 && t.nb == 4));
     if (t.bm == 64 && t.bn == 256)  // weight streaming at 64 rows or fewer (two or three stage buffers)
         return t.waves == 4 && t.kb == 64 && t.nbb == 0 && !t.pp && t.kg == 1 && (t.nb == 0 || t.nb == 2 || t.nb == 3);
@@ -1849,8 +1852,6 @@ void launch_gemm(const GemmPlan& p, GemmKArgs ka, hipStream_t stream) {
         else launch_tile<64, 128, 2, 2, true>(ka, blocks, stream);
     } else {
         if (t.bm == 32 && t.bn == 256) launch_tile<32, 256, 1, 4, false, 64, false, 4>(ka, blocks, stream);
-        else if (t.bm == 32 && t.kg == 1 && t.nb == 2) launch_tile<32, 128, 1, 2, false, 64, false, 2>(ka, blocks, stream);
-        else if (t.bm == 32 && t.kg == 1 && t.nb == 3) launch_tile<32, 128, 1, 2, false, 64, false, 3>(ka, blocks, stream);
         else if (t.bm == 32 && t.kg == 1 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4>(ka, blocks, stream);
         else if (t.bm == 32 && t.kg == 1) launch_tile<32, 128, 1, 2, false, 64, false, 7>(ka, blocks, stream);
         else if (t.bm == 32 && t.nb == 4) launch_tile<32, 128, 1, 2, false, 64, false, 4, 0, 2>(ka, blocks, stream);

@@ -37,7 +37,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 constexpr int64_t kMaxGridX = 2147483647LL;
-constexpr int64_t kMaxGridYZ = 65535LL;
 
 uno_status check_workspace(void* ws, size_t have, size_t need) {
     if (need == 0) return UNO_OK;

@@ -207,9 +207,13 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(
                               c2, stats, i0, rows_full, tokens, gz, gd);
 }
 
-// Merge the chunk statistics of one row in fp64: M = max, S = sum s_c e^{(m_c - M)/T}.
+// Merge the chunk statistics of one row: M = max_c m_c, S = sum_c s_c
+// 2^{(m_c - M) c2} (c2 = log2(e) / T) in chunk order, each factor the fp32
+// exponential of the statistics passes (within an ulp: the same relative
+// error as every term of the chunk sums) and the sum in fp64.  A row of one
+// chunk keeps its values (the factor is 2^0 = 1).
 __device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, bool use_b,
-                                             double invT, float& M, double& S) {
+                                             float c2, float& M, double& S) {
     // (unrolled so that the chunk loads of a pass are in flight together)
     float m = -INFINITY;
 #pragma unroll 8
@@ -221,7 +225,7 @@ __device__ __forceinline__ void merge_chunks(const ChunkStat* st, int32_t n, boo
             const float mc = use_b ? st[c].mB : st[c].mA;
             if (mc == -INFINITY) continue;
             const double sc = use_b ? st[c].sB : st[c].sA;
-            s += sc * exp((static_cast<double>(mc) - static_cast<double>(m)) * invT);
+            s += sc * static_cast<double>(fast_exp2((mc - m) * c2));  // (mc - m: exact, both bf16-valued)
         }
     }
     M = m;
@@ -289,6 +293,7 @@ struct DecideArgs {
     int32_t L, nb;
     int64_t V;
     double invT;
+    float c2;  // log2(e) / T, the statistics passes' scale
     const ChunkStat* stats;
     int32_t n_chunks;
     // ChunkStats between sequences (-1: rows x n_chunks, the stats array's
@@ -353,8 +358,8 @@ __device__ __forceinline__ LaneDecision lane_decision(const DecideArgs& a, int64
     if (stat_row) {
         const ChunkStat* st = a.stats + (a.stats_seq >= 0 ? s * a.stats_seq : s * rows * a.n_chunks) +
                               static_cast<int64_t>(lane) * a.n_chunks;
-        merge_chunks(st, a.n_chunks, false, a.invT, d.Mz, d.Sz);
-        if (drafted) merge_chunks(st, a.n_chunks, true, a.invT, d.Md, d.Sd);
+        merge_chunks(st, a.n_chunks, false, a.c2, d.Mz, d.Sz);
+        if (drafted) merge_chunks(st, a.n_chunks, true, a.c2, d.Md, d.Sd);
     }
     if (drafted) {
         d.acc = false;
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_gated_kernel(
 // ---------------------------------------------------------------- draft_decide
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void draft_decide_kernel(
-    const void* D, int64_t d_stride, int32_t L, int64_t V, int64_t rows, double invT,
+    const void* D, int64_t d_stride, int32_t L, int64_t V, int64_t rows, float c2,
     const ChunkStat* stats, int32_t n_chunks, const float* uniforms, int32_t* sampled,
     RedrawJob* jobs) {
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void draft_decide_kernel(
     const int32_t i = static_cast<int32_t>(row % L);
     float M;
     double S;
-    merge_chunks(stats + row * n_chunks, n_chunks, false, invT, M, S);
+    merge_chunks(stats + row * n_chunks, n_chunks, false, c2, M, S);
     RedrawJob job;
     job.a = static_cast<const char*>(D) + (s * d_stride + static_cast<int64_t>(i) * V) * (BF16 ? 2 : 4);
     job.b = nullptr;
@@ -1268,6 +1273,7 @@ hipError_t verify_impl(const VerifyProblem& pr, void* ws, hipStream_t stream, in
     da.nb = nb;
     da.V = pr.V;
     da.invT = invT;
+    da.c2 = c2;
     da.stats = stats;
     da.n_chunks = p.c1;
     da.jobs = jobs;
@@ -1317,13 +1323,12 @@ hipError_t draft_impl(const VerifyProblem& pr, void* ws, hipStream_t stream) {
     ChunkStat* stats = reinterpret_cast<ChunkStat*>(base + p.off_stats);
     RedrawJob* jobs = reinterpret_cast<RedrawJob*>(base + p.off_jobs);
     float* seg = reinterpret_cast<float*>(base + p.off_seg);
-    const double invT = 1.0 / static_cast<double>(pr.temperature);
     const float c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(pr.temperature));
     hipLaunchKernelGGL((row_stats_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(p.rows * p.c1)), dim3(kThreads), 0,
                        stream, pr.draft, pr.d_stride, nullptr, int64_t(0), pr.L, 0, pr.V, p.chunk1, p.c1, c2,
                        stats, 0, pr.L, nullptr, nullptr, nullptr);
     hipLaunchKernelGGL((draft_decide_kernel<BF16>), dim3(static_cast<uint32_t>((rows + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, invT, stats, p.c1,
+                       dim3(kThreads), 0, stream, pr.draft, pr.d_stride, pr.L, pr.V, rows, c2, stats, p.c1,
                        pr.uniforms, pr.sampled, jobs);
     hipLaunchKernelGGL((redraw_mass_kernel<BF16, VEC>), dim3(static_cast<uint32_t>(rows * p.c3)), dim3(kThreads), 0,
                        stream, jobs, p.c3, p.spc3, p.nseg, 1, pr.V, c2, seg);
@@ -1806,6 +1811,7 @@ hipError_t lm_head_verify_launch(const LmHeadProblem& pr, void* ws, hipStream_t 
     da.nb = nb;
     da.V = pr.V;
     da.invT = invT;
+    da.c2 = c2;
     da.stats = merged;
     da.n_chunks = 1;
     da.jobs = reinterpret_cast<RedrawJob*>(base + l.jobs);
