@@ -206,6 +206,39 @@ def main():
                                 "p90_us": round(pct(ts, 90), 2),
                                 "tflops_at_median": round(evs[0][2] / med / 1e6, 1)}
 
+    # The LoRA down-projections (the launch and its split-K reduction) of one
+    # more forward pass, outside the timed region: per-launch HIP events, the
+    # algorithmic rate against the bf16 peak and their share of a step.
+    lora_events = []
+    stack.t_timer = lora_events
+    stack.forward(x0)
+    stack.t_timer = None
+    torch.cuda.synchronize()
+    lora_s = sum(ev[0].elapsed_time(ev[1]) for ev in lora_events) / 1e3
+    lora_flop = sum(ev[2] for ev in lora_events)
+    lora_bytes = sum(ev[3] for ev in lora_events)
+    lora_kinds = {}
+    if len(lora_events) % len(kinds) == 0:
+        for j, kind in enumerate(kinds):
+            evs = lora_events[j::len(kinds)]
+            ts = sorted(ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs)
+            lora_kinds[kind] = {"median_us": round(pct(ts, 50), 2), "gflop": round(evs[0][2] / 1e9, 3),
+                                "mb": round(evs[0][3] / 1e6, 2)}
+    lora_roofline = {
+        "bound": "latency",
+        "kernel": "LoRA down-projection (T-mode tile and its split-K reduction, or the weight-streaming kernel) "
+                  "of every projection group of one forward pass",
+        "launches": len(lora_events),
+        "avg_launch_us": round(lora_s / max(len(lora_events), 1) * 1e6, 3),
+        "per_step_ms": round(lora_s * 1e3, 3),
+        "share_of_step": round(lora_s * 1e3 / ms_per_step, 4),
+        "achieved_tflops": round(lora_flop / lora_s / 1e12, 2) if lora_s > 0 else None,
+        "frac_of_bf16_peak": round(lora_flop / lora_s / 1e12 / PEAK_BF16_TFLOPS, 4) if lora_s > 0 else None,
+        "achieved_gbs": round(lora_bytes / lora_s / 1e9, 1) if lora_s > 0 else None,
+        "traffic": committed_traffic("lora_down", digest) if args.workload == "stack32_b32" else None,
+        "per_launch": lora_kinds,
+    }
+
     # Block verification per call with its logits cold (outside the timed
     # region): back-to-back calls over three logit sets -- the step's and two
     # more of the same recipe, 0.79 GB, three times the 256 MB MALL -- with
@@ -309,6 +342,7 @@ def main():
             "algorithmic_mb_per_launch": round(gemm_bytes / n_gemm / 1e6, 3),
             "per_launch": per_launch,
         },
+        "lora_down_roofline": lora_roofline,
         "verify_roofline": {
             "bound": "hbm",
             "achieved": round(v_gbs, 1),

@@ -96,6 +96,7 @@ class GatedLoraStack:
         self.M, self.hidden, self.kv, self.ffn, self.r = M, hidden, kv, ffn, r
         self.Md = int(gate.to(torch.int64).sum().item())  # draft rows (one host sync, here)
         self.timer = None
+        self.t_timer = None
         self.h = torch.empty((M, hidden), dtype=bf, device=dev)
         self.q = torch.empty((M, hidden), dtype=bf, device=dev)
         self.k = torch.empty((M, kv), dtype=bf, device=dev)
@@ -150,15 +151,31 @@ class GatedLoraStack:
         nbytes = 2.0 * (N * K + N * r + M * K + M * out_cols + Md * t_cols)
         self.timer.append((e0, e1, flops, nbytes))
 
+    def _lora(self, inp, a):
+        """T for the draft rows; with t_timer set, bracketed by HIP events on the
+        current stream and recorded with its algorithmic flops (2 Md K r) and
+        bytes (the draft rows of x, A, and T's rows up to the next multiple of 32)."""
+        if self.t_timer is None:
+            _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+            return
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+        e1.record()
+        r, K = a.shape
+        Md = self.Md
+        Md_pad = (Md + 31) // 32 * 32
+        self.t_timer.append((e0, e1, 2.0 * Md * K * r, 2.0 * (Md * K + r * K + Md_pad * r)))
+
     def _proj(self, layer, name, inp, out):
         w, a, b = layer[name]
-        _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+        self._lora(inp, a)
         self._timed(w.shape[1], w.shape[0],
                     lambda: _lib.gated_gemm(inp, w, self.t, b, self.plan, out=out, workspace=self.ws))
 
     def _group(self, li, names, inp, outs):
         w, a, b, ns = self.groups[li][names]
-        _lib.lora_down(inp, a, self.plan, self.scale, t=self.t, workspace=self.ws)
+        self._lora(inp, a)
         self._timed(w.shape[1], w.shape[0],
                     lambda: _lib.gated_gemm_grouped(inp, w, self.t, b, self.plan, ns, outs=outs,
                                                     workspace=self.ws))
@@ -166,7 +183,7 @@ class GatedLoraStack:
     def _swiglu(self, li, inp):
         """act = silu(P_gate(inp)) * P_up(inp) in one launch."""
         w_p, a_st, b_p = self.swiglu[li]
-        _lib.lora_down(inp, a_st, self.plan, self.scale, t=self.t, workspace=self.ws)
+        self._lora(inp, a_st)
         self._timed(w_p.shape[1], w_p.shape[0],
                     lambda: _lib.gated_gemm_swiglu(inp, w_p, self.t, b_p, self.plan, out=self.act,
                                                    workspace=self.ws),
