@@ -528,7 +528,8 @@ def _layer_gemm_measure(uno, sdev, torch, wl, dev, copies=3, reps=6):
     touches about 320 MB of weights; a copy is reused only after the others'
     640 MB).  Per launch kind: median time of the gated GEMM (HIP events) and
     its algorithmic rate; the whole layer (LoRA down-projections and glue
-    included) per repetition."""
+    included) per repetition, timed in a forward pass of its own without the
+    per-launch events."""
     from synthetic import gate_vector
 
     gate = torch.from_numpy(gate_vector(wl.n_seq, wl.verify_rows, wl.draft_rows)).to(dev)
@@ -542,8 +543,11 @@ def _layer_gemm_measure(uno, sdev, torch, wl, dev, copies=3, reps=6):
     per = {k: [] for k in kinds}
     layer_us = []
     for i in range(reps * copies):
-        st = stacks[i % copies]
-        st.timer = []
+        st = stacks[(2 * i) % copies]
+        # the whole layer without per-launch events (each event pair costs the
+        # stream a few microseconds), then the same layer on the next copy of
+        # the weights with an event pair around each gated GEMM (the copies
+        # are used in turn, each again only after the other two)
         a, b = _events(torch)
         # (the GPU spins while the host enqueues the layer, so that the events
         # time the kernels and not the host's launch rate)
@@ -553,6 +557,11 @@ def _layer_gemm_measure(uno, sdev, torch, wl, dev, copies=3, reps=6):
         b.record()
         torch.cuda.synchronize()
         layer_us.append(a.elapsed_time(b) * 1e3)
+        st = stacks[(2 * i + 1) % copies]
+        st.timer = []
+        torch.cuda._sleep(1_000_000)
+        st.forward(x0)
+        torch.cuda.synchronize()
         for k, ev in zip(kinds, st.timer):
             per[k].append((ev[0].elapsed_time(ev[1]) * 1e3, ev[2], ev[3]))
         st.timer = None
