@@ -77,6 +77,20 @@ def test_gated_lora_validation(lib):
     assert lib.uno_gated_lora_workspace_size(24, 512, 512, 128, 1) == lib.uno_row_plan_size(24) + 24 * 128 * 4
 
 
+def test_few_row_plans_through_workspace_sizes(lib, monkeypatch):
+    """At 32 rows or fewer the launches take the compact 32-row tiles: the SwiGLU launch
+    needs no split of K (224 tiles for 28672 interleaved columns: no workspace), a plain
+    projection of 4096 columns splits K eight ways over 32 column blocks (fp32 partials of
+    the plan's 64 rows); with UNO_COMPACT=0 the SwiGLU launch splits K again."""
+    for var in ("UNO_GEMM_TILE", "UNO_GEMM_SPLIT", "UNO_STREAM", "UNO_COMPACT"):
+        monkeypatch.delenv(var, raising=False)
+    assert lib.uno_gated_gemm_swiglu_workspace_size(32, 14336, 4096, 256) == 0
+    assert lib.uno_gated_gemm_workspace_size(32, 4096, 4096, 128) == 8 * 64 * 4096 * 4
+    assert lib.uno_gated_gemm_workspace_size(32, 4096, 14336, 128) == 8 * 64 * 4096 * 4
+    monkeypatch.setenv("UNO_COMPACT", "0")
+    assert lib.uno_gated_gemm_swiglu_workspace_size(32, 14336, 4096, 256) > 0
+
+
 def test_row_plan_gate_error_query(lib):
     # the plan holds a 256-byte header (gate-error count and first bad row
     # among it), the permutation over 32-row-padded segments, and the list of
