@@ -120,6 +120,72 @@ __device__ __forceinline__ Online wave_merge(Online o, float c2) {
 // workgroup whose chunk holds the drafted token also copies its two logits
 // to gz and gd (same layout as the tokens), so that the decision reads them
 // with the statistics instead of after the token.
+// The statistics loop over 16-byte bf16 vectors, software-pipelined: two
+// register sets take turns, and the loads of the next step issue before the
+// arithmetic of the current one, so that a thread keeps one step's vectors
+// in flight (two per array) while it adds the step before.  The values are
+// added in the plain loop's order: the same bits.  Every pass issues the same
+// loads (where no further step exists, the set re-reads the step just
+// loaded: cache hits, left unused), so that the waits stay exact.  Returns
+// the first position not yet added (the plain loop's tail takes it).
+template <bool HAS_B>
+__device__ __forceinline__ int64_t stats_pipelined(const char* arow, const char* brow, int64_t k, int64_t k1,
+                                                   float c2, Online& oa, Online& ob) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    if (!(k + kStatTile < k1)) return k;
+    auto ld = [](const char* row, int64_t kk) {
+        const u32x4_t r = gptr<u32x4_t>(reinterpret_cast<const uint16_t*>(row) + kk)[0];
+        uint4 v;
+        v.x = r.x; v.y = r.y; v.z = r.z; v.w = r.w;
+        return v;
+    };
+    struct Set {
+        uint4 a0, a1, b0, b1;
+    };
+    auto load_set = [&](int64_t kk) {
+        Set t{};
+        t.a0 = ld(arow, kk);
+        t.a1 = ld(arow, kk + kStatTile);
+        if constexpr (HAS_B) {
+            t.b0 = ld(brow, kk);
+            t.b1 = ld(brow, kk + kStatTile);
+        }
+        return t;
+    };
+    auto add_set = [&](const Set& t) {
+        float v[2 * kVec];
+        if constexpr (HAS_B) {
+            unpack8(t.b0, v);
+            unpack8(t.b1, v + kVec);
+            online_add16(ob, v, c2);
+        }
+        unpack8(t.a0, v);
+        unpack8(t.a1, v + kVec);
+        online_add16(oa, v, c2);
+    };
+    // two register sets in turn (no copies between them, so that the loads
+    // of one stay in flight while the other is added); n steps of two
+    // vectors per array, the last odd one after the loop
+    const int64_t n = (k1 - k - kStatTile - 1) / (2 * kStatTile) + 1;
+    Set s0 = load_set(k), s1;
+    int64_t j = 0;
+    for (; j + 1 < n; j += 2) {
+        s1 = load_set(k + 2 * kStatTile);
+        __builtin_amdgcn_sched_barrier(0);  // (the loads issue before the arithmetic)
+        add_set(s0);
+        // (without a step j + 2 the set re-reads step j + 1: cache hits, unused)
+        s0 = load_set(j + 2 < n ? k + 4 * kStatTile : k + 2 * kStatTile);
+        __builtin_amdgcn_sched_barrier(0);
+        add_set(s1);
+        k += 4 * kStatTile;
+    }
+    if (j < n) {
+        add_set(s0);
+        k += 2 * kStatTile;
+    }
+    return k;
+}
+
 template <bool BF16, bool VEC>
 __device__ __forceinline__ void row_stats_body(
     int64_t blk, const void* A, int64_t a_stride, const void* B, int64_t b_stride, int32_t rows_per_seq,
@@ -144,7 +210,14 @@ __device__ __forceinline__ void row_stats_body(
 
     Online oa{-INFINITY, 0.0}, ob{-INFINITY, 0.0};
     int64_t k = k0 + static_cast<int64_t>(threadIdx.x) * kVec;
-    // two vectors per array in flight per iteration, added sixteen values at a time
+    if constexpr (BF16 && VEC) {
+        if (has_b)
+            k = stats_pipelined<true>(arow, brow, k, k1, c2, oa, ob);
+        else
+            k = stats_pipelined<false>(arow, brow, k, k1, c2, oa, ob);
+    }
+    // (other forms) two vectors per array in flight per iteration, added
+    // sixteen values at a time
     for (; k + kStatTile < k1; k += 2 * kStatTile) {
         float va[2 * kVec];
         load8<BF16, VEC>(arow, k, V, va);
@@ -1055,16 +1128,24 @@ struct Plan {
 };
 
 constexpr int64_t kTargetBlocks = 2048;
-constexpr int64_t kMaxStatChunks = 16;
+constexpr int64_t kStatTargetBlocks = 1536;
+constexpr int64_t kMaxStatChunks = 4;
 
 Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
     Plan p{};
     p.rows = B * rows_per_seq;
-    // (at most kMaxStatChunks chunks per row: the decision merges a row's
-    // chunks one after another in fp64, about 0.25 us per chunk, which at one
-    // sequence cost more than the wider grid saved)
+    // Chunks per row: about kStatTargetBlocks workgroups for the one-pass
+    // statistics launch, at most kMaxStatChunks per row.  The decision merges
+    // a row's chunks one after another (two dependent rounds of loads per
+    // eight chunks), so few chunks pay, and with its pipelined loads one
+    // workgroup streams a long chunk at full rate.  The early-exit verifier
+    // keeps this chunking (its statistics are then the same bits) while its
+    // first launch covers only the first positions: the target is set so
+    // that such a launch still spreads over the CUs (32 sequences x 17 rows:
+    // three chunks per row, 576 workgroups for a first chunk of six
+    // positions; one chunk per row from 91 such sequences up).
     const int64_t max_c1 = std::min<int64_t>(kMaxStatChunks, (V + kStatTile - 1) / kStatTile);
-    int64_t c1 = p.rows > 0 ? (kTargetBlocks + p.rows - 1) / p.rows : 1;
+    int64_t c1 = p.rows > 0 ? (kStatTargetBlocks + p.rows - 1) / p.rows : 1;
     c1 = std::max<int64_t>(1, std::min(c1, max_c1));
     int64_t chunk = (V + c1 - 1) / c1;
     chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
