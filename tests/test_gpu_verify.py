@@ -60,6 +60,12 @@ CASES = [  # B, L, V, dtype, kind, sigma, T, bonus
     (5, 3, 1, "bf16", "normal", 1.0, 1.0, True),          # single-token vocabulary
     (300, 2, 17, "f32", "normal", 1.0, 2.0, False),       # many sequences, odd V
     (3, 4, 300000, "bf16", "normal", 1.0, 1.0, True),     # rows past the one-workgroup tail's LDS staging
+    # one statistics chunk per row (96 x 17 rows): the pipelined loop's steps
+    # of 2 x 2048 tokens -- one step then the plain tail, two steps (the loop
+    # once, its last loads re-reading), three (the loop once, then the odd
+    # step) -- and the bonus row's target-only form
+    (96, 16, 6152, "bf16", "normal", 1.0, 1.0, True),
+    (96, 16, 10248, "bf16", "normal", 1.0, 1.0, False),
 ]
 
 
@@ -210,6 +216,7 @@ EARLY = [  # B, L, V, dtype, kind, sigma, T, bonus, chunk
     (64, 16, 2048, "bf16", "zipf", 0.5, 0.6, False, 1),     # one position per chunk
     (64, 16, 2048, "bf16", "zipf", 0.5, 0.6, True, 64),     # one chunk: the one-pass schedule
     (300, 2, 17, "f32", "normal", 1.0, 2.0, False, 1),
+    (96, 16, 10248, "bf16", "normal", 1.0, 1.0, True, 6),   # one statistics chunk per row, pipelined steps
 ]
 
 
