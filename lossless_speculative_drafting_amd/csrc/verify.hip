@@ -1130,22 +1130,32 @@ struct Plan {
 constexpr int64_t kTargetBlocks = 2048;
 constexpr int64_t kStatTargetBlocks = 1536;
 constexpr int64_t kMaxStatChunks = 4;
+constexpr int64_t kStatCoverBlocks = 256;   // one statistics workgroup per CU
+constexpr int64_t kMaxCoverChunks = 8;
 
 Plan make_plan(int64_t B, int32_t L, int64_t V, int32_t rows_per_seq, int64_t n_jobs, int32_t n_arr) {
     Plan p{};
     p.rows = B * rows_per_seq;
     // Chunks per row: about kStatTargetBlocks workgroups for the one-pass
-    // statistics launch, at most kMaxStatChunks per row.  The decision merges
-    // a row's chunks one after another (two dependent rounds of loads per
-    // eight chunks), so few chunks pay, and with its pipelined loads one
-    // workgroup streams a long chunk at full rate.  The early-exit verifier
-    // keeps this chunking (its statistics are then the same bits) while its
-    // first launch covers only the first positions: the target is set so
-    // that such a launch still spreads over the CUs (32 sequences x 17 rows:
-    // three chunks per row, 576 workgroups for a first chunk of six
-    // positions; one chunk per row from 91 such sequences up).
-    const int64_t max_c1 = std::min<int64_t>(kMaxStatChunks, (V + kStatTile - 1) / kStatTile);
-    int64_t c1 = p.rows > 0 ? (kStatTargetBlocks + p.rows - 1) / p.rows : 1;
+    // statistics launch, at most kMaxStatChunks per row -- or, for the
+    // smallest batches, as many as give a workgroup per CU, at most
+    // kMaxCoverChunks.  The decision merges a row's chunks one after another
+    // (two dependent rounds of loads per eight chunks), so few chunks pay,
+    // and with its pipelined loads one workgroup streams a long chunk at full
+    // rate.  The early-exit verifier keeps this chunking (its statistics are
+    // then the same bits) while its first launch covers only the first
+    // positions: the target is set so that such a launch still spreads over
+    // the CUs.  With 17 rows per sequence: eight chunks per row at one and
+    // two sequences, six at three, four from 4 to 30, three from 31 to 45
+    // (576 workgroups for a first chunk of six positions at 32 sequences),
+    // two from 46 to 90, one from 91 up.
+    const int64_t max_c1 = (V + kStatTile - 1) / kStatTile;
+    int64_t c1 = 1;
+    if (p.rows > 0) {
+        const int64_t by_target = std::min(kMaxStatChunks, (kStatTargetBlocks + p.rows - 1) / p.rows);
+        const int64_t by_cover = std::min(kMaxCoverChunks, (kStatCoverBlocks + p.rows - 1) / p.rows);
+        c1 = std::max(by_target, by_cover);
+    }
     c1 = std::max<int64_t>(1, std::min(c1, max_c1));
     int64_t chunk = (V + c1 - 1) / c1;
     chunk = (chunk + kStatTile - 1) / kStatTile * kStatTile;
